@@ -1,0 +1,314 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle (TEST INFRASTRUCTURE ONLY; see oracle.h).
+ *
+ * Written for a reader who checks it against the definition by eye: every row
+ * is handled on its own in a few sequential passes over its columns, in double
+ * precision, with no blocking, fusion or reordering beyond the definition.
+ * OpenMP only distributes whole rows over host threads.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 is the upper half of an IEEE binary32: widen by shifting 16 bits up. */
+static double decode_bf16(uint16_t bits) {
+    uint32_t w = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* Logit x[row, col] widened to double. */
+static double logit_at(const void *logits, int dtype, int64_t ld, int64_t row,
+                       int64_t col) {
+    int64_t off = row * ld + col;
+    if (dtype == ORACLE_BF16) return decode_bf16(((const uint16_t *)logits)[off]);
+    return (double)((const float *)logits)[off];
+}
+
+static int dtype_ok(int dtype) {
+    return dtype == ORACLE_BF16 || dtype == ORACLE_FP32;
+}
+
+static int tau_ok(double tau) { return isfinite(tau) && tau > 0.0; }
+
+/* Row id of output i. */
+static int64_t row_of(const int32_t *rows, int64_t i) {
+    return rows ? (int64_t)rows[i] : i;
+}
+
+static int check_rows(const int32_t *rows, int64_t m, int64_t n_rows) {
+    if (!rows) return m == n_rows ? 0 : -1;
+    for (int64_t i = 0; i < m; ++i)
+        if (rows[i] < 0 || (int64_t)rows[i] >= n_rows) return -3;
+    return 0;
+}
+
+static int check_targets(const int32_t *targets, const int32_t *rows, int64_t m,
+                         int64_t vocab) {
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t t = targets[row_of(rows, i)];
+        if (t < 0 || t >= vocab) return -2;
+    }
+    return 0;
+}
+
+/*
+ * Log-sum-exp of z_j = x[row, c0 + j] / tau over j in [0, n):
+ *   M = max z_j;  S = sum exp(z_j - M);  LSE = M + log S.
+ * Two passes, columns in ascending order.
+ */
+static void row_max_sum(const void *logits, int dtype, int64_t ld, int64_t row,
+                        int64_t c0, int64_t n, double tau, double *M_out,
+                        double *S_out) {
+    double M = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        double z = logit_at(logits, dtype, ld, row, c0 + j) / tau;
+        if (z > M) M = z;
+    }
+    double S = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        double z = logit_at(logits, dtype, ld, row, c0 + j) / tau;
+        S += exp(z - M);
+    }
+    *M_out = M;
+    *S_out = S;
+}
+
+/* Entropy -sum_j p_j log p_j with p_j = exp(z_j - LSE) and log p_j = z_j - LSE. */
+static double row_entropy(const void *logits, int dtype, int64_t ld,
+                          int64_t row, int64_t vocab, double tau, double LSE) {
+    double H = 0.0;
+    for (int64_t j = 0; j < vocab; ++j) {
+        double z = logit_at(logits, dtype, ld, row, j) / tau;
+        double p = exp(z - LSE);
+        H -= p * (z - LSE);
+    }
+    return H;
+}
+
+int oracle_forward(const void *logits, int dtype, int64_t n_rows, int64_t vocab,
+                   int64_t ld, const int32_t *targets, const int32_t *rows,
+                   int64_t m, double tau, int64_t row_chunk, double *logprob,
+                   double *lse, double *entropy) {
+    /* Non-positive chunk sizes are rejected, as in the chunked local kernel
+       described in "fix: chunk target logprobs without tensor parallelism",
+       section "Changes". */
+    if (row_chunk <= 0) return -1;
+    if (!logits || !dtype_ok(dtype) || n_rows < 0 || m < 0 || vocab <= 0 ||
+        ld < vocab || !tau_ok(tau))
+        return -1;
+    if (logprob && !targets) return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+    if (logprob && (rc = check_targets(targets, rows, m, vocab))) return rc;
+
+    for (int64_t c0 = 0; c0 < m; c0 += row_chunk) {
+        int64_t c1 = c0 + row_chunk < m ? c0 + row_chunk : m;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t i = c0; i < c1; ++i) {
+            int64_t r = row_of(rows, i);
+            double M, S;
+            row_max_sum(logits, dtype, ld, r, 0, vocab, tau, &M, &S);
+            double LSE = M + log(S);
+            if (lse) lse[i] = LSE;
+            if (logprob) {
+                /* log_softmax(z)[t] = z_t - LSE, which is -cross_entropy(z, t). */
+                double zt = logit_at(logits, dtype, ld, r, targets[r]) / tau;
+                logprob[i] = zt - LSE;
+            }
+            if (entropy)
+                entropy[i] = row_entropy(logits, dtype, ld, r, vocab, tau, LSE);
+        }
+    }
+    return 0;
+}
+
+int oracle_backward(const void *logits, int dtype, int64_t n_rows,
+                    int64_t vocab, int64_t ld, const int32_t *targets,
+                    const int32_t *rows, int64_t m, double tau,
+                    const float *grad_out, double *grad) {
+    if (!logits || !dtype_ok(dtype) || n_rows < 0 || m < 0 || vocab <= 0 ||
+        ld < vocab || !tau_ok(tau) || !targets || !grad_out || (m && !grad))
+        return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+    if ((rc = check_targets(targets, rows, m, vocab))) return rc;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t r = row_of(rows, i);
+        double *gi = grad + i * vocab;
+        double g = (double)grad_out[i];
+        if (g == 0.0) {
+            /* Rows without loss get an exact +0.0 gradient ("Avoid
+               full-vocabulary TP gather ...", section "Prototype correctness"). */
+            for (int64_t j = 0; j < vocab; ++j) gi[j] = 0.0;
+            continue;
+        }
+        /* The logZ is recomputed here from the logits; nothing comes from the
+           forward of the code under test. */
+        double M, S;
+        row_max_sum(logits, dtype, ld, r, 0, vocab, tau, &M, &S);
+        double LSE = M + log(S);
+        int64_t t = targets[r];
+        for (int64_t j = 0; j < vocab; ++j) {
+            double z = logit_at(logits, dtype, ld, r, j) / tau;
+            double p = exp(z - LSE);
+            double onehot = (j == t) ? 1.0 : 0.0;
+            /* d(z_t - LSE)/dx_j = (onehot_j - p_j) / tau, times the incoming g. */
+            gi[j] = g * (onehot - p) / tau;
+        }
+    }
+    return 0;
+}
+
+int oracle_slice_partial(const void *logits_slice, int dtype, int64_t n_rows,
+                         int64_t v_local, int64_t ld, int64_t v_start,
+                         const int32_t *targets, const int32_t *rows, int64_t m,
+                         double tau, double *pm, double *ps, double *pw,
+                         double *pt) {
+    if (!logits_slice || !dtype_ok(dtype) || n_rows < 0 || m < 0 ||
+        v_local <= 0 || ld < v_local || v_start < 0 || !tau_ok(tau) ||
+        (m && (!pm || !ps || !pw)) || (pt && !targets))
+        return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t r = row_of(rows, i);
+        double M, S;
+        row_max_sum(logits_slice, dtype, ld, r, 0, v_local, tau, &M, &S);
+        double W = 0.0;
+        for (int64_t j = 0; j < v_local; ++j) {
+            double z = logit_at(logits_slice, dtype, ld, r, j) / tau;
+            W += exp(z - M) * (z - M);
+        }
+        pm[i] = M;
+        ps[i] = S;
+        pw[i] = W;
+        if (pt) {
+            /* Only the slice that owns the target contributes its logit
+               ("Reduce reference model memory ...", section "Implementation"). */
+            int64_t t = targets[r];
+            if (t >= v_start && t < v_start + v_local)
+                pt[i] = logit_at(logits_slice, dtype, ld, r, t - v_start) / tau;
+            else
+                pt[i] = -INFINITY;
+        }
+    }
+    return 0;
+}
+
+int oracle_combine(int64_t k, int64_t m, const double *pm, const double *ps,
+                   const double *pw, const double *pt, double *logprob,
+                   double *lse, double *entropy) {
+    if (k <= 0 || m < 0 || (m && (!pm || !ps || !pw)) || (logprob && !pt))
+        return -1;
+    for (int64_t i = 0; i < m; ++i) {
+        /* Global max over the slices. */
+        double M = -INFINITY;
+        for (int64_t q = 0; q < k; ++q)
+            if (pm[q * m + i] > M) M = pm[q * m + i];
+        /* Sum of exp(z - M): each slice's sum rescaled from its own max. */
+        double S = 0.0, W = 0.0, T = -INFINITY;
+        for (int64_t q = 0; q < k; ++q) {
+            double d = pm[q * m + i] - M;
+            double f = exp(d);
+            S += ps[q * m + i] * f;
+            /* sum exp(z - M)(z - M) = sum exp(z - M_q) e^d ((z - M_q) + d) */
+            W += f * (pw[q * m + i] + d * ps[q * m + i]);
+            if (pt && pt[q * m + i] > T) T = pt[q * m + i];
+        }
+        double LSE = M + log(S);
+        if (lse) lse[i] = LSE;
+        if (logprob) logprob[i] = T - LSE;
+        /* H = LSE - E_p[z] = log S - W / S. */
+        if (entropy) entropy[i] = log(S) - W / S;
+    }
+    return 0;
+}
+
+int oracle_forward_vchunk(const void *logits, int dtype, int64_t n_rows,
+                          int64_t vocab, int64_t ld, const int32_t *targets,
+                          const int32_t *rows, int64_t m, double tau,
+                          int64_t vchunk, double *logprob, double *lse,
+                          double *entropy) {
+    if (vchunk <= 0) return -1;
+    if (!logits || !dtype_ok(dtype) || n_rows < 0 || m < 0 || vocab <= 0 ||
+        ld < vocab || !tau_ok(tau) || (logprob && !targets))
+        return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+    if (logprob && (rc = check_targets(targets, rows, m, vocab))) return rc;
+    if (m == 0) return 0;
+
+    int64_t k = (vocab + vchunk - 1) / vchunk;
+    size_t n = (size_t)(k * m);
+    double *pm = malloc(n * sizeof(double)), *ps = malloc(n * sizeof(double));
+    double *pw = malloc(n * sizeof(double)), *pt = malloc(n * sizeof(double));
+    if (!pm || !ps || !pw || !pt) {
+        free(pm); free(ps); free(pw); free(pt);
+        return -4;
+    }
+    const size_t esize = dtype == ORACLE_BF16 ? 2 : 4;
+    for (int64_t q = 0; q < k; ++q) {
+        int64_t v0 = q * vchunk;
+        int64_t vl = v0 + vchunk <= vocab ? vchunk : vocab - v0;
+        const char *slice = (const char *)logits + (size_t)v0 * esize;
+        rc = oracle_slice_partial(slice, dtype, n_rows, vl, ld, v0,
+                                  logprob ? targets : NULL, rows, m, tau,
+                                  pm + q * m, ps + q * m, pw + q * m,
+                                  logprob ? pt + q * m : NULL);
+        if (rc) break;
+    }
+    if (!rc)
+        rc = oracle_combine(k, m, pm, ps, pw, logprob ? pt : NULL, logprob, lse,
+                            entropy);
+    free(pm); free(ps); free(pw); free(pt);
+    return rc;
+}
+
+/*
+ * Nearest bf16 to v, ties to even, straight from the double (no detour through
+ * float, which would round twice).  bf16 has fp32's exponent range and 8
+ * significant bits; below 2^-126 its spacing is the fixed 2^-133.  Dividing by
+ * the spacing is exact (a power of two), rint() rounds to nearest-even in the
+ * default rounding mode, and the product is exactly representable in float.
+ */
+uint16_t oracle_bf16_rne(double v) {
+    if (isnan(v)) return 0x7FC0;
+    if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;
+    if (v == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+    int e;
+    frexp(v, &e); /* |v| = f * 2^e with f in [0.5, 1): the leading bit is 2^(e-1) */
+    int lead = e - 1;
+    int q_exp = lead < -126 ? -133 : lead - 7;
+    double q = ldexp(1.0, q_exp);
+    double r = rint(v / q) * q;
+    if (fabs(r) >= ldexp(1.0, 128)) return v > 0 ? 0x7F80 : 0xFF80;
+    float f = (float)r; /* exact */
+    uint32_t w;
+    memcpy(&w, &f, sizeof w);
+    if (r == 0.0) return signbit(v) ? 0x8000 : 0x0000;
+    return (uint16_t)(w >> 16);
+}
+
+void oracle_bf16_rne_array(const double *v, uint16_t *out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(v[i]);
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,356 @@
+"""Pins for the fp64 oracle, each against something other than the oracle itself:
+library routines (torch fp64 cross_entropy, log_softmax autograd, Categorical
+entropy), closed forms, invariants, brute force and central finite differences.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a wrong
+sign or index, tau applied on one side only, a transposed partial) fails at least
+one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = W.get("tiny_fp32_64x2048")
+    return w, W.all_logits(w), W.targets(w), W.grad_out(w)
+
+
+# ----------------------------------------------------------------------------- logprob
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_logprob_is_minus_cross_entropy(tiny, tau):
+    """log_softmax(x/tau)[t] == -cross_entropy(x/tau, t): the identity the Megatron
+    issue builds on ("Avoid full-vocabulary TP gather ...", "Proposed solution")."""
+    _, x, t, _ = tiny
+    o = oracle.forward(x, t, tau=tau)
+    z = torch.from_numpy(x).double() / float(np.float32(tau))
+    ce = torch.nn.functional.cross_entropy(z, torch.from_numpy(t).long(), reduction="none")
+    np.testing.assert_allclose(o["logprob"], -ce.numpy(), rtol=0, atol=1e-12)
+    lse = torch.logsumexp(z, dim=1).numpy()
+    np.testing.assert_allclose(o["lse"], lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["masked_bf16_4096x151936", "spiked_bf16_8192x248320",
+                                  "packed_bf16_32768x248320", "extreme_fp32_16384x248320"])
+def test_logprob_identity_sampled_rows(name):
+    """Same identity on a few rows of every full-size workload (bf16 decode included)."""
+    w = W.get(name)
+    rows = np.array([0, 1, w.n_rows // 2, w.n_rows - 1])
+    x = W.logits_rows(w, rows)
+    t = W.targets(w)[rows]
+    o = oracle.forward(x, t, tau=w.tau)
+    xf = W.bf16_bits_to_float32(x) if w.dtype == "bf16" else x
+    z = torch.from_numpy(xf).double() / float(np.float32(w.tau))
+    ce = torch.nn.functional.cross_entropy(z, torch.from_numpy(t).long(), reduction="none")
+    # |lp| reaches 1.4e4 in the extreme workload: compare relative to the magnitude.
+    np.testing.assert_allclose(o["logprob"], -ce.numpy(), rtol=1e-13, atol=1e-12)
+
+
+def test_logprob_brute_force(tiny):
+    """Naive softmax without the max shift (safe for N(0,1) logits), pure numpy."""
+    _, x, t, _ = tiny
+    o = oracle.forward(x, t)
+    e = np.exp(x.astype(np.float64))
+    naive = np.log(e[np.arange(x.shape[0]), t] / e.sum(axis=1))
+    np.testing.assert_allclose(o["logprob"], naive, rtol=0, atol=1e-12)
+
+
+def test_logprob_normalizes(tiny):
+    """sum_t exp(logprob(t)) == 1 for every row (all V targets of 3 rows)."""
+    _, x, _, _ = tiny
+    V = x.shape[1]
+    for r in (0, 17, 63):
+        xr = np.repeat(x[r:r + 1], V, axis=0)
+        o = oracle.forward(xr, np.arange(V, dtype=np.int32), want=("logprob",))
+        assert abs(np.exp(o["logprob"]).sum() - 1.0) < 1e-12
+
+
+def test_uniform_logits():
+    for V in (1, 2, 7, 2048, 151936):
+        x = np.full((1, V), 0.25, np.float32)
+        o = oracle.forward(x, np.array([V - 1], np.int32), tau=0.7)
+        assert abs(o["logprob"][0] + math.log(V)) < 1e-12
+        assert abs(o["entropy"][0] - math.log(V)) < 1e-12 * max(1.0, math.log(V))
+
+
+def test_shift_invariance():
+    """lp(x + c) == lp(x) with exactly representable shifted logits."""
+    rng = np.random.default_rng(5)
+    x = (rng.integers(-256, 256, size=(8, 1000)) / 64.0).astype(np.float32)
+    t = rng.integers(0, 1000, size=8).astype(np.int32)
+    a = oracle.forward(x, t)
+    b = oracle.forward((x + np.float32(5.0)).astype(np.float32), t)
+    np.testing.assert_allclose(a["logprob"], b["logprob"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["entropy"], b["entropy"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b["lse"] - a["lse"], 5.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("tau", [0.5, 2.0, 0.25])
+def test_temperature_is_logit_scaling(tiny, tau):
+    """lp(x, tau) == lp(x / tau, 1) for power-of-two tau (x / tau exact in fp32).
+    Pins that tau divides both the target logit and the log-sum-exp."""
+    _, x, t, _ = tiny
+    a = oracle.forward(x, t, tau=tau)
+    b = oracle.forward((x / np.float32(tau)).astype(np.float32), t, tau=1.0)
+    for k in ("logprob", "lse", "entropy"):
+        np.testing.assert_allclose(a[k], b[k], rtol=0, atol=1e-12)
+
+
+def test_golden_closed_forms():
+    path = os.path.join(GOLDEN, "closed_forms.txt")
+    env = {"log": math.log, "log1p": math.log1p, "exp": math.exp}
+    n = 0
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, xs, t, tau, lp_expr, h_expr, _src = [s.strip() for s in line.split("|")]
+        x = np.array([[float(v) for v in xs.split(",")]], np.float32)
+        o = oracle.forward(x, np.array([int(t)], np.int32), tau=float(tau))
+        assert abs(o["logprob"][0] - eval(lp_expr, env)) < 1e-14, name
+        assert abs(o["entropy"][0] - eval(h_expr, env)) < 1e-14, name
+        n += 1
+    assert n >= 6
+
+
+def test_golden_uniform_payload_mass():
+    """Printed example: a uniform payload has top-k log-probs of -log V and top-k mass
+    K / V = 2.11e-4 (verl PR, tail-aware top-k KL text, VeOmni notes)."""
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "uniform_payload_mass.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = [s.strip() for s in line.split("=")]
+            vals[k] = float(v)
+    V, K = int(vals["vocab"]), int(vals["k"])
+    x = np.zeros((K, V), np.float32)
+    t = np.linspace(0, V - 1, K).astype(np.int32)
+    o = oracle.forward(x, t, want=("logprob",))
+    assert np.all(np.abs(o["logprob"] + math.log(V)) < 1e-12)
+    mass = float(np.exp(o["logprob"]).sum())
+    assert float(f"{mass:.{int(vals['printed_digits']) - 1}e}") == vals["printed_mass"]
+
+
+# ----------------------------------------------------------------------------- entropy
+
+
+def test_entropy_brute_force_and_library(tiny):
+    _, x, t, _ = tiny
+    for tau in (1.0, 0.7):
+        o = oracle.forward(x, t, tau=tau)
+        z = x.astype(np.float64) / float(np.float32(tau))
+        p = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
+        brute = -(p * np.log(p)).sum(axis=1)
+        np.testing.assert_allclose(o["entropy"], brute, rtol=0, atol=1e-12)
+        cat = torch.distributions.Categorical(logits=torch.from_numpy(z)).entropy().numpy()
+        np.testing.assert_allclose(o["entropy"], cat, rtol=0, atol=1e-12)
+
+
+def test_entropy_one_dominant_entry():
+    x = np.zeros((1, 4096), np.float32)
+    x[0, 123] = 1000.0
+    o = oracle.forward(x, np.array([123], np.int32))
+    assert abs(o["logprob"][0]) < 1e-300 or o["logprob"][0] == 0.0
+    assert 0.0 <= o["entropy"][0] < 1e-300 or o["entropy"][0] == 0.0
+
+
+def test_extreme_workload_closed_form():
+    """In the +-1e4 workload every non-extreme term underflows next to the +1e4
+    entries, so H = ln c and lp = -ln c at a +1e4 target, else (x_t - 1e4)/tau - ln c,
+    where c counts the +1e4 entries of the row."""
+    w = W.get("extreme_fp32_16384x248320")
+    rows = np.array([3, 4096])
+    x = W.logits_rows(w, rows)
+    t = W.targets(w)[rows]
+    t[1] = int(np.flatnonzero(x[1] == np.float32(1e4))[0])  # one row with a +1e4 target
+    o = oracle.forward(x, t, tau=w.tau)
+    tau = float(np.float32(w.tau))
+    for i in range(2):
+        c = int((x[i] == np.float32(1e4)).sum())
+        assert 1000 < c < 1500
+        assert abs(o["entropy"][i] - math.log(c)) < 1e-9
+        xt = float(x[i, t[i]])
+        want = -math.log(c) if xt == 1e4 else (xt - 1e4) / tau - math.log(c)
+        assert abs(o["logprob"][i] - want) < 1e-9 * max(1.0, abs(want))
+
+
+# ----------------------------------------------------------------------------- gradient
+
+
+def test_grad_rows_sum_to_zero(tiny):
+    _, x, t, g = tiny
+    for tau in (1.0, 0.7):
+        gr = oracle.backward(x, t, g, tau=tau)
+        assert np.abs(gr.sum(axis=1)).max() < x.shape[1] * 1e-16 * 4
+
+
+def test_grad_matches_torch_autograd(tiny):
+    _, x, t, g = tiny
+    for tau in (1.0, 0.7):
+        gr = oracle.backward(x, t, g, tau=tau)
+        xt = torch.from_numpy(x).double().requires_grad_(True)
+        lp = torch.log_softmax(xt / float(np.float32(tau)), dim=1)
+        lp = lp[torch.arange(x.shape[0]), torch.from_numpy(t).long()]
+        (lp * torch.from_numpy(g).double()).sum().backward()
+        np.testing.assert_allclose(gr, xt.grad.numpy(), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_grad_central_finite_differences(tiny, tau):
+    """d lp_r / d x_rj by central differences of the oracle's own forward, on the
+    target column and a spread of other columns of 3 rows."""
+    _, x, t, _ = tiny
+    V = x.shape[1]
+    h = 2.0 ** -10
+    for r in (0, 31, 63):
+        cols = np.unique(np.concatenate([[t[r]], np.linspace(0, V - 1, 24).astype(int)]))
+        plus = np.repeat(x[r:r + 1], len(cols), axis=0)
+        minus = plus.copy()
+        plus[np.arange(len(cols)), cols] += np.float32(h)
+        minus[np.arange(len(cols)), cols] -= np.float32(h)
+        step = (plus[np.arange(len(cols)), cols].astype(np.float64)
+                - minus[np.arange(len(cols)), cols].astype(np.float64))
+        tt = np.full(len(cols), t[r], np.int32)
+        lp_p = oracle.forward(plus, tt, tau=tau, want=("logprob",))["logprob"]
+        lp_m = oracle.forward(minus, tt, tau=tau, want=("logprob",))["logprob"]
+        fd = (lp_p - lp_m) / step
+        gr = oracle.backward(x[r:r + 1], t[r:r + 1], np.ones(1, np.float32), tau=tau)[0]
+        np.testing.assert_allclose(gr[cols], fd, rtol=0, atol=1e-8)
+
+
+def test_grad_zero_rows_are_positive_zero(tiny):
+    """Rows whose incoming gradient is 0 get exactly +0.0 ("Avoid full-vocabulary TP
+    gather ...", "Prototype correctness": masked positions have exactly zero gradient)."""
+    _, x, t, g = tiny
+    g = g.copy()
+    g[::3] = 0.0
+    g[1] = -0.0
+    gr = oracle.backward(x, t, g)
+    z = (g == 0.0)
+    assert np.all(gr[z] == 0.0) and not np.any(np.signbit(gr[z]))
+    assert np.all(np.abs(gr[~z]).max(axis=1) > 0)
+
+
+# ----------------------------------------------------------------------------- split-V
+
+
+@pytest.mark.parametrize("vchunk", [7, 64, 4096, 1000])
+def test_vocab_chunks_match_single_pass(tiny, vchunk):
+    """Vocabulary chunks merged by the shard combine reproduce the single pass
+    (chunk sizes of the verl PR's small test: 7, 64, 4096)."""
+    _, x, t, _ = tiny
+    for tau in (1.0, 0.7):
+        a = oracle.forward(x, t, tau=tau)
+        b = oracle.forward_vchunk(x, t, tau=tau, vchunk=vchunk)
+        for k in ("logprob", "lse", "entropy"):
+            np.testing.assert_allclose(b[k], a[k], rtol=1e-12, atol=1e-12)
+
+
+def test_split4_extreme_rows():
+    """The 4 x 62080 slicing of the extreme fp32 workload against the single pass."""
+    w = W.get("extreme_fp32_16384x248320")
+    rows = np.array([0, 9999])
+    x = W.logits_rows(w, rows)
+    t = W.targets(w)[rows]
+    a = oracle.forward(x, t, tau=w.tau)
+    parts = [oracle.slice_partial(x, q * 62080, 62080, t, w.tau) for q in range(4)]
+    pm, ps, pw, pt = (np.stack([p[i] for p in parts]) for i in range(4))
+    # exactly one slice owns each target
+    assert np.all((pt > -np.inf).sum(axis=0) == 1)
+    b = oracle.combine(pm, ps, pw, pt)
+    for k in ("logprob", "lse", "entropy"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-12, atol=1e-12)
+
+
+def test_unowned_target_is_visible():
+    x = np.zeros((1, 16), np.float32)
+    pm, ps, pw, pt = oracle.slice_partial(x, 0, 8, np.array([12], np.int32), 1.0)
+    assert pt[0] == -np.inf
+    o = oracle.combine(pm[None], ps[None], pw[None], pt[None])
+    assert o["logprob"][0] == -np.inf
+
+
+# ----------------------------------------------------------------------------- chunks / rows
+
+
+def test_row_chunks_bitwise(tiny):
+    """Row chunking (chunk sizes 7, 64, 4096) changes nothing, bit for bit."""
+    _, x, t, _ = tiny
+    a = oracle.forward(x, t, row_chunk=4096)
+    for c in (7, 64, 1):
+        b = oracle.forward(x, t, row_chunk=c)
+        for k in a:
+            assert np.array_equal(a[k], b[k])
+
+
+def test_compact_rows_equal_dense_rows():
+    w = W.scaled("masked_bf16_4096x151936", 96, 3001)
+    x = W.all_logits(w)
+    t = W.targets(w)
+    idx = W.row_index(w)
+    assert np.array_equal(idx, np.nonzero(W.loss_mask(w))[0])
+    d = oracle.forward(x, t)
+    c = oracle.forward(x, t, rows=idx)
+    for k in d:
+        assert np.array_equal(d[k][idx], c[k])
+
+
+def test_errors():
+    x = np.zeros((2, 8), np.float32)
+    t = np.array([0, 9], np.int32)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.forward(x, t)
+    assert e.value.code == -2
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(x, np.array([0, 1], np.int32), row_chunk=0)
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(x, np.array([0, 1], np.int32), row_chunk=-3)
+    with pytest.raises(oracle.OracleError):
+        oracle.forward(x, np.array([0, 1], np.int32), tau=0.0)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.forward(x, np.array([0, 1], np.int32), rows=np.array([0, 2], np.int32))
+    assert e.value.code == -3
+    # zero-length row sets are a no-op
+    o = oracle.forward(x, np.array([0, 1], np.int32), rows=np.zeros(0, np.int32))
+    assert o["logprob"].shape == (0,)
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+
+
+def test_bf16_rne_against_torch():
+    """fp64 -> bf16 RNE equals torch's fp32 -> bf16 for fp32-representable values."""
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-40, 38, 100000),
+                        [0.0, -0.0, 1e-45, -1e-45, 3.4e38, -3.4e38, np.inf, -np.inf]])
+    v32 = v.astype(np.float32)
+    want = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_rne(v32.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rne_ties_and_double_rounding():
+    cases = {
+        1.0 + 2.0 ** -8: 0x3F80,                   # tie -> even (1.0)
+        1.0 + 3 * 2.0 ** -8: 0x3F82,               # tie -> even (1 + 2^-6)
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,      # above the tie: no double rounding
+        -(1.0 + 2.0 ** -8 + 2.0 ** -30): 0xBF81,
+        2.0 ** -133: 0x0001,                       # smallest bf16 subnormal
+        2.0 ** -134: 0x0000,                       # tie with zero -> even (0)
+        3 * 2.0 ** -134: 0x0002,                   # tie 1.5 ulp -> even (2 ulp)
+        (2 - 2.0 ** -8) * 2.0 ** 127: 0x7F80,      # tie at the top -> overflow
+        float("nan"): 0x7FC0,
+    }
+    for v, want in cases.items():
+        assert oracle.bf16_rne(np.array([v]))[0] == want, (v, hex(want))

@@ -1,0 +1,243 @@
+"""Seeded synthetic inputs for selected-token log-probability workloads.
+
+This module is the only code that the HIP path's tests/benchmark and the CPU
+oracle share.  It draws inputs and holds none of the method's arithmetic: no
+softmax, no log-sum-exp, no gradient.
+
+Every random quantity comes from its own counter-based stream,
+``numpy.random.Philox`` keyed by (seed, stream name, row), so any row of any
+workload can be regenerated on its own, bit for bit, without drawing the rows
+before it.  That is what lets a test regenerate a handful of sampled rows of a
+multi-gigabyte input for the oracle.
+
+Workload shapes follow the pages' own workloads:
+  * V = 248320 is the Qwen3.5 vocabulary named in "[megatron] feat: add
+    memory-efficient chunked top-k KL computation" (section "Test") and in the
+    slime issue on full-vocab fp32 logits (section "Bug Description");
+  * V = 151936 stands for the "vocab=150k" of the torchforge parallel-logprob PR
+    (section "Memory savings");
+  * 62080 columns per slice is the TP=4 V_local of the verl PR (section "Peak
+    memory");
+  * packed sequences where only response spans carry loss follow the slime
+    issue ("Steps to Reproduce");
+  * the tiny [64, 2048] case follows the verl PR's small test (V=2048, odd
+    chunk sizes).
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Callable
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "get", "scaled", "logits_rows", "targets", "loss_mask",
+           "grad_out", "row_index", "fill_logits", "bf16_bits_to_float32", "float32_to_bf16_bits"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "bf16" or "fp32"
+    n_rows: int
+    vocab: int
+    sigma: float          # standard deviation of the Gaussian logits
+    seed: int
+    tau: float = 1.0
+    spike_row_prob: float = 0.0    # rows that get +spike_value at one uniform column
+    spike_value: float = 0.0
+    extreme_prob: float = 0.0      # entries replaced by +-extreme_value (fair sign)
+    extreme_value: float = 0.0
+    mask: str = "none"             # "none" | "bernoulli" | "packed"
+    mask_prob: float = 0.0
+    n_seqs: int = 0                # packed: sequences of n_rows / n_seqs tokens
+    response_len: int = 0          # packed: one contiguous response span per sequence
+    grad: str = "uniform"          # grad_out ~ U(-1, 1)
+    grad_zero_prob: float = 0.0    # rows whose grad_out is set to 0
+    n_slices: int = 1              # vocabulary slices for the split-V path
+
+    @property
+    def esize(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def np_dtype(self):
+        return np.uint16 if self.dtype == "bf16" else np.float32
+
+
+WORKLOADS = {
+    # fp32 [64, 2048] ~ N(0,1): forward logprob + entropy + fp32 backward.
+    "tiny_fp32_64x2048": Workload(
+        "tiny_fp32_64x2048", "fp32", 64, 2048, 1.0, seed=0),
+    # bf16 [4096, 151936] ~ N(0, 3^2), Bernoulli(0.5) loss mask, compacted rows.
+    "masked_bf16_4096x151936": Workload(
+        "masked_bf16_4096x151936", "bf16", 4096, 151936, 3.0, seed=1,
+        mask="bernoulli", mask_prob=0.5),
+    # bf16 [8192, 248320] ~ N(0, 3^2) with a +8 spike in 10% of rows; 30% of
+    # rows carry zero grad_out.
+    "spiked_bf16_8192x248320": Workload(
+        "spiked_bf16_8192x248320", "bf16", 8192, 248320, 3.0, seed=2,
+        spike_row_prob=0.1, spike_value=8.0, grad_zero_prob=0.3),
+    # bf16 [32768, 248320] ~ N(0, 2^2): 8 packed sequences of 4096 tokens, one
+    # contiguous 1024-token response span each (25% of tokens).
+    "packed_bf16_32768x248320": Workload(
+        "packed_bf16_32768x248320", "bf16", 32768, 248320, 2.0, seed=3,
+        mask="packed", n_seqs=8, response_len=1024),
+    # fp32 [16384, 248320] ~ N(0, 4^2) with 1% of entries at +-1e4, tau=0.7,
+    # vocabulary in 4 slices of 62080.
+    "extreme_fp32_16384x248320": Workload(
+        "extreme_fp32_16384x248320", "fp32", 16384, 248320, 4.0, seed=4, tau=0.7,
+        extreme_prob=0.01, extreme_value=1.0e4, n_slices=4),
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def scaled(name: str, n_rows: int, vocab: int, **overrides) -> Workload:
+    """Same distributions as a named workload at another shape (parity sizes)."""
+    w = WORKLOADS[name]
+    kw = dict(n_rows=n_rows, vocab=vocab, name=f"{w.name}@{n_rows}x{vocab}")
+    if w.mask == "packed" and "response_len" not in overrides:
+        kw["response_len"] = max(1, (n_rows // max(w.n_seqs, 1)) // 4)
+    kw.update(overrides)
+    return dataclasses.replace(w, **kw)
+
+
+# --------------------------------------------------------------------------- streams
+
+def _stream_key(seed: int, stream: str) -> int:
+    h = hashlib.sha256(f"{seed}:{stream}".encode()).digest()
+    return int.from_bytes(h[:8], "little")
+
+
+def _gen(w: Workload, stream: str, index: int = 0) -> np.random.Generator:
+    key = np.array([_stream_key(w.seed, stream), index], dtype=np.uint64)
+    return np.random.Generator(np.random.Philox(key=key))
+
+
+def float32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); NaN stays NaN. Input quantization."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    b = ((u + r) >> 16).astype(np.uint16)
+    if nan.any():
+        b[nan] = 0x7FC0
+    return b
+
+
+def bf16_bits_to_float32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _row_values(w: Workload, r: int) -> np.ndarray:
+    """float32 values of row r before storage rounding."""
+    x = _gen(w, "logits", r).standard_normal(w.vocab, dtype=np.float32)
+    x *= np.float32(w.sigma)
+    if w.spike_row_prob > 0.0:
+        g = _gen(w, "spike", r)
+        has = g.random() < w.spike_row_prob
+        col = int(g.integers(0, w.vocab))
+        if has:
+            x[col] += np.float32(w.spike_value)
+    if w.extreme_prob > 0.0:
+        g = _gen(w, "extreme", r)
+        hit = g.random(w.vocab) < w.extreme_prob
+        sign = g.random(w.vocab) < 0.5
+        x[hit & sign] = np.float32(w.extreme_value)
+        x[hit & ~sign] = np.float32(-w.extreme_value)
+    return x
+
+
+def logits_rows(w: Workload, rows, ld: int | None = None) -> np.ndarray:
+    """Rows `rows` of the workload's logits: uint16 bf16 bits or float32, [len(rows), ld]."""
+    rows = np.atleast_1d(np.asarray(rows, dtype=np.int64))
+    ld = w.vocab if ld is None else ld
+    out = np.zeros((rows.shape[0], ld), dtype=w.np_dtype)
+    for i, r in enumerate(rows):
+        if not 0 <= r < w.n_rows:
+            raise IndexError(f"row {r} outside [0, {w.n_rows})")
+        x = _row_values(w, int(r))
+        out[i, : w.vocab] = float32_to_bf16_bits(x) if w.dtype == "bf16" else x
+    return out
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def fill_logits(w: Workload, sink: Callable[[int, np.ndarray], None], block_rows: int = 256,
+                threads: int | None = None, ld: int | None = None) -> None:
+    """Generate all rows in blocks; sink(row0, block) is called in row order."""
+    threads = threads or default_threads()
+    starts = list(range(0, w.n_rows, block_rows))
+
+    def make(r0):
+        return logits_rows(w, np.arange(r0, min(r0 + block_rows, w.n_rows)), ld=ld)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        # Keep at most 2 * threads blocks in flight so host memory stays bounded.
+        pending = {}
+        nxt = 0
+        for i, r0 in enumerate(starts):
+            while nxt < len(starts) and nxt < i + 2 * threads:
+                pending[nxt] = ex.submit(make, starts[nxt])
+                nxt += 1
+            sink(r0, pending.pop(i).result())
+
+
+def all_logits(w: Workload, ld: int | None = None) -> np.ndarray:
+    """Whole logits array on the host (small workloads only)."""
+    ld = w.vocab if ld is None else ld
+    out = np.empty((w.n_rows, ld), dtype=w.np_dtype)
+
+    def sink(r0, blk):
+        out[r0: r0 + blk.shape[0]] = blk
+
+    fill_logits(w, sink, block_rows=64)
+    return out
+
+
+def targets(w: Workload) -> np.ndarray:
+    """int32[n_rows], i.i.d. uniform over [0, vocab)."""
+    return _gen(w, "targets").integers(0, w.vocab, size=w.n_rows, dtype=np.int64).astype(np.int32)
+
+
+def loss_mask(w: Workload) -> np.ndarray:
+    """uint8[n_rows] loss mask (all ones when the workload has none)."""
+    if w.mask == "none":
+        return np.ones(w.n_rows, np.uint8)
+    if w.mask == "bernoulli":
+        return (_gen(w, "mask").random(w.n_rows) < w.mask_prob).astype(np.uint8)
+    if w.mask == "packed":
+        seq = w.n_rows // w.n_seqs
+        if w.response_len > seq:
+            raise ValueError("response span longer than its sequence")
+        m = np.zeros(w.n_rows, np.uint8)
+        g = _gen(w, "spans")
+        # Each packed sequence holds a prompt/tool prefix, one contiguous response
+        # span at a seeded offset, and possibly a suffix.
+        for s in range(w.n_seqs):
+            off = int(g.integers(0, seq - w.response_len + 1))
+            m[s * seq + off: s * seq + off + w.response_len] = 1
+        return m
+    raise ValueError(w.mask)
+
+
+def row_index(w: Workload) -> np.ndarray:
+    """Ascending int32 row ids where the loss mask is set."""
+    return np.flatnonzero(loss_mask(w)).astype(np.int32)
+
+
+def grad_out(w: Workload) -> np.ndarray:
+    """float32[n_rows] incoming gradient of each row's logprob, U(-1, 1); zero on a
+    Bernoulli(grad_zero_prob) subset of rows."""
+    g = _gen(w, "grad").uniform(-1.0, 1.0, size=w.n_rows).astype(np.float32)
+    if w.grad_zero_prob > 0.0:
+        z = _gen(w, "grad_zero").random(w.n_rows) < w.grad_zero_prob
+        g[z] = 0.0
+    return g

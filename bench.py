@@ -1,0 +1,210 @@
+"""Benchmark: selected-token log-probabilities + entropy + backward on one MI355X.
+
+One step = the whole hot path over one batch of seeded synthetic logits already
+resident in HBM: the forward (logprob, lse and entropy of every row, one read
+of the logits) and the backward with softmax recompute (bf16 gradient of every
+row; rows whose incoming gradient is 0 are written as +0.0 without reading
+their logits).
+
+Default workload: bf16 logits [8192, 248320] ~ N(0, 3^2) with a +8 spike in
+10% of rows, uniform targets, grad_out ~ U(-1, 1) set to 0 on 30% of rows.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the backward):
+algorithmic bytes per launch / its average duration from HIP events recorded
+on the stream it runs on.  `cpu_baseline` times the fp64 CPU oracle (the
+test-infrastructure reference, untuned) on a bounded sample of rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="spiked_bf16_8192x248320")
+    ap.add_argument("--no-entropy", action="store_true", help="forward without the entropy output")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of the logits' size (for counter scaling)")
+    return ap.parse_args()
+
+
+def alg_bytes(n_rows, vocab, esize, gsize, live_rows, entropy):
+    """Algorithmic HBM bytes of one forward and one backward launch."""
+    out_f = 4 * (3 if entropy else 2)
+    fwd = n_rows * (vocab * esize + 4 + out_f)
+    # every row: read g (4 B) and write V gradients; live rows also read logits,
+    # the target and lse.
+    bwd = n_rows * (4 + vocab * gsize) + live_rows * (vocab * esize + 8)
+    return fwd, bwd
+
+
+def cpu_baseline(w, seconds):
+    """Time the fp64 oracle (fwd + bwd) on rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    t_all = W.targets(w)
+    g_all = W.grad_out(w)
+    rng = np.random.default_rng(12345)
+    chunk = 32
+    rows_done, elapsed, chunks = 0, 0.0, 0
+    while elapsed < seconds and chunks < 64:
+        rows = np.sort(rng.choice(w.n_rows, size=chunk, replace=False))
+        x = W.logits_rows(w, rows)
+        t0 = time.perf_counter()
+        oracle.forward(x, t_all[rows])
+        oracle.backward(x, t_all[rows], g_all[rows])
+        elapsed += time.perf_counter() - t0
+        rows_done += chunk
+        chunks += 1
+    return {"value": rows_done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{rows_done} random rows of {w.name} (fwd logprob+lse+entropy and fp64 "
+                      f"gradient), {elapsed:.1f} s of wall time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import vocab_wide_cross_amd as vwc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.get(args.workload)
+    esize = 2 if w.dtype == "bf16" else 4
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    if args.copy_calibration:
+        n = w.n_rows * w.vocab * esize
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+
+    # Inputs, generated on the host in row blocks and left resident in HBM.
+    t0 = time.time()
+    x = torch.empty((w.n_rows, w.vocab), dtype=dt, device=dev)
+
+    def sink(r0, blk):
+        src = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
+            else torch.from_numpy(blk)
+        x[r0:r0 + blk.shape[0]].copy_(src.to(dev))
+
+    W.fill_logits(w, sink, block_rows=512)
+    t_host = W.targets(w)
+    g_host = W.grad_out(w)
+    targets = torch.from_numpy(t_host).to(dev)
+    grad_out = torch.from_numpy(g_host).to(dev)
+    live = int((g_host != 0).sum())
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    want_ent = not args.no_entropy
+    lp = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
+    lse = torch.empty_like(lp)
+    ent = torch.empty_like(lp) if want_ent else None
+    grad = torch.empty((w.n_rows, w.vocab), dtype=dt, device=dev)
+    ws_bytes = vwc.workspace_bytes(w.n_rows, w.vocab, dt)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        vwc.selected_logprob_fwd(x, targets, w.tau, logprob=lp, lse=lse, entropy=ent,
+                                 workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        vwc.selected_logprob_bwd(x, targets, lse, grad_out, w.tau, grad_logits=grad,
+                                 stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_b, bwd_b = alg_bytes(w.n_rows, w.vocab, esize, esize, live, want_ent)
+
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "tokens/s + achieved HBM GB/s (fwd, fwd+bwd) at N=8192 V=248320 bf16",
+        "value": w.n_rows / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": w.name, "rows": w.n_rows, "vocab": w.vocab,
+                   "temperature": w.tau, "live_grad_rows": live,
+                   "step": "fwd(logprob,lse" + (",entropy" if want_ent else "") +
+                           ") + bwd(" + w.dtype + " grad)"},
+        "fwd": {"ms": fwd_avg, "tokens_per_s": w.n_rows / (fwd_avg * 1e-3),
+                "gbs_alg": gbs(fwd_b, fwd_avg), "frac": gbs(fwd_b, fwd_avg) / HBM_PEAK_GBS,
+                "bytes_alg": fwd_b},
+        "bwd": {"ms": bwd_avg, "gbs_alg": gbs(bwd_b, bwd_avg),
+                "frac": gbs(bwd_b, bwd_avg) / HBM_PEAK_GBS, "bytes_alg": bwd_b},
+        "fwd_bwd": {"ms": fwd_avg + bwd_avg,
+                    "tokens_per_s": w.n_rows / ((fwd_avg + bwd_avg) * 1e-3),
+                    "gbs_alg": gbs(fwd_b + bwd_b, fwd_avg + bwd_avg),
+                    "frac": gbs(fwd_b + bwd_b, fwd_avg + bwd_avg) / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "bwd_segment_kernel",
+                     "achieved": gbs(bwd_b, bwd_avg), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs(bwd_b, bwd_avg) / HBM_PEAK_GBS, "traffic": None},
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

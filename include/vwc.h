@@ -1,0 +1,241 @@
+/*
+ * vwc.h -- selected-token log-probabilities, entropy and the logit gradient
+ * from LM-head logits, on one AMD Instinct MI355X (gfx950).
+ *
+ * For each row r of a logits matrix x and a temperature tau, with z = x / tau:
+ *   lse[r]     = log sum_j exp(z[r, j])
+ *   logprob[r] = z[r, t_r] - lse[r]            (= log_softmax(z)[t_r])
+ *   entropy[r] = -sum_j p_rj log p_rj,  p_rj = exp(z[r, j] - lse[r])
+ *   grad[r, j] = g_r * ([j == t_r] - p_rj) / tau
+ * No [rows, V] float32 log-softmax or probability tensor is ever formed: each
+ * call streams the logits once and keeps O(rows) state.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [A] "[RL][Performance] Avoid full-vocabulary TP gather for selected-token
+ *      logprobs" -- "Proposed solution": the selected log-probability equals
+ *      minus the token cross entropy; "Prototype correctness": masked positions
+ *      get exactly zero gradient; "Problem": only one selected token per
+ *      position is needed, not the full-vocabulary tensor.
+ *  [B] "fix: chunk target logprobs without tensor parallelism (long-context
+ *      OOM)" -- "Changes": forward = float32 logsumexp + gather of the target
+ *      logit, saving only the logits (own dtype) and targets; backward =
+ *      recompute the softmax and write (onehot - softmax) * grad_output into a
+ *      buffer of the logits' dtype; "Verification": zero-length sequences.
+ *  [C] "[megatron] feat: add memory-efficient chunked top-k KL computation" --
+ *      "Design & Code Changes": the backward keeps the low-precision logits
+ *      and a per-token fp32 logZ and recomputes probabilities.
+ *  [D] "[Bug] Training/log-prob forward materializes full-vocab fp32 logits
+ *      over the entire packed sequence ..." -- maintainer comment: compute
+ *      log-prob and entropy on the compact loss-mask rows, scatter scalars
+ *      back; empty masks.
+ *  [E] "feat: Reduce reference model memory with with parallel logprob
+ *      computation" -- "Implementation": vocabulary shards merge a max, a sum
+ *      of exp(x - max) and the target logit held by its owning shard.
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    where stated.  The library allocates nothing, keeps no pointer after the
+ *    call returns and holds no state between calls.
+ *  - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *    synchronize the host.  Results are ready when the stream reaches them.
+ *  - Logits are row-major: element (r, j) sits at logits + (r * ld + j) * e,
+ *    e = 2 (bf16) or 4 (fp32), 0 <= j < vocab <= ld.  The logits pointer must
+ *    be aligned to e bytes.  Rows whose start is 16-byte aligned (aligned base
+ *    and ld * e a multiple of 16) take the 16-byte vector path; other layouts
+ *    are computed element by element (correct, slower).
+ *  - logprob / lse / entropy are float32, one per output row.  Gradients are
+ *    written in grad_dt (bf16 rounded to nearest-even, or fp32).
+ *  - Row sets: the dense calls cover rows 0..n_rows-1.  The `_rows` calls
+ *    cover rows row_idx[0..m) (int32 row ids in [0, n_rows); any order,
+ *    duplicates allowed), and their per-row outputs are COMPACT: output i
+ *    belongs to row row_idx[i].  targets are always indexed by ROW ID
+ *    (length n_rows).
+ *  - Results are deterministic: no floating-point atomics; the reduction
+ *    order of a row depends only on vocab, dtype and the row's alignment, so a
+ *    row gives bit-identical results through the dense and the `_rows` calls.
+ *  - Errors: every argument check runs on the host before any HIP call; a
+ *    failing check returns a status and launches nothing.  n_rows == 0 or
+ *    m == 0 returns VWC_OK without a launch.  Data errors cannot be seen on
+ *    the host: a target outside [0, vocab) gives logprob = NaN in that row
+ *    (dense and `_rows`), and -infinity through the split-vocabulary calls
+ *    when no slice owns it.  NaN logits propagate to that row's outputs.
+ *  - Detail for the last failure on the calling thread: vwc_last_error().
+ */
+#ifndef VWC_H
+#define VWC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VWC_ABI_VERSION 1
+
+typedef enum vwc_status {
+    VWC_OK = 0,
+    VWC_ERR_INVALID_ARG = 1, /* a null required pointer, a negative size, ld < vocab, ... */
+    VWC_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle (e.g. misaligned dtype) */
+    VWC_ERR_HIP = 3          /* a HIP launch failed; see vwc_last_error() */
+} vwc_status;
+
+typedef enum vwc_dtype {
+    VWC_BF16 = 0, /* bfloat16, stored as its 16-bit pattern */
+    VWC_FP32 = 1  /* IEEE binary32 */
+} vwc_dtype;
+
+typedef enum vwc_grad_layout {
+    VWC_GRAD_COMPACT = 0, /* gradient row i of a [m, ld_grad] buffer */
+    VWC_GRAD_SCATTER = 1  /* gradient row row_idx[i] of a [n_rows, ld_grad] buffer */
+} vwc_grad_layout;
+
+/*
+ * Partial of one vocabulary slice of one row ([E] "Implementation"; the
+ * entropy term w is this library's addition so the merge also yields the
+ * entropy).  With columns j of the slice and z = x / tau:
+ *   m  a logit of the slice used as the reference point: m <= max_j x_j and
+ *      (max_j x_j - m) / tau <= 44 (so s stays far from overflow);
+ *      -infinity when the slice is empty.
+ *   s  sum_j exp((x_j - m) / tau)                              (>= 1)
+ *   t  the raw target logit x_t if the slice owns the target column, else
+ *      -infinity (NaN when the dense calls see an out-of-range target)
+ *   w  sum_j exp((x_j - m) / tau) * (x_j - m) / tau            (nats)
+ * Merging k partials of the same row with M = max_k m_k, d_k = (m_k - M)/tau:
+ *   S = sum_k s_k e^{d_k},  W = sum_k e^{d_k} (w_k + d_k s_k),  T = max_k t_k
+ *   lse = M / tau + ln S,  logprob = (T - M) / tau - ln S,  H = ln S - W / S
+ * Partials only merge with partials made at the same temperature.
+ */
+typedef struct vwc_partial {
+    float m, s, t, w;
+} vwc_partial;
+
+/* Bytes of workspace the forward, entropy and partial calls need for `rows`
+   output rows of a `vocab`-wide row (or slice) of dtype dt: 16 bytes per row
+   per internal row segment, 0 when a row is handled by a single workgroup.
+   Never O(rows * vocab). */
+size_t vwc_workspace_bytes(int64_t rows, int64_t vocab, vwc_dtype dt);
+
+/*
+ * Forward over every row ([A] "Proposed solution", [B] "Changes").
+ *  logits   [n_rows, ld] of dt.
+ *  targets  int32[n_rows], the selected token of each row.
+ *  logprob  float[n_rows] (nullable), lse float[n_rows] (nullable; the fp32
+ *           logZ the backward reads, [C]), entropy float[n_rows] (nullable).
+ *  workspace / workspace_bytes: at least vwc_workspace_bytes(n_rows, vocab,
+ *           dt) bytes, 16-byte aligned (nullable when that is 0).
+ * At least one output must be non-null.
+ */
+vwc_status vwc_selected_logprob_fwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                    int64_t vocab, int64_t ld, const int32_t *targets,
+                                    float temperature, float *logprob, float *lse,
+                                    float *entropy, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * Forward over the compact row set row_idx[0..m) ([D] maintainer comment).
+ * Outputs are float[m]; workspace sized by vwc_workspace_bytes(m, vocab, dt).
+ */
+vwc_status vwc_selected_logprob_fwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                         int64_t vocab, int64_t ld, const int32_t *targets,
+                                         const int32_t *row_idx, int64_t m, float temperature,
+                                         float *logprob, float *lse, float *entropy,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* Entropy of softmax(x / tau) per row, no target ([D] "Bug Description":
+   log-probs and entropy from the same logits).  entropy float[n_rows]
+   required, lse nullable. */
+vwc_status vwc_entropy(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                       int64_t ld, float temperature, float *entropy, float *lse,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Entropy over the compact row set row_idx[0..m); outputs float[m]. */
+vwc_status vwc_entropy_rows(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                            int64_t ld, const int32_t *row_idx, int64_t m, float temperature,
+                            float *entropy, float *lse, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward with softmax recompute over every row ([B] "Changes", [C] "Design &
+ * Code Changes", [A] "Prototype correctness").
+ *  lse           float[n_rows] as written by the forward at the same temperature.
+ *  grad_logprob  float[n_rows], the incoming gradient g_r of logprob[r].
+ *  grad_logits   [n_rows, ld_grad] of grad_dt (ld_grad >= vocab); columns
+ *                [vocab, ld_grad) are not touched.  Rows with g_r == 0 are
+ *                written as +0.0 without reading their logits or lse.
+ * grad_logits must not overlap logits (VWC_ERR_INVALID_ARG when the two
+ * address ranges intersect).
+ */
+vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                    int64_t vocab, int64_t ld, const int32_t *targets,
+                                    float temperature, const float *lse,
+                                    const float *grad_logprob, void *grad_logits,
+                                    vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream);
+
+/*
+ * Backward over the compact row set row_idx[0..m).  lse and grad_logprob are
+ * float[m] (compact, as the `_rows` forward writes them).  layout selects
+ * where gradient row i goes: VWC_GRAD_COMPACT -> row i of [m, ld_grad];
+ * VWC_GRAD_SCATTER -> row row_idx[i] of [n_rows, ld_grad], other rows
+ * untouched (the caller clears them; [D] "values outside the selected loss
+ * mask").  With VWC_GRAD_SCATTER, duplicate row ids race.
+ */
+vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                         int64_t vocab, int64_t ld, const int32_t *targets,
+                                         const int32_t *row_idx, int64_t m, float temperature,
+                                         const float *lse, const float *grad_logprob,
+                                         void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                         vwc_grad_layout layout, hipStream_t stream);
+
+/*
+ * Partial of one vocabulary slice ([E] "Implementation", steps 1-3 in one
+ * pass).  logits_slice points at global column v_start of row 0; the slice is
+ * columns [0, v_local) of each row, rows ld elements apart.  targets hold
+ * GLOBAL column ids (int32[n_rows], nullable: then every t is -infinity);
+ * the slice owns t when v_start <= t < v_start + v_local.  row_idx is
+ * nullable (then m must equal n_rows).  out is vwc_partial[m].
+ * workspace: vwc_workspace_bytes(m, v_local, dt) bytes.
+ */
+vwc_status vwc_vocab_partial(const void *logits_slice, vwc_dtype dt, int64_t n_rows,
+                             int64_t v_local, int64_t ld, int64_t v_start,
+                             const int32_t *targets, const int32_t *row_idx, int64_t m,
+                             float temperature, vwc_partial *out, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Merge k slice partials per row ([E] "Implementation", step 4; the merge
+ * formulas are in the vwc_partial comment).  parts is vwc_partial[k][rows]
+ * (slice-major: slice q's partial of row i at parts[q * rows + i]), merged in
+ * slice order.  Outputs float[rows], each nullable (at least one non-null).
+ */
+vwc_status vwc_partial_combine(const vwc_partial *parts, int32_t k, int64_t rows,
+                               float temperature, float *logprob, float *lse, float *entropy,
+                               hipStream_t stream);
+
+/*
+ * Row-set selection ([D] maintainer comment: keep the loss-mask rows).
+ * Writes the ascending ids of the nonzero entries of mask[0..n) to
+ * row_idx[0..count) and the count to *count (device int32).  row_idx must
+ * hold n entries.  n <= INT32_MAX.
+ */
+vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,
+                             hipStream_t stream);
+
+/* Static description of a status code (host pointer, never NULL). */
+const char *vwc_status_string(vwc_status status);
+
+/* Detail of the last failure on the calling thread ("" if none; host pointer,
+   valid until the next call on this thread). */
+const char *vwc_last_error(void);
+
+/* VWC_ABI_VERSION of the loaded library. */
+int vwc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VWC_H */

@@ -1,0 +1,69 @@
+"""Helpers for the GPU tests: upload seeded workloads, compare with tolerances."""
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads as W
+from helpers import bf16_ulp_distance, fp32_ulp
+
+DEV = torch.device("cuda:0")
+
+
+def log(msg: str):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_logits(host: np.ndarray) -> torch.Tensor:
+    if host.dtype == np.uint16:
+        return torch.from_numpy(host.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(host).to(DEV)
+
+
+def upload_workload(w: W.Workload, ld: int | None = None, block_rows: int = 512) -> torch.Tensor:
+    """Generate every row on the host in blocks and copy it into one device tensor."""
+    ld = w.vocab if ld is None else ld
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = torch.empty((w.n_rows, ld), dtype=dt, device=DEV)
+    t0 = time.time()
+    last = [t0]
+
+    def sink(r0, blk):
+        t[r0:r0 + blk.shape[0]].copy_(to_dev_logits(blk))
+        if time.time() - last[0] > 10:
+            last[0] = time.time()
+            log(f"  {w.name}: {r0 + blk.shape[0]} of {w.n_rows} rows uploaded")
+
+    W.fill_logits(w, sink, block_rows=block_rows, ld=ld)
+    torch.cuda.synchronize()
+    log(f"uploaded {w.name} [{w.n_rows}, {ld}] {w.dtype} in {time.time() - t0:.1f}s")
+    return t
+
+
+def grad_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_close_scalar(got, ref, what, atol=5e-5, ulps=0):
+    """|got - ref| <= max(atol, ulps * ulp_fp32(ref)) elementwise (NaN must match)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), f"{what}: NaN pattern differs"
+    ok = ~nan_r
+    tol = np.maximum(atol, ulps * fp32_ulp(ref[ok])) if ulps else atol
+    err = np.abs(got[ok] - ref[ok])
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {ok.sum()} beyond tolerance, max err "
+                           f"{err.max():.3g} at {np.argmax(err)}")
+    return float(err.max()) if err.size else 0.0
+
+
+def assert_bf16_grad(got_bits, ref_grad64, what, oracle):
+    ref_bits = oracle.bf16_rne(ref_grad64)
+    d = bf16_ulp_distance(got_bits, ref_bits)
+    assert d.max() <= 1, f"{what}: bf16 gradient {d.max()} steps from the rounded oracle"
+    return int(d.max())

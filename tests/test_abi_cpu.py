@@ -1,0 +1,152 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vwc.h")
+LIB = os.path.join(ROOT, "vocab_wide_cross_amd", "libvwc.so")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+BF16, FP32 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from vocab_wide_cross_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vwc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    lib.vwc_abi_version.restype = ctypes.c_int
+    assert lib.vwc_abi_version() == 1
+    lib.vwc_status_string.restype = ctypes.c_char_p
+    lib.vwc_status_string.argtypes = [ctypes.c_int]
+    assert lib.vwc_status_string(0) == b"ok"
+    assert lib.vwc_status_string(1) == b"invalid argument"
+    assert lib.vwc_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.vwc_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    # bf16 rows of 248320 (485 KiB) are cut into 4 segments of <= 128 KiB
+    assert f(8192, 248320, BF16) == 8192 * 4 * 16
+    assert f(8192, 248320, FP32) == 8192 * 8 * 16
+    assert f(64, 2048, FP32) == 0          # one segment: no workspace
+    assert f(0, 248320, BF16) == 0
+    assert f(10, 0, BF16) == 0
+    assert f(10, 10, 7) == 0
+
+
+def _fwd(lib):
+    f = lib.vwc_selected_logprob_fwd
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [p, ctypes.c_int, i64, i64, i64, p, ctypes.c_float, p, p, p, p, ctypes.c_size_t,
+                  p]
+    f.restype = ctypes.c_int
+    return f
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def test_forward_validation(lib):
+    f = _fwd(lib)
+    err = lib.vwc_last_error
+    err.restype = ctypes.c_char_p
+    ws = ctypes.c_void_p(0x200000)
+    # unknown dtype
+    assert f(FAKE, 7, 4, 16, 16, FAKE, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    assert b"dtype" in err()
+    # ld < vocab, vocab <= 0, n_rows < 0
+    assert f(FAKE, BF16, 4, 16, 8, FAKE, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    assert f(FAKE, BF16, 4, 0, 8, FAKE, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    assert f(FAKE, BF16, -1, 16, 16, FAKE, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    # temperature must be finite and positive
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert f(FAKE, BF16, 4, 16, 16, FAKE, tau, FAKE, None, None, None, 0, None) == INVALID
+    # missing targets / no output / null logits
+    assert f(FAKE, BF16, 4, 16, 16, None, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    assert f(FAKE, BF16, 4, 16, 16, FAKE, 1.0, None, None, None, None, 0, None) == INVALID
+    assert f(None, BF16, 4, 16, 16, FAKE, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    # misaligned for its dtype
+    assert f(ctypes.c_void_p(0x100001), BF16, 4, 16, 16, FAKE, 1.0, FAKE, None, None, None, 0,
+             None) == UNSUPPORTED
+    # workspace required for multi-segment rows, and must be large enough
+    assert f(FAKE, BF16, 4, 248320, 248320, FAKE, 1.0, FAKE, None, None, None, 0,
+             None) == INVALID
+    assert b"workspace" in err()
+    assert f(FAKE, BF16, 4, 248320, 248320, FAKE, 1.0, FAKE, None, None, ws, 4 * 4 * 16 - 1,
+             None) == INVALID
+    # zero rows: OK, nothing launched (no GPU is touched here)
+    assert f(None, BF16, 0, 16, 16, None, 1.0, None, None, None, None, 0, None) == OK
+    assert err() == b""
+
+
+def test_rows_and_backward_validation(lib):
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    fr = lib.vwc_selected_logprob_fwd_rows
+    fr.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, ctypes.c_float, p, p, p, p,
+                   ctypes.c_size_t, p]
+    # null row_idx with m > 0; m < 0; empty row set is a no-op
+    assert fr(FAKE, BF16, 8, 16, 16, FAKE, None, 3, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    assert fr(FAKE, BF16, 8, 16, 16, FAKE, FAKE, -1, 1.0, FAKE, None, None, None, 0, None) == INVALID
+    assert fr(FAKE, BF16, 8, 16, 16, FAKE, FAKE, 0, 1.0, FAKE, None, None, None, 0, None) == OK
+    b = lib.vwc_selected_logprob_bwd
+    b.argtypes = [p, ctypes.c_int, i64, i64, i64, p, ctypes.c_float, p, p, p, ctypes.c_int, i64, p]
+    g = ctypes.c_void_p(0x900000)
+    # ld_grad < vocab, bad grad dtype, null lse
+    assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, g, BF16, 8, None) == INVALID
+    assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, g, 5, 16, None) == INVALID
+    assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, None, FAKE, g, BF16, 16, None) == INVALID
+    # gradient overlapping the logits
+    assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, ctypes.c_void_p(0x100010), BF16, 16,
+             None) == INVALID
+    br = lib.vwc_selected_logprob_bwd_rows
+    br.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, ctypes.c_float, p, p, p,
+                   ctypes.c_int, i64, ctypes.c_int, p]
+    assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 2, 1.0, FAKE, FAKE, g, BF16, 16, 9,
+              None) == INVALID
+    assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 0, 1.0, FAKE, FAKE, g, BF16, 16, 0, None) == OK
+
+
+def test_partial_combine_and_mask_validation(lib):
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    c = lib.vwc_partial_combine
+    c.argtypes = [p, ctypes.c_int32, i64, ctypes.c_float, p, p, p, p]
+    assert c(FAKE, 0, 4, 1.0, FAKE, None, None, None) == INVALID
+    assert c(FAKE, 2, -1, 1.0, FAKE, None, None, None) == INVALID
+    assert c(FAKE, 2, 4, 0.0, FAKE, None, None, None) == INVALID
+    assert c(FAKE, 2, 4, 1.0, None, None, None, None) == INVALID
+    assert c(None, 2, 0, 1.0, None, None, None, None) == OK
+    vp = lib.vwc_vocab_partial
+    vp.argtypes = [p, ctypes.c_int, i64, i64, i64, i64, p, p, i64, ctypes.c_float, p, p,
+                   ctypes.c_size_t, p]
+    assert vp(FAKE, FP32, 4, 16, 64, -1, FAKE, None, 4, 1.0, FAKE, None, 0, None) == INVALID
+    assert vp(FAKE, FP32, 4, 16, 64, 0, FAKE, None, 4, 1.0, None, None, 0, None) == INVALID
+    mk = lib.vwc_mask_to_index
+    mk.argtypes = [p, i64, p, p, p]
+    assert mk(FAKE, -1, FAKE, FAKE, None) == INVALID
+    assert mk(FAKE, 2 ** 31, FAKE, FAKE, None) == INVALID
+    assert mk(FAKE, 4, FAKE, None, None) == INVALID
+    assert mk(None, 4, FAKE, FAKE, None) == INVALID

@@ -1,0 +1,167 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  The oracle recomputes sampled rows one by one (regenerated
+on the host from the same seeds); properties that hold at any size are checked
+on every row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocab_wide_cross_amd as vwc
+import workloads as W
+from gpu_util import (DEV, assert_bf16_grad, assert_close_scalar, grad_bits, log,
+                      upload_workload)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+@pytest.fixture(autouse=True)
+def _release_memory():
+    """Each test holds up to ~20 GB of device tensors; hand them back afterwards."""
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _row_properties(xmax, lse, ent, tau, vocab):
+    """At any size: max_j z_j <= lse <= max_j z_j + ln V and 0 <= H <= ln V.
+    xmax holds max_j x_j of each checked row."""
+    zmax = xmax.double() / float(np.float32(tau))
+    l = lse.double()
+    assert torch.all(l >= zmax - 1e-5 * zmax.abs().clamp(min=1))
+    assert torch.all(l <= zmax + math.log(vocab) + 1e-4)
+    if ent is not None:
+        assert torch.all(ent >= -5e-5) and torch.all(ent <= math.log(vocab) + 5e-5)
+
+
+def test_spiked_bf16_8192x248320_fwd_bwd():
+    w = W.get("spiked_bf16_8192x248320")
+    x = upload_workload(w)
+    t_host, g_host = W.targets(w), W.grad_out(w)
+    td, gd = torch.from_numpy(t_host).to(DEV), torch.from_numpy(g_host).to(DEV)
+    ws = torch.empty(vwc.workspace_bytes(w.n_rows, w.vocab, torch.bfloat16), dtype=torch.uint8,
+                     device=DEV)
+    lp, lse, ent = vwc.selected_logprob_fwd(x, td, want=("logprob", "lse", "entropy"),
+                                            workspace=ws)
+    grad = vwc.selected_logprob_bwd(x, td, lse, gd)
+    torch.cuda.synchronize()
+    log("spiked: GPU done; checking")
+    _row_properties(x.amax(dim=1), lse, ent, w.tau, w.vocab)
+    assert torch.all(lp <= 0) and torch.all(torch.isfinite(lp))
+    # rows with zero grad_out: +0.0 everywhere, on every row
+    zero = torch.from_numpy(np.flatnonzero(g_host == 0)).to(DEV)
+    assert zero.numel() > 2000
+    assert torch.all(grad[zero].view(torch.int16) == 0)
+    # gradient rows sum to zero up to the bf16 rounding of their entries
+    live = torch.from_numpy(np.flatnonzero(g_host != 0)).to(DEV)
+    for blk in torch.split(live, 512):
+        gb = grad[blk].float()
+        s = gb.sum(dim=1).abs()
+        assert torch.all(s <= gb.abs().sum(dim=1) * 2.0 ** -8 + 1e-30)
+    # sampled rows against the oracle: spike rows, zero-grad rows, ends
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, w.n_rows - 1], rng.choice(w.n_rows, 21, replace=False)]))
+    xh = W.logits_rows(w, rows)
+    ref = oracle.forward(xh, t_host[rows])
+    ri = torch.from_numpy(rows).to(DEV)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        e = assert_close_scalar(_np(v[ri]), ref[k], k)
+        log(f"spiked {k}: max err {e:.3g} over {rows.size} sampled rows")
+    brow = rows[:8]
+    gref = oracle.backward(xh[:8], t_host[brow], g_host[brow])
+    assert_bf16_grad(grad_bits(grad[torch.from_numpy(brow).to(DEV)]), gref, "spiked grad", oracle)
+
+
+def test_masked_bf16_4096x151936_compact_rows():
+    w = W.get("masked_bf16_4096x151936")
+    x = upload_workload(w)
+    t_host = W.targets(w)
+    td = torch.from_numpy(t_host).to(DEV)
+    mask = torch.from_numpy(W.loss_mask(w)).to(DEV)
+    idx, cnt = vwc.mask_to_index(mask)
+    m = int(cnt.item())
+    want_idx = W.row_index(w)
+    assert m == want_idx.size and np.array_equal(_np(idx[:m]), want_idx)
+    idx = idx[:m]
+    lp, lse, ent = vwc.selected_logprob_fwd_rows(x, td, idx, want=("logprob", "lse", "entropy"))
+    dlp, dlse, dent = vwc.selected_logprob_fwd(x, td, want=("logprob", "lse", "entropy"))
+    torch.cuda.synchronize()
+    for a, b in ((lp, dlp), (lse, dlse), (ent, dent)):
+        assert torch.equal(a, b[idx.long()]), "compact rows differ from dense rows"
+    _row_properties(x.amax(dim=1)[idx.long()], lse, ent, w.tau, w.vocab)
+    rng = np.random.default_rng(1)
+    pick = np.sort(rng.choice(m, 24, replace=False))
+    rows = want_idx[pick]
+    ref = oracle.forward(W.logits_rows(w, rows), t_host[rows])
+    pi = torch.from_numpy(pick).to(DEV)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        e = assert_close_scalar(_np(v[pi]), ref[k], k)
+        log(f"masked {k}: max err {e:.3g}")
+
+
+def test_packed_bf16_32768x248320_compact_fwd_bwd():
+    w = W.get("packed_bf16_32768x248320")
+    x = upload_workload(w)
+    t_host, g_host = W.targets(w), W.grad_out(w)
+    td = torch.from_numpy(t_host).to(DEV)
+    idx_h = W.row_index(w)
+    assert idx_h.size == 8192
+    idx = torch.from_numpy(idx_h).to(DEV)
+    gc = torch.from_numpy(g_host[idx_h]).to(DEV)
+    lp, lse, ent = vwc.selected_logprob_fwd_rows(x, td, idx, want=("logprob", "lse", "entropy"))
+    grad = vwc.selected_logprob_bwd_rows(x, td, idx, lse, gc, layout=vwc.VWC_GRAD_COMPACT)
+    torch.cuda.synchronize()
+    log("packed: GPU done; checking")
+    _row_properties(x.amax(dim=1)[idx.long()], lse, ent, w.tau, w.vocab)
+    rng = np.random.default_rng(2)
+    pick = np.sort(rng.choice(idx_h.size, 16, replace=False))
+    rows = idx_h[pick]
+    xh = W.logits_rows(w, rows)
+    ref = oracle.forward(xh, t_host[rows])
+    pi = torch.from_numpy(pick).to(DEV)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        e = assert_close_scalar(_np(v[pi]), ref[k], k)
+        log(f"packed {k}: max err {e:.3g}")
+    gref = oracle.backward(xh[:6], t_host[rows[:6]], g_host[rows[:6]])
+    assert_bf16_grad(grad_bits(grad[pi[:6]]), gref, "packed grad", oracle)
+
+
+def test_extreme_fp32_16384x248320_split_vocab():
+    w = W.get("extreme_fp32_16384x248320")
+    x = upload_workload(w)
+    t_host = W.targets(w)
+    td = torch.from_numpy(t_host).to(DEV)
+    vl = w.vocab // w.n_slices
+    parts = torch.empty((w.n_slices, w.n_rows, 4), dtype=torch.float32, device=DEV)
+    for q in range(w.n_slices):
+        vwc.vocab_partial(x[:, q * vl:(q + 1) * vl], q * vl, td, None, w.tau, out=parts[q])
+    lp, lse, ent = vwc.partial_combine(parts, w.tau)
+    slp, slse, sent = vwc.selected_logprob_fwd(x, td, w.tau, want=("logprob", "lse", "entropy"))
+    torch.cuda.synchronize()
+    log("extreme: GPU done; checking")
+    tau = float(np.float32(w.tau))
+    # closed form on every row: only the +1e4 entries carry mass
+    c = (x == 1.0e4).sum(dim=1).double()
+    xt = x.gather(1, td.long()[:, None])[:, 0].double()
+    h_cf = torch.log(c)
+    lp_cf = torch.where(xt == 1.0e4, -torch.log(c), (xt - 1.0e4) / tau - torch.log(c))
+    lse_cf = 1.0e4 / tau + torch.log(c)
+    for name, got_s, got_1 in (("entropy", ent, sent), ("logprob", lp, slp), ("lse", lse, slse)):
+        ref = {"entropy": h_cf, "logprob": lp_cf, "lse": lse_cf}[name]
+        ulps = 0 if name == "entropy" else 4
+        e1 = assert_close_scalar(_np(got_s), _np(ref), f"split {name}", ulps=ulps)
+        e2 = assert_close_scalar(_np(got_1), _np(ref), f"single {name}", ulps=ulps)
+        log(f"extreme {name}: split max err {e1:.3g}, single-pass {e2:.3g} (all rows)")
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(w.n_rows, 8, replace=False))
+    ref = oracle.forward(W.logits_rows(w, rows), t_host[rows], tau=w.tau)
+    ri = torch.from_numpy(rows).to(DEV)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        assert_close_scalar(_np(v[ri]), ref[k], f"oracle {k}", ulps=0 if k == "entropy" else 4)

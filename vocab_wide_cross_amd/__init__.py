@@ -1,0 +1,14 @@
+"""Selected-token log-probabilities, entropy and logit gradients on MI355X.
+
+The computation runs in the HIP library ``libvwc.so`` (hand-written gfx950
+kernels behind a C ABI declared in ``include/vwc.h``).  This package is its
+thin Python binding: it turns torch tensors into pointers, sizes and a stream
+and calls the library.  There is no fallback: if the library is missing the
+import of the binding raises.
+"""
+from ._binding import (  # noqa: F401
+    VWC_BF16, VWC_FP32, VWC_GRAD_COMPACT, VWC_GRAD_SCATTER, VwcError, abi_version, entropy,
+    entropy_rows, library_path, mask_to_index, partial_combine, selected_logprob_bwd,
+    selected_logprob_bwd_rows, selected_logprob_fwd, selected_logprob_fwd_rows, vocab_partial,
+    workspace_bytes,
+)

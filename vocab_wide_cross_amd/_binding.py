@@ -1,0 +1,278 @@
+"""ctypes binding of libvwc.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks their
+dtypes/shapes just enough to build the C call, and launches on the current
+torch stream (or ``stream``).  All arithmetic happens in the library's HIP
+kernels.  Output tensors are allocated by the caller, or here with torch when
+``None`` is passed (device memory is PyTorch's job).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libvwc.so")
+
+VWC_OK, VWC_ERR_INVALID_ARG, VWC_ERR_UNSUPPORTED, VWC_ERR_HIP = 0, 1, 2, 3
+VWC_BF16, VWC_FP32 = 0, 1
+VWC_GRAD_COMPACT, VWC_GRAD_SCATTER = 0, 1
+PARTIAL_BYTES = 16
+
+
+class VwcError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i64, f32, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                            ctypes.c_size_t)
+    sig = {
+        "vwc_workspace_bytes": ([i64, i64, i32], sz),
+        "vwc_selected_logprob_fwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, sz, p], i32),
+        "vwc_selected_logprob_fwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, sz,
+                                           p], i32),
+        "vwc_entropy": ([p, i32, i64, i64, i64, f32, p, p, p, sz, p], i32),
+        "vwc_entropy_rows": ([p, i32, i64, i64, i64, p, i64, f32, p, p, p, sz, p], i32),
+        "vwc_selected_logprob_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, i32, i64, p], i32),
+        "vwc_selected_logprob_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, i32,
+                                           i64, i32, p], i32),
+        "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
+        "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
+        "vwc_mask_to_index": ([p, i64, p, p, p], i32),
+        "vwc_status_string": ([i32], ctypes.c_char_p),
+        "vwc_last_error": ([], ctypes.c_char_p),
+        "vwc_abi_version": ([], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != VWC_OK:
+        raise VwcError(status, _lib.vwc_last_error().decode() or
+                       _lib.vwc_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, like: torch.Tensor):
+    s = stream if stream is not None else torch.cuda.current_stream(like.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return VWC_BF16
+    if t.dtype == torch.float32:
+        return VWC_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _rows_view(logits: torch.Tensor):
+    """(n_rows, vocab, ld) of a 2-D row-major view (unit column stride)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [rows, vocab]")
+    if logits.size(1) > 1 and logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    ld = logits.stride(0) if logits.size(0) > 1 else max(logits.size(1), 1)
+    return logits.size(0), logits.size(1), ld
+
+
+def _f32(n, like, out):
+    if out is None:
+        return torch.empty(n, dtype=torch.float32, device=like.device)
+    if out.dtype != torch.float32 or out.numel() != n or not out.is_contiguous():
+        raise ValueError("float32 outputs must be contiguous with one entry per row")
+    return out
+
+
+def _i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return t
+
+
+def workspace_bytes(rows: int, vocab: int, dtype) -> int:
+    dt = dtype if isinstance(dtype, int) else _dtype(torch.empty(0, dtype=dtype))
+    return int(_lib.vwc_workspace_bytes(rows, vocab, dt))
+
+
+def _workspace(rows, vocab, logits, workspace):
+    need = workspace_bytes(rows, vocab, _dtype(logits))
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def abi_version() -> int:
+    return int(_lib.vwc_abi_version())
+
+
+def selected_logprob_fwd(logits, targets, temperature=1.0, logprob=None, lse=None,
+                         entropy=None, want=("logprob", "lse"), workspace=None, stream=None):
+    """Dense forward; returns (logprob, lse, entropy), None for outputs not asked for."""
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets")
+    lp = _f32(n, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(n, logits, lse) if (lse is not None or "lse" in want) else None
+    en = _f32(n, logits, entropy) if (entropy is not None or "entropy" in want) else None
+    ws, wsb = _workspace(n, v, logits, workspace)
+    _check(_lib.vwc_selected_logprob_fwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(targets),
+                                         float(temperature), _ptr(lp), _ptr(ls), _ptr(en),
+                                         _ptr(ws), wsb, _stream(stream, logits)))
+    return lp, ls, en
+
+
+def selected_logprob_fwd_rows(logits, targets, row_idx, temperature=1.0, logprob=None, lse=None,
+                              entropy=None, want=("logprob", "lse"), workspace=None, stream=None):
+    """Forward on rows row_idx; outputs are compact [m]."""
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets")
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    lp = _f32(m, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(m, logits, lse) if (lse is not None or "lse" in want) else None
+    en = _f32(m, logits, entropy) if (entropy is not None or "entropy" in want) else None
+    ws, wsb = _workspace(m, v, logits, workspace)
+    _check(_lib.vwc_selected_logprob_fwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
+                                              _ptr(targets), _ptr(row_idx), m, float(temperature),
+                                              _ptr(lp), _ptr(ls), _ptr(en), _ptr(ws), wsb,
+                                              _stream(stream, logits)))
+    return lp, ls, en
+
+
+def entropy(logits, temperature=1.0, out=None, lse=None, workspace=None, stream=None):
+    n, v, ld = _rows_view(logits)
+    en = _f32(n, logits, out)
+    ws, wsb = _workspace(n, v, logits, workspace)
+    _check(_lib.vwc_entropy(_ptr(logits), _dtype(logits), n, v, ld, float(temperature), _ptr(en),
+                            _ptr(lse), _ptr(ws), wsb, _stream(stream, logits)))
+    return en
+
+
+def entropy_rows(logits, row_idx, temperature=1.0, out=None, lse=None, workspace=None,
+                 stream=None):
+    n, v, ld = _rows_view(logits)
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    en = _f32(m, logits, out)
+    ws, wsb = _workspace(m, v, logits, workspace)
+    _check(_lib.vwc_entropy_rows(_ptr(logits), _dtype(logits), n, v, ld, _ptr(row_idx), m,
+                                 float(temperature), _ptr(en), _ptr(lse), _ptr(ws), wsb,
+                                 _stream(stream, logits)))
+    return en
+
+
+def _grad_out(logits, rows, grad_logits, grad_dtype):
+    if grad_logits is None:
+        return torch.empty((rows, logits.size(1)), dtype=grad_dtype or logits.dtype,
+                           device=logits.device)
+    return grad_logits
+
+
+def selected_logprob_bwd(logits, targets, lse, grad_logprob, temperature=1.0, grad_logits=None,
+                         grad_dtype=None, stream=None):
+    """Dense backward: grad_logits[r, j] = g_r ([j == t_r] - p_rj) / tau."""
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets")
+    g = _grad_out(logits, n, grad_logits, grad_dtype)
+    gn, gv, gld = _rows_view(g)
+    if gn != n or gv < v:
+        raise ValueError("grad_logits must be [n_rows, >= vocab]")
+    _check(_lib.vwc_selected_logprob_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(targets),
+                                         float(temperature), _ptr(lse), _ptr(grad_logprob),
+                                         _ptr(g), _dtype(g), gld, _stream(stream, logits)))
+    return g
+
+
+def selected_logprob_bwd_rows(logits, targets, row_idx, lse, grad_logprob, temperature=1.0,
+                              grad_logits=None, grad_dtype=None, layout=VWC_GRAD_COMPACT,
+                              stream=None):
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets")
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    if grad_logits is None:
+        rows = m if layout == VWC_GRAD_COMPACT else n
+        grad_logits = _grad_out(logits, rows, None, grad_dtype)
+        if layout == VWC_GRAD_SCATTER:
+            grad_logits.zero_()
+    _, gv, gld = _rows_view(grad_logits)
+    _check(_lib.vwc_selected_logprob_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
+                                              _ptr(targets), _ptr(row_idx), m,
+                                              float(temperature), _ptr(lse), _ptr(grad_logprob),
+                                              _ptr(grad_logits), _dtype(grad_logits), gld,
+                                              layout, _stream(stream, logits)))
+    return grad_logits
+
+
+def vocab_partial(logits_slice, v_start, targets=None, row_idx=None, temperature=1.0, out=None,
+                  workspace=None, stream=None):
+    """Partial (m, s, t, w) of a vocabulary slice; returns a [m, 4] float32 tensor."""
+    n, v, ld = _rows_view(logits_slice)
+    if targets is not None:
+        _i32(targets, "targets")
+    if row_idx is not None:
+        _i32(row_idx, "row_idx")
+    m = n if row_idx is None else row_idx.numel()
+    if out is None:
+        out = torch.empty((m, 4), dtype=torch.float32, device=logits_slice.device)
+    ws, wsb = _workspace(m, v, logits_slice, workspace)
+    _check(_lib.vwc_vocab_partial(_ptr(logits_slice), _dtype(logits_slice), n, v, ld, v_start,
+                                  _ptr(targets), _ptr(row_idx), m, float(temperature), _ptr(out),
+                                  _ptr(ws), wsb, _stream(stream, logits_slice)))
+    return out
+
+
+def partial_combine(parts, temperature=1.0, logprob=None, lse=None, entropy=None,
+                    want=("logprob", "lse", "entropy"), stream=None):
+    """Merge [k, rows, 4] float32 partials (slice-major) into per-row outputs."""
+    if parts.dim() != 3 or parts.size(2) != 4 or parts.dtype != torch.float32 \
+            or not parts.is_contiguous():
+        raise ValueError("parts must be a contiguous float32 [k, rows, 4] tensor")
+    k, rows = parts.size(0), parts.size(1)
+    lp = _f32(rows, parts, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(rows, parts, lse) if (lse is not None or "lse" in want) else None
+    en = _f32(rows, parts, entropy) if (entropy is not None or "entropy" in want) else None
+    _check(_lib.vwc_partial_combine(_ptr(parts), k, rows, float(temperature), _ptr(lp), _ptr(ls),
+                                    _ptr(en), _stream(stream, parts)))
+    return lp, ls, en
+
+
+def mask_to_index(mask, row_idx=None, count=None, stream=None):
+    """Ascending int32 ids of the nonzero entries of a uint8/bool mask (device count)."""
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    if mask.dtype != torch.uint8 or not mask.is_contiguous():
+        raise TypeError("mask must be a contiguous uint8 or bool tensor")
+    n = mask.numel()
+    if row_idx is None:
+        row_idx = torch.empty(max(n, 1), dtype=torch.int32, device=mask.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=mask.device)
+    _check(_lib.vwc_mask_to_index(_ptr(mask), n, _ptr(row_idx), _ptr(count),
+                                  _stream(stream, mask)))
+    return row_idx, count

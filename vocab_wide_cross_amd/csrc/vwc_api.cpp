@@ -1,0 +1,344 @@
+// vwc_api.cpp -- the extern "C" boundary: argument checks (host only, before
+// any HIP call), launch planning, status codes.  The arithmetic is in
+// vwc_kernels.hip.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "vwc.h"
+#include "vwc_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vwc_status fail(vwc_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+vwc_status ok() {
+    g_last_error.clear();
+    return VWC_OK;
+}
+
+vwc_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(VWC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int dt) { return dt == VWC_BF16 || dt == VWC_FP32; }
+int64_t esize(int dt) { return dt == VWC_BF16 ? 2 : 4; }
+
+// Row segments of a `vocab`-wide row: a function of (vocab, dtype) only.
+int64_t segments(int64_t vocab, int dt, int64_t seg_bytes) {
+    const int64_t bytes = vocab * esize(dt);
+    const int64_t s = (bytes + seg_bytes - 1) / seg_bytes;
+    return s < 1 ? 1 : s;
+}
+
+bool rows_aligned16(const void *p, int64_t ld, int64_t e) {
+    return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * e) % 16 == 0);
+}
+
+// Common checks of a logits operand.
+vwc_status check_logits(const char *fn, const void *logits, int dt, int64_t n_rows, int64_t vocab,
+                        int64_t ld, float temperature) {
+    if (!dtype_ok(dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
+    if (n_rows < 0) return fail(VWC_ERR_INVALID_ARG, "%s: n_rows < 0", fn);
+    if (vocab <= 0) return fail(VWC_ERR_INVALID_ARG, "%s: vocab must be positive", fn);
+    if (ld < vocab) return fail(VWC_ERR_INVALID_ARG, "%s: ld < vocab", fn);
+    if (!(temperature > 0.f) || !isfinite(temperature))
+        return fail(VWC_ERR_INVALID_ARG, "%s: temperature must be finite and > 0", fn);
+    if (vocab > INT32_MAX / 4 || ld > INT64_MAX / 16 / (n_rows > 0 ? n_rows : 1))
+        return fail(VWC_ERR_UNSUPPORTED, "%s: vocab or tensor too large", fn);
+    if (n_rows > 0 && !logits) return fail(VWC_ERR_INVALID_ARG, "%s: logits is null", fn);
+    if (reinterpret_cast<uintptr_t>(logits) % esize(dt) != 0)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: logits not aligned to its dtype", fn);
+    return VWC_OK;
+}
+
+vwc_status check_workspace(const char *fn, int64_t rows, int64_t nseg, const void *ws,
+                           size_t ws_bytes) {
+    if (nseg <= 1) return VWC_OK;
+    const size_t need = static_cast<size_t>(rows) * static_cast<size_t>(nseg) * sizeof(vwc_partial);
+    if (!ws || ws_bytes < need)
+        return fail(VWC_ERR_INVALID_ARG, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                    ws ? ws_bytes : static_cast<size_t>(0));
+    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return fail(VWC_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+    return VWC_OK;
+}
+
+vwc_status check_grid(const char *fn, int64_t rows, int64_t nseg) {
+    if (rows > INT32_MAX / nseg)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: %lld rows x %lld segments exceed one launch", fn,
+                    static_cast<long long>(rows), static_cast<long long>(nseg));
+    return VWC_OK;
+}
+
+// Shared body of the forward, entropy and partial calls.
+vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_rows,
+                          int64_t vocab, int64_t ld, int64_t v_start, const int32_t *targets,
+                          int target_mode, const int32_t *row_idx, int64_t m, float temperature,
+                          float *logprob, float *lse, float *entropy, vwc_partial *partial_out,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
+    if (st != VWC_OK) return st;
+    if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
+    if (m == 0) return ok();  // empty row sets: nothing to do (pointers may be null)
+    if (!row_idx && m != n_rows)
+        return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
+    if (target_mode == vwc::kTargetFull && !targets && logprob)
+        return fail(VWC_ERR_INVALID_ARG, "%s: targets is null", fn);
+    if (!partial_out && !logprob && !lse && !entropy)
+        return fail(VWC_ERR_INVALID_ARG, "%s: no output requested", fn);
+    if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
+
+    const int64_t nseg = segments(vocab, dt, vwc::kFwdSegBytes);
+    if ((st = check_workspace(fn, m, nseg, workspace, workspace_bytes)) != VWC_OK) return st;
+    if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;
+
+    vwc::FwdPlan p{};
+    p.logits = logits;
+    p.ld = ld;
+    p.vocab = static_cast<int32_t>(vocab);
+    p.v_start = v_start;
+    p.targets = targets;
+    p.row_idx = row_idx;
+    p.n_rows = n_rows;
+    p.m = m;
+    // The target logit is read only when a log-probability (or a slice
+    // partial with targets) is asked for.
+    p.target_mode = target_mode;
+    if (target_mode == vwc::kTargetFull && !logprob) p.target_mode = vwc::kTargetNone;
+    if (target_mode == vwc::kTargetSlice && !targets) p.target_mode = vwc::kTargetNone;
+    p.tau = static_cast<double>(temperature);
+    p.c = static_cast<float>(1.44269504088896340736 / p.tau);
+    p.vector = rows_aligned16(logits, ld, esize(dt));
+    const int64_t unit = p.vector ? 16 / esize(dt) : 1;
+    const int64_t nunits = vocab / unit;
+    p.nseg = static_cast<int>(nseg);
+    p.seg_units = static_cast<int32_t>((nunits + nseg - 1) / nseg);
+    if (p.seg_units < 1) p.seg_units = 1;
+    p.want_entropy = entropy != nullptr || partial_out != nullptr;
+    p.logprob = logprob;
+    p.lse = lse;
+    p.entropy = entropy;
+    p.seg_part = nseg > 1 ? static_cast<vwc_partial *>(workspace) : nullptr;
+    p.partial_out = partial_out;
+    return hip_status(vwc::launch_fwd(p, dt, stream), fn);
+}
+
+vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n_rows,
+                           int64_t vocab, int64_t ld, const int32_t *targets,
+                           const int32_t *row_idx, int64_t m, float temperature, const float *lse,
+                           const float *grad_logprob, void *grad_logits, int grad_dt,
+                           int64_t ld_grad, bool by_row_id, hipStream_t stream) {
+    vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
+    if (st != VWC_OK) return st;
+    if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
+    if (ld_grad < vocab) return fail(VWC_ERR_INVALID_ARG, "%s: ld_grad < vocab", fn);
+    if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
+    if (m == 0) return ok();
+    if (!row_idx && m != n_rows)
+        return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
+    if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
+    if (!targets || !lse || !grad_logprob || !grad_logits)
+        return fail(VWC_ERR_INVALID_ARG, "%s: null targets, lse, grad_logprob or grad_logits",
+                    fn);
+    if (reinterpret_cast<uintptr_t>(grad_logits) % esize(grad_dt) != 0)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: grad_logits not aligned to its dtype", fn);
+    if (ld_grad > INT64_MAX / 16 / n_rows)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: gradient tensor too large", fn);
+    // The gradient must not overlap the logits it is computed from.
+    const int64_t grad_rows = by_row_id ? n_rows : m;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(logits);
+    const uintptr_t x1 = x0 + static_cast<uintptr_t>(((n_rows - 1) * ld + vocab) * esize(dt));
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_logits);
+    const uintptr_t g1 =
+        g0 + static_cast<uintptr_t>(((grad_rows - 1) * ld_grad + vocab) * esize(grad_dt));
+    if (g0 < x1 && x0 < g1)
+        return fail(VWC_ERR_INVALID_ARG, "%s: grad_logits overlaps logits", fn);
+
+    const int64_t nseg = segments(vocab, dt, vwc::kBwdSegBytes);
+    if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;
+
+    vwc::BwdPlan p{};
+    p.logits = logits;
+    p.ld = ld;
+    p.vocab = static_cast<int32_t>(vocab);
+    p.dt = dt;
+    p.gdt = grad_dt;
+    p.targets = targets;
+    p.row_idx = row_idx;
+    p.n_rows = n_rows;
+    p.m = m;
+    p.tau = static_cast<double>(temperature);
+    p.c = static_cast<float>(1.44269504088896340736 / p.tau);
+    p.lse = lse;
+    p.grad_out = grad_logprob;
+    p.grad = grad_logits;
+    p.ld_grad = ld_grad;
+    p.grad_by_row_id = by_row_id;
+    p.vector = rows_aligned16(logits, ld, esize(dt)) &&
+               rows_aligned16(grad_logits, ld_grad, esize(grad_dt));
+    const int64_t unit = p.vector ? 16 / esize(dt) : 1;
+    const int64_t nunits = vocab / unit;
+    p.nseg = static_cast<int>(nseg);
+    p.seg_units = static_cast<int32_t>((nunits + nseg - 1) / nseg);
+    if (p.seg_units < 1) p.seg_units = 1;
+    return hip_status(vwc::launch_bwd(p, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vwc_workspace_bytes(int64_t rows, int64_t vocab, vwc_dtype dt) {
+    if (rows <= 0 || vocab <= 0 || !dtype_ok(dt)) return 0;
+    const int64_t nseg = segments(vocab, dt, vwc::kFwdSegBytes);
+    if (nseg <= 1) return 0;
+    return static_cast<size_t>(rows) * static_cast<size_t>(nseg) * sizeof(vwc_partial);
+}
+
+vwc_status vwc_selected_logprob_fwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                    int64_t vocab, int64_t ld, const int32_t *targets,
+                                    float temperature, float *logprob, float *lse,
+                                    float *entropy, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    return forward_common("vwc_selected_logprob_fwd", logits, dt, n_rows, vocab, ld, 0, targets,
+                          vwc::kTargetFull, nullptr, n_rows, temperature, logprob, lse, entropy,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+vwc_status vwc_selected_logprob_fwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                         int64_t vocab, int64_t ld, const int32_t *targets,
+                                         const int32_t *row_idx, int64_t m, float temperature,
+                                         float *logprob, float *lse, float *entropy,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+    if (m > 0 && !row_idx)
+        return fail(VWC_ERR_INVALID_ARG, "vwc_selected_logprob_fwd_rows: row_idx is null");
+    return forward_common("vwc_selected_logprob_fwd_rows", logits, dt, n_rows, vocab, ld, 0,
+                          targets, vwc::kTargetFull, row_idx, m, temperature, logprob, lse,
+                          entropy, nullptr, workspace, workspace_bytes, stream);
+}
+
+vwc_status vwc_entropy(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                       int64_t ld, float temperature, float *entropy, float *lse,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n_rows > 0 && !entropy) return fail(VWC_ERR_INVALID_ARG, "vwc_entropy: entropy is null");
+    return forward_common("vwc_entropy", logits, dt, n_rows, vocab, ld, 0, nullptr,
+                          vwc::kTargetNone, nullptr, n_rows, temperature, nullptr, lse, entropy,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+vwc_status vwc_entropy_rows(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                            int64_t ld, const int32_t *row_idx, int64_t m, float temperature,
+                            float *entropy, float *lse, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "vwc_entropy_rows: row_idx is null");
+    if (m > 0 && !entropy) return fail(VWC_ERR_INVALID_ARG, "vwc_entropy_rows: entropy is null");
+    return forward_common("vwc_entropy_rows", logits, dt, n_rows, vocab, ld, 0, nullptr,
+                          vwc::kTargetNone, row_idx, m, temperature, nullptr, lse, entropy,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                    int64_t vocab, int64_t ld, const int32_t *targets,
+                                    float temperature, const float *lse,
+                                    const float *grad_logprob, void *grad_logits,
+                                    vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream) {
+    return backward_common("vwc_selected_logprob_bwd", logits, dt, n_rows, vocab, ld, targets,
+                           nullptr, n_rows, temperature, lse, grad_logprob, grad_logits, grad_dt,
+                           ld_grad, true, stream);
+}
+
+vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                         int64_t vocab, int64_t ld, const int32_t *targets,
+                                         const int32_t *row_idx, int64_t m, float temperature,
+                                         const float *lse, const float *grad_logprob,
+                                         void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                         vwc_grad_layout layout, hipStream_t stream) {
+    const char *fn = "vwc_selected_logprob_bwd_rows";
+    if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
+                           lse, grad_logprob, grad_logits, grad_dt, ld_grad,
+                           layout == VWC_GRAD_SCATTER, stream);
+}
+
+vwc_status vwc_vocab_partial(const void *logits_slice, vwc_dtype dt, int64_t n_rows,
+                             int64_t v_local, int64_t ld, int64_t v_start,
+                             const int32_t *targets, const int32_t *row_idx, int64_t m,
+                             float temperature, vwc_partial *out, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "vwc_vocab_partial";
+    if (v_start < 0) return fail(VWC_ERR_INVALID_ARG, "%s: v_start < 0", fn);
+    if (m > 0 && !out) return fail(VWC_ERR_INVALID_ARG, "%s: out is null", fn);
+    return forward_common(fn, logits_slice, dt, n_rows, v_local, ld, v_start, targets,
+                          vwc::kTargetSlice, row_idx, m, temperature, nullptr, nullptr, nullptr,
+                          out, workspace, workspace_bytes, stream);
+}
+
+vwc_status vwc_partial_combine(const vwc_partial *parts, int32_t k, int64_t rows,
+                               float temperature, float *logprob, float *lse, float *entropy,
+                               hipStream_t stream) {
+    const char *fn = "vwc_partial_combine";
+    if (k <= 0) return fail(VWC_ERR_INVALID_ARG, "%s: k must be positive", fn);
+    if (rows < 0) return fail(VWC_ERR_INVALID_ARG, "%s: rows < 0", fn);
+    if (!(temperature > 0.f) || !isfinite(temperature))
+        return fail(VWC_ERR_INVALID_ARG, "%s: temperature must be finite and > 0", fn);
+    if (rows == 0) return ok();
+    if (!parts) return fail(VWC_ERR_INVALID_ARG, "%s: parts is null", fn);
+    if (!logprob && !lse && !entropy)
+        return fail(VWC_ERR_INVALID_ARG, "%s: no output requested", fn);
+    if (rows > INT32_MAX - 256) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    vwc::CombinePlan p{};
+    p.parts = parts;
+    p.k = k;
+    p.stride = rows;
+    p.rows = rows;
+    p.tau = static_cast<double>(temperature);
+    p.logprob = logprob;
+    p.lse = lse;
+    p.entropy = entropy;
+    return hip_status(vwc::launch_combine(p, stream), fn);
+}
+
+vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,
+                             hipStream_t stream) {
+    const char *fn = "vwc_mask_to_index";
+    if (n < 0 || n > INT32_MAX) return fail(VWC_ERR_INVALID_ARG, "%s: n outside [0, 2^31)", fn);
+    if (!count) return fail(VWC_ERR_INVALID_ARG, "%s: count is null", fn);
+    if (n > 0 && (!mask || !row_idx))
+        return fail(VWC_ERR_INVALID_ARG, "%s: null mask or row_idx", fn);
+    return hip_status(vwc::launch_mask_to_index(mask, n, row_idx, count, stream), fn);
+}
+
+const char *vwc_status_string(vwc_status status) {
+    switch (status) {
+        case VWC_OK: return "ok";
+        case VWC_ERR_INVALID_ARG: return "invalid argument";
+        case VWC_ERR_UNSUPPORTED: return "unsupported";
+        case VWC_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *vwc_last_error(void) { return g_last_error.c_str(); }
+
+int vwc_abi_version(void) { return VWC_ABI_VERSION; }
+
+}  // extern "C"

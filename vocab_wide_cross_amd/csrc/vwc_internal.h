@@ -1,0 +1,100 @@
+// vwc_internal.h -- launch plans shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "vwc.h"
+
+namespace vwc {
+
+// Workgroup size of every streaming kernel (wave64s x 64).
+#ifndef VWC_BLOCK
+#define VWC_BLOCK 256
+#endif
+constexpr int kBlock = VWC_BLOCK;
+
+// Bytes of one row that one forward workgroup reduces.  A row of `vocab`
+// elements is cut into ceil(vocab * e / kFwdSegBytes) segments, a function of
+// (vocab, dtype) only, so a row's reduction order never depends on how many
+// rows a call covers.
+#ifndef VWC_FWD_SEG_BYTES
+#define VWC_FWD_SEG_BYTES (128 * 1024)
+#endif
+#ifndef VWC_BWD_SEG_BYTES
+#define VWC_BWD_SEG_BYTES (64 * 1024)
+#endif
+constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
+constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;
+
+enum TargetMode : int {
+    kTargetNone = 0,   // entropy only
+    kTargetFull = 1,   // targets index the full row; out of range -> NaN
+    kTargetSlice = 2,  // global targets, owned by this slice or -inf
+};
+
+// One forward (or partial) launch.
+struct FwdPlan {
+    const void *logits;       // column 0 of row 0 of the (slice of the) rows
+    int64_t ld;               // elements between rows
+    int32_t vocab;            // columns handled per row (slice width for partials)
+    int64_t v_start;          // global id of column 0 (slice calls), else 0
+    const int32_t *targets;   // by row id; null in kTargetNone
+    const int32_t *row_idx;   // null: output i is row i
+    int64_t n_rows;           // rows of the tensor (row ids are checked against it)
+    int64_t m;                // output rows
+    int target_mode;
+    float c;                  // log2(e) / tau rounded to float
+    double tau;               // the float temperature widened
+    int nseg;                 // segments per row
+    int32_t seg_units;        // load units (16-byte vectors, or elements) per segment
+    bool vector;              // 16-byte vector path
+    bool want_entropy;
+    // Final outputs (nseg == 1 and !partial_out), compact [m]:
+    float *logprob, *lse, *entropy;
+    // Segment partials, [nseg][m] (when nseg > 1) in workspace:
+    vwc_partial *seg_part;
+    // Slice partial output [m] (vwc_vocab_partial):
+    vwc_partial *partial_out;
+};
+
+struct BwdPlan {
+    const void *logits;
+    int64_t ld;
+    int32_t vocab;
+    int dt;                   // vwc_dtype of logits
+    int gdt;                  // vwc_dtype of the gradient
+    const int32_t *targets;   // by row id
+    const int32_t *row_idx;   // null: dense
+    int64_t n_rows;
+    int64_t m;
+    float c;
+    double tau;
+    const float *lse;         // [m]
+    const float *grad_out;    // [m]
+    void *grad;
+    int64_t ld_grad;
+    bool grad_by_row_id;      // true: gradient row = row id; false: = output index
+    int nseg;
+    int32_t seg_units;
+    bool vector;
+};
+
+struct CombinePlan {
+    const vwc_partial *parts;   // [k][stride]
+    int k;
+    int64_t stride;
+    int64_t rows;
+    double tau;
+    float *logprob, *lse, *entropy;
+    vwc_partial *partial_out;   // merge into partials instead of final outputs
+};
+
+hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream);
+hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream);
+hipError_t launch_combine(const CombinePlan &p, hipStream_t stream);
+hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, int32_t *count,
+                                hipStream_t stream);
+
+}  // namespace vwc

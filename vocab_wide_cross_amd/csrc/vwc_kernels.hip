@@ -1,0 +1,771 @@
+// vwc_kernels.hip -- gfx950 kernels for selected-token log-probabilities,
+// entropy and the logit gradient.
+//
+// Method (web pages, cited by title and section):
+//  * "fix: chunk target logprobs without tensor parallelism (long-context
+//    OOM)", "Changes": forward = float32 logsumexp of each row plus a gather
+//    of the target logit; backward = recompute the softmax and write
+//    (onehot - softmax) * grad_output in the logits' dtype.
+//  * "[megatron] feat: add memory-efficient chunked top-k KL computation",
+//    "Design & Code Changes": the backward keeps the low-precision logits and
+//    a per-token fp32 logZ and recomputes the probabilities from them.
+//  * "feat: Reduce reference model memory with with parallel logprob
+//    computation", "Implementation": per-shard max, per-shard sum of
+//    exp(x - max), target logit from the owning shard, then one merge.  Here
+//    the same merge joins the segments of one row inside one GPU, and the
+//    vocabulary slices of the split-vocabulary entry points.
+//
+// Design for gfx950 (a bandwidth-bound streaming reduction, no MFMA):
+//  * One 256-thread workgroup streams one segment (<= 128 KiB) of one row.
+//    Consecutive lanes read consecutive 16-byte vectors, so every wave load
+//    instruction covers 1 KiB of contiguous HBM; each lane keeps U loads in
+//    flight.
+//  * Each lane keeps (K, s, w) in fp32 registers: K is a shift in log2
+//    units, s = sum 2^u and w = sum 2^u * u with u = x * c - K, c = log2(e)/tau
+//    (one FMA and one v_exp_f32 per element).  K only moves when a chunk's sum
+//    would leave [1, 2^64] -- the first chunk, or a new maximum more than
+//    44 nats above the current reference -- so the common path carries no
+//    per-element max and no per-chunk rescale.  Every quantity is kept
+//    relative to the K it was accumulated with, so the lag costs no accuracy.
+//  * Lane states merge through DPP (quad_perm, row mirrors) and ds_swizzle
+//    within the wave, then through LDS across the 4 waves, in a fixed order.
+//  * Rows longer than one segment write one 16-byte partial per segment; a
+//    second small kernel merges them in segment order in fp64 (the pages'
+//    shard merge).  The epilogue arithmetic (partials, merge, log) is fp64,
+//    once per row.
+#include <math.h>
+#include <stdint.h>
+
+#include "vwc_internal.h"
+
+namespace vwc {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr double kLog2e = 1.44269504088896340736;
+// A chunk whose sum of 2^u exceeds this re-centres K (u > 64 means the logit
+// is more than 64 * ln 2 = 44.4 nats above the reference).
+constexpr float kChunkBound = 0x1p64f;
+// Entropy terms use max(u, -256) so a -inf logit adds 0 * (-256) = 0 to w
+// instead of 0 * (-inf) = NaN; 2^-256 is 0 in fp32 anyway.
+constexpr float kUFloor = -256.0f;
+
+#ifndef VWC_FWD_UNROLL
+#define VWC_FWD_UNROLL 8
+#endif
+#ifndef VWC_BWD_UNROLL
+#define VWC_BWD_UNROLL 4
+#endif
+// Cache policy of the streaming loads/stores: non-temporal (1) or default (0).
+#ifndef VWC_NT_LOAD
+#define VWC_NT_LOAD 1
+#endif
+#ifndef VWC_NT_STORE
+#define VWC_NT_STORE 1
+#endif
+constexpr int kFwdU = VWC_FWD_UNROLL;
+constexpr int kBwdU = VWC_BWD_UNROLL;
+
+template <class T>
+__device__ __forceinline__ T stream_load(const T *p) {
+#if VWC_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <class T>
+__device__ __forceinline__ void stream_store(T v, T *p) {
+#if VWC_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+__device__ __forceinline__ float bits_to_float(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+// ---------------------------------------------------------------- load units
+// A load unit is a 16-byte vector (vector path) or one element (any layout).
+
+template <int DT, bool VEC>
+struct Unit;
+
+template <>
+struct Unit<VWC_BF16, true> {
+    using T = u32x4;
+    static constexpr int N = 8;
+    static __device__ __forceinline__ T load(const T *p) { return stream_load(p); }
+    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
+    // Element k of 8 bf16 packed little-endian in 4 dwords.
+    static __device__ __forceinline__ float get(const T &v, int k) {
+        uint32_t w = v[k >> 1];
+        return bits_to_float((k & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+template <>
+struct Unit<VWC_FP32, true> {
+    using T = f32x4;
+    static constexpr int N = 4;
+    static __device__ __forceinline__ T load(const T *p) { return stream_load(p); }
+    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
+    static __device__ __forceinline__ float get(const T &v, int k) { return v[k]; }
+};
+
+template <>
+struct Unit<VWC_BF16, false> {
+    using T = uint16_t;
+    static constexpr int N = 1;
+    static __device__ __forceinline__ T load(const T *p) { return *p; }
+    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
+    static __device__ __forceinline__ float get(const T &v, int) {
+        return bits_to_float(static_cast<uint32_t>(v) << 16);
+    }
+};
+
+template <>
+struct Unit<VWC_FP32, false> {
+    using T = float;
+    static constexpr int N = 1;
+    static __device__ __forceinline__ T load(const T *p) { return *p; }
+    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
+    static __device__ __forceinline__ float get(const T &v, int) { return v; }
+};
+
+template <int DT>
+__device__ __forceinline__ float load_element(const char *row, int64_t j) {
+    return Unit<DT, false>::get(reinterpret_cast<const typename Unit<DT, false>::T *>(row)[j], 0);
+}
+
+// ---------------------------------------------------------------- lane state
+
+struct Lane {
+    float K;  // shift, log2 units; -inf until the first finite logit
+    float m;  // reference logit: K == fl(m * c)
+    float s;  // sum of 2^u, u = fl(x * c - K)
+    float w;  // sum of 2^u * max(u, kUFloor)
+};
+
+__device__ __forceinline__ Lane lane_init() { return Lane{-INFINITY, -INFINITY, 0.f, 0.f}; }
+
+// Re-centre a lane on the chunk at `p` (units [0, nvalid) spaced by `stride`)
+// and return the chunk's (sum, w) relative to the new K.  Rare: the first
+// chunk of a lane, a new maximum far above the reference, or NaN/-inf data.
+template <int DT, bool VEC, int U, bool W>
+__device__ __forceinline__ f32x2 recentre(const typename Unit<DT, VEC>::T *p,
+                                                     int stride, int nvalid, float c, Lane &L) {
+    using Un = Unit<DT, VEC>;
+    float cm = -INFINITY;
+    bool nan = false;
+    for (int j = 0; j < nvalid; ++j) {
+        typename Un::T v = Un::load_cached(p + j * stride);
+#pragma unroll
+        for (int k = 0; k < Un::N; ++k) {
+            float x = Un::get(v, k);
+            cm = fmaxf(cm, x);
+            nan |= (x != x);
+        }
+    }
+    float Kn = cm * c;
+    if (Kn > L.K) {
+        if (L.s != 0.f) {  // move the mass seen so far (possibly NaN) onto Kn
+            float d = L.K - Kn;
+            float r = __builtin_amdgcn_exp2f(d);
+            L.w = r * __builtin_fmaf(d, L.s, L.w);
+            L.s = r * L.s;
+        }
+        L.K = Kn;
+        L.m = cm;
+    }
+    if (L.K == -INFINITY) return f32x2{nan ? NAN : 0.f, 0.f};  // nothing finite yet
+    float cs = 0.f, cw = 0.f;
+    for (int j = 0; j < nvalid; ++j) {
+        typename Un::T v = Un::load_cached(p + j * stride);
+#pragma unroll
+        for (int k = 0; k < Un::N; ++k) {
+            float u = __builtin_fmaf(Un::get(v, k), c, -L.K);
+            float e = __builtin_amdgcn_exp2f(u);
+            cs += e;
+            if (W) cw = __builtin_fmaf(e, fmaxf(u, kUFloor), cw);
+        }
+    }
+    return f32x2{cs, cw};
+}
+
+// Fold one chunk (U units per lane, the first `nvalid` valid) into the lane.
+template <int DT, bool VEC, int U, bool W>
+__device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[U],
+                                           const typename Unit<DT, VEC>::T *p, int stride,
+                                           int nvalid, float c, Lane &L) {
+    using Un = Unit<DT, VEC>;
+    float s0 = 0.f, s1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        if (j < nvalid) {
+#pragma unroll
+            for (int k = 0; k < Un::N; ++k) {
+                float u = __builtin_fmaf(Un::get(v[j], k), c, -L.K);
+                float e = __builtin_amdgcn_exp2f(u);
+                if (((j * Un::N + k) & 1) == 0) {
+                    s0 += e;
+                    if (W) w0 = __builtin_fmaf(e, fmaxf(u, kUFloor), w0);
+                } else {
+                    s1 += e;
+                    if (W) w1 = __builtin_fmaf(e, fmaxf(u, kUFloor), w1);
+                }
+            }
+        }
+    }
+    float cs = s0 + s1;
+    float cw = w0 + w1;
+    if (!(cs <= kChunkBound)) {
+        f32x2 r = recentre<DT, VEC, U, W>(p, stride, nvalid, c, L);
+        cs = r[0];
+        cw = r[1];
+    }
+    L.s += cs;
+    if (W) L.w += cw;
+}
+
+// Stream units [u0, u1) of a row (lane l takes u0 + l, u0 + l + kBlock, ...).
+template <int DT, bool VEC, int U, bool W>
+__device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_t u1, float c,
+                                             Lane &L) {
+    using Un = Unit<DT, VEC>;
+    using T = typename Un::T;
+    const T *p = reinterpret_cast<const T *>(row);
+    int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
+    for (; b + (U - 1) * kBlock < u1; b += U * kBlock) {
+        T v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = Un::load(p + b + j * kBlock);
+        fold_chunk<DT, VEC, U, W>(v, p + b, kBlock, U, c, L);
+    }
+    if (b < u1) {
+        T v[U];
+        int nv = 0;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            v[j] = T{};
+            if (b + j * kBlock < u1) {
+                v[j] = Un::load(p + b + j * kBlock);
+                nv = j + 1;
+            }
+        }
+        fold_chunk<DT, VEC, U, W>(v, p + b, kBlock, nv, c, L);
+    }
+}
+
+// Merge lane state b into a (fixed, commutative rule: the larger K is kept).
+__device__ __forceinline__ void merge(Lane &a, const Lane &b) {
+    const bool swap = b.K > a.K;
+    const Lane &big = swap ? b : a;
+    const Lane &sml = swap ? a : b;
+    const float d = sml.K - big.K;  // <= 0 (NaN when both are empty)
+    const float r = __builtin_amdgcn_exp2f(d);
+    const bool has = sml.s != 0.f;  // true for NaN too, so NaN propagates
+    const float add_s = has ? r * sml.s : 0.f;
+    const float add_w = has ? r * __builtin_fmaf(d, sml.s, sml.w) : 0.f;
+    Lane o;
+    o.K = big.K;
+    o.m = (a.K == b.K) ? fmaxf(a.m, b.m) : big.m;
+    o.s = big.s + add_s;
+    o.w = big.w + add_w;
+    a = o;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return bits_to_float(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(__builtin_bit_cast(uint32_t, v)), CTRL, 0xf, 0xf, false)));
+}
+
+template <int PATTERN>
+__device__ __forceinline__ float swz(float v) {
+    return bits_to_float(static_cast<uint32_t>(
+        __builtin_amdgcn_ds_swizzle(static_cast<int>(__builtin_bit_cast(uint32_t, v)), PATTERN)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void wave_step_dpp(Lane &L) {
+    Lane o{dpp<CTRL>(L.K), dpp<CTRL>(L.m), dpp<CTRL>(L.s), dpp<CTRL>(L.w)};
+    merge(L, o);
+}
+
+template <int PATTERN>
+__device__ __forceinline__ void wave_step_swz(Lane &L) {
+    Lane o{swz<PATTERN>(L.K), swz<PATTERN>(L.m), swz<PATTERN>(L.s), swz<PATTERN>(L.w)};
+    merge(L, o);
+}
+
+// Reduce the lane states of a workgroup; the result is valid in thread 0.
+__device__ __forceinline__ Lane block_reduce(Lane L) {
+    // Within a wave: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+    // row_mirror (all lanes of a row of 16 then hold the row's state), then a
+    // swizzle exchanging rows 0<->1 and 2<->3 (xor 16 inside each 32-lane half).
+    wave_step_dpp<0xB1>(L);
+    wave_step_dpp<0x4E>(L);
+    wave_step_dpp<0x141>(L);
+    wave_step_dpp<0x140>(L);
+    wave_step_swz<0x401F>(L);
+    // Lanes 0 and 32 now hold the two halves.
+    Lane hi{bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.K), 32)),
+            bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.m), 32)),
+            bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.s), 32)),
+            bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.w), 32))};
+    Lane lo{bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.K), 0)),
+            bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.m), 0)),
+            bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.s), 0)),
+            bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.w), 0))};
+    merge(lo, hi);
+    __shared__ Lane wave_state[kBlock / 64];
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) wave_state[wave] = lo;
+    __syncthreads();
+    Lane acc = wave_state[0];
+#pragma unroll
+    for (int q = 1; q < kBlock / 64; ++q) merge(acc, wave_state[q]);
+    return acc;
+}
+
+// fp64 view of a partial.
+struct P64 {
+    double m, s, t, w;
+};
+
+// Lane state -> partial relative to its reference logit m (see vwc_partial).
+__device__ __forceinline__ P64 to_partial(const Lane &L, float c, double t) {
+    P64 p;
+    p.t = t;
+    if (!(L.s != 0.f)) {  // empty segment
+        p.m = -INFINITY;
+        p.s = 0.0;
+        p.w = 0.0;
+        return p;
+    }
+    // sum 2^{(x - m) c} = 2^rho * s with rho = K - m c, exact in fp64.
+    const double rho = static_cast<double>(L.K) - static_cast<double>(L.m) * static_cast<double>(c);
+    const double f = exp2(rho);
+    p.m = L.m;
+    p.s = static_cast<double>(L.s) * f;
+    p.w = kLn2 * f * (static_cast<double>(L.w) + rho * static_cast<double>(L.s));
+    return p;
+}
+
+// Merge partials in order (formulas in the vwc_partial comment).
+struct Merged {
+    double M, S, W, T;
+};
+
+// Two passes, slices in order: the global reference first (the pages' MAX
+// step), then the rescaled sums (their SUM steps).  `at(q)` yields partial q.
+template <class At>
+__device__ __forceinline__ Merged merge_partials(At at, int k, double tau) {
+    double M = -INFINITY;
+    for (int q = 0; q < k; ++q) {
+        const P64 v = at(q);
+        if (v.s != 0.0 && v.m > M) M = v.m;
+    }
+    double S = 0.0, W = 0.0, T = -INFINITY;
+    bool tnan = false;
+    for (int q = 0; q < k; ++q) {
+        const P64 v = at(q);
+        if (v.t != v.t)
+            tnan = true;
+        else if (v.t > T)
+            T = v.t;
+        if (v.s != 0.0) {  // empty slices add nothing; NaN partials poison S
+            const double d = (v.m - M) / tau;
+            const double f = exp(d);
+            S += v.s * f;
+            W += f * (v.w + d * v.s);
+        }
+    }
+    return Merged{M, S, W, tnan ? NAN : T};
+}
+
+__device__ __forceinline__ void write_final(const Merged &g, double tau, int64_t i, float *logprob,
+                                            float *lse, float *entropy) {
+    const double lnS = log(g.S);
+    if (lse) lse[i] = static_cast<float>(g.M / tau + lnS);
+    if (logprob) logprob[i] = static_cast<float>((g.T - g.M) / tau - lnS);
+    if (entropy) entropy[i] = static_cast<float>(lnS - g.W / g.S);
+}
+
+__device__ __forceinline__ vwc_partial to_f32(const Merged &g) {
+    return vwc_partial{static_cast<float>(g.M), static_cast<float>(g.S), static_cast<float>(g.T),
+                       static_cast<float>(g.W)};
+}
+
+// ---------------------------------------------------------------- forward
+
+template <int DT, bool VEC, bool W>
+__global__ __launch_bounds__(kBlock) void fwd_segment_kernel(FwdPlan p) {
+    using Un = Unit<DT, VEC>;
+    constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
+    const int q = static_cast<int>(blockIdx.x - i * p.nseg);
+    const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+    if (r < 0 || r >= p.n_rows) {  // row id outside the tensor: NaN, no reads
+        if (threadIdx.x == 0) {
+            const vwc_partial bad{NAN, NAN, NAN, NAN};
+            if (p.nseg > 1)
+                p.seg_part[static_cast<int64_t>(q) * p.m + i] = bad;
+            else if (p.partial_out)
+                p.partial_out[i] = bad;
+            else {
+                if (p.logprob && p.target_mode != kTargetNone) p.logprob[i] = NAN;
+                if (p.lse) p.lse[i] = NAN;
+                if (p.entropy) p.entropy[i] = NAN;
+            }
+        }
+        return;
+    }
+    const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
+
+    const int32_t nunits = p.vocab / Un::N;  // whole units; the rest is the tail
+    const int32_t u0 = q * p.seg_units;
+    const int32_t u1 = min(u0 + p.seg_units, nunits);
+    const bool last = q == p.nseg - 1;
+
+    Lane L = lane_init();
+    if (u0 < u1) stream_units<DT, VEC, kFwdU, W>(row, u0, u1, p.c, L);
+    if (VEC && last) {  // tail elements past the last whole vector
+        const int32_t j = nunits * Un::N + static_cast<int32_t>(threadIdx.x);
+        if (j < p.vocab) {
+            using Us = Unit<DT, false>;
+            typename Us::T v[1];
+            const typename Us::T *ptr = reinterpret_cast<const typename Us::T *>(row) + j;
+            v[0] = *ptr;
+            fold_chunk<DT, false, 1, W>(v, ptr, 1, 1, p.c, L);
+        }
+    }
+    const Lane B = block_reduce(L);
+    if (threadIdx.x != 0) return;
+
+    // Target logit from the segment that owns its column.
+    double t = -INFINITY;
+    if (p.target_mode != kTargetNone) {
+        const int64_t tl = static_cast<int64_t>(p.targets[r]) - p.v_start;
+        const int64_t span = static_cast<int64_t>(p.seg_units) * Un::N;
+        const bool in_range = tl >= 0 && tl < p.vocab;
+        if (in_range) {
+            const int64_t owner = min(tl / span, static_cast<int64_t>(p.nseg - 1));
+            if (owner == q) t = load_element<DT>(row, tl);
+        } else if (p.target_mode == kTargetFull && q == 0) {
+            t = NAN;
+        }
+    }
+    const P64 part = to_partial(B, p.c, t);
+    if (p.nseg > 1) {
+        p.seg_part[static_cast<int64_t>(q) * p.m + i] =
+            vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
+                        static_cast<float>(part.t), static_cast<float>(part.w)};
+    } else if (p.partial_out) {
+        p.partial_out[i] = vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
+                                       static_cast<float>(part.t), static_cast<float>(part.w)};
+    } else {
+        const Merged g = merge_partials([&](int) { return part; }, 1, p.tau);
+        write_final(g, p.tau, i, p.target_mode == kTargetNone ? nullptr : p.logprob, p.lse,
+                    p.entropy);
+    }
+}
+
+// One thread per row: merge k partials ([k][stride]) in slice order.
+__global__ __launch_bounds__(kBlock) void combine_kernel(CombinePlan p) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= p.rows) return;
+    const vwc_partial *base = p.parts + i;
+    const int64_t stride = p.stride;
+    const Merged g = merge_partials(
+        [=](int q) {
+            const vwc_partial v = base[static_cast<int64_t>(q) * stride];
+            return P64{v.m, v.s, v.t, v.w};
+        },
+        p.k, p.tau);
+    if (p.partial_out)
+        p.partial_out[i] = to_f32(g);
+    else
+        write_final(g, p.tau, i, p.logprob, p.lse, p.entropy);
+}
+
+// ---------------------------------------------------------------- backward
+
+template <int GDT, int N>
+struct GradStore;
+
+// N gradients to bf16 (round to nearest-even through v_cvt_pk_bf16_f32) or fp32.
+template <int N>
+struct GradStore<VWC_BF16, N> {
+    static __device__ __forceinline__ void store(char *dst, const float (&o)[N]) {
+        if constexpr (N == 1) {
+            const bf16x2 b = __builtin_convertvector((f32x2{o[0], 0.f}), bf16x2);
+            *reinterpret_cast<uint16_t *>(dst) =
+                static_cast<uint16_t>(__builtin_bit_cast(uint32_t, b) & 0xffffu);
+        } else {
+            uint32_t packed[N / 2];
+#pragma unroll
+            for (int k = 0; k < N / 2; ++k) {
+                const bf16x2 b = __builtin_convertvector((f32x2{o[2 * k], o[2 * k + 1]}), bf16x2);
+                packed[k] = __builtin_bit_cast(uint32_t, b);
+            }
+            if constexpr (N == 8)
+                stream_store(u32x4{packed[0], packed[1], packed[2], packed[3]},
+                                            reinterpret_cast<u32x4 *>(dst));
+            else
+                stream_store(u32x2{packed[0], packed[1]},
+                                            reinterpret_cast<u32x2 *>(dst));
+        }
+    }
+};
+
+template <int N>
+struct GradStore<VWC_FP32, N> {
+    static __device__ __forceinline__ void store(char *dst, const float (&o)[N]) {
+        if constexpr (N == 1) {
+            *reinterpret_cast<float *>(dst) = o[0];
+        } else {
+#pragma unroll
+            for (int k = 0; k < N; k += 4)
+                stream_store(f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]},
+                                            reinterpret_cast<f32x4 *>(dst + 4 * k));
+        }
+    }
+};
+
+// Uniform per-row constants of the backward.
+struct RowGrad {
+    float c;       // log2(e) / tau
+    float B;       // lse * log2(e), rounded to float
+    float gs;      // -g / tau
+    double gt;     // g / tau
+    double lse;    // the saved logZ, widened
+    double tau;
+    int32_t t;     // target column
+};
+
+// Gradient of one unit: o_k = gs * p_k with p_k = exp2(x_k c - B) (exp2f keeps
+// denormal results).  The target column gets g/tau * (1 - p_t), computed as
+// -expm1(x_t / tau - lse) in fp64 so that p_t -> 1 does not cancel (a row
+// with a single column gets exactly 0).
+template <int DT, bool VEC>
+__device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, int32_t col0,
+                                          const RowGrad &R, float (&o)[Unit<DT, VEC>::N]) {
+    using Un = Unit<DT, VEC>;
+#pragma unroll
+    for (int k = 0; k < Un::N; ++k)
+        o[k] = exp2f(__builtin_fmaf(Un::get(v, k), R.c, -R.B)) * R.gs;
+    if (static_cast<uint32_t>(R.t - col0) < static_cast<uint32_t>(Un::N)) {
+#pragma unroll
+        for (int k = 0; k < Un::N; ++k)
+            if (col0 + k == R.t) {
+                const double d = static_cast<double>(Un::get(v, k)) / R.tau - R.lse;
+                o[k] = static_cast<float>(R.gt * -expm1(d));
+            }
+    }
+}
+
+template <int DT, int GDT, bool VEC>
+__global__ __launch_bounds__(kBlock) void bwd_segment_kernel(BwdPlan p) {
+    using Un = Unit<DT, VEC>;
+    using T = typename Un::T;
+    constexpr int N = Un::N;
+    constexpr int U = kBwdU;
+    constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
+    constexpr int64_t kGE = GDT == VWC_BF16 ? 2 : 4;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
+    const int q = static_cast<int>(blockIdx.x - i * p.nseg);
+    const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+    if (r < 0 || r >= p.n_rows) return;  // row id outside the tensor: nothing is written
+    const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
+    char *grow = static_cast<char *>(p.grad) + (p.grad_by_row_id ? r : i) * p.ld_grad * kGE;
+
+    const int32_t nunits = p.vocab / N;
+    const int32_t u0 = q * p.seg_units;
+    const int32_t u1 = min(u0 + p.seg_units, nunits);
+    const bool last = q == p.nseg - 1;
+    const float g = p.grad_out[i];
+
+    if (g == 0.f) {
+        // Rows without loss: +0.0, no logits read.
+        float z[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) z[k] = 0.f;
+        for (int32_t b = u0 + static_cast<int32_t>(threadIdx.x); b < u1; b += kBlock)
+            GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, z);
+        if (VEC && last) {
+            const int32_t j = nunits * N + static_cast<int32_t>(threadIdx.x);
+            if (j < p.vocab) {
+                float z1[1] = {0.f};
+                GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, z1);
+            }
+        }
+        return;
+    }
+
+    RowGrad R;
+    R.c = p.c;
+    R.tau = p.tau;
+    R.gt = static_cast<double>(g) / p.tau;
+    R.gs = static_cast<float>(-R.gt);
+    R.lse = static_cast<double>(p.lse[i]);
+    R.B = static_cast<float>(R.lse * kLog2e);
+    R.t = p.targets[r];
+    const T *src = reinterpret_cast<const T *>(row);
+
+    int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
+    for (; b + (U - 1) * kBlock < u1; b += U * kBlock) {
+        T v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = Un::load(src + b + j * kBlock);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int32_t unit = b + j * kBlock;
+            float o[N];
+            unit_grad<DT, VEC>(v[j], unit * N, R, o);
+            GradStore<GDT, N>::store(grow + static_cast<int64_t>(unit) * N * kGE, o);
+        }
+    }
+    for (; b < u1; b += kBlock) {
+        const T v = Un::load(src + b);
+        float o[N];
+        unit_grad<DT, VEC>(v, b * N, R, o);
+        GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, o);
+    }
+    if (VEC && last) {
+        const int32_t j = nunits * N + static_cast<int32_t>(threadIdx.x);
+        if (j < p.vocab) {
+            using Us = Unit<DT, false>;
+            const typename Us::T v = reinterpret_cast<const typename Us::T *>(row)[j];
+            float o[1];
+            unit_grad<DT, false>(v, j, R, o);
+            GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- mask -> index
+
+constexpr int kScanBlock = 1024;
+constexpr int kScanItems = 16;
+
+__global__ __launch_bounds__(kScanBlock) void mask_to_index_kernel(const uint8_t *mask, int64_t n,
+                                                                   int32_t *idx, int32_t *count) {
+    __shared__ int32_t wave_tot[kScanBlock / 64];
+    __shared__ int32_t wave_off[kScanBlock / 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < n; base += static_cast<int64_t>(kScanBlock) * kScanItems) {
+        const int64_t b = base + static_cast<int64_t>(threadIdx.x) * kScanItems;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k)
+            if (b + k < n && mask[b + k] != 0) bits |= 1u << k;
+        const int32_t c = __builtin_popcount(bits);
+        // Inclusive scan of c across the wave.
+        int32_t x = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wave_tot[wave] = x;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t acc = 0;
+            for (int w = 0; w < kScanBlock / 64; ++w) {
+                wave_off[w] = acc;
+                acc += wave_tot[w];
+            }
+            wave_tot[0] = acc;  // block total (read after the barrier below)
+        }
+        __syncthreads();
+        int32_t off = carry + wave_off[wave] + x - c;
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k)
+            if (bits & (1u << k)) idx[off++] = static_cast<int32_t>(b + k);
+        carry += wave_tot[0];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *count = carry;
+}
+
+// ---------------------------------------------------------------- launch helpers
+
+template <int DT>
+hipError_t launch_fwd_dt(const FwdPlan &p, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBlock);
+    if (p.vector) {
+        if (p.want_entropy)
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, false>), grid, block, 0, s, p);
+    } else {
+        if (p.want_entropy)
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, false>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <int DT, int GDT>
+hipError_t launch_bwd_dt(const BwdPlan &p, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBlock);
+    if (p.vector)
+        hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream) {
+    hipError_t e = dt == VWC_BF16 ? launch_fwd_dt<VWC_BF16>(p, stream)
+                                  : launch_fwd_dt<VWC_FP32>(p, stream);
+    if (e != hipSuccess || p.nseg == 1) return e;
+    CombinePlan c{};
+    c.parts = p.seg_part;
+    c.k = p.nseg;
+    c.stride = p.m;
+    c.rows = p.m;
+    c.tau = p.tau;
+    c.logprob = p.target_mode == kTargetNone ? nullptr : p.logprob;
+    c.lse = p.lse;
+    c.entropy = p.entropy;
+    c.partial_out = p.partial_out;
+    return launch_combine(c, stream);
+}
+
+hipError_t launch_combine(const CombinePlan &p, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>((p.rows + kBlock - 1) / kBlock)), block(kBlock);
+    hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream) {
+    if (p.dt == VWC_BF16)
+        return p.gdt == VWC_BF16 ? launch_bwd_dt<VWC_BF16, VWC_BF16>(p, stream)
+                                 : launch_bwd_dt<VWC_BF16, VWC_FP32>(p, stream);
+    return p.gdt == VWC_BF16 ? launch_bwd_dt<VWC_FP32, VWC_BF16>(p, stream)
+                             : launch_bwd_dt<VWC_FP32, VWC_FP32>(p, stream);
+}
+
+hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, int32_t *count,
+                                hipStream_t stream) {
+    hipLaunchKernelGGL(mask_to_index_kernel, dim3(1), dim3(kScanBlock), 0, stream, mask, n, idx,
+                       count);
+    return hipGetLastError();
+}
+
+}  // namespace vwc

@@ -1,10 +1,11 @@
 """Benchmark: selected-token log-probabilities + entropy + backward on one MI355X.
 
-One step = the whole hot path over one batch of seeded synthetic logits already
-resident in HBM: the forward (logprob, lse and entropy of every row, one read
-of the logits) and the backward with softmax recompute (bf16 gradient of every
-row; rows whose incoming gradient is 0 are written as +0.0 without reading
-their logits).
+One step = the hot path over one batch of seeded synthetic logits already
+resident in HBM: the forward (logprob and lse of every row, one read of the
+logits) and the backward with softmax recompute (bf16 gradient of every row;
+rows whose incoming gradient is 0 are written as +0.0 without reading their
+logits).  The forward that also returns the entropy (same single read) is timed
+on its own as `fwd_entropy`; `--entropy-in-step` puts it in the step instead.
 
 Default workload: bf16 logits [8192, 248320] ~ N(0, 3^2) with a +8 spike in
 10% of rows, uniform targets, grad_out ~ U(-1, 1) set to 0 on 30% of rows.
@@ -34,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="spiked_bf16_8192x248320")
-    ap.add_argument("--no-entropy", action="store_true", help="forward without the entropy output")
+    ap.add_argument("--entropy-in-step", action="store_true",
+                    help="the step's forward also writes the entropy")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -53,7 +55,8 @@ def alg_bytes(n_rows, vocab, esize, gsize, live_rows, entropy):
 
 
 def cpu_baseline(w, seconds):
-    """Time the fp64 oracle (fwd + bwd) on rows of the same workload."""
+    """Time the fp64 oracle (forward + gradient) over rows of the same workload:
+    passes over all rows, in blocks of 128, until `seconds` of oracle time."""
     import numpy as np
 
     import oracle
@@ -61,22 +64,51 @@ def cpu_baseline(w, seconds):
 
     t_all = W.targets(w)
     g_all = W.grad_out(w)
-    rng = np.random.default_rng(12345)
-    chunk = 32
-    rows_done, elapsed, chunks = 0, 0.0, 0
-    while elapsed < seconds and chunks < 64:
-        rows = np.sort(rng.choice(w.n_rows, size=chunk, replace=False))
-        x = W.logits_rows(w, rows)
-        t0 = time.perf_counter()
-        oracle.forward(x, t_all[rows])
-        oracle.backward(x, t_all[rows], g_all[rows])
-        elapsed += time.perf_counter() - t0
-        rows_done += chunk
-        chunks += 1
+    x = np.empty((w.n_rows, w.vocab), dtype=w.np_dtype)
+
+    def sink(r0, blk):
+        x[r0:r0 + blk.shape[0]] = blk
+
+    W.fill_logits(w, sink, block_rows=256)
+    block = 128
+    rows_done, elapsed = 0, 0.0
+    while elapsed < seconds:
+        for r0 in range(0, w.n_rows, block):
+            rows = np.arange(r0, min(r0 + block, w.n_rows))
+            t0 = time.perf_counter()
+            oracle.forward(x[rows], t_all[rows])
+            oracle.backward(x[rows], t_all[rows], g_all[rows])
+            elapsed += time.perf_counter() - t0
+            rows_done += rows.size
+            if elapsed >= seconds:
+                break
     return {"value": rows_done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{rows_done} random rows of {w.name} (fwd logprob+lse+entropy and fp64 "
-                      f"gradient), {elapsed:.1f} s of wall time"}
+            "sample": f"{rows_done} rows of {w.name} in order, cycling over all {w.n_rows} rows "
+                      f"(fwd logprob+lse+entropy and the fp64 gradient of each row), "
+                      f"{elapsed:.1f} s of oracle time"}
+
+
+def recorded_traffic(kernel_key):
+    """Per-launch HBM bytes measured by rocprofv3 counters (see profiles/), valid only
+    while the kernel source is the one they were measured on."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic_spiked_bf16_8192x248320.json")
+    src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", "vwc_kernels.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    total = 0
+    for k in kernel_key:
+        if k not in rec["per_launch_bytes"]:
+            return None
+        total += rec["per_launch_bytes"][k]["total"]
+    return total
 
 
 def main():
@@ -127,10 +159,11 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    want_ent = not args.no_entropy
+    want_ent = args.entropy_in_step
     lp = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
     lse = torch.empty_like(lp)
-    ent = torch.empty_like(lp) if want_ent else None
+    ent_buf = torch.empty_like(lp)
+    ent = ent_buf if want_ent else None
     grad = torch.empty((w.n_rows, w.vocab), dtype=dt, device=dev)
     ws_bytes = vwc.workspace_bytes(w.n_rows, w.vocab, dt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -166,9 +199,31 @@ def main():
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     ms_per_step = wall * 1e3 / args.steps
     fwd_b, bwd_b = alg_bytes(w.n_rows, w.vocab, esize, esize, live, want_ent)
+    fwd_e_b, _ = alg_bytes(w.n_rows, w.vocab, esize, esize, live, True)
+
+    # The forward with the entropy output as well, timed on its own.
+    ent_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                  for _ in range(args.steps)]
+    for k in range(args.steps):
+        ent_events[k][0].record(stream)
+        vwc.selected_logprob_fwd(x, targets, w.tau, logprob=lp, lse=lse, entropy=ent_buf,
+                                 workspace=ws, stream=stream)
+        ent_events[k][1].record(stream)
+    torch.cuda.synchronize()
+    fwd_e_avg = sum(e[0].elapsed_time(e[1]) for e in ent_events) / args.steps
 
     def gbs(b, ms):
         return b / (ms * 1e-3) / 1e9
+
+    # Dominant kernel: the launch with the longest average duration.  The
+    # backward is one kernel; the forward is the segment kernel plus a small
+    # merge kernel (its events bracket both).
+    if bwd_avg >= fwd_avg:
+        dom = ("bwd_segment_kernel", bwd_b, bwd_avg, ["bwd_segment_kernel<0, 0, true>"])
+    else:
+        dom = ("fwd_segment_kernel+combine_kernel", fwd_b, fwd_avg,
+               ["fwd_segment_kernel<0, true, false>", "combine_kernel"])
+    traffic = recorded_traffic(dom[3]) if w.name == "spiked_bf16_8192x248320" else None
 
     result = {
         "metric": "tokens/s + achieved HBM GB/s (fwd, fwd+bwd) at N=8192 V=248320 bf16",
@@ -190,15 +245,20 @@ def main():
         "fwd": {"ms": fwd_avg, "tokens_per_s": w.n_rows / (fwd_avg * 1e-3),
                 "gbs_alg": gbs(fwd_b, fwd_avg), "frac": gbs(fwd_b, fwd_avg) / HBM_PEAK_GBS,
                 "bytes_alg": fwd_b},
-        "bwd": {"ms": bwd_avg, "gbs_alg": gbs(bwd_b, bwd_avg),
-                "frac": gbs(bwd_b, bwd_avg) / HBM_PEAK_GBS, "bytes_alg": bwd_b},
+        "fwd_entropy": {"ms": fwd_e_avg, "tokens_per_s": w.n_rows / (fwd_e_avg * 1e-3),
+                        "gbs_alg": gbs(fwd_e_b, fwd_e_avg),
+                        "frac": gbs(fwd_e_b, fwd_e_avg) / HBM_PEAK_GBS, "bytes_alg": fwd_e_b},
+        "bwd": {"ms": bwd_avg, "tokens_per_s": w.n_rows / (bwd_avg * 1e-3),
+                "gbs_alg": gbs(bwd_b, bwd_avg), "frac": gbs(bwd_b, bwd_avg) / HBM_PEAK_GBS,
+                "bytes_alg": bwd_b},
         "fwd_bwd": {"ms": fwd_avg + bwd_avg,
                     "tokens_per_s": w.n_rows / ((fwd_avg + bwd_avg) * 1e-3),
                     "gbs_alg": gbs(fwd_b + bwd_b, fwd_avg + bwd_avg),
                     "frac": gbs(fwd_b + bwd_b, fwd_avg + bwd_avg) / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "bwd_segment_kernel",
-                     "achieved": gbs(bwd_b, bwd_avg), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs(bwd_b, bwd_avg) / HBM_PEAK_GBS, "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dom[0],
+                     "achieved": gbs(dom[1], dom[2]), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs(dom[1], dom[2]) / HBM_PEAK_GBS, "traffic": traffic,
+                     "avg_launch_ms": dom[2], "bytes_alg_per_launch": dom[1]},
     }
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -52,8 +52,8 @@ constexpr double kLog2e = 1.44269504088896340736;
 // A chunk whose sum of 2^u exceeds this re-centres K (u > 64 means the logit
 // is more than 64 * ln 2 = 44.4 nats above the reference).
 constexpr float kChunkBound = 0x1p64f;
-// Entropy terms use max(u, -256) so a -inf logit adds 0 * (-256) = 0 to w
-// instead of 0 * (-inf) = NaN; 2^-256 is 0 in fp32 anyway.
+// In the slow path, entropy terms use max(u, -256) so a -inf logit adds
+// 0 * (-256) = 0 to w instead of 0 * (-inf) = NaN; 2^-256 is 0 in fp32.
 constexpr float kUFloor = -256.0f;
 
 #ifndef VWC_FWD_UNROLL
@@ -151,7 +151,7 @@ struct Lane {
     float K;  // shift, log2 units; -inf until the first finite logit
     float m;  // reference logit: K == fl(m * c)
     float s;  // sum of 2^u, u = fl(x * c - K)
-    float w;  // sum of 2^u * max(u, kUFloor)
+    float w;  // sum of 2^u * u (terms with 2^u == 0 add 0)
 };
 
 __device__ __forceinline__ Lane lane_init() { return Lane{-INFINITY, -INFINITY, 0.f, 0.f}; }
@@ -216,17 +216,20 @@ __device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[
                 float e = __builtin_amdgcn_exp2f(u);
                 if (((j * Un::N + k) & 1) == 0) {
                     s0 += e;
-                    if (W) w0 = __builtin_fmaf(e, fmaxf(u, kUFloor), w0);
+                    if (W) w0 = __builtin_fmaf(e, u, w0);
                 } else {
                     s1 += e;
-                    if (W) w1 = __builtin_fmaf(e, fmaxf(u, kUFloor), w1);
+                    if (W) w1 = __builtin_fmaf(e, u, w1);
                 }
             }
         }
     }
     float cs = s0 + s1;
     float cw = w0 + w1;
-    if (!(cs <= kChunkBound)) {
+    // Leave the fast path when the chunk needs a new shift, or when a -inf
+    // logit made w NaN (2^-inf * -inf); the slow path clamps u for w.  NaN
+    // logits also land there and stay NaN through s.
+    if (!(cs <= kChunkBound) || (W && cw != cw)) {
         f32x2 r = recentre<DT, VEC, U, W>(p, stride, nvalid, c, L);
         cs = r[0];
         cw = r[1];
@@ -236,6 +239,11 @@ __device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[
 }
 
 // Stream units [u0, u1) of a row (lane l takes u0 + l, u0 + l + kBlock, ...).
+// With prefetch on, the loads of chunk k+1 are issued before chunk k is folded,
+// so each wave keeps loads in flight while its ALU work runs.
+#ifndef VWC_FWD_PREFETCH
+#define VWC_FWD_PREFETCH 0
+#endif
 template <int DT, bool VEC, int U, bool W>
 __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_t u1, float c,
                                              Lane &L) {
@@ -243,12 +251,34 @@ __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_
     using T = typename Un::T;
     const T *p = reinterpret_cast<const T *>(row);
     int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
+#if VWC_FWD_PREFETCH
+    if (b + (U - 1) * kBlock < u1) {
+        T cur[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) cur[j] = Un::load(p + b + j * kBlock);
+        for (;;) {
+            const int32_t nb = b + U * kBlock;
+            const bool more = nb + (U - 1) * kBlock < u1;
+            T nxt[U];
+            if (more) {
+#pragma unroll
+                for (int j = 0; j < U; ++j) nxt[j] = Un::load(p + nb + j * kBlock);
+            }
+            fold_chunk<DT, VEC, U, W>(cur, p + b, kBlock, U, c, L);
+            b = nb;
+            if (!more) break;
+#pragma unroll
+            for (int j = 0; j < U; ++j) cur[j] = nxt[j];
+        }
+    }
+#else
     for (; b + (U - 1) * kBlock < u1; b += U * kBlock) {
         T v[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) v[j] = Un::load(p + b + j * kBlock);
         fold_chunk<DT, VEC, U, W>(v, p + b, kBlock, U, c, L);
     }
+#endif
     if (b < u1) {
         T v[U];
         int nv = 0;

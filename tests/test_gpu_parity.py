@@ -152,6 +152,12 @@ def test_mask_to_index_matches_nonzero():
             want = np.flatnonzero(mask).astype(np.int32)
             assert c == want.size
             assert np.array_equal(_np(idx[:c]), want)
+    # a mask that does not start on 16 bytes takes the byte-by-byte path
+    mask = (rng.random(40001) < 0.3).astype(np.uint8)
+    md = torch.from_numpy(mask).to(DEV)[1:]
+    idx, cnt = vwc.mask_to_index(md)
+    c = int(cnt.item())
+    assert np.array_equal(_np(idx[:c]), np.flatnonzero(mask[1:]).astype(np.int32))
     # packed workload mask: the response spans
     w = W.get("packed_bf16_32768x248320")
     m = W.loss_mask(w)

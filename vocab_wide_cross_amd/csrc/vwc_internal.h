@@ -9,21 +9,27 @@
 
 namespace vwc {
 
-// Workgroup size of every streaming kernel (wave64s x 64).
-#ifndef VWC_BLOCK
-#define VWC_BLOCK 256
+// Workgroup sizes (multiples of the 64-lane wave).
+#ifndef VWC_FWD_BLOCK
+#define VWC_FWD_BLOCK 256
 #endif
-constexpr int kBlock = VWC_BLOCK;
+#ifndef VWC_BWD_BLOCK
+#define VWC_BWD_BLOCK 1024
+#endif
+constexpr int kFwdBlock = VWC_FWD_BLOCK;
+constexpr int kBwdBlock = VWC_BWD_BLOCK;
+constexpr int kCombineBlock = 64;
 
 // Bytes of one row that one forward workgroup reduces.  A row of `vocab`
 // elements is cut into ceil(vocab * e / kFwdSegBytes) segments, a function of
 // (vocab, dtype) only, so a row's reduction order never depends on how many
-// rows a call covers.
+// rows a call covers.  The backward has no reduction; its segment size only
+// sets the work per workgroup.  Sizes were chosen by timing on MI355X.
 #ifndef VWC_FWD_SEG_BYTES
 #define VWC_FWD_SEG_BYTES (128 * 1024)
 #endif
 #ifndef VWC_BWD_SEG_BYTES
-#define VWC_BWD_SEG_BYTES (64 * 1024)
+#define VWC_BWD_SEG_BYTES (256 * 1024)
 #endif
 constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;

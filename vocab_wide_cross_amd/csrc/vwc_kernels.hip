@@ -69,6 +69,13 @@ constexpr float kUFloor = -256.0f;
 #ifndef VWC_NT_STORE
 #define VWC_NT_STORE 1
 #endif
+// Optional occupancy attributes, e.g. __attribute__((amdgpu_waves_per_eu(8, 8))).
+#ifndef VWC_FWD_ATTR
+#define VWC_FWD_ATTR
+#endif
+#ifndef VWC_BWD_ATTR
+#define VWC_BWD_ATTR
+#endif
 constexpr int kFwdU = VWC_FWD_UNROLL;
 constexpr int kBwdU = VWC_BWD_UNROLL;
 
@@ -103,7 +110,6 @@ struct Unit<VWC_BF16, true> {
     using T = u32x4;
     static constexpr int N = 8;
     static __device__ __forceinline__ T load(const T *p) { return stream_load(p); }
-    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
     // Element k of 8 bf16 packed little-endian in 4 dwords.
     static __device__ __forceinline__ float get(const T &v, int k) {
         uint32_t w = v[k >> 1];
@@ -116,7 +122,6 @@ struct Unit<VWC_FP32, true> {
     using T = f32x4;
     static constexpr int N = 4;
     static __device__ __forceinline__ T load(const T *p) { return stream_load(p); }
-    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
     static __device__ __forceinline__ float get(const T &v, int k) { return v[k]; }
 };
 
@@ -125,7 +130,6 @@ struct Unit<VWC_BF16, false> {
     using T = uint16_t;
     static constexpr int N = 1;
     static __device__ __forceinline__ T load(const T *p) { return *p; }
-    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
     static __device__ __forceinline__ float get(const T &v, int) {
         return bits_to_float(static_cast<uint32_t>(v) << 16);
     }
@@ -136,7 +140,6 @@ struct Unit<VWC_FP32, false> {
     using T = float;
     static constexpr int N = 1;
     static __device__ __forceinline__ T load(const T *p) { return *p; }
-    static __device__ __forceinline__ T load_cached(const T *p) { return *p; }
     static __device__ __forceinline__ float get(const T &v, int) { return v; }
 };
 
@@ -156,29 +159,31 @@ struct Lane {
 
 __device__ __forceinline__ Lane lane_init() { return Lane{-INFINITY, -INFINITY, 0.f, 0.f}; }
 
-// Re-centre a lane on the chunk at `p` (units [0, nvalid) spaced by `stride`)
-// and return the chunk's (sum, w) relative to the new K.  Rare: the first
-// chunk of a lane, a new maximum far above the reference, or NaN/-inf data.
+// Re-centre a lane on a chunk (units [0, nvalid) of v, still in registers)
+// and return the chunk's (sum, w) relative to the new K.  Rare: a new maximum
+// far above the reference, or NaN/-inf data.
 template <int DT, bool VEC, int U, bool W>
-__device__ __forceinline__ f32x2 recentre(const typename Unit<DT, VEC>::T *p,
-                                                     int stride, int nvalid, float c, Lane &L) {
+__device__ __forceinline__ f32x2 recentre(const typename Unit<DT, VEC>::T (&v)[U], int nvalid,
+                                          float c, Lane &L) {
     using Un = Unit<DT, VEC>;
     float cm = -INFINITY;
     bool nan = false;
-    for (int j = 0; j < nvalid; ++j) {
-        typename Un::T v = Un::load_cached(p + j * stride);
 #pragma unroll
-        for (int k = 0; k < Un::N; ++k) {
-            float x = Un::get(v, k);
-            cm = fmaxf(cm, x);
-            nan |= (x != x);
+    for (int j = 0; j < U; ++j) {
+        if (j < nvalid) {
+#pragma unroll
+            for (int k = 0; k < Un::N; ++k) {
+                const float x = Un::get(v[j], k);
+                cm = fmaxf(cm, x);
+                nan |= (x != x);
+            }
         }
     }
-    float Kn = cm * c;
+    const float Kn = cm * c;
     if (Kn > L.K) {
         if (L.s != 0.f) {  // move the mass seen so far (possibly NaN) onto Kn
-            float d = L.K - Kn;
-            float r = __builtin_amdgcn_exp2f(d);
+            const float d = L.K - Kn;
+            const float r = __builtin_amdgcn_exp2f(d);
             L.w = r * __builtin_fmaf(d, L.s, L.w);
             L.s = r * L.s;
         }
@@ -187,14 +192,16 @@ __device__ __forceinline__ f32x2 recentre(const typename Unit<DT, VEC>::T *p,
     }
     if (L.K == -INFINITY) return f32x2{nan ? NAN : 0.f, 0.f};  // nothing finite yet
     float cs = 0.f, cw = 0.f;
-    for (int j = 0; j < nvalid; ++j) {
-        typename Un::T v = Un::load_cached(p + j * stride);
 #pragma unroll
-        for (int k = 0; k < Un::N; ++k) {
-            float u = __builtin_fmaf(Un::get(v, k), c, -L.K);
-            float e = __builtin_amdgcn_exp2f(u);
-            cs += e;
-            if (W) cw = __builtin_fmaf(e, fmaxf(u, kUFloor), cw);
+    for (int j = 0; j < U; ++j) {
+        if (j < nvalid) {
+#pragma unroll
+            for (int k = 0; k < Un::N; ++k) {
+                const float u = __builtin_fmaf(Un::get(v[j], k), c, -L.K);
+                const float e = __builtin_amdgcn_exp2f(u);
+                cs += e;
+                if (W) cw = __builtin_fmaf(e, fmaxf(u, kUFloor), cw);
+            }
         }
     }
     return f32x2{cs, cw};
@@ -202,10 +209,19 @@ __device__ __forceinline__ f32x2 recentre(const typename Unit<DT, VEC>::T *p,
 
 // Fold one chunk (U units per lane, the first `nvalid` valid) into the lane.
 template <int DT, bool VEC, int U, bool W>
-__device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[U],
-                                           const typename Unit<DT, VEC>::T *p, int stride,
-                                           int nvalid, float c, Lane &L) {
+__device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[U], int nvalid,
+                                           float c, Lane &L) {
     using Un = Unit<DT, VEC>;
+    // A lane's first chunk seeds the shift with its first logit, so the common
+    // case never enters the re-centre path (nor re-reads the chunk).  NaN and
+    // -inf seeds are left to that path.
+    if (L.K == -INFINITY) {
+        const float x0 = Un::get(v[0], 0);
+        if (x0 > -INFINITY) {
+            L.m = x0;
+            L.K = x0 * c;
+        }
+    }
     float s0 = 0.f, s1 = 0.f, w0 = 0.f, w1 = 0.f;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -230,7 +246,7 @@ __device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[
     // logit made w NaN (2^-inf * -inf); the slow path clamps u for w.  NaN
     // logits also land there and stay NaN through s.
     if (!(cs <= kChunkBound) || (W && cw != cw)) {
-        f32x2 r = recentre<DT, VEC, U, W>(p, stride, nvalid, c, L);
+        const f32x2 r = recentre<DT, VEC, U, W>(v, nvalid, c, L);
         cs = r[0];
         cw = r[1];
     }
@@ -238,7 +254,7 @@ __device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[
     if (W) L.w += cw;
 }
 
-// Stream units [u0, u1) of a row (lane l takes u0 + l, u0 + l + kBlock, ...).
+// Stream units [u0, u1) of a row (lane l takes u0 + l, u0 + l + kFwdBlock, ...).
 // With prefetch on, the loads of chunk k+1 are issued before chunk k is folded,
 // so each wave keeps loads in flight while its ALU work runs.
 #ifndef VWC_FWD_PREFETCH
@@ -252,19 +268,19 @@ __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_
     const T *p = reinterpret_cast<const T *>(row);
     int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
 #if VWC_FWD_PREFETCH
-    if (b + (U - 1) * kBlock < u1) {
+    if (b + (U - 1) * kFwdBlock < u1) {
         T cur[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) cur[j] = Un::load(p + b + j * kBlock);
+        for (int j = 0; j < U; ++j) cur[j] = Un::load(p + b + j * kFwdBlock);
         for (;;) {
-            const int32_t nb = b + U * kBlock;
-            const bool more = nb + (U - 1) * kBlock < u1;
+            const int32_t nb = b + U * kFwdBlock;
+            const bool more = nb + (U - 1) * kFwdBlock < u1;
             T nxt[U];
             if (more) {
 #pragma unroll
-                for (int j = 0; j < U; ++j) nxt[j] = Un::load(p + nb + j * kBlock);
+                for (int j = 0; j < U; ++j) nxt[j] = Un::load(p + nb + j * kFwdBlock);
             }
-            fold_chunk<DT, VEC, U, W>(cur, p + b, kBlock, U, c, L);
+            fold_chunk<DT, VEC, U, W>(cur, U, c, L);
             b = nb;
             if (!more) break;
 #pragma unroll
@@ -272,11 +288,11 @@ __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_
         }
     }
 #else
-    for (; b + (U - 1) * kBlock < u1; b += U * kBlock) {
+    for (; b + (U - 1) * kFwdBlock < u1; b += U * kFwdBlock) {
         T v[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) v[j] = Un::load(p + b + j * kBlock);
-        fold_chunk<DT, VEC, U, W>(v, p + b, kBlock, U, c, L);
+        for (int j = 0; j < U; ++j) v[j] = Un::load(p + b + j * kFwdBlock);
+        fold_chunk<DT, VEC, U, W>(v, U, c, L);
     }
 #endif
     if (b < u1) {
@@ -285,12 +301,12 @@ __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             v[j] = T{};
-            if (b + j * kBlock < u1) {
-                v[j] = Un::load(p + b + j * kBlock);
+            if (b + j * kFwdBlock < u1) {
+                v[j] = Un::load(p + b + j * kFwdBlock);
                 nv = j + 1;
             }
         }
-        fold_chunk<DT, VEC, U, W>(v, p + b, kBlock, nv, c, L);
+        fold_chunk<DT, VEC, U, W>(v, nv, c, L);
     }
 }
 
@@ -356,13 +372,13 @@ __device__ __forceinline__ Lane block_reduce(Lane L) {
             bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.s), 0)),
             bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.w), 0))};
     merge(lo, hi);
-    __shared__ Lane wave_state[kBlock / 64];
+    __shared__ Lane wave_state[kFwdBlock / 64];
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) wave_state[wave] = lo;
     __syncthreads();
     Lane acc = wave_state[0];
 #pragma unroll
-    for (int q = 1; q < kBlock / 64; ++q) merge(acc, wave_state[q]);
+    for (int q = 1; q < kFwdBlock / 64; ++q) merge(acc, wave_state[q]);
     return acc;
 }
 
@@ -438,7 +454,7 @@ __device__ __forceinline__ vwc_partial to_f32(const Merged &g) {
 // ---------------------------------------------------------------- forward
 
 template <int DT, bool VEC, bool W>
-__global__ __launch_bounds__(kBlock) void fwd_segment_kernel(FwdPlan p) {
+__global__ __launch_bounds__(kFwdBlock) VWC_FWD_ATTR void fwd_segment_kernel(FwdPlan p) {
     using Un = Unit<DT, VEC>;
     constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
     const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
@@ -475,7 +491,7 @@ __global__ __launch_bounds__(kBlock) void fwd_segment_kernel(FwdPlan p) {
             typename Us::T v[1];
             const typename Us::T *ptr = reinterpret_cast<const typename Us::T *>(row) + j;
             v[0] = *ptr;
-            fold_chunk<DT, false, 1, W>(v, ptr, 1, 1, p.c, L);
+            fold_chunk<DT, false, 1, W>(v, 1, p.c, L);
         }
     }
     const Lane B = block_reduce(L);
@@ -510,8 +526,8 @@ __global__ __launch_bounds__(kBlock) void fwd_segment_kernel(FwdPlan p) {
 }
 
 // One thread per row: merge k partials ([k][stride]) in slice order.
-__global__ __launch_bounds__(kBlock) void combine_kernel(CombinePlan p) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+__global__ __launch_bounds__(kCombineBlock) void combine_kernel(CombinePlan p) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kCombineBlock + threadIdx.x;
     if (i >= p.rows) return;
     const vwc_partial *base = p.parts + i;
     const int64_t stride = p.stride;
@@ -604,7 +620,7 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
 }
 
 template <int DT, int GDT, bool VEC>
-__global__ __launch_bounds__(kBlock) void bwd_segment_kernel(BwdPlan p) {
+__global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(BwdPlan p) {
     using Un = Unit<DT, VEC>;
     using T = typename Un::T;
     constexpr int N = Un::N;
@@ -629,7 +645,7 @@ __global__ __launch_bounds__(kBlock) void bwd_segment_kernel(BwdPlan p) {
         float z[N];
 #pragma unroll
         for (int k = 0; k < N; ++k) z[k] = 0.f;
-        for (int32_t b = u0 + static_cast<int32_t>(threadIdx.x); b < u1; b += kBlock)
+        for (int32_t b = u0 + static_cast<int32_t>(threadIdx.x); b < u1; b += kBwdBlock)
             GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, z);
         if (VEC && last) {
             const int32_t j = nunits * N + static_cast<int32_t>(threadIdx.x);
@@ -652,19 +668,19 @@ __global__ __launch_bounds__(kBlock) void bwd_segment_kernel(BwdPlan p) {
     const T *src = reinterpret_cast<const T *>(row);
 
     int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
-    for (; b + (U - 1) * kBlock < u1; b += U * kBlock) {
+    for (; b + (U - 1) * kBwdBlock < u1; b += U * kBwdBlock) {
         T v[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) v[j] = Un::load(src + b + j * kBlock);
+        for (int j = 0; j < U; ++j) v[j] = Un::load(src + b + j * kBwdBlock);
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int32_t unit = b + j * kBlock;
+            const int32_t unit = b + j * kBwdBlock;
             float o[N];
             unit_grad<DT, VEC>(v[j], unit * N, R, o);
             GradStore<GDT, N>::store(grow + static_cast<int64_t>(unit) * N * kGE, o);
         }
     }
-    for (; b < u1; b += kBlock) {
+    for (; b < u1; b += kBwdBlock) {
         const T v = Un::load(src + b);
         float o[N];
         unit_grad<DT, VEC>(v, b * N, R, o);
@@ -693,13 +709,22 @@ __global__ __launch_bounds__(kScanBlock) void mask_to_index_kernel(const uint8_t
     __shared__ int32_t wave_off[kScanBlock / 64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const bool aligned = (reinterpret_cast<uintptr_t>(mask) & 15) == 0;
     int32_t carry = 0;
     for (int64_t base = 0; base < n; base += static_cast<int64_t>(kScanBlock) * kScanItems) {
         const int64_t b = base + static_cast<int64_t>(threadIdx.x) * kScanItems;
         uint32_t bits = 0;
+        if (aligned && b + kScanItems <= n) {
+            // one 16-byte load: bit k is set when byte k is nonzero
+            const u32x4 q = *reinterpret_cast<const u32x4 *>(mask + b);
 #pragma unroll
-        for (int k = 0; k < kScanItems; ++k)
-            if (b + k < n && mask[b + k] != 0) bits |= 1u << k;
+            for (int k = 0; k < kScanItems; ++k)
+                if ((q[k >> 2] >> (8 * (k & 3))) & 0xffu) bits |= 1u << k;
+        } else {
+#pragma unroll
+            for (int k = 0; k < kScanItems; ++k)
+                if (b + k < n && mask[b + k] != 0) bits |= 1u << k;
+        }
         const int32_t c = __builtin_popcount(bits);
         // Inclusive scan of c across the wave.
         int32_t x = c;
@@ -733,7 +758,7 @@ __global__ __launch_bounds__(kScanBlock) void mask_to_index_kernel(const uint8_t
 
 template <int DT>
 hipError_t launch_fwd_dt(const FwdPlan &p, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBlock);
+    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kFwdBlock);
     if (p.vector) {
         if (p.want_entropy)
             hipLaunchKernelGGL((fwd_segment_kernel<DT, true, true>), grid, block, 0, s, p);
@@ -750,7 +775,7 @@ hipError_t launch_fwd_dt(const FwdPlan &p, hipStream_t s) {
 
 template <int DT, int GDT>
 hipError_t launch_bwd_dt(const BwdPlan &p, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBlock);
+    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBwdBlock);
     if (p.vector)
         hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true>), grid, block, 0, s, p);
     else
@@ -778,7 +803,8 @@ hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombinePlan &p, hipStream_t stream) {
-    const dim3 grid(static_cast<uint32_t>((p.rows + kBlock - 1) / kBlock)), block(kBlock);
+    const dim3 grid(static_cast<uint32_t>((p.rows + kCombineBlock - 1) / kCombineBlock)),
+        block(kCombineBlock);
     hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p);
     return hipGetLastError();
 }

@@ -619,16 +619,15 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
     }
 }
 
+// Gradient of segment q of output row i.
 template <int DT, int GDT, bool VEC>
-__global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(BwdPlan p) {
+__device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     using Un = Unit<DT, VEC>;
     using T = typename Un::T;
     constexpr int N = Un::N;
     constexpr int U = kBwdU;
     constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
     constexpr int64_t kGE = GDT == VWC_BF16 ? 2 : 4;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
-    const int q = static_cast<int>(blockIdx.x - i * p.nseg);
     const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
     if (r < 0 || r >= p.n_rows) return;  // row id outside the tensor: nothing is written
     const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
@@ -696,6 +695,13 @@ __global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(Bwd
             GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, o);
         }
     }
+}
+
+// One workgroup per (row, segment) item.
+template <int DT, int GDT, bool VEC>
+__global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(BwdPlan p) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
+    bwd_item<DT, GDT, VEC>(p, i, static_cast<int>(blockIdx.x - i * p.nseg));
 }
 
 // ---------------------------------------------------------------- mask -> index

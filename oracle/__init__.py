@@ -61,6 +61,8 @@ def _load():
         p, i64, d = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
         lib.oracle_forward.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, d, i64, p, p, p]
         lib.oracle_backward.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, d, p, p]
+        lib.oracle_backward_entropy.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, d, p,
+                                                p, p]
         lib.oracle_slice_partial.argtypes = [p, ctypes.c_int, i64, i64, i64, i64, p, p, i64, d,
                                              p, p, p, p]
         lib.oracle_combine.argtypes = [i64, i64, p, p, p, p, p, p, p]
@@ -70,8 +72,8 @@ def _load():
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_bf16_rne_array.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
-        for f in ("oracle_forward", "oracle_backward", "oracle_slice_partial", "oracle_combine",
-                  "oracle_forward_vchunk"):
+        for f in ("oracle_forward", "oracle_backward", "oracle_backward_entropy",
+                  "oracle_slice_partial", "oracle_combine", "oracle_forward_vchunk"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -165,6 +167,28 @@ def backward(x: np.ndarray, targets, grad_out, tau: float = 1.0, rows=None,
     rc = _load().oracle_backward(_ptr(x), _dtype_code(x), n_rows, vocab, ld, _ptr(targets),
                                  _ptr(rows), m, _tau(tau), _ptr(g), _ptr(grad))
     _check(rc, "oracle_backward")
+    return grad
+
+
+def backward_entropy(x: np.ndarray, targets, grad_logprob, grad_entropy, tau: float = 1.0,
+                     rows=None, vocab: int | None = None) -> np.ndarray:
+    """[m, vocab] float64 gradient of sum_i g_i logprob_i + h_i entropy_i w.r.t. the logits;
+    grad_logprob (g) or grad_entropy (h) may be None (zero)."""
+    x = np.ascontiguousarray(x)
+    n_rows, ld = x.shape
+    vocab = ld if vocab is None else vocab
+    rows, m = _rows_arg(rows, n_rows)
+    targets = _targets_arg(targets)
+    g = None if grad_logprob is None else np.ascontiguousarray(grad_logprob, dtype=np.float32)
+    h = None if grad_entropy is None else np.ascontiguousarray(grad_entropy, dtype=np.float32)
+    for a in (g, h):
+        if a is not None and a.shape != (m,):
+            raise ValueError("gradients must have one entry per output row")
+    grad = np.empty((m, vocab), np.float64)
+    rc = _load().oracle_backward_entropy(_ptr(x), _dtype_code(x), n_rows, vocab, ld,
+                                         _ptr(targets), _ptr(rows), m, _tau(tau), _ptr(g),
+                                         _ptr(h), _ptr(grad))
+    _check(rc, "oracle_backward_entropy")
     return grad
 
 

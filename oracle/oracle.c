@@ -168,6 +168,45 @@ int oracle_backward(const void *logits, int dtype, int64_t n_rows,
     return 0;
 }
 
+int oracle_backward_entropy(const void *logits, int dtype, int64_t n_rows,
+                            int64_t vocab, int64_t ld, const int32_t *targets,
+                            const int32_t *rows, int64_t m, double tau,
+                            const float *grad_logprob,
+                            const float *grad_entropy, double *grad) {
+    if (!logits || !dtype_ok(dtype) || n_rows < 0 || m < 0 || vocab <= 0 ||
+        ld < vocab || !tau_ok(tau) || (grad_logprob && !targets) ||
+        (m && !grad))
+        return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+    if (grad_logprob && (rc = check_targets(targets, rows, m, vocab))) return rc;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t r = row_of(rows, i);
+        double *gi = grad + i * vocab;
+        double g = grad_logprob ? (double)grad_logprob[i] : 0.0;
+        double h = grad_entropy ? (double)grad_entropy[i] : 0.0;
+        if (g == 0.0 && h == 0.0) {
+            for (int64_t j = 0; j < vocab; ++j) gi[j] = 0.0;
+            continue;
+        }
+        double M, S;
+        row_max_sum(logits, dtype, ld, r, 0, vocab, tau, &M, &S);
+        double LSE = M + log(S);
+        double H = row_entropy(logits, dtype, ld, r, vocab, tau, LSE);
+        int64_t t = grad_logprob ? targets[r] : -1;
+        for (int64_t j = 0; j < vocab; ++j) {
+            double z = logit_at(logits, dtype, ld, r, j) / tau;
+            double p = exp(z - LSE);
+            double onehot = (j == t) ? 1.0 : 0.0;
+            /* d logprob / dz_j = onehot_j - p_j;  dH / dz_j = -p_j (z_j - LSE + H). */
+            gi[j] = (g * (onehot - p) - h * p * (z - LSE + H)) / tau;
+        }
+    }
+    return 0;
+}
+
 int oracle_slice_partial(const void *logits_slice, int dtype, int64_t n_rows,
                          int64_t v_local, int64_t ld, int64_t v_start,
                          const int32_t *targets, const int32_t *rows, int64_t m,

@@ -75,6 +75,21 @@ int oracle_backward(const void *logits, int dtype, int64_t n_rows,
                     const float *grad_out, double *grad);
 
 /*
+ * Backward of a loss that uses both outputs of a row:
+ *   L = sum_i g_i * logprob_i + h_i * entropy_i
+ * grad[i * vocab + j] = dL/dx_j
+ *                     = (g_i ([j == t] - p_j) - h_i p_j (z_j - LSE + H)) / tau,
+ * since dH/dz_j = -p_j (log p_j + H) and log p_j = z_j - LSE.  grad_logprob
+ * and grad_entropy are float[m] and each may be NULL (treated as 0); targets
+ * may be NULL when grad_logprob is.  Rows where both are 0 get +0.0.
+ */
+int oracle_backward_entropy(const void *logits, int dtype, int64_t n_rows,
+                            int64_t vocab, int64_t ld, const int32_t *targets,
+                            const int32_t *rows, int64_t m, double tau,
+                            const float *grad_logprob,
+                            const float *grad_entropy, double *grad);
+
+/*
  * Partial of one vocabulary slice: the slice's columns are
  * [v_start, v_start + v_local) of the full vocabulary; logits_slice points at
  * column v_start of row 0 and rows are ld elements apart.  Per output i:

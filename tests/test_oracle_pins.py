@@ -354,3 +354,57 @@ def test_bf16_rne_ties_and_double_rounding():
     }
     for v, want in cases.items():
         assert oracle.bf16_rne(np.array([v]))[0] == want, (v, hex(want))
+
+
+# ----------------------------------------------------------------------------- entropy gradient
+
+
+def test_entropy_grad_matches_torch_autograd(tiny):
+    """d(g lp + h H)/dx against torch fp64 autograd of log_softmax and Categorical entropy."""
+    _, x, t, g = tiny
+    h = np.random.default_rng(4).uniform(-1, 1, x.shape[0]).astype(np.float32)
+    for tau in (1.0, 0.7):
+        gr = oracle.backward_entropy(x, t, g, h, tau=tau)
+        xt = torch.from_numpy(x).double().requires_grad_(True)
+        z = xt / float(np.float32(tau))
+        lp = torch.log_softmax(z, dim=1)[torch.arange(x.shape[0]), torch.from_numpy(t).long()]
+        H = torch.distributions.Categorical(logits=z).entropy()
+        (lp * torch.from_numpy(g).double() + H * torch.from_numpy(h).double()).sum().backward()
+        np.testing.assert_allclose(gr, xt.grad.numpy(), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_entropy_grad_central_finite_differences(tiny, tau):
+    """dH_r/dx_rj by central differences of the oracle's own forward entropy."""
+    _, x, t, _ = tiny
+    V = x.shape[1]
+    h = 2.0 ** -10
+    for r in (2, 40):
+        cols = np.linspace(0, V - 1, 24).astype(int)
+        plus = np.repeat(x[r:r + 1], len(cols), axis=0)
+        minus = plus.copy()
+        plus[np.arange(len(cols)), cols] += np.float32(h)
+        minus[np.arange(len(cols)), cols] -= np.float32(h)
+        step = (plus[np.arange(len(cols)), cols].astype(np.float64)
+                - minus[np.arange(len(cols)), cols].astype(np.float64))
+        tt = np.full(len(cols), t[r], np.int32)
+        hp = oracle.forward(plus, tt, tau=tau, want=("entropy",))["entropy"]
+        hm = oracle.forward(minus, tt, tau=tau, want=("entropy",))["entropy"]
+        fd = (hp - hm) / step
+        gr = oracle.backward_entropy(x[r:r + 1], None, None, np.ones(1, np.float32), tau=tau)[0]
+        np.testing.assert_allclose(gr[cols], fd, rtol=0, atol=1e-8)
+
+
+def test_entropy_grad_rows_sum_to_zero_and_reduce_to_logprob_grad(tiny):
+    _, x, t, g = tiny
+    h = np.random.default_rng(9).uniform(-1, 1, x.shape[0]).astype(np.float32)
+    both = oracle.backward_entropy(x, t, g, h, tau=0.7)
+    assert np.abs(both.sum(axis=1)).max() < x.shape[1] * 1e-16 * 8
+    only_lp = oracle.backward_entropy(x, t, g, None, tau=0.7)
+    np.testing.assert_array_equal(only_lp, oracle.backward(x, t, g, tau=0.7))
+    zero = oracle.backward_entropy(x, t, np.zeros_like(g), np.zeros_like(h))
+    assert np.all(zero == 0.0) and not np.any(np.signbit(zero))
+    # uniform rows have zero entropy gradient (H is at its maximum)
+    u = np.full((2, 64), 0.5, np.float32)
+    gu = oracle.backward_entropy(u, None, None, np.ones(2, np.float32))
+    assert np.abs(gu).max() < 1e-15

@@ -172,6 +172,8 @@ def bench_other(args, w, x):
                        M * (V * e + 20)))
         if w.mask == "packed":
             gc = torch.from_numpy(g_all[W.row_index(w)]).to(dev)
+            hc = torch.from_numpy(np.random.default_rng(8).uniform(-1, 1, M)
+                                  .astype(np.float32)).to(dev)
             grad = torch.empty((M, V), dtype=x.dtype, device=dev)
             passes.append(("bwd_rows(compact)",
                            lambda: vwc.selected_logprob_bwd_rows(x, t, idx, lse, gc, w.tau,
@@ -179,6 +181,12 @@ def bench_other(args, w, x):
                                                                  layout=vwc.VWC_GRAD_COMPACT,
                                                                  stream=stream),
                            M * (2 * V * e + 16)))
+            passes.append(("bwd_rows(logprob+entropy grads, compact)",
+                           lambda: vwc.logprob_entropy_bwd_rows(x, t, idx, lse, ent, gc, hc,
+                                                                w.tau, grad_logits=grad,
+                                                                layout=vwc.VWC_GRAD_COMPACT,
+                                                                stream=stream),
+                           M * (2 * V * e + 24)))
     elif w.n_slices > 1:
         k, vl = w.n_slices, V // w.n_slices
         parts = torch.empty((k, N, 4), dtype=torch.float32, device=dev)

@@ -191,6 +191,40 @@ vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64
                                          vwc_grad_layout layout, hipStream_t stream);
 
 /*
+ * Backward of a loss that uses both forward outputs of a row,
+ *   L = sum_r g_r * logprob_r + h_r * entropy_r,
+ * fused into the same single pass over the logits:
+ *   grad[r, j] = (g_r ([j == t_r] - p_rj) - h_r p_rj (z_rj - lse_r + H_r)) / tau,
+ * since dH/dz_j = -p_j (log p_j + H).  The pages' RL losses consume both the
+ * log-probabilities and the entropy of the same logits ([D] "Bug
+ * Description": get_log_probs_and_entropy; maintainer comment).
+ *  lse, entropy   float[n_rows] from the forward at the same temperature
+ *                 (entropy may be NULL when grad_entropy is NULL).
+ *  grad_logprob   float[n_rows] (g) or NULL (g = 0; targets may then be NULL).
+ *  grad_entropy   float[n_rows] (h) or NULL (h = 0: same result as
+ *                 vwc_selected_logprob_bwd).  At least one must be non-NULL.
+ * Rows with g == 0 and h == 0 are written as +0.0 without reading the logits.
+ * Other arguments as vwc_selected_logprob_bwd.
+ */
+vwc_status vwc_logprob_entropy_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                                   int64_t ld, const int32_t *targets, float temperature,
+                                   const float *lse, const float *entropy,
+                                   const float *grad_logprob, const float *grad_entropy,
+                                   void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                   hipStream_t stream);
+
+/* The same over the compact row set row_idx[0..m): lse, entropy,
+   grad_logprob and grad_entropy are float[m]; layout as in
+   vwc_selected_logprob_bwd_rows. */
+vwc_status vwc_logprob_entropy_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                        int64_t vocab, int64_t ld, const int32_t *targets,
+                                        const int32_t *row_idx, int64_t m, float temperature,
+                                        const float *lse, const float *entropy,
+                                        const float *grad_logprob, const float *grad_entropy,
+                                        void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                        vwc_grad_layout layout, hipStream_t stream);
+
+/*
  * Partial of one vocabulary slice ([E] "Implementation", steps 1-3 in one
  * pass).  logits_slice points at global column v_start of row 0; the slice is
  * columns [0, v_local) of each row, rows ld elements apart.  targets hold

@@ -49,6 +49,9 @@ def _load() -> ctypes.CDLL:
         "vwc_selected_logprob_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, i32, i64, p], i32),
         "vwc_selected_logprob_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, i32,
                                            i64, i32, p], i32),
+        "vwc_logprob_entropy_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64, p], i32),
+        "vwc_logprob_entropy_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, p, i32,
+                                          i64, i32, p], i32),
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
@@ -226,6 +229,47 @@ def selected_logprob_bwd_rows(logits, targets, row_idx, lse, grad_logprob, tempe
                                               float(temperature), _ptr(lse), _ptr(grad_logprob),
                                               _ptr(grad_logits), _dtype(grad_logits), gld,
                                               layout, _stream(stream, logits)))
+    return grad_logits
+
+
+def logprob_entropy_bwd(logits, targets, lse, entropy, grad_logprob=None, grad_entropy=None,
+                        temperature=1.0, grad_logits=None, grad_dtype=None, stream=None):
+    """Dense backward of sum_r g_r logprob_r + h_r entropy_r (g or h may be None)."""
+    n, v, ld = _rows_view(logits)
+    if targets is not None:
+        _i32(targets, "targets")
+    g = _grad_out(logits, n, grad_logits, grad_dtype)
+    gn, gv, gld = _rows_view(g)
+    if gn != n or gv < v:
+        raise ValueError("grad_logits must be [n_rows, >= vocab]")
+    _check(_lib.vwc_logprob_entropy_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(targets),
+                                        float(temperature), _ptr(lse), _ptr(entropy),
+                                        _ptr(grad_logprob), _ptr(grad_entropy), _ptr(g), _dtype(g),
+                                        gld, _stream(stream, logits)))
+    return g
+
+
+def logprob_entropy_bwd_rows(logits, targets, row_idx, lse, entropy, grad_logprob=None,
+                             grad_entropy=None, temperature=1.0, grad_logits=None, grad_dtype=None,
+                             layout=VWC_GRAD_COMPACT, stream=None):
+    """Compact-row version of logprob_entropy_bwd (lse/entropy/gradients are [m])."""
+    n, v, ld = _rows_view(logits)
+    if targets is not None:
+        _i32(targets, "targets")
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    if grad_logits is None:
+        rows = m if layout == VWC_GRAD_COMPACT else n
+        grad_logits = _grad_out(logits, rows, None, grad_dtype)
+        if layout == VWC_GRAD_SCATTER:
+            grad_logits.zero_()
+    _, gv, gld = _rows_view(grad_logits)
+    _check(_lib.vwc_logprob_entropy_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
+                                             _ptr(targets), _ptr(row_idx), m, float(temperature),
+                                             _ptr(lse), _ptr(entropy), _ptr(grad_logprob),
+                                             _ptr(grad_entropy), _ptr(grad_logits),
+                                             _dtype(grad_logits), gld, layout,
+                                             _stream(stream, logits)))
     return grad_logits
 
 

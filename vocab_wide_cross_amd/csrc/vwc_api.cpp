@@ -142,7 +142,8 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
 vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n_rows,
                            int64_t vocab, int64_t ld, const int32_t *targets,
                            const int32_t *row_idx, int64_t m, float temperature, const float *lse,
-                           const float *grad_logprob, void *grad_logits, int grad_dt,
+                           const float *entropy, const float *grad_logprob,
+                           const float *grad_entropy, void *grad_logits, int grad_dt,
                            int64_t ld_grad, bool by_row_id, hipStream_t stream) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
@@ -153,9 +154,12 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     if (!row_idx && m != n_rows)
         return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
     if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
-    if (!targets || !lse || !grad_logprob || !grad_logits)
-        return fail(VWC_ERR_INVALID_ARG, "%s: null targets, lse, grad_logprob or grad_logits",
-                    fn);
+    if (!grad_logprob && !grad_entropy)
+        return fail(VWC_ERR_INVALID_ARG, "%s: no incoming gradient", fn);
+    if (grad_logprob && !targets) return fail(VWC_ERR_INVALID_ARG, "%s: targets is null", fn);
+    if (grad_entropy && !entropy) return fail(VWC_ERR_INVALID_ARG, "%s: entropy is null", fn);
+    if (!lse || !grad_logits)
+        return fail(VWC_ERR_INVALID_ARG, "%s: null lse or grad_logits", fn);
     if (reinterpret_cast<uintptr_t>(grad_logits) % esize(grad_dt) != 0)
         return fail(VWC_ERR_UNSUPPORTED, "%s: grad_logits not aligned to its dtype", fn);
     if (ld_grad > INT64_MAX / 16 / n_rows)
@@ -187,6 +191,8 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     p.c = static_cast<float>(1.44269504088896340736 / p.tau);
     p.lse = lse;
     p.grad_out = grad_logprob;
+    p.entropy = entropy;
+    p.grad_ent = grad_entropy;
     p.grad = grad_logits;
     p.ld_grad = ld_grad;
     p.grad_by_row_id = by_row_id;
@@ -259,9 +265,11 @@ vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_
                                     float temperature, const float *lse,
                                     const float *grad_logprob, void *grad_logits,
                                     vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream) {
+    if (n_rows > 0 && !grad_logprob)
+        return fail(VWC_ERR_INVALID_ARG, "vwc_selected_logprob_bwd: grad_logprob is null");
     return backward_common("vwc_selected_logprob_bwd", logits, dt, n_rows, vocab, ld, targets,
-                           nullptr, n_rows, temperature, lse, grad_logprob, grad_logits, grad_dt,
-                           ld_grad, true, stream);
+                           nullptr, n_rows, temperature, lse, nullptr, grad_logprob, nullptr,
+                           grad_logits, grad_dt, ld_grad, true, stream);
 }
 
 vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
@@ -274,9 +282,37 @@ vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64
     if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
         return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
     if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    if (m > 0 && !grad_logprob) return fail(VWC_ERR_INVALID_ARG, "%s: grad_logprob is null", fn);
     return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
-                           lse, grad_logprob, grad_logits, grad_dt, ld_grad,
+                           lse, nullptr, grad_logprob, nullptr, grad_logits, grad_dt, ld_grad,
                            layout == VWC_GRAD_SCATTER, stream);
+}
+
+vwc_status vwc_logprob_entropy_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                                   int64_t ld, const int32_t *targets, float temperature,
+                                   const float *lse, const float *entropy,
+                                   const float *grad_logprob, const float *grad_entropy,
+                                   void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                   hipStream_t stream) {
+    return backward_common("vwc_logprob_entropy_bwd", logits, dt, n_rows, vocab, ld, targets,
+                           nullptr, n_rows, temperature, lse, entropy, grad_logprob, grad_entropy,
+                           grad_logits, grad_dt, ld_grad, true, stream);
+}
+
+vwc_status vwc_logprob_entropy_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                        int64_t vocab, int64_t ld, const int32_t *targets,
+                                        const int32_t *row_idx, int64_t m, float temperature,
+                                        const float *lse, const float *entropy,
+                                        const float *grad_logprob, const float *grad_entropy,
+                                        void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                        vwc_grad_layout layout, hipStream_t stream) {
+    const char *fn = "vwc_logprob_entropy_bwd_rows";
+    if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
+                           lse, entropy, grad_logprob, grad_entropy, grad_logits, grad_dt,
+                           ld_grad, layout == VWC_GRAD_SCATTER, stream);
 }
 
 vwc_status vwc_vocab_partial(const void *logits_slice, vwc_dtype dt, int64_t n_rows,

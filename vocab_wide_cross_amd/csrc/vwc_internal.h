@@ -78,7 +78,9 @@ struct BwdPlan {
     float c;
     double tau;
     const float *lse;         // [m]
-    const float *grad_out;    // [m]
+    const float *grad_out;    // [m] incoming d/d logprob, or null (0)
+    const float *entropy;     // [m] the forward's entropy (entropy gradient only)
+    const float *grad_ent;    // [m] incoming d/d entropy, or null (0)
     void *grad;
     int64_t ld_grad;
     bool grad_by_row_id;      // true: gradient row = row id; false: = output index

@@ -592,35 +592,45 @@ struct RowGrad {
     float c;       // log2(e) / tau
     float B;       // lse * log2(e), rounded to float
     float gs;      // -g / tau
+    float a, b;    // entropy gradient: o = p * (a + b u) with u = x c - B
     double gt;     // g / tau
+    double hs;     // -h / tau
+    double H;      // the saved entropy, widened
     double lse;    // the saved logZ, widened
     double tau;
-    int32_t t;     // target column
+    int32_t t;     // target column (-1: no logprob term)
 };
 
-// Gradient of one unit: o_k = gs * p_k with p_k = exp2(x_k c - B) (exp2f keeps
-// denormal results).  The target column gets g/tau * (1 - p_t), computed as
-// -expm1(x_t / tau - lse) in fp64 so that p_t -> 1 does not cancel (a row
-// with a single column gets exactly 0).
-template <int DT, bool VEC>
+// Gradient of one unit.  Logprob only: o_k = gs p_k with p_k = exp2(x_k c - B)
+// (exp2f keeps denormal results).  With the entropy term (WH):
+//   o_k = p_k (-g/tau - h/tau (z_k - lse + H)) = p_k (a + b u_k),
+// u_k = x_k c - B = (z_k - lse) log2(e), a = -(g + h H)/tau, b = -h ln2/tau.
+// The target column adds g/tau (1 - p_t), computed as -expm1(x_t/tau - lse) in
+// fp64 so that p_t -> 1 does not cancel.
+template <int DT, bool VEC, bool WH>
 __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, int32_t col0,
                                           const RowGrad &R, float (&o)[Unit<DT, VEC>::N]) {
     using Un = Unit<DT, VEC>;
 #pragma unroll
-    for (int k = 0; k < Un::N; ++k)
-        o[k] = exp2f(__builtin_fmaf(Un::get(v, k), R.c, -R.B)) * R.gs;
+    for (int k = 0; k < Un::N; ++k) {
+        const float u = __builtin_fmaf(Un::get(v, k), R.c, -R.B);
+        const float pk = exp2f(u);
+        o[k] = WH ? pk * __builtin_fmaf(R.b, u, R.a) : pk * R.gs;
+    }
     if (static_cast<uint32_t>(R.t - col0) < static_cast<uint32_t>(Un::N)) {
 #pragma unroll
         for (int k = 0; k < Un::N; ++k)
             if (col0 + k == R.t) {
                 const double d = static_cast<double>(Un::get(v, k)) / R.tau - R.lse;
-                o[k] = static_cast<float>(R.gt * -expm1(d));
+                double ot = R.gt * -expm1(d);
+                if (WH) ot += R.hs * exp(d) * (d + R.H);
+                o[k] = static_cast<float>(ot);
             }
     }
 }
 
 // Gradient of segment q of output row i.
-template <int DT, int GDT, bool VEC>
+template <int DT, int GDT, bool VEC, bool WH>
 __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     using Un = Unit<DT, VEC>;
     using T = typename Un::T;
@@ -637,9 +647,10 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     const int32_t u0 = q * p.seg_units;
     const int32_t u1 = min(u0 + p.seg_units, nunits);
     const bool last = q == p.nseg - 1;
-    const float g = p.grad_out[i];
+    const float g = p.grad_out ? p.grad_out[i] : 0.f;
+    const float h = WH ? p.grad_ent[i] : 0.f;
 
-    if (g == 0.f) {
+    if (g == 0.f && h == 0.f) {
         // Rows without loss: +0.0, no logits read.
         float z[N];
 #pragma unroll
@@ -663,7 +674,11 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     R.gs = static_cast<float>(-R.gt);
     R.lse = static_cast<double>(p.lse[i]);
     R.B = static_cast<float>(R.lse * kLog2e);
-    R.t = p.targets[r];
+    R.hs = -static_cast<double>(h) / p.tau;
+    R.H = WH ? static_cast<double>(p.entropy[i]) : 0.0;
+    R.a = static_cast<float>(-R.gt + R.hs * R.H);
+    R.b = static_cast<float>(R.hs * kLn2);
+    R.t = g != 0.f ? p.targets[r] : -1;
     const T *src = reinterpret_cast<const T *>(row);
 
     int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
@@ -675,14 +690,14 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         for (int j = 0; j < U; ++j) {
             const int32_t unit = b + j * kBwdBlock;
             float o[N];
-            unit_grad<DT, VEC>(v[j], unit * N, R, o);
+            unit_grad<DT, VEC, WH>(v[j], unit * N, R, o);
             GradStore<GDT, N>::store(grow + static_cast<int64_t>(unit) * N * kGE, o);
         }
     }
     for (; b < u1; b += kBwdBlock) {
         const T v = Un::load(src + b);
         float o[N];
-        unit_grad<DT, VEC>(v, b * N, R, o);
+        unit_grad<DT, VEC, WH>(v, b * N, R, o);
         GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, o);
     }
     if (VEC && last) {
@@ -691,17 +706,17 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
             using Us = Unit<DT, false>;
             const typename Us::T v = reinterpret_cast<const typename Us::T *>(row)[j];
             float o[1];
-            unit_grad<DT, false>(v, j, R, o);
+            unit_grad<DT, false, WH>(v, j, R, o);
             GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, o);
         }
     }
 }
 
 // One workgroup per (row, segment) item.
-template <int DT, int GDT, bool VEC>
+template <int DT, int GDT, bool VEC, bool WH>
 __global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(BwdPlan p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
-    bwd_item<DT, GDT, VEC>(p, i, static_cast<int>(blockIdx.x - i * p.nseg));
+    bwd_item<DT, GDT, VEC, WH>(p, i, static_cast<int>(blockIdx.x - i * p.nseg));
 }
 
 // ---------------------------------------------------------------- mask -> index
@@ -782,10 +797,18 @@ hipError_t launch_fwd_dt(const FwdPlan &p, hipStream_t s) {
 template <int DT, int GDT>
 hipError_t launch_bwd_dt(const BwdPlan &p, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBwdBlock);
-    if (p.vector)
-        hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, false>), grid, block, 0, s, p);
+    const bool wh = p.grad_ent != nullptr;
+    if (p.vector) {
+        if (wh)
+            hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true, false>), grid, block, 0, s, p);
+    } else {
+        if (wh)
+            hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, false, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, false, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -63,6 +63,10 @@ def _load():
         lib.oracle_backward.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, d, p, p]
         lib.oracle_backward_entropy.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, d, p,
                                                 p, p]
+        lib.oracle_topk_kl_forward.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64,
+                                               ctypes.c_int, d, d, p, p, p]
+        lib.oracle_topk_kl_backward.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64,
+                                                ctypes.c_int, d, d, p, p]
         lib.oracle_slice_partial.argtypes = [p, ctypes.c_int, i64, i64, i64, i64, p, p, i64, d,
                                              p, p, p, p]
         lib.oracle_combine.argtypes = [i64, i64, p, p, p, p, p, p, p]
@@ -73,6 +77,7 @@ def _load():
         lib.oracle_bf16_rne_array.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_forward", "oracle_backward", "oracle_backward_entropy",
+                  "oracle_topk_kl_forward", "oracle_topk_kl_backward",
                   "oracle_slice_partial", "oracle_combine", "oracle_forward_vchunk"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -189,6 +194,44 @@ def backward_entropy(x: np.ndarray, targets, grad_logprob, grad_entropy, tau: fl
                                          _ptr(targets), _ptr(rows), m, _tau(tau), _ptr(g),
                                          _ptr(h), _ptr(grad))
     _check(rc, "oracle_backward_entropy")
+    return grad
+
+
+KL_TRUNCATED = 0
+KL_TAIL = 1
+
+
+def topk_kl_forward(x: np.ndarray, topk_idx, teacher_logprob, mode: int, tail_eps: float = 1e-6,
+                    tau: float = 1.0, vocab: int | None = None):
+    """Per-row top-k KL loss, student top-k mass Q and teacher mass P (float64)."""
+    x = np.ascontiguousarray(x)
+    n_rows, ld = x.shape
+    vocab = ld if vocab is None else vocab
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    tlp = np.ascontiguousarray(teacher_logprob, dtype=np.float32)
+    k = idx.shape[1]
+    loss, q, pm = (np.empty(n_rows, np.float64) for _ in range(3))
+    rc = _load().oracle_topk_kl_forward(_ptr(x), _dtype_code(x), n_rows, vocab, ld, _ptr(idx),
+                                        _ptr(tlp), k, int(mode), float(tail_eps), _tau(tau),
+                                        _ptr(loss), _ptr(q), _ptr(pm))
+    _check(rc, "oracle_topk_kl_forward")
+    return {"loss": loss, "student_mass": q, "teacher_mass": pm}
+
+
+def topk_kl_backward(x: np.ndarray, topk_idx, teacher_logprob, mode: int, grad_loss,
+                     tail_eps: float = 1e-6, tau: float = 1.0, vocab: int | None = None):
+    """[n_rows, vocab] float64 gradient of sum_i g_i L_i w.r.t. the student logits."""
+    x = np.ascontiguousarray(x)
+    n_rows, ld = x.shape
+    vocab = ld if vocab is None else vocab
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    tlp = np.ascontiguousarray(teacher_logprob, dtype=np.float32)
+    g = np.ascontiguousarray(grad_loss, dtype=np.float32)
+    grad = np.empty((n_rows, vocab), np.float64)
+    rc = _load().oracle_topk_kl_backward(_ptr(x), _dtype_code(x), n_rows, vocab, ld, _ptr(idx),
+                                         _ptr(tlp), idx.shape[1], int(mode), float(tail_eps),
+                                         _tau(tau), _ptr(g), _ptr(grad))
+    _check(rc, "oracle_topk_kl_backward")
     return grad
 
 

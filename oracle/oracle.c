@@ -207,6 +207,127 @@ int oracle_backward_entropy(const void *logits, int dtype, int64_t n_rows,
     return 0;
 }
 
+/* 0 log 0 = 0 */
+static double xlogx_term(double a, double log_a) { return a == 0.0 ? 0.0 : a * log_a; }
+
+static int topk_args_ok(const void *logits, int dtype, int64_t n_rows, int64_t vocab,
+                        int64_t ld, const int32_t *topk_idx,
+                        const float *teacher_logprob, int64_t k, int mode,
+                        double tail_eps, double tau) {
+    if (!logits || !dtype_ok(dtype) || n_rows < 0 || vocab <= 0 || ld < vocab ||
+        !tau_ok(tau) || k <= 0 || k > vocab || (mode != 0 && mode != 1))
+        return -1;
+    if (n_rows > 0 && (!topk_idx || !teacher_logprob)) return -1;
+    if (mode == 1 && !(tail_eps > 0.0 && tail_eps < 1.0)) return -1;
+    for (int64_t i = 0; i < n_rows * k; ++i)
+        if (topk_idx[i] < 0 || (int64_t)topk_idx[i] >= vocab) return -2;
+    return 0;
+}
+
+/* Per-row pieces of the top-k KL: LSE, P, Q and the loss. */
+static void topk_row(const void *logits, int dtype, int64_t ld, int64_t i,
+                     int64_t vocab, const int32_t *idx, const float *tlp,
+                     int64_t k, int mode, double tail_eps, double tau,
+                     double *LSE_out, double *P_out, double *Q_out,
+                     double *L_out) {
+    double M, S;
+    row_max_sum(logits, dtype, ld, i, 0, vocab, tau, &M, &S);
+    double LSE = M + log(S);
+    double P = 0.0, Q = 0.0, L = 0.0;
+    for (int64_t n = 0; n < k; ++n) {
+        double a = (double)tlp[n];
+        double p = exp(a);
+        double logq = logit_at(logits, dtype, ld, i, idx[n]) / tau - LSE;
+        P += p;
+        Q += exp(logq);
+        L += p * (a - logq);
+    }
+    if (mode == 0) {
+        if (L < 0.0) L = 0.0; /* clamp_min(0) of the truncated objective */
+    } else {
+        /* A payload whose fp32 log-probs sum above 1 has an empty tail. */
+        double pt = P < 1.0 ? 1.0 - P : 0.0;
+        double qt = 1.0 - Q;
+        if (qt < tail_eps) qt = tail_eps;
+        L += xlogx_term(pt, log(pt)) - (pt == 0.0 ? 0.0 : pt * log(qt));
+    }
+    *LSE_out = LSE;
+    *P_out = P;
+    *Q_out = Q;
+    *L_out = L;
+}
+
+int oracle_topk_kl_forward(const void *logits, int dtype, int64_t n_rows,
+                           int64_t vocab, int64_t ld, const int32_t *topk_idx,
+                           const float *teacher_logprob, int64_t k, int mode,
+                           double tail_eps, double tau, double *loss,
+                           double *student_mass, double *teacher_mass) {
+    int rc = topk_args_ok(logits, dtype, n_rows, vocab, ld, topk_idx,
+                          teacher_logprob, k, mode, tail_eps, tau);
+    if (rc) return rc;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        double LSE, P, Q, L;
+        topk_row(logits, dtype, ld, i, vocab, topk_idx + i * k,
+                 teacher_logprob + i * k, k, mode, tail_eps, tau, &LSE, &P, &Q, &L);
+        if (loss) loss[i] = L;
+        if (student_mass) student_mass[i] = Q;
+        if (teacher_mass) teacher_mass[i] = P;
+    }
+    return 0;
+}
+
+int oracle_topk_kl_backward(const void *logits, int dtype, int64_t n_rows,
+                            int64_t vocab, int64_t ld, const int32_t *topk_idx,
+                            const float *teacher_logprob, int64_t k, int mode,
+                            double tail_eps, double tau, const float *grad_loss,
+                            double *grad) {
+    int rc = topk_args_ok(logits, dtype, n_rows, vocab, ld, topk_idx,
+                          teacher_logprob, k, mode, tail_eps, tau);
+    if (rc) return rc;
+    if (n_rows > 0 && (!grad_loss || !grad)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int32_t *idx = topk_idx + i * k;
+        const float *tlp = teacher_logprob + i * k;
+        double *gi = grad + i * vocab;
+        double LSE, P, Q, L;
+        topk_row(logits, dtype, ld, i, vocab, idx, tlp, k, mode, tail_eps, tau,
+                 &LSE, &P, &Q, &L);
+        double g = (double)grad_loss[i];
+        /* the truncated loss before its clamp: a clamped row has no gradient */
+        double Lraw = 0.0;
+        for (int64_t n = 0; n < k; ++n) {
+            double a = (double)tlp[n];
+            Lraw += exp(a) * (a - (logit_at(logits, dtype, ld, i, idx[n]) / tau - LSE));
+        }
+        int row_dead = (mode == 0 && Lraw < 0.0) || g == 0.0;
+        /* dL/d log q_{T_n} = -p_n;  tail: dL/d log qtail = -(1 - P), active guard: 0 */
+        double dl_dlogqt = 0.0;
+        if (mode == 1 && 1.0 - Q >= tail_eps) dl_dlogqt = -(P < 1.0 ? 1.0 - P : 0.0);
+        for (int64_t j = 0; j < vocab; ++j) {
+            if (row_dead) {
+                gi[j] = 0.0;
+                continue;
+            }
+            double qj = exp(logit_at(logits, dtype, ld, i, j) / tau - LSE);
+            double in_t = 0.0;
+            double d = 0.0;
+            for (int64_t n = 0; n < k; ++n) {
+                double p = exp((double)tlp[n]);
+                double dlogq = (idx[n] == j ? 1.0 : 0.0) - qj; /* d log q_{T_n} / dz_j */
+                d += -p * dlogq;
+                if (idx[n] == j) in_t = 1.0;
+            }
+            /* d log qtail / dz_j = -(q_j [j in T] - q_j Q) / (1 - Q) */
+            if (dl_dlogqt != 0.0)
+                d += dl_dlogqt * (-(qj * in_t - qj * Q) / (1.0 - Q));
+            gi[j] = g * d / tau;
+        }
+    }
+    return 0;
+}
+
 int oracle_slice_partial(const void *logits_slice, int dtype, int64_t n_rows,
                          int64_t v_local, int64_t ld, int64_t v_start,
                          const int32_t *targets, const int32_t *rows, int64_t m,

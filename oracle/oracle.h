@@ -90,6 +90,40 @@ int oracle_backward_entropy(const void *logits, int dtype, int64_t n_rows,
                             const float *grad_entropy, double *grad);
 
 /*
+ * Top-k forward KL of a teacher payload against the student softmax
+ * ("[megatron] feat: add memory-efficient chunked top-k KL computation",
+ * commit text of the tail-aware top-k KL change, "What does this PR do?").
+ * Per row i: T = topk_idx[i*k .. i*k+k) (distinct student columns), teacher
+ * log-probs a_n = teacher_logprob[i*k + n], p_n = exp(a_n), student
+ * q_j = exp(z_j - LSE).  P = sum_n p_n, Q = sum_n q_{T_n},
+ *   truncated:  L = max(0, sum_n p_n (a_n - log q_{T_n}))
+ *   tail:       L = sum_n p_n (a_n - log q_{T_n})
+ *                   + (1 - P) (log(1 - P) - log(max(1 - Q, eps)))
+ * with 0 log 0 = 0, and 1 - P read as max(0, 1 - P) (a payload whose fp32
+ * log-probs sum above 1 has an empty tail).  Outputs (each nullable) loss[i], student_mass[i] = Q,
+ * teacher_mass[i] = P.  mode: 0 truncated, 1 tail.
+ */
+int oracle_topk_kl_forward(const void *logits, int dtype, int64_t n_rows,
+                           int64_t vocab, int64_t ld, const int32_t *topk_idx,
+                           const float *teacher_logprob, int64_t k, int mode,
+                           double tail_eps, double tau, double *loss,
+                           double *student_mass, double *teacher_mass);
+
+/*
+ * Gradient of sum_i g_i L_i with respect to the student logits, from the
+ * definition: L as a function of log q_{T_n} and, in tail mode, of
+ * log max(1 - Q, eps) (whose derivative is 0 while the guard is active), with
+ * d log q_i / dz_j = [i == j] - q_j and dQ/dz_j = q_j [j in T] - q_j Q; then
+ * d/dx = d/dz / tau.  A truncated row whose loss is clamped gets 0.
+ * grad is [n_rows][vocab]; grad_loss is float[n_rows].
+ */
+int oracle_topk_kl_backward(const void *logits, int dtype, int64_t n_rows,
+                            int64_t vocab, int64_t ld, const int32_t *topk_idx,
+                            const float *teacher_logprob, int64_t k, int mode,
+                            double tail_eps, double tau, const float *grad_loss,
+                            double *grad);
+
+/*
  * Partial of one vocabulary slice: the slice's columns are
  * [v_start, v_start + v_local) of the full vocabulary; logits_slice points at
  * column v_start of row 0 and rows are ld elements apart.  Per output i:

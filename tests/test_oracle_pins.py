@@ -408,3 +408,136 @@ def test_entropy_grad_rows_sum_to_zero_and_reduce_to_logprob_grad(tiny):
     u = np.full((2, 64), 0.5, np.float32)
     gu = oracle.backward_entropy(u, None, None, np.ones(2, np.float32))
     assert np.abs(gu).max() < 1e-15
+
+
+# ----------------------------------------------------------------------------- top-k KL
+# Source: "[megatron] feat: add memory-efficient chunked top-k KL computation", commit
+# text of the tail-aware top-k KL change ("What does this PR do?", "Design & Code Changes").
+
+
+@pytest.fixture(scope="module")
+def distill():
+    w = W.get("distill_fp32_192x2048_k32")
+    x = W.all_logits(w)[:48]
+    idx, tlp = W.topk_payload_rows(w, np.arange(48))
+    return x, idx, tlp
+
+
+def _torch_kl(x, idx, tlp, mode, eps, tau):
+    """The loss written independently in torch (fp64): log_softmax + gather."""
+    xt = torch.from_numpy(x).double().requires_grad_(True)
+    logq = torch.log_softmax(xt / float(np.float32(tau)), dim=1)
+    lq = logq.gather(1, torch.from_numpy(idx).long())
+    a = torch.from_numpy(tlp).double()
+    p = a.exp()
+    L = (p * (a - lq)).sum(1)
+    if mode == oracle.KL_TRUNCATED:
+        L = L.clamp_min(0.0)
+    else:
+        P, Q = p.sum(1), lq.exp().sum(1)
+        pt, qt = 1 - P, (1 - Q).clamp_min(eps)
+        L = L + torch.where(pt > 0, pt * (pt.log() - qt.log()), torch.zeros_like(pt))
+    return xt, L
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_topk_kl_matches_torch_autograd(distill, mode, tau):
+    x, idx, tlp = distill
+    g = np.random.default_rng(2).uniform(-1, 1, x.shape[0]).astype(np.float32)
+    o = oracle.topk_kl_forward(x, idx, tlp, mode, tau=tau)
+    gr = oracle.topk_kl_backward(x, idx, tlp, mode, g, tau=tau)
+    xt, L = _torch_kl(x, idx, tlp, mode, 1e-6, tau)
+    np.testing.assert_allclose(o["loss"], L.detach().numpy(), rtol=0, atol=1e-12)
+    (L * torch.from_numpy(g).double()).sum().backward()
+    np.testing.assert_allclose(gr, xt.grad.numpy(), rtol=0, atol=1e-14)
+
+
+def test_topk_kl_tail_gradient_closed_form(distill):
+    """The page's analytic gradient: q_j - p_j inside the teacher top-k,
+    q_j (P - Q) / (1 - Q) outside."""
+    x, idx, tlp = distill
+    g = np.ones(x.shape[0], np.float32)
+    gr = oracle.topk_kl_backward(x, idx, tlp, oracle.KL_TAIL, g)
+    o = oracle.topk_kl_forward(x, idx, tlp, oracle.KL_TAIL)
+    z = x.astype(np.float64)
+    q = np.exp(z - z.max(1, keepdims=True))
+    q /= q.sum(1, keepdims=True)
+    P, Q = o["teacher_mass"], o["student_mass"]
+    want = q * ((P - Q) / (1 - Q))[:, None]
+    rows = np.arange(x.shape[0])[:, None]
+    want[rows, idx] = q[rows, idx] - np.exp(tlp.astype(np.float64))
+    np.testing.assert_allclose(gr, want, rtol=0, atol=1e-14)
+
+
+def test_topk_kl_finite_differences(distill):
+    x, idx, tlp = distill
+    V = x.shape[1]
+    hh = 2.0 ** -10
+    for mode in (0, 1):
+        r = 5
+        cols = np.unique(np.concatenate([idx[r, :4], np.linspace(0, V - 1, 12).astype(int)]))
+        plus = np.repeat(x[r:r + 1], len(cols), axis=0)
+        minus = plus.copy()
+        plus[np.arange(len(cols)), cols] += np.float32(hh)
+        minus[np.arange(len(cols)), cols] -= np.float32(hh)
+        step = (plus[np.arange(len(cols)), cols].astype(np.float64)
+                - minus[np.arange(len(cols)), cols].astype(np.float64))
+        rep = lambda a: np.repeat(a[r:r + 1], len(cols), axis=0)
+        lp = oracle.topk_kl_forward(plus, rep(idx), rep(tlp), mode)["loss"]
+        lm = oracle.topk_kl_forward(minus, rep(idx), rep(tlp), mode)["loss"]
+        gr = oracle.topk_kl_backward(x[r:r + 1], idx[r:r + 1], tlp[r:r + 1], mode,
+                                     np.ones(1, np.float32))[0]
+        np.testing.assert_allclose(gr[cols], (lp - lm) / step, rtol=0, atol=1e-8)
+
+
+def test_topk_kl_full_vocabulary_and_lower_bound():
+    """With K = V the tail-aware loss is the full forward KL; with K < V it is a
+    non-negative lower bound of it, growing with K."""
+    rng = np.random.default_rng(3)
+    V = 512
+    x = rng.standard_normal((6, V)).astype(np.float32)
+    w = rng.exponential(size=(6, V)) ** 3
+    pfull = w / w.sum(1, keepdims=True)
+    z = x.astype(np.float64)
+    logq = z - z.max(1, keepdims=True)
+    logq -= np.log(np.exp(logq).sum(1, keepdims=True))
+    kl_full = (pfull * (np.log(pfull) - logq)).sum(1)
+    prev = np.zeros(6)
+    for K in (8, 32, 128, V):
+        order = np.argsort(-pfull, axis=1)[:, :K]
+        tlp = np.log(np.take_along_axis(pfull, order, 1)).astype(np.float32)
+        o = oracle.topk_kl_forward(x, order.astype(np.int32), tlp, oracle.KL_TAIL)
+        assert np.all(o["loss"] >= -1e-12)
+        assert np.all(o["loss"] <= kl_full + 1e-6)
+        assert np.all(o["loss"] >= prev - 1e-6)  # more categories: the bound tightens
+        prev = o["loss"]
+    # K = V: equal to the full KL up to the fp32 rounding of the payload log-probs
+    np.testing.assert_allclose(prev, kl_full, rtol=0, atol=1e-5)
+
+
+def test_topk_kl_truncated_clamp_and_tail_guard():
+    """A student that puts more top-k mass than the teacher (Q > P) makes the
+    truncated sum negative: clamped to 0 with zero gradient.  A student with
+    1 - Q below eps turns the tail term's gradient off."""
+    V, K = 256, 8
+    idx = np.arange(K, dtype=np.int32)[None].repeat(2, 0)
+    tlp = np.log(np.full((2, K), 0.5 / K)).astype(np.float32)     # P = 0.5
+    x = np.zeros((2, V), np.float32)
+    x[0, :K] = 6.0                                                # Q ~ 0.93 > P
+    x[1, :K] = 40.0                                               # 1 - Q ~ 1e-15 < eps
+    tr = oracle.topk_kl_forward(x, idx, tlp, oracle.KL_TRUNCATED)
+    assert tr["loss"][0] == 0.0 and tr["student_mass"][0] > 0.5
+    gtr = oracle.topk_kl_backward(x, idx, tlp, oracle.KL_TRUNCATED, np.ones(2, np.float32))
+    assert np.all(gtr[0] == 0.0)
+    tl = oracle.topk_kl_forward(x, idx, tlp, oracle.KL_TAIL, tail_eps=1e-6)
+    assert np.all(tl["loss"] > 0)
+    gtl = oracle.topk_kl_backward(x, idx, tlp, oracle.KL_TAIL, np.ones(2, np.float32),
+                                  tail_eps=1e-6)
+    # guard active on row 1: the gradient is the truncated one, q_j P - p_j [j in T]
+    z = x[1].astype(np.float64)
+    q = np.exp(z - z.max())
+    q /= q.sum()
+    want = q * 0.5
+    want[:K] -= 0.5 / K
+    np.testing.assert_allclose(gtl[1], want, rtol=0, atol=1e-15)

@@ -57,6 +57,8 @@ class Workload:
     grad: str = "uniform"          # grad_out ~ U(-1, 1)
     grad_zero_prob: float = 0.0    # rows whose grad_out is set to 0
     n_slices: int = 1              # vocabulary slices for the split-V path
+    topk: int = 0                  # teacher top-k payload size (distillation workloads)
+    topk_boost: float = 0.0        # student logits at the teacher's columns get + U(0, boost)
 
     @property
     def esize(self) -> int:
@@ -90,6 +92,14 @@ WORKLOADS = {
     "extreme_fp32_16384x248320": Workload(
         "extreme_fp32_16384x248320", "fp32", 16384, 248320, 4.0, seed=4, tau=0.7,
         extreme_prob=0.01, extreme_value=1.0e4, n_slices=4),
+    # Top-k distillation (verl PR, "Test": b=2, s=96, V=2048, K=32): fp32 student
+    # logits ~ N(0,1) boosted at the teacher's 32 columns.
+    "distill_fp32_192x2048_k32": Workload(
+        "distill_fp32_192x2048_k32", "fp32", 192, 2048, 1.0, seed=5, topk=32, topk_boost=4.0),
+    # The page's Qwen3.5-4B distillation dimensions: V=248320, K=128, N=4096 tokens.
+    "distill_bf16_4096x248320_k128": Workload(
+        "distill_bf16_4096x248320_k128", "bf16", 4096, 248320, 2.0, seed=6, topk=128,
+        topk_boost=6.0),
 }
 
 
@@ -134,10 +144,35 @@ def bf16_bits_to_float32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def topk_payload_rows(w: Workload, rows):
+    """Teacher top-k payload of rows `rows`: (int32 [n, K] distinct columns,
+    float32 [n, K] teacher log-probabilities, descending).  Teacher
+    probabilities are exponential weights scaled to a per-row mass P ~ U(0.5, 0.98)."""
+    rows = np.atleast_1d(np.asarray(rows, dtype=np.int64))
+    K = w.topk
+    idx = np.empty((rows.size, K), np.int32)
+    tlp = np.empty((rows.size, K), np.float32)
+    for i, r in enumerate(rows):
+        g = _gen(w, "topk", int(r))
+        idx[i] = g.choice(w.vocab, size=K, replace=False).astype(np.int32)
+        mass = g.uniform(0.5, 0.98)
+        e = np.sort(g.exponential(size=K))[::-1]
+        tlp[i] = np.log(mass * e / e.sum()).astype(np.float32)
+    return idx, tlp
+
+
+def topk_payload(w: Workload):
+    return topk_payload_rows(w, np.arange(w.n_rows))
+
+
 def _row_values(w: Workload, r: int) -> np.ndarray:
     """float32 values of row r before storage rounding."""
     x = _gen(w, "logits", r).standard_normal(w.vocab, dtype=np.float32)
     x *= np.float32(w.sigma)
+    if w.topk > 0:
+        idx, _ = topk_payload_rows(w, [r])
+        boost = _gen(w, "boost", r).uniform(0.0, w.topk_boost, size=w.topk).astype(np.float32)
+        x[idx[0]] += boost
     if w.spike_row_prob > 0.0:
         g = _gen(w, "spike", r)
         has = g.random() < w.spike_row_prob

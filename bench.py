@@ -187,6 +187,30 @@ def bench_other(args, w, x):
                                                                 layout=vwc.VWC_GRAD_COMPACT,
                                                                 stream=stream),
                            M * (2 * V * e + 24)))
+    elif w.topk > 0:
+        idx_h, tlp_h = W.topk_payload(w)
+        idx = torch.from_numpy(idx_h).to(dev)
+        tlp = torch.from_numpy(tlp_h).to(dev)
+        K = w.topk
+        g = torch.from_numpy(g_all).to(dev)
+        ws = torch.empty(max(vwc.workspace_bytes(N, V, x.dtype), 1), dtype=torch.uint8,
+                         device=dev)
+        fwd = vwc.topk_kl_fwd(x, idx, tlp, vwc.VWC_KL_TAIL, workspace=ws)
+        grad = torch.empty_like(x)
+        passes.append(("topk_kl_fwd(tail, K=%d)" % K,
+                       lambda: vwc._binding._lib.vwc_topk_kl_fwd(
+                           vwc._binding._ptr(x), vwc._binding._dtype(x), N, V, V,
+                           vwc._binding._ptr(idx), vwc._binding._ptr(tlp), K, vwc.VWC_KL_TAIL,
+                           1e-6, float(w.tau), vwc._binding._ptr(fwd["loss"]),
+                           vwc._binding._ptr(fwd["student_mass"]),
+                           vwc._binding._ptr(fwd["teacher_mass"]),
+                           vwc._binding._ptr(fwd["topk_sum"]), vwc._binding._ptr(fwd["lse"]),
+                           vwc._binding._ptr(ws), ws.numel(), vwc._binding._stream(stream, x)),
+                       N * (V * e + K * (8 + e) + 20)))
+        passes.append(("topk_kl_bwd(tail, K=%d)" % K,
+                       lambda: vwc.topk_kl_bwd(x, idx, tlp, fwd, g, vwc.VWC_KL_TAIL,
+                                               grad_logits=grad, stream=stream),
+                       N * (2 * V * e + K * (8 + 2 * e) + 20)))
     elif w.n_slices > 1:
         k, vl = w.n_slices, V // w.n_slices
         parts = torch.empty((k, N, 4), dtype=torch.float32, device=dev)

@@ -224,6 +224,55 @@ vwc_status vwc_logprob_entropy_bwd_rows(const void *logits, vwc_dtype dt, int64_
                                         void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
                                         vwc_grad_layout layout, hipStream_t stream);
 
+typedef enum vwc_kl_mode {
+    VWC_KL_TRUNCATED = 0, /* sum over the teacher top-k, clamped at 0 */
+    VWC_KL_TAIL = 1       /* K+1 categories: the top-k plus one aggregate tail */
+} vwc_kl_mode;
+
+/*
+ * Top-k forward KL of a teacher payload against the student softmax, from the
+ * verl top-k KL pages ("[megatron] feat: add memory-efficient chunked top-k KL
+ * computation"; its commit text of the tail-aware top-k KL change, "What does
+ * this PR do?" and "Design & Code Changes").  Per row r, T_r =
+ * topk_idx[r*k .. r*k+k) (distinct student columns, int32), teacher
+ * log-probs a_n = teacher_logprob[r*k + n] (float), p_n = exp(a_n),
+ * q_j = softmax(x_r / tau)_j, P = sum p_n, Q = sum q_{T_n},
+ * S = sum p_n (a_n - log q_{T_n}):
+ *   VWC_KL_TRUNCATED: loss = max(0, S)
+ *   VWC_KL_TAIL:      loss = S + p_tail (log p_tail - log max(1 - Q, eps)),
+ *                     p_tail = max(0, 1 - P), 0 log 0 = 0
+ * Outputs float[n_rows]: loss, student_mass (Q), teacher_mass (P), topk_sum
+ * (S, before any clamp) and lse; each nullable except lse and the ones the
+ * backward needs (it reads lse, student_mass, teacher_mass, topk_sum).
+ * tail_mass_eps must lie in (0, 1) for VWC_KL_TAIL (the page's default is
+ * 1e-6).  A column id outside [0, vocab) gives NaN outputs for its row.
+ * workspace: vwc_workspace_bytes(n_rows, vocab, dt).
+ */
+vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                           float *loss, float *student_mass, float *teacher_mass, float *topk_sum,
+                           float *lse, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Gradient of sum_r g_r loss_r with respect to the student logits, in one
+ * streaming pass plus a fix-up of the k payload columns per row (the page's
+ * analytic form: q_j - p_j inside the top-k and q_j (P - Q)/(1 - Q) outside
+ * for the tail objective; q_j P - p_j [j in T] for the truncated one, and 0
+ * for a clamped truncated row or while the eps guard is active on the tail
+ * term's q_tail; all divided by tau).  lse, student_mass, teacher_mass and
+ * topk_sum come from vwc_topk_kl_fwd; grad_loss is float[n_rows].  Rows with
+ * g == 0 or a clamped truncated loss are written as +0.0 without reading the
+ * logits.  Other arguments as vwc_selected_logprob_bwd.
+ */
+vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                           const float *lse, const float *student_mass, const float *teacher_mass,
+                           const float *topk_sum, const float *grad_loss, void *grad_logits,
+                           vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream);
+
 /*
  * Partial of one vocabulary slice ([E] "Implementation", steps 1-3 in one
  * pass).  logits_slice points at global column v_start of row 0; the slice is

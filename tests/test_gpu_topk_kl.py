@@ -1,0 +1,160 @@
+"""GPU parity of the truncated and tail-aware top-k KL against the fp64 oracle.
+
+Forward outputs (loss, student/teacher top-k mass, raw top-k sum): abs err <= 5e-5.
+Gradients: fp32 within 1e-6; bf16 within one bf16 step of the rounded oracle, or,
+where a coefficient cancels (q_j - p_j inside the payload, alpha = P - p_tail Q /
+(1 - Q) outside), within the error that the forward's fp32 lse, P and Q carry
+into it (first-order bound from their measured deviations) plus one spacing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocab_wide_cross_amd as vwc
+import workloads as W
+from gpu_util import DEV, assert_close_scalar, grad_bits, log, to_dev_logits, upload_workload
+from helpers import bf16_ulp_distance
+
+pytestmark = pytest.mark.gpu
+
+MODES = [vwc.VWC_KL_TRUNCATED, vwc.VWC_KL_TAIL]
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _dev(w, x, idx, tlp):
+    return to_dev_logits(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV)
+
+
+def check_fwd(fwd, x, idx, tlp, mode, tau, eps=1e-6):
+    ref = oracle.topk_kl_forward(x, idx, tlp, mode, tail_eps=eps, tau=tau)
+    assert_close_scalar(_np(fwd["loss"]), ref["loss"], "loss")
+    assert_close_scalar(_np(fwd["student_mass"]), ref["student_mass"], "student_mass")
+    assert_close_scalar(_np(fwd["teacher_mass"]), ref["teacher_mass"], "teacher_mass")
+    return ref
+
+
+def grad_bound(x, idx, tlp, mode, tau, fwd, ref_fwd, g, eps=1e-6):
+    """Per-element allowance from the forward's fp32 deviations (first order)."""
+    tau32 = float(np.float32(tau))
+    o = oracle.forward(x, None, tau=tau, want=("lse",))
+    xf = (W.bf16_bits_to_float32(x) if x.dtype == np.uint16 else x).astype(np.float64)
+    q = np.exp(xf / tau32 - o["lse"][:, None])
+    dl = np.abs(_np(fwd["lse"]).astype(np.float64) - o["lse"])
+    P, Q = ref_fwd["teacher_mass"], ref_fwd["student_mass"]
+    dP = np.abs(_np(fwd["teacher_mass"]).astype(np.float64) - P)
+    dQ = np.abs(_np(fwd["student_mass"]).astype(np.float64) - Q)
+    pt = np.maximum(0.0, 1.0 - P)
+    if mode == vwc.VWC_KL_TAIL:
+        qt = np.maximum(1.0 - Q, eps)
+        d_alpha = (dP + pt * dQ / qt) / qt
+        alpha = P - pt * Q / qt
+    else:
+        d_alpha = dP
+        alpha = P
+    e = (d_alpha + (np.abs(alpha) + 2) * dl + 1e-6)[:, None] + np.zeros_like(q)
+    return np.abs(g / tau32)[:, None] * q * 2 * e
+
+
+def check_bf16_grad(got_bits, ref, bound):
+    steps = bf16_ulp_distance(got_bits, oracle.bf16_rne(ref))
+    got = W.bf16_bits_to_float32(got_bits).astype(np.float64)
+    ok = (steps <= 1) | (np.abs(got - ref) <= bound + np.abs(ref) * 2.0 ** -7 + 2.0 ** -133)
+    assert ok.all(), f"{(~ok).sum()} elements beyond the bar"
+    return int((steps > 1).sum())
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_topk_kl_fp32_tiny(mode, tau):
+    """The verl PR's small test shape: b=2, s=96 (192 rows), V=2048, K=32, fp32."""
+    w = W.get("distill_fp32_192x2048_k32")
+    x = W.all_logits(w)
+    idx, tlp = W.topk_payload(w)
+    g = np.random.default_rng(1).uniform(-1, 1, w.n_rows).astype(np.float32)
+    xd, idd, tld = _dev(w, x, idx, tlp)
+    fwd = vwc.topk_kl_fwd(xd, idd, tld, mode, temperature=tau)
+    check_fwd(fwd, x, idx, tlp, mode, tau)
+    grad = vwc.topk_kl_bwd(xd, idd, tld, fwd, torch.from_numpy(g).to(DEV), mode, temperature=tau)
+    ref = oracle.topk_kl_backward(x, idx, tlp, mode, g, tau=tau)
+    assert np.abs(_np(grad).astype(np.float64) - ref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_topk_kl_bf16_multi_segment(mode):
+    w = W.scaled("distill_bf16_4096x248320_k128", 24, 151936)
+    x = W.all_logits(w)
+    idx, tlp = W.topk_payload(w)
+    g = np.random.default_rng(2).uniform(-1, 1, w.n_rows).astype(np.float32)
+    g[3] = 0.0
+    xd, idd, tld = _dev(w, x, idx, tlp)
+    fwd = vwc.topk_kl_fwd(xd, idd, tld, mode)
+    ref_fwd = check_fwd(fwd, x, idx, tlp, mode, 1.0)
+    grad = vwc.topk_kl_bwd(xd, idd, tld, fwd, torch.from_numpy(g).to(DEV), mode)
+    ref = oracle.topk_kl_backward(x, idx, tlp, mode, g)
+    n = check_bf16_grad(grad_bits(grad), ref, grad_bound(x, idx, tlp, mode, 1.0, fwd, ref_fwd, g))
+    log(f"top-k KL bf16 mode={mode}: {n} elements beyond one bf16 step (within the bar)")
+    assert np.all(grad_bits(grad)[3] == 0)
+
+
+def test_topk_kl_clamp_guard_and_bad_index():
+    """Q > P clamps the truncated loss (row gradient +0.0); 1 - Q < eps turns off
+    the tail term's gradient; an out-of-range payload column gives NaN."""
+    V, K = 4096, 8
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((4, V)).astype(np.float32)
+    idx = np.stack([rng.choice(V, K, replace=False) for _ in range(4)]).astype(np.int32)
+    tlp = np.log(np.full((4, K), 0.5 / K)).astype(np.float32)
+    x[0, idx[0]] = 12.0      # Q ~ 1 - 1e-3 > P: truncated clamp
+    x[1, idx[1]] = 40.0      # 1 - Q < eps: guard active
+    g = np.ones(4, np.float32)
+    xd, idd, tld = to_dev_logits(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV)
+    gd = torch.from_numpy(g).to(DEV)
+    for mode in MODES:
+        fwd = vwc.topk_kl_fwd(xd, idd, tld, mode)
+        check_fwd(fwd, x, idx, tlp, mode, 1.0)
+        grad = vwc.topk_kl_bwd(xd, idd, tld, fwd, gd, mode)
+        ref = oracle.topk_kl_backward(x, idx, tlp, mode, g)
+        assert np.abs(_np(grad).astype(np.float64) - ref).max() <= 1e-6
+        if mode == vwc.VWC_KL_TRUNCATED:
+            assert _np(fwd["loss"])[0] == 0.0
+            gz = _np(grad[0]).view(np.uint32)
+            assert np.all(gz == 0)
+    bad = idx.copy()
+    bad[2, 3] = V
+    fwd = vwc.topk_kl_fwd(xd, torch.from_numpy(bad).to(DEV), tld, vwc.VWC_KL_TAIL)
+    loss = _np(fwd["loss"])
+    assert np.isnan(loss[2]) and np.all(np.isfinite(np.delete(loss, 2)))
+
+
+@pytest.mark.timeout(900)
+def test_topk_kl_full_size_k128():
+    """The page's distillation dimensions: N=4096, V=248320 bf16, K=128; sampled
+    rows against the oracle for both objectives."""
+    w = W.get("distill_bf16_4096x248320_k128")
+    x = upload_workload(w)
+    idx, tlp = W.topk_payload(w)
+    g = np.random.default_rng(5).uniform(-1, 1, w.n_rows).astype(np.float32)
+    idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
+    rows = np.array([0, 1777, 4095])
+    xh = W.logits_rows(w, rows)
+    ri = torch.from_numpy(rows).to(DEV)
+    for mode in MODES:
+        fwd = vwc.topk_kl_fwd(x, idd, tld, mode)
+        grad = vwc.topk_kl_bwd(x, idd, tld, fwd, gd, mode)
+        torch.cuda.synchronize()
+        sub = {k: v[ri] for k, v in fwd.items()}
+        ref_fwd = check_fwd(sub, xh, idx[rows], tlp[rows], mode, 1.0)
+        ref = oracle.topk_kl_backward(xh, idx[rows], tlp[rows], mode, g[rows])
+        n = check_bf16_grad(grad_bits(grad[ri]), ref,
+                            grad_bound(xh, idx[rows], tlp[rows], mode, 1.0, sub, ref_fwd, g[rows]))
+        log(f"top-k KL full size mode={mode}: {n} elements beyond one bf16 step (within the bar)")
+        assert torch.all(torch.isfinite(fwd["loss"]))
+        if mode == vwc.VWC_KL_TAIL:
+            assert torch.all(fwd["loss"] >= -5e-5)
+        del grad
+    del x
+    torch.cuda.empty_cache()

@@ -7,8 +7,9 @@ and calls the library.  There is no fallback: if the library is missing the
 import of the binding raises.
 """
 from ._binding import (  # noqa: F401
-    VWC_BF16, VWC_FP32, VWC_GRAD_COMPACT, VWC_GRAD_SCATTER, VwcError, abi_version, entropy,
+    VWC_BF16, VWC_FP32, VWC_GRAD_COMPACT, VWC_GRAD_SCATTER, VWC_KL_TAIL, VWC_KL_TRUNCATED,
+    VwcError, abi_version, entropy,
     entropy_rows, library_path, logprob_entropy_bwd, logprob_entropy_bwd_rows, mask_to_index,
     partial_combine, selected_logprob_bwd, selected_logprob_bwd_rows, selected_logprob_fwd,
-    selected_logprob_fwd_rows, vocab_partial, workspace_bytes,
+    selected_logprob_fwd_rows, topk_kl_bwd, topk_kl_fwd, vocab_partial, workspace_bytes,
 )

@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(_HERE, "libvwc.so")
 VWC_OK, VWC_ERR_INVALID_ARG, VWC_ERR_UNSUPPORTED, VWC_ERR_HIP = 0, 1, 2, 3
 VWC_BF16, VWC_FP32 = 0, 1
 VWC_GRAD_COMPACT, VWC_GRAD_SCATTER = 0, 1
+VWC_KL_TRUNCATED, VWC_KL_TAIL = 0, 1
 PARTIAL_BYTES = 16
 
 
@@ -52,6 +53,10 @@ def _load() -> ctypes.CDLL:
         "vwc_logprob_entropy_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64, p], i32),
         "vwc_logprob_entropy_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, p, i32,
                                           i64, i32, p], i32),
+        "vwc_topk_kl_fwd": ([p, i32, i64, i64, i64, p, p, ctypes.c_int32, i32, f32, f32, p, p, p,
+                             p, p, p, sz, p], i32),
+        "vwc_topk_kl_bwd": ([p, i32, i64, i64, i64, p, p, ctypes.c_int32, i32, f32, f32, p, p, p,
+                             p, p, p, i32, i64, p], i32),
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
@@ -271,6 +276,47 @@ def logprob_entropy_bwd_rows(logits, targets, row_idx, lse, entropy, grad_logpro
                                              _dtype(grad_logits), gld, layout,
                                              _stream(stream, logits)))
     return grad_logits
+
+
+def topk_kl_fwd(logits, topk_idx, teacher_logprob, mode=VWC_KL_TAIL, tail_mass_eps=1e-6,
+                temperature=1.0, workspace=None, stream=None):
+    """Top-k forward KL per row; returns dict of float32 [n_rows] tensors:
+    loss, student_mass, teacher_mass, topk_sum, lse."""
+    n, v, ld = _rows_view(logits)
+    _i32(topk_idx, "topk_idx")
+    if topk_idx.dim() != 2 or topk_idx.size(0) != n or teacher_logprob.shape != topk_idx.shape \
+            or teacher_logprob.dtype != torch.float32 or not teacher_logprob.is_contiguous():
+        raise ValueError("topk_idx int32 and teacher_logprob float32 must both be [n_rows, k]")
+    k = topk_idx.size(1)
+    out = {name: torch.empty(n, dtype=torch.float32, device=logits.device)
+           for name in ("loss", "student_mass", "teacher_mass", "topk_sum", "lse")}
+    ws, wsb = _workspace(n, v, logits, workspace)
+    _check(_lib.vwc_topk_kl_fwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(topk_idx),
+                                _ptr(teacher_logprob), k, int(mode), float(tail_mass_eps),
+                                float(temperature), _ptr(out["loss"]), _ptr(out["student_mass"]),
+                                _ptr(out["teacher_mass"]), _ptr(out["topk_sum"]),
+                                _ptr(out["lse"]), _ptr(ws), wsb, _stream(stream, logits)))
+    return out
+
+
+def topk_kl_bwd(logits, topk_idx, teacher_logprob, fwd, grad_loss, mode=VWC_KL_TAIL,
+                tail_mass_eps=1e-6, temperature=1.0, grad_logits=None, grad_dtype=None,
+                stream=None):
+    """Gradient of sum_r grad_loss[r] * loss[r] w.r.t. the student logits; `fwd` is the
+    dict topk_kl_fwd returned."""
+    n, v, ld = _rows_view(logits)
+    _i32(topk_idx, "topk_idx")
+    g = _grad_out(logits, n, grad_logits, grad_dtype)
+    gn, gv, gld = _rows_view(g)
+    if gn != n or gv < v:
+        raise ValueError("grad_logits must be [n_rows, >= vocab]")
+    _check(_lib.vwc_topk_kl_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(topk_idx),
+                                _ptr(teacher_logprob), topk_idx.size(1), int(mode),
+                                float(tail_mass_eps), float(temperature), _ptr(fwd["lse"]),
+                                _ptr(fwd["student_mass"]), _ptr(fwd["teacher_mass"]),
+                                _ptr(fwd["topk_sum"]), _ptr(grad_loss), _ptr(g), _dtype(g), gld,
+                                _stream(stream, logits)))
+    return g
 
 
 def vocab_partial(logits_slice, v_start, targets=None, row_idx=None, temperature=1.0, out=None,

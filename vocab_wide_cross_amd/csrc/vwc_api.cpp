@@ -139,12 +139,19 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
     return hip_status(vwc::launch_fwd(p, dt, stream), fn);
 }
 
+struct KlArgs {
+    const float *P, *Q, *S;
+    int mode;
+    double eps;
+};
+
 vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n_rows,
                            int64_t vocab, int64_t ld, const int32_t *targets,
                            const int32_t *row_idx, int64_t m, float temperature, const float *lse,
                            const float *entropy, const float *grad_logprob,
                            const float *grad_entropy, void *grad_logits, int grad_dt,
-                           int64_t ld_grad, bool by_row_id, hipStream_t stream) {
+                           int64_t ld_grad, bool by_row_id, hipStream_t stream,
+                           const KlArgs *kl = nullptr) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
     if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
@@ -156,7 +163,8 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
     if (!grad_logprob && !grad_entropy)
         return fail(VWC_ERR_INVALID_ARG, "%s: no incoming gradient", fn);
-    if (grad_logprob && !targets) return fail(VWC_ERR_INVALID_ARG, "%s: targets is null", fn);
+    if (grad_logprob && !targets && !kl)
+        return fail(VWC_ERR_INVALID_ARG, "%s: targets is null", fn);
     if (grad_entropy && !entropy) return fail(VWC_ERR_INVALID_ARG, "%s: entropy is null", fn);
     if (!lse || !grad_logits)
         return fail(VWC_ERR_INVALID_ARG, "%s: null lse or grad_logits", fn);
@@ -193,6 +201,13 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     p.grad_out = grad_logprob;
     p.entropy = entropy;
     p.grad_ent = grad_entropy;
+    if (kl) {
+        p.kl_P = kl->P;
+        p.kl_Q = kl->Q;
+        p.kl_S = kl->S;
+        p.kl_mode = kl->mode;
+        p.kl_eps = kl->eps;
+    }
     p.grad = grad_logits;
     p.ld_grad = ld_grad;
     p.grad_by_row_id = by_row_id;
@@ -313,6 +328,100 @@ vwc_status vwc_logprob_entropy_bwd_rows(const void *logits, vwc_dtype dt, int64_
     return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
                            lse, entropy, grad_logprob, grad_entropy, grad_logits, grad_dt,
                            ld_grad, layout == VWC_GRAD_SCATTER, stream);
+}
+
+static vwc_status check_topk(const char *fn, const int32_t *topk_idx, const float *tlp, int32_t k,
+                             int64_t vocab, int mode, float eps, int64_t n_rows) {
+    if (k <= 0 || k > vocab) return fail(VWC_ERR_INVALID_ARG, "%s: k must be in [1, vocab]", fn);
+    if (mode != VWC_KL_TRUNCATED && mode != VWC_KL_TAIL)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown mode %d", fn, mode);
+    if (mode == VWC_KL_TAIL && !(eps > 0.f && eps < 1.f))
+        return fail(VWC_ERR_INVALID_ARG, "%s: tail_mass_eps must lie in (0, 1)", fn);
+    if (n_rows > 0 && (!topk_idx || !tlp))
+        return fail(VWC_ERR_INVALID_ARG, "%s: null topk_idx or teacher_logprob", fn);
+    if (n_rows > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (static_cast<int64_t>(k) * n_rows > INT64_MAX / 8)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: payload too large", fn);
+    return VWC_OK;
+}
+
+vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                           float *loss, float *student_mass, float *teacher_mass, float *topk_sum,
+                           float *lse, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    const char *fn = "vwc_topk_kl_fwd";
+    vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
+    if (st != VWC_OK) return st;
+    if ((st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps, n_rows)) !=
+        VWC_OK)
+        return st;
+    if (n_rows == 0) return ok();
+    if (!lse) return fail(VWC_ERR_INVALID_ARG, "%s: lse is null", fn);
+    st = forward_common(fn, logits, dt, n_rows, vocab, ld, 0, nullptr, vwc::kTargetNone, nullptr,
+                        n_rows, temperature, nullptr, lse, nullptr, nullptr, workspace,
+                        workspace_bytes, stream);
+    if (st != VWC_OK) return st;
+    vwc::TopkPlan p{};
+    p.logits = logits;
+    p.ld = ld;
+    p.vocab = static_cast<int32_t>(vocab);
+    p.dt = dt;
+    p.n_rows = n_rows;
+    p.idx = topk_idx;
+    p.tlp = teacher_logprob;
+    p.k = k;
+    p.mode = mode;
+    p.eps = tail_mass_eps;
+    p.tau = temperature;
+    p.lse = lse;
+    p.loss = loss;
+    p.Q = student_mass;
+    p.P = teacher_mass;
+    p.S = topk_sum;
+    return hip_status(vwc::launch_topk_fwd(p, stream), fn);
+}
+
+vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                           const float *lse, const float *student_mass, const float *teacher_mass,
+                           const float *topk_sum, const float *grad_loss, void *grad_logits,
+                           vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream) {
+    const char *fn = "vwc_topk_kl_bwd";
+    vwc_status st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps,
+                               n_rows);
+    if (st != VWC_OK) return st;
+    if (n_rows > 0 && (!student_mass || !teacher_mass || !topk_sum || !grad_loss))
+        return fail(VWC_ERR_INVALID_ARG,
+                    "%s: null student_mass, teacher_mass, topk_sum or grad_loss", fn);
+    KlArgs kl{teacher_mass, student_mass, topk_sum, static_cast<int>(mode), tail_mass_eps};
+    st = backward_common(fn, logits, dt, n_rows, vocab, ld, nullptr, nullptr, n_rows, temperature,
+                         lse, nullptr, grad_loss, nullptr, grad_logits, grad_dt, ld_grad, true,
+                         stream, &kl);
+    if (st != VWC_OK || n_rows == 0) return st;
+    vwc::TopkPlan p{};
+    p.logits = logits;
+    p.ld = ld;
+    p.vocab = static_cast<int32_t>(vocab);
+    p.dt = dt;
+    p.gdt = grad_dt;
+    p.n_rows = n_rows;
+    p.idx = topk_idx;
+    p.tlp = teacher_logprob;
+    p.k = k;
+    p.mode = mode;
+    p.eps = tail_mass_eps;
+    p.tau = temperature;
+    p.lse = lse;
+    p.inP = teacher_mass;
+    p.inQ = student_mass;
+    p.inS = topk_sum;
+    p.grad_loss = grad_loss;
+    p.grad = grad_logits;
+    p.ld_grad = ld_grad;
+    return hip_status(vwc::launch_topk_fixup(p, stream), fn);
 }
 
 vwc_status vwc_vocab_partial(const void *logits_slice, vwc_dtype dt, int64_t n_rows,

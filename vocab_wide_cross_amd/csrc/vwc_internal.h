@@ -81,6 +81,11 @@ struct BwdPlan {
     const float *grad_out;    // [m] incoming d/d logprob, or null (0)
     const float *entropy;     // [m] the forward's entropy (entropy gradient only)
     const float *grad_ent;    // [m] incoming d/d entropy, or null (0)
+    // Top-k KL coefficient mode (kl_P non-null): o_j = q_j * g alpha / tau,
+    // alpha from (P, Q, S) of the row; no target column.
+    const float *kl_P, *kl_Q, *kl_S;
+    int kl_mode;
+    double kl_eps;
     void *grad;
     int64_t ld_grad;
     bool grad_by_row_id;      // true: gradient row = row id; false: = output index
@@ -99,7 +104,31 @@ struct CombinePlan {
     vwc_partial *partial_out;   // merge into partials instead of final outputs
 };
 
+// Top-k KL per-row pieces: gathers k student logits per row.
+struct TopkPlan {
+    const void *logits;
+    int64_t ld;
+    int32_t vocab;
+    int dt, gdt;
+    int64_t n_rows;
+    const int32_t *idx;        // [n_rows][k]
+    const float *tlp;          // [n_rows][k]
+    int32_t k;
+    int mode;
+    double eps;
+    double tau;
+    const float *lse;          // [n_rows]
+    // forward outputs (nullable)
+    float *loss, *Q, *P, *S;
+    // backward (fix-up) inputs/outputs
+    const float *inP, *inQ, *inS, *grad_loss;
+    void *grad;
+    int64_t ld_grad;
+};
+
 hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream);
+hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream);
+hipError_t launch_topk_fixup(const TopkPlan &p, hipStream_t stream);
 hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream);
 hipError_t launch_combine(const CombinePlan &p, hipStream_t stream);
 hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, int32_t *count,

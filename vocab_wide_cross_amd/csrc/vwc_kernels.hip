@@ -587,6 +587,33 @@ struct GradStore<VWC_FP32, N> {
     }
 };
 
+// Top-k KL gradient per row, with p_tail = max(0, 1 - P) and q_tail = 1 - Q:
+//   dL/dz_j = alpha q_j              for j outside the payload,
+//           = beta q_j - kappa p_j   for j in it,
+// tail (guard off): alpha = P - p_tail Q / q_tail, beta = P + p_tail, kappa = 1
+// (q - p inside, q (P - Q)/(1 - Q) outside when P < 1); tail with the eps guard
+// on, or truncated: alpha = beta = P; a truncated row whose sum S < 0 was
+// clamped and has no gradient.
+struct KlCoef {
+    double alpha, beta, kappa;
+    bool dead;
+};
+
+__device__ __forceinline__ KlCoef kl_coef(int mode, double eps, double P, double Q, double S) {
+    KlCoef c{P, P, 1.0, false};
+    if (mode == VWC_KL_TRUNCATED) {
+        c.dead = S < 0.0;
+    } else {
+        const double pt = P < 1.0 ? 1.0 - P : 0.0;
+        const double qt = 1.0 - Q;
+        if (qt >= eps) {
+            c.alpha = P - pt * Q / qt;
+            c.beta = P + pt;
+        }
+    }
+    return c;
+}
+
 // Uniform per-row constants of the backward.
 struct RowGrad {
     float c;       // log2(e) / tau
@@ -649,8 +676,13 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     const bool last = q == p.nseg - 1;
     const float g = p.grad_out ? p.grad_out[i] : 0.f;
     const float h = WH ? p.grad_ent[i] : 0.f;
+    const bool kl = p.kl_P != nullptr;
+    KlCoef klc{0.0, 0.0, 0.0, false};
+    if (kl && g != 0.f)
+        klc = kl_coef(p.kl_mode, p.kl_eps, static_cast<double>(p.kl_P[i]),
+                      static_cast<double>(p.kl_Q[i]), static_cast<double>(p.kl_S[i]));
 
-    if (g == 0.f && h == 0.f) {
+    if ((g == 0.f && h == 0.f) || klc.dead) {
         // Rows without loss: +0.0, no logits read.
         float z[N];
 #pragma unroll
@@ -678,7 +710,8 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     R.H = WH ? static_cast<double>(p.entropy[i]) : 0.0;
     R.a = static_cast<float>(-R.gt + R.hs * R.H);
     R.b = static_cast<float>(R.hs * kLn2);
-    R.t = g != 0.f ? p.targets[r] : -1;
+    R.t = (g != 0.f && !kl) ? p.targets[r] : -1;
+    if (kl) R.gs = static_cast<float>(R.gt * klc.alpha);  // o = q (g alpha / tau)
     const T *src = reinterpret_cast<const T *>(row);
 
     int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
@@ -717,6 +750,81 @@ template <int DT, int GDT, bool VEC, bool WH>
 __global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(BwdPlan p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
     bwd_item<DT, GDT, VEC, WH>(p, i, static_cast<int>(blockIdx.x - i * p.nseg));
+}
+
+// ---------------------------------------------------------------- top-k KL
+
+constexpr int kTopkBlock = 64;  // one wave per row
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    return v;
+}
+
+// Per row: gather the k payload columns of the student row and reduce P, Q and
+// S = sum p (a - log q) in fp64 (lane-strided, then a fixed butterfly).
+template <int DT>
+__global__ __launch_bounds__(kTopkBlock) void topk_fwd_kernel(TopkPlan p) {
+    const int64_t r = blockIdx.x;
+    const char *row = static_cast<const char *>(p.logits) + r * p.ld * (DT == VWC_BF16 ? 2 : 4);
+    const double lse = static_cast<double>(p.lse[r]);
+    double P = 0.0, Q = 0.0, S = 0.0, bad = 0.0;
+    for (int n = threadIdx.x; n < p.k; n += kTopkBlock) {
+        const int32_t j = p.idx[r * p.k + n];
+        if (j < 0 || j >= p.vocab) {
+            bad = 1.0;
+            continue;
+        }
+        const double a = static_cast<double>(p.tlp[r * p.k + n]);
+        const double lq = static_cast<double>(load_element<DT>(row, j)) / p.tau - lse;
+        const double pn = exp(a);
+        P += pn;
+        Q += exp(lq);
+        S += pn * (a - lq);
+    }
+    P = wave_sum(P);
+    Q = wave_sum(Q);
+    S = wave_sum(S);
+    bad = wave_sum(bad);
+    if (threadIdx.x != 0) return;
+    double L;
+    if (p.mode == VWC_KL_TRUNCATED) {
+        L = S < 0.0 ? 0.0 : S;
+    } else {
+        const double pt = P < 1.0 ? 1.0 - P : 0.0;
+        const double qt = fmax(1.0 - Q, p.eps);
+        L = S + (pt == 0.0 ? 0.0 : pt * (log(pt) - log(qt)));
+    }
+    if (bad != 0.0) L = P = Q = S = NAN;
+    if (p.loss) p.loss[r] = static_cast<float>(L);
+    if (p.Q) p.Q[r] = static_cast<float>(Q);
+    if (p.P) p.P[r] = static_cast<float>(P);
+    if (p.S) p.S[r] = static_cast<float>(S);
+}
+
+// After the streaming backward wrote alpha q_j g / tau everywhere: overwrite
+// the k payload columns with (beta q_j - kappa p_j) g / tau.
+template <int DT, int GDT>
+__global__ __launch_bounds__(kTopkBlock) void topk_fixup_kernel(TopkPlan p) {
+    const int64_t r = blockIdx.x;
+    const float g = p.grad_loss[r];
+    if (g == 0.f) return;
+    const KlCoef c = kl_coef(p.mode, p.eps, static_cast<double>(p.inP[r]),
+                             static_cast<double>(p.inQ[r]), static_cast<double>(p.inS[r]));
+    if (c.dead) return;
+    const char *row = static_cast<const char *>(p.logits) + r * p.ld * (DT == VWC_BF16 ? 2 : 4);
+    char *grow = static_cast<char *>(p.grad) + r * p.ld_grad * (GDT == VWC_BF16 ? 2 : 4);
+    const double lse = static_cast<double>(p.lse[r]);
+    const double gt = static_cast<double>(g) / p.tau;
+    for (int n = threadIdx.x; n < p.k; n += kTopkBlock) {
+        const int32_t j = p.idx[r * p.k + n];
+        if (j < 0 || j >= p.vocab) continue;
+        const double q = exp(static_cast<double>(load_element<DT>(row, j)) / p.tau - lse);
+        const double pn = exp(static_cast<double>(p.tlp[r * p.k + n]));
+        const float o[1] = {static_cast<float>(gt * (c.beta * q - c.kappa * pn))};
+        GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * (GDT == VWC_BF16 ? 2 : 4), o);
+    }
 }
 
 // ---------------------------------------------------------------- mask -> index
@@ -844,6 +952,31 @@ hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream) {
                                  : launch_bwd_dt<VWC_BF16, VWC_FP32>(p, stream);
     return p.gdt == VWC_BF16 ? launch_bwd_dt<VWC_FP32, VWC_BF16>(p, stream)
                              : launch_bwd_dt<VWC_FP32, VWC_FP32>(p, stream);
+}
+
+hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(p.n_rows)), block(kTopkBlock);
+    if (p.dt == VWC_BF16)
+        hipLaunchKernelGGL(topk_fwd_kernel<VWC_BF16>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(topk_fwd_kernel<VWC_FP32>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_fixup(const TopkPlan &p, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(p.n_rows)), block(kTopkBlock);
+    if (p.dt == VWC_BF16) {
+        if (p.gdt == VWC_BF16)
+            hipLaunchKernelGGL((topk_fixup_kernel<VWC_BF16, VWC_BF16>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((topk_fixup_kernel<VWC_BF16, VWC_FP32>), grid, block, 0, stream, p);
+    } else {
+        if (p.gdt == VWC_BF16)
+            hipLaunchKernelGGL((topk_fixup_kernel<VWC_FP32, VWC_BF16>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((topk_fixup_kernel<VWC_FP32, VWC_FP32>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, int32_t *count,

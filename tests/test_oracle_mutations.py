@@ -1,0 +1,61 @@
+"""The oracle pins must catch plausible mistakes.  Each case plants one mistake in a
+private copy of oracle.c (on the CPU only), builds it, and runs the pin suite
+against it in a subprocess: the suite must fail."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, original text, mutated text, pin tests to run)
+MUTATIONS = [
+    ("entropy sign", "H -= p * (z - LSE);", "H += p * (z - LSE);", "entropy"),
+    ("tau dropped on the target", "double zt = logit_at(logits, dtype, ld, r, targets[r]) / tau;",
+     "double zt = logit_at(logits, dtype, ld, r, targets[r]);", "logprob or temperature"),
+    ("max dropped from LSE", "double LSE = M + log(S);\n            if (lse) lse[i] = LSE;",
+     "double LSE = log(S);\n            if (lse) lse[i] = LSE;", "logprob"),
+    ("gradient sign", "gi[j] = g * (onehot - p) / tau;", "gi[j] = g * (p - onehot) / tau;",
+     "grad"),
+    ("gradient without tau", "gi[j] = g * (onehot - p) / tau;", "gi[j] = g * (onehot - p);",
+     "grad"),
+    ("combine drops the shift term", "W += f * (pw[q * m + i] + d * ps[q * m + i]);",
+     "W += f * pw[q * m + i];", "vocab_chunks or split4"),
+    # (a transposed read of only the maxima would be harmless: the merge is exact for
+    # any reference point, so the planted mistake transposes the sums)
+    ("combine reads partial sums transposed", "S += ps[q * m + i] * f;",
+     "S += ps[i * k + q] * f;", "vocab_chunks or split4"),
+    ("bf16 decode off by one bit", "uint32_t w = ((uint32_t)bits) << 16;",
+     "uint32_t w = ((uint32_t)bits) << 15;", "sampled_rows"),
+    ("target read by output index", "double zt = logit_at(logits, dtype, ld, r, targets[r]) / tau;",
+     "double zt = logit_at(logits, dtype, ld, r, targets[i]) / tau;", "compact or chunks or errors"),
+    ("entropy gradient sign of H", "gi[j] = (g * (onehot - p) - h * p * (z - LSE + H)) / tau;",
+     "gi[j] = (g * (onehot - p) - h * p * (z - LSE - H)) / tau;", "entropy_grad"),
+    ("tail mass from the student", "double pt = P < 1.0 ? 1.0 - P : 0.0;",
+     "double pt = Q < 1.0 ? 1.0 - Q : 0.0;", "topk"),
+    ("truncated clamp dropped", "if (L < 0.0) L = 0.0; /* clamp_min(0) of the truncated objective */",
+     "/* no clamp */", "topk"),
+    ("bf16 rounding ties away", "double r = rint(v / q) * q;", "double r = round(v / q) * q;",
+     "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut,select", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, name, orig, mut, select):
+    src = open(SRC).read()
+    assert src.count(orig) >= 1, f"mutation anchor for '{name}' not found in oracle.c"
+    bad = src.replace(orig, mut, 1)
+    csrc = tmp_path / "oracle.c"
+    csrc.write_text(bad)
+    (tmp_path / "oracle.h").write_text(open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", str(lib), str(csrc), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-k", select],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, (f"the pins did not catch '{name}' (exit {r.returncode}):\n"
+                               f"{r.stdout[-2000:]}")

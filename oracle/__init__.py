@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 BF16 = 0
 FP32 = 1
+FP64 = 2
 
 _ERRORS = {
     -1: "invalid argument",
@@ -74,13 +75,17 @@ def _load():
         lib.oracle_combine.argtypes = [i64, i64, p, p, p, p, p, p, p]
         lib.oracle_forward_vchunk.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, d, i64,
                                               p, p, p]
+        lib.oracle_lmhead_logits.argtypes = [p, i64, i64, p, i64, i64, i64, p, i64, p, p]
+        lib.oracle_lmhead_forward.argtypes = [p, i64, i64, p, i64, i64, i64, p, p, i64, d, i64,
+                                              p, p, p, p]
         lib.oracle_bf16_rne.argtypes = [d]
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_bf16_rne_array.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_forward", "oracle_backward", "oracle_backward_entropy",
                   "oracle_topk_kl_forward", "oracle_topk_kl_backward",
-                  "oracle_slice_partial", "oracle_combine", "oracle_forward_vchunk"):
+                  "oracle_slice_partial", "oracle_combine", "oracle_forward_vchunk",
+                  "oracle_lmhead_logits", "oracle_lmhead_forward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -281,3 +286,52 @@ def bf16_rne(v) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def _lmhead_operands(hidden, weight, d):
+    hidden = np.ascontiguousarray(hidden)
+    weight = np.ascontiguousarray(weight)
+    if hidden.dtype != np.uint16 or weight.dtype != np.uint16:
+        raise TypeError("hidden and weight must be uint16 (bf16 bit patterns)")
+    n_rows, ldh = hidden.shape
+    vocab, ldw = weight.shape
+    d = min(ldh, ldw) if d is None else d
+    return hidden, weight, n_rows, ldh, vocab, ldw, d
+
+
+def lmhead_logits(hidden, weight, d: int | None = None, rows=None, want_abs: bool = False):
+    """float64 [m, vocab] logits x = hidden[rows, :d] @ weight[:, :d].T (and, with
+    want_abs, the matching sums of |products|)."""
+    hidden, weight, n_rows, ldh, vocab, ldw, d = _lmhead_operands(hidden, weight, d)
+    rows, m = _rows_arg(rows, n_rows)
+    x = np.empty((m, vocab), np.float64)
+    a = np.empty((m, vocab), np.float64) if want_abs else None
+    rc = _load().oracle_lmhead_logits(_ptr(hidden), n_rows, ldh, _ptr(weight), vocab, ldw, d,
+                                      _ptr(rows), m, _ptr(x), _ptr(a))
+    _check(rc, "oracle_lmhead_logits")
+    return (x, a) if want_abs else x
+
+
+def lmhead_forward(hidden, weight, targets, tau: float = 1.0, rows=None, d: int | None = None,
+                   want=("logprob", "lse", "entropy"), row_chunk: int = 16,
+                   err_scale: bool = False):
+    """Per-row logprob / lse / entropy of the LM head over hidden[rows] in float64.
+
+    hidden: uint16 [n_rows, ldh]; weight: uint16 [vocab, ldw]; the first d
+    columns of each are the hidden dimension.  With err_scale, the dict also
+    holds (A_t + max_j A_j) / tau per row (see oracle.h)."""
+    hidden, weight, n_rows, ldh, vocab, ldw, d = _lmhead_operands(hidden, weight, d)
+    rows, m = _rows_arg(rows, n_rows)
+    targets = _targets_arg(targets)
+    out = {k: (np.empty(m, np.float64) if k in want else None)
+           for k in ("logprob", "lse", "entropy")}
+    es = np.empty(m, np.float64) if err_scale else None
+    rc = _load().oracle_lmhead_forward(_ptr(hidden), n_rows, ldh, _ptr(weight), vocab, ldw, d,
+                                       _ptr(targets), _ptr(rows), m, _tau(tau), row_chunk,
+                                       _ptr(out["logprob"]), _ptr(out["lse"]),
+                                       _ptr(out["entropy"]), _ptr(es))
+    _check(rc, "oracle_lmhead_forward")
+    res = {k: v for k, v in out.items() if v is not None}
+    if err_scale:
+        res["err_scale"] = es
+    return res

@@ -28,11 +28,12 @@ static double logit_at(const void *logits, int dtype, int64_t ld, int64_t row,
                        int64_t col) {
     int64_t off = row * ld + col;
     if (dtype == ORACLE_BF16) return decode_bf16(((const uint16_t *)logits)[off]);
+    if (dtype == ORACLE_FP64) return ((const double *)logits)[off];
     return (double)((const float *)logits)[off];
 }
 
 static int dtype_ok(int dtype) {
-    return dtype == ORACLE_BF16 || dtype == ORACLE_FP32;
+    return dtype == ORACLE_BF16 || dtype == ORACLE_FP32 || dtype == ORACLE_FP64;
 }
 
 static int tau_ok(double tau) { return isfinite(tau) && tau > 0.0; }
@@ -442,6 +443,99 @@ int oracle_forward_vchunk(const void *logits, int dtype, int64_t n_rows,
  * the spacing is exact (a power of two), rint() rounds to nearest-even in the
  * default rounding mode, and the product is exactly representable in float.
  */
+/* ------------------------------------------------------------ LM head */
+
+static int lmhead_args_ok(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
+                          const uint16_t *weight, int64_t vocab, int64_t ldw,
+                          int64_t d, int64_t m) {
+    return hidden && weight && n_rows >= 0 && m >= 0 && vocab > 0 && d > 0 &&
+           ldh >= d && ldw >= d;
+}
+
+int oracle_lmhead_logits(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
+                         const uint16_t *weight, int64_t vocab, int64_t ldw,
+                         int64_t d, const int32_t *rows, int64_t m, double *x,
+                         double *abs_sum) {
+    if (!lmhead_args_ok(hidden, n_rows, ldh, weight, vocab, ldw, d, m) || (m && !x))
+        return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+    for (int64_t i = 0; i < m; ++i) {
+        const uint16_t *h = hidden + row_of(rows, i) * ldh;
+        /* Columns are independent dot products; threads split the columns. */
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < vocab; ++j) {
+            const uint16_t *w = weight + j * ldw;
+            double s = 0.0, a = 0.0;
+            for (int64_t k = 0; k < d; ++k) {
+                double p = decode_bf16(h[k]) * decode_bf16(w[k]);
+                s += p;
+                a += fabs(p);
+            }
+            x[i * vocab + j] = s;
+            if (abs_sum) abs_sum[i * vocab + j] = a;
+        }
+    }
+    return 0;
+}
+
+int oracle_lmhead_forward(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
+                          const uint16_t *weight, int64_t vocab, int64_t ldw,
+                          int64_t d, const int32_t *targets, const int32_t *rows,
+                          int64_t m, double tau, int64_t row_chunk,
+                          double *logprob, double *lse, double *entropy,
+                          double *err_scale) {
+    if (row_chunk <= 0 || !tau_ok(tau) ||
+        !lmhead_args_ok(hidden, n_rows, ldh, weight, vocab, ldw, d, m))
+        return -1;
+    if (logprob && !targets) return -1;
+    int rc = check_rows(rows, m, n_rows);
+    if (rc) return rc;
+    if (logprob && (rc = check_targets(targets, rows, m, vocab))) return rc;
+    if (m == 0) return 0;
+
+    int64_t cap = row_chunk < m ? row_chunk : m;
+    double *x = malloc((size_t)(cap * vocab) * sizeof(double));
+    double *a = err_scale ? malloc((size_t)(cap * vocab) * sizeof(double)) : NULL;
+    int32_t *sub_rows = malloc((size_t)cap * sizeof(int32_t));
+    int32_t *sub_targets = malloc((size_t)cap * sizeof(int32_t));
+    if (!x || (err_scale && !a) || !sub_rows || !sub_targets) {
+        free(x);
+        free(a);
+        free(sub_rows);
+        free(sub_targets);
+        return -4;
+    }
+    for (int64_t c0 = 0; c0 < m && rc == 0; c0 += cap) {
+        int64_t n = c0 + cap < m ? cap : m - c0;
+        for (int64_t i = 0; i < n; ++i) {
+            sub_rows[i] = (int32_t)row_of(rows, c0 + i);
+            sub_targets[i] = targets ? targets[sub_rows[i]] : 0;
+        }
+        rc = oracle_lmhead_logits(hidden, n_rows, ldh, weight, vocab, ldw, d, sub_rows,
+                                  n, x, a);
+        /* The chunk's logits are rows 0..n-1 of an fp64 matrix; targets follow. */
+        if (rc == 0)
+            rc = oracle_forward(x, ORACLE_FP64, n, vocab, vocab, targets ? sub_targets : NULL,
+                                NULL, n, tau, n, logprob ? logprob + c0 : NULL,
+                                lse ? lse + c0 : NULL, entropy ? entropy + c0 : NULL);
+        if (rc == 0 && err_scale) {
+            for (int64_t i = 0; i < n; ++i) {
+                const double *ai = a + i * vocab;
+                double amax = 0.0;
+                for (int64_t j = 0; j < vocab; ++j)
+                    if (ai[j] > amax) amax = ai[j];
+                err_scale[c0 + i] = ((targets ? ai[sub_targets[i]] : 0.0) + amax) / tau;
+            }
+        }
+    }
+    free(x);
+    free(a);
+    free(sub_rows);
+    free(sub_targets);
+    return rc;
+}
+
 uint16_t oracle_bf16_rne(double v) {
     if (isnan(v)) return 0x7FC0;
     if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;

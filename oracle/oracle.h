@@ -50,6 +50,7 @@ extern "C" {
 
 #define ORACLE_BF16 0 /* logits are raw bf16 bit patterns (uint16) */
 #define ORACLE_FP32 1 /* logits are IEEE binary32 */
+#define ORACLE_FP64 2 /* logits are IEEE binary64 (the LM-head oracle's own logits) */
 
 /*
  * Forward over a row set.  logits is a host buffer [n_rows, ld] of `dtype`.
@@ -156,6 +157,40 @@ int oracle_forward_vchunk(const void *logits, int dtype, int64_t n_rows,
                           const int32_t *rows, int64_t m, double tau,
                           int64_t vchunk, double *logprob, double *lse,
                           double *entropy);
+
+/*
+ * LM-head logits of a row set ("[Bug] Training/log-prob forward materializes
+ * full-vocab fp32 logits ...", maintainer comment: keep the loss-mask rows of
+ * the final hidden state before the vocabulary projection; "[RL][Performance]
+ * Avoid full-vocabulary TP gather ...", "Alternatives considered": a fused
+ * LM-head / cross-entropy kernel).  hidden is bf16 bits [n_rows, ldh], weight
+ * is bf16 bits [vocab, ldw] (one row per vocabulary entry, as the output
+ * layer stores it).  For output i with row r = rows ? rows[i] : i:
+ *   x[i * vocab + j] = sum_{k=0}^{d-1} hidden[r, k] * weight[j, k]
+ * summed in ascending k in double (every bf16 product is exact in double).
+ * abs_sum (nullable) gets sum_k |hidden[r, k] * weight[j, k]| at the same
+ * index, the scale of the rounding error of any finite-precision evaluation.
+ */
+int oracle_lmhead_logits(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
+                         const uint16_t *weight, int64_t vocab, int64_t ldw,
+                         int64_t d, const int32_t *rows, int64_t m, double *x,
+                         double *abs_sum);
+
+/*
+ * Forward of the fused LM head: the logits above followed by oracle_forward's
+ * definitions (z_j = x_j / tau; lse, logprob = z_t - lse, entropy), computed
+ * row_chunk rows at a time.  targets is indexed by row id (length n_rows) and
+ * may be NULL when logprob is NULL.  err_scale (nullable, [m]) gets
+ * (A_t + max_j A_j) / tau with A_j the abs_sum of column j and t the target
+ * (max_j A_j / tau alone when targets is NULL): the bound on how far an
+ * evaluation with logit errors |dx_j| <= eps * A_j can move logprob.
+ */
+int oracle_lmhead_forward(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
+                          const uint16_t *weight, int64_t vocab, int64_t ldw,
+                          int64_t d, const int32_t *targets, const int32_t *rows,
+                          int64_t m, double tau, int64_t row_chunk,
+                          double *logprob, double *lse, double *entropy,
+                          double *err_scale);
 
 /* Round a double to the nearest bf16 (ties to even); returns the bit pattern. */
 uint16_t oracle_bf16_rne(double v);

@@ -39,6 +39,16 @@ MUTATIONS = [
      "/* no clamp */", "topk"),
     ("bf16 rounding ties away", "double r = rint(v / q) * q;", "double r = round(v / q) * q;",
      "bf16"),
+    ("LM head reads the weight transposed",
+     "double p = decode_bf16(h[k]) * decode_bf16(w[k]);",
+     "double p = decode_bf16(h[k]) * decode_bf16(weight[k * ldw + j]);", "lmhead"),
+    ("LM head hidden row by output index", "const uint16_t *h = hidden + row_of(rows, i) * ldh;",
+     "const uint16_t *h = hidden + i * ldh;", "lmhead"),
+    ("LM head drops the last hidden column", "for (int64_t k = 0; k < d; ++k) {",
+     "for (int64_t k = 0; k + 1 < d; ++k) {", "lmhead"),
+    ("LM head target of the output index",
+     "sub_targets[i] = targets ? targets[sub_rows[i]] : 0;",
+     "sub_targets[i] = targets ? targets[c0 + i] : 0;", "lmhead"),
 ]
 
 

@@ -541,3 +541,164 @@ def test_topk_kl_truncated_clamp_and_tail_guard():
     want = q * 0.5
     want[:K] -= 0.5 / K
     np.testing.assert_allclose(gtl[1], want, rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- LM head
+#
+# The fused LM head ("[Bug] Training/log-prob forward materializes full-vocab fp32
+# logits ...", maintainer comment: project only the loss-mask rows of the final
+# hidden state; "[RL][Performance] Avoid full-vocabulary TP gather ...",
+# "Alternatives considered": a fused LM-head / cross-entropy kernel): logits
+# x = hidden @ weight^T, then the same logprob / lse / entropy.
+
+
+def _bf16(a):
+    return W.float32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+@pytest.fixture(scope="module")
+def lm_tiny():
+    w = W.get("lmhead_bf16_300x2000_d320")
+    wt = W.lmhead_weight(w)
+    return w, W.lmhead_hidden(w, weight=wt), wt, W.targets(w)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_lmhead_matches_torch_fp64(lm_tiny, tau):
+    """torch fp64 matmul of the decoded operands, then torch's cross_entropy,
+    logsumexp and Categorical entropy."""
+    _, h, wt, t = lm_tiny
+    rows = np.array([0, 5, 17, 255, 256, 299], np.int32)
+    o = oracle.lmhead_forward(h, wt, t, tau=tau, rows=rows)
+    hf = torch.from_numpy(W.bf16_bits_to_float32(h[rows])).double()
+    wf = torch.from_numpy(W.bf16_bits_to_float32(wt)).double()
+    z = (hf @ wf.T) / float(np.float32(tau))
+    ce = torch.nn.functional.cross_entropy(z, torch.from_numpy(t[rows]).long(), reduction="none")
+    np.testing.assert_allclose(o["logprob"], -ce.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(o["lse"], torch.logsumexp(z, 1).numpy(), rtol=0, atol=1e-11)
+    ent = torch.distributions.Categorical(logits=z).entropy().numpy()
+    np.testing.assert_allclose(o["entropy"], ent, rtol=0, atol=1e-11)
+
+
+def test_lmhead_logits_exact_sums(lm_tiny):
+    """Each logit equals the exactly rounded sum of its bf16 products (math.fsum)."""
+    _, h, wt, _ = lm_tiny
+    x = oracle.lmhead_logits(h[:3], wt[:40])
+    hf = W.bf16_bits_to_float32(h[:3]).astype(np.float64)
+    wf = W.bf16_bits_to_float32(wt[:40]).astype(np.float64)
+    for i in range(3):
+        for j in range(40):
+            exact = math.fsum(hf[i] * wf[j])
+            assert abs(x[i, j] - exact) <= 1e-12 * max(1.0, abs(exact))
+
+
+def test_lmhead_onehot_hidden_reads_weight_column():
+    """A hidden row c * e_k projects onto column k of the weight: the result equals
+    the plain forward on the logits c * weight[:, k] (catches a transposed weight or
+    a wrong hidden row)."""
+    rng = np.random.default_rng(11)
+    vocab, d = 37, 12
+    wt = _bf16(rng.standard_normal((vocab, d)))
+    ks = np.array([3, 0, 11, 7])
+    h = np.zeros((4, d), np.float32)
+    h[np.arange(4), ks] = [2.0, 0.5, 1.0, 4.0]
+    t = np.array([5, 36, 0, 19], np.int32)
+    o = oracle.lmhead_forward(_bf16(h), wt, t, tau=0.7)
+    cols = W.bf16_bits_to_float32(wt)[:, ks].T * np.array([[2.0], [0.5], [1.0], [4.0]],
+                                                           np.float32)
+    ref = oracle.forward(cols.astype(np.float32), t, tau=0.7)
+    for k in ("logprob", "lse", "entropy"):
+        np.testing.assert_allclose(o[k], ref[k], rtol=0, atol=1e-13)
+
+
+def test_lmhead_zero_weight_is_uniform():
+    """All logits zero: logprob = -ln V, lse = ln V, entropy = ln V (to the rounding
+    of a 1000-term double sum)."""
+    vocab, d = 1000, 64
+    h = _bf16(np.random.default_rng(2).standard_normal((5, d)))
+    o = oracle.lmhead_forward(h, np.zeros((vocab, d), np.uint16), np.arange(5, dtype=np.int32))
+    np.testing.assert_allclose(o["logprob"], -math.log(vocab), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o["lse"], math.log(vocab), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o["entropy"], math.log(vocab), rtol=0, atol=1e-12)
+
+
+def test_lmhead_two_entries_closed_form():
+    """V = 2: with D = (x_1 - x_0) / tau, logprob of entry 0 is -log(1 + e^D), of entry
+    1 is -log(1 + e^-D), and the entropy is the binary entropy of sigmoid(D)."""
+    rng = np.random.default_rng(5)
+    d, tau = 24, 0.7
+    wt = _bf16(rng.standard_normal((2, d)))
+    h = _bf16(rng.standard_normal((6, d)))
+    t = np.array([0, 1, 0, 1, 0, 1], np.int32)
+    o = oracle.lmhead_forward(h, wt, t, tau=tau)
+    hf = W.bf16_bits_to_float32(h).astype(np.float64)
+    wf = W.bf16_bits_to_float32(wt).astype(np.float64)
+    tf = float(np.float32(tau))
+    for i in range(6):
+        D = (math.fsum(hf[i] * wf[1]) - math.fsum(hf[i] * wf[0])) / tf
+        lp = -math.log1p(math.exp(D)) if t[i] == 0 else -math.log1p(math.exp(-D))
+        p1 = 1.0 / (1.0 + math.exp(-D))
+        ent = -(p1 * math.log(p1) + (1 - p1) * math.log(1 - p1))
+        x0 = math.fsum(hf[i] * wf[0]) / tf
+        assert abs(o["logprob"][i] - lp) <= 1e-13
+        assert abs(o["lse"][i] - (x0 + math.log1p(math.exp(D)))) <= 1e-13
+        assert abs(o["entropy"][i] - ent) <= 1e-13
+
+
+def test_lmhead_shift_invariance():
+    """Adding one vector u to every weight row moves every logit by h . u: logprob
+    and entropy stay, lse moves by (h . u) / tau.  Small integers keep the bf16
+    operands and their sums exact."""
+    rng = np.random.default_rng(8)
+    vocab, d, tau = 300, 16, 0.7
+    wi = rng.integers(-8, 9, size=(vocab, d)).astype(np.float32)
+    u = rng.integers(-4, 5, size=d).astype(np.float32)
+    hi = (rng.integers(-8, 9, size=(7, d)) / 8.0).astype(np.float32)
+    t = rng.integers(0, vocab, size=7).astype(np.int32)
+    a = oracle.lmhead_forward(_bf16(hi), _bf16(wi), t, tau=tau)
+    b = oracle.lmhead_forward(_bf16(hi), _bf16(wi + u), t, tau=tau)
+    shift = np.array([math.fsum(hi[i].astype(np.float64) * u) for i in range(7)])
+    tf = float(np.float32(tau))
+    np.testing.assert_allclose(b["logprob"], a["logprob"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b["entropy"], a["entropy"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(b["lse"] - a["lse"], shift / tf, rtol=0, atol=1e-12)
+
+
+def test_lmhead_compact_rows_and_padding(lm_tiny):
+    """A row subset gives the dense result at those rows, and columns past d (here
+    NaN) are never read."""
+    w, h, wt, t = lm_tiny
+    rows = np.array([299, 3, 3, 128, 0], np.int32)
+    dense = oracle.lmhead_forward(h, wt, t)
+    hp = np.full((h.shape[0], w.hidden + 24), 0x7FC0, np.uint16)
+    hp[:, : w.hidden] = h
+    wp = np.full((wt.shape[0], w.hidden + 8), 0x7FC0, np.uint16)
+    wp[:, : w.hidden] = wt
+    comp = oracle.lmhead_forward(hp, wp, t, rows=rows, d=w.hidden)
+    for k in ("logprob", "lse", "entropy"):
+        np.testing.assert_array_equal(comp[k], dense[k][rows])
+
+
+def test_lmhead_err_scale():
+    """With every product positive, A_j equals the logit itself: err_scale is
+    (x_t + max_j x_j) / tau."""
+    rng = np.random.default_rng(3)
+    vocab, d, tau = 50, 8, 0.7
+    wt = _bf16(rng.uniform(0.1, 1.0, (vocab, d)))
+    h = _bf16(rng.uniform(0.1, 1.0, (4, d)))
+    t = np.array([1, 2, 3, 49], np.int32)
+    o = oracle.lmhead_forward(h, wt, t, tau=tau, err_scale=True)
+    x = oracle.lmhead_logits(h, wt)
+    tf = float(np.float32(tau))
+    np.testing.assert_allclose(o["err_scale"], (x[np.arange(4), t] + x.max(1)) / tf,
+                               rtol=1e-14, atol=0)
+
+
+def test_lmhead_rejects_bad_arguments(lm_tiny):
+    _, h, wt, t = lm_tiny
+    with pytest.raises(oracle.OracleError):
+        oracle.lmhead_forward(h, wt, np.full_like(t, 2000))
+    with pytest.raises(oracle.OracleError):
+        oracle.lmhead_forward(h, wt, t, rows=np.array([300], np.int32))
+    with pytest.raises(oracle.OracleError):
+        oracle.lmhead_forward(h, wt, t, d=321)

@@ -21,7 +21,11 @@ Workload shapes follow the pages' own workloads:
   * packed sequences where only response spans carry loss follow the slime
     issue ("Steps to Reproduce");
   * the tiny [64, 2048] case follows the verl PR's small test (V=2048, odd
-    chunk sizes).
+    chunk sizes);
+  * the LM-head workloads project bf16 hidden states of size d = 2560 (the pages
+    name 4B-class Qwen models but not their hidden size; 2560 is that size) onto
+    the 248320-entry vocabulary, keeping the loss-mask rows of packed sequences
+    before the projection, as the slime issue's maintainer comment proposes.
 """
 from __future__ import annotations
 
@@ -34,7 +38,8 @@ from typing import Callable
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "scaled", "logits_rows", "targets", "loss_mask",
-           "grad_out", "row_index", "fill_logits", "bf16_bits_to_float32", "float32_to_bf16_bits"]
+           "grad_out", "row_index", "fill_logits", "bf16_bits_to_float32", "float32_to_bf16_bits",
+           "lmhead_weight", "lmhead_weight_rows", "lmhead_hidden", "lmhead_hidden_rows"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -59,6 +64,11 @@ class Workload:
     n_slices: int = 1              # vocabulary slices for the split-V path
     topk: int = 0                  # teacher top-k payload size (distillation workloads)
     topk_boost: float = 0.0        # student logits at the teacher's columns get + U(0, boost)
+    hidden: int = 0                # LM-head workloads: hidden size d (> 0); sigma is then the
+                                   # standard deviation of the logits hidden . weight_j
+    align_prob: float = 0.0        # LM head: rows whose hidden state leans toward the target's
+    align_lo: float = 0.0          # weight row, raising the target logit by U(align_lo,
+    align_hi: float = 0.0          # align_hi) on average
 
     @property
     def esize(self) -> int:
@@ -100,6 +110,17 @@ WORKLOADS = {
     "distill_bf16_4096x248320_k128": Workload(
         "distill_bf16_4096x248320_k128", "bf16", 4096, 248320, 2.0, seed=6, topk=128,
         topk_boost=6.0),
+    # Fused LM head, small: bf16 hidden [300, 320] and weight [2000, 320] (ragged in
+    # every tile dimension), logits ~ N(0, 2^2), half of the rows confident.
+    "lmhead_bf16_300x2000_d320": Workload(
+        "lmhead_bf16_300x2000_d320", "bf16", 300, 2000, 2.0, seed=7, hidden=320,
+        align_prob=0.5, align_lo=2.0, align_hi=10.0),
+    # Fused LM head at the pages' vocabulary: 4 packed sequences of 4096 tokens with a
+    # 2048-token response span each (8192 loss rows of 16384), d = 2560.
+    "lmhead_bf16_16384x248320_d2560": Workload(
+        "lmhead_bf16_16384x248320_d2560", "bf16", 16384, 248320, 2.0, seed=8, hidden=2560,
+        mask="packed", n_seqs=4, response_len=2048, align_prob=0.5, align_lo=4.0,
+        align_hi=16.0),
 }
 
 
@@ -266,6 +287,99 @@ def loss_mask(w: Workload) -> np.ndarray:
 def row_index(w: Workload) -> np.ndarray:
     """Ascending int32 row ids where the loss mask is set."""
     return np.flatnonzero(loss_mask(w)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------- LM head
+
+def _weight_sigma(w: Workload) -> float:
+    return w.sigma / float(np.sqrt(w.hidden))
+
+
+_WEIGHT_BLOCK = 256
+
+
+def _weight_block_values(w: Workload, b: int) -> np.ndarray:
+    """float32 weight rows [b * 256, min((b + 1) * 256, vocab)) before storage rounding;
+    one counter-based stream per block of 256 vocabulary rows."""
+    j0 = b * _WEIGHT_BLOCK
+    n = min(_WEIGHT_BLOCK, w.vocab - j0)
+    x = _gen(w, "weight", b).standard_normal((n, w.hidden), dtype=np.float32)
+    x *= np.float32(_weight_sigma(w))
+    return x
+
+
+def lmhead_weight_rows(w: Workload, rows, ld: int | None = None) -> np.ndarray:
+    """bf16 bits [len(rows), ld] of the output-layer weight (one row per vocabulary
+    entry), entries N(0, (sigma / sqrt(d))^2) so that a N(0, 1) hidden state gives
+    logits of standard deviation sigma."""
+    rows = np.atleast_1d(np.asarray(rows, dtype=np.int64))
+    ld = w.hidden if ld is None else ld
+    if rows.size and (rows.min() < 0 or rows.max() >= w.vocab):
+        raise IndexError(f"weight rows outside [0, {w.vocab})")
+    out = np.zeros((rows.shape[0], ld), np.uint16)
+    for b in np.unique(rows // _WEIGHT_BLOCK):
+        sel = np.flatnonzero(rows // _WEIGHT_BLOCK == b)
+        blk = float32_to_bf16_bits(_weight_block_values(w, int(b)))
+        out[sel, : w.hidden] = blk[rows[sel] - b * _WEIGHT_BLOCK]
+    return out
+
+
+def lmhead_weight(w: Workload, ld: int | None = None, threads: int | None = None) -> np.ndarray:
+    """The whole weight [vocab, ld] as bf16 bits (blocks generated in parallel)."""
+    ld = w.hidden if ld is None else ld
+    out = np.zeros((w.vocab, ld), np.uint16)
+
+    def make(b):
+        j0 = b * _WEIGHT_BLOCK
+        out[j0: j0 + _WEIGHT_BLOCK, : w.hidden] = float32_to_bf16_bits(_weight_block_values(w, b))
+
+    nblk = (w.vocab + _WEIGHT_BLOCK - 1) // _WEIGHT_BLOCK
+    with ThreadPoolExecutor(max_workers=threads or default_threads()) as ex:
+        list(ex.map(make, range(nblk)))
+    return out
+
+
+def lmhead_hidden_rows(w: Workload, rows, ld: int | None = None,
+                       weight: np.ndarray | None = None) -> np.ndarray:
+    """bf16 bits [len(rows), ld] of the final hidden states.  Each row is N(0, 1); on a
+    Bernoulli(align_prob) subset a multiple of the target's weight row is added,
+    alpha * W_t / (sigma_w^2 d) with alpha ~ U(align_lo, align_hi), which raises the
+    target logit by about alpha.  `weight` (the bf16 weight, if already generated)
+    saves regenerating the target rows."""
+    rows = np.atleast_1d(np.asarray(rows, dtype=np.int64))
+    ld = w.hidden if ld is None else ld
+    tg = targets(w)
+    out = np.zeros((rows.shape[0], ld), np.uint16)
+    sw2d = np.float32(_weight_sigma(w) ** 2 * w.hidden)
+    for i, r in enumerate(rows):
+        if not 0 <= r < w.n_rows:
+            raise IndexError(f"row {r} outside [0, {w.n_rows})")
+        x = _gen(w, "hidden", int(r)).standard_normal(w.hidden, dtype=np.float32)
+        if w.align_prob > 0.0:
+            g = _gen(w, "align", int(r))
+            if g.random() < w.align_prob:
+                alpha = np.float32(g.uniform(w.align_lo, w.align_hi))
+                wrow = (weight[tg[r], : w.hidden] if weight is not None
+                        else lmhead_weight_rows(w, [tg[r]])[0])
+                x += alpha * bf16_bits_to_float32(wrow) / sw2d
+        out[i, : w.hidden] = float32_to_bf16_bits(x)
+    return out
+
+
+def lmhead_hidden(w: Workload, ld: int | None = None, threads: int | None = None,
+                  weight: np.ndarray | None = None) -> np.ndarray:
+    """All hidden rows [n_rows, ld] as bf16 bits."""
+    ld = w.hidden if ld is None else ld
+    out = np.empty((w.n_rows, ld), np.uint16)
+    starts = list(range(0, w.n_rows, 256))
+
+    def make(r0):
+        out[r0: r0 + 256] = lmhead_hidden_rows(w, np.arange(r0, min(r0 + 256, w.n_rows)), ld,
+                                               weight=weight)
+
+    with ThreadPoolExecutor(max_workers=threads or default_threads()) as ex:
+        list(ex.map(make, starts))
+    return out
 
 
 def grad_out(w: Workload) -> np.ndarray:

@@ -307,6 +307,40 @@ vwc_status vwc_partial_combine(const vwc_partial *parts, int32_t k, int64_t rows
 vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,
                              hipStream_t stream);
 
+/*
+ * Fused LM head ([D] maintainer comment: keep the loss-mask rows of the final
+ * hidden state before the vocabulary projection and compute log-prob and
+ * entropy on those rows only; [A] "Alternatives considered": a fused
+ * LM-head / cross-entropy kernel; the merge of [E] "Implementation" joins the
+ * vocabulary segments).  For output i with row r = row_idx ? row_idx[i] : i:
+ *   x_j = sum_{k<d} hidden[r, k] * weight[j, k]      (bf16 x bf16, fp32 sum)
+ * and then lse / logprob / entropy of x as above.  The logits exist only in
+ * registers: nothing of size rows x vocab is ever written.
+ *  hidden   bf16 [n_rows, ldh], the final hidden states (after the last norm).
+ *  weight   bf16 [vocab, ldw], the output layer, one row per vocabulary entry.
+ *  d        the hidden size: columns [0, d) of both are used; d <= ldh, ldw.
+ *  targets  int32[n_rows] by row id (required when logprob is requested).
+ *  row_idx  int32[m] kept row ids (nullable: then m must equal n_rows).
+ *  logprob, lse, entropy  float[m], compact, each nullable (one required).
+ *  workspace  16-byte aligned, at least vwc_lmhead_workspace_bytes(m, vocab, d)
+ *           bytes with row_idx (16 bytes per row per segment of 1024
+ *           vocabulary entries, then the m kept rows compacted, m * d * 2
+ *           bytes rounded up to 16); without row_idx the partials alone.
+ * Layout limits (VWC_ERR_UNSUPPORTED otherwise): hidden and weight 16-byte
+ * aligned, d, ldh and ldw multiples of 8, ldh and ldw below 2^22.  m > 0
+ * needs n_rows >= 1.  A row id
+ * outside [0, n_rows) gives NaN outputs; a target outside [0, vocab) gives a
+ * NaN logprob.  The reduction order of a row depends only on vocab and d,
+ * so a row gives bit-identical results whatever row set it is computed in.
+ */
+size_t vwc_lmhead_workspace_bytes(int64_t rows, int64_t vocab, int64_t d);
+
+vwc_status vwc_lmhead_logprob_fwd(const void *hidden, int64_t n_rows, int64_t ldh,
+                                  const void *weight, int64_t vocab, int64_t ldw, int64_t d,
+                                  const int32_t *targets, const int32_t *row_idx, int64_t m,
+                                  float temperature, float *logprob, float *lse, float *entropy,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code (host pointer, never NULL). */
 const char *vwc_status_string(vwc_status status);
 

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
 
@@ -150,3 +150,68 @@ def test_partial_combine_and_mask_validation(lib):
     assert mk(FAKE, 2 ** 31, FAKE, FAKE, None) == INVALID
     assert mk(FAKE, 4, FAKE, None, None) == INVALID
     assert mk(None, 4, FAKE, FAKE, None) == INVALID
+
+
+def _lmhead(lib):
+    f = lib.vwc_lmhead_logprob_fwd
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [p, i64, i64, p, i64, i64, i64, p, p, i64, ctypes.c_float, p, p, p, p,
+                  ctypes.c_size_t, p]
+    f.restype = ctypes.c_int
+    return f
+
+
+def test_lmhead_workspace_bytes(lib):
+    f = lib.vwc_lmhead_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    # 248320 = 970 tiles of 256 -> 243 segments of 4 tiles, then the kept rows
+    assert f(8192, 248320, 2560) == 8192 * 243 * 16 + 8192 * 2560 * 2
+    assert f(300, 2000, 320) == 300 * 2 * 16 + 300 * 320 * 2
+    assert f(1, 1, 8) == 16 + 16
+    assert f(0, 2000, 8) == 0
+    assert f(5, 0, 8) == 0
+    assert f(5, 10, 0) == 0
+
+
+def test_lmhead_validation(lib):
+    f = _lmhead(lib)
+    err = lib.vwc_last_error
+    err.restype = ctypes.c_char_p
+    ws = ctypes.c_void_p(0x200000)
+    big = 1 << 40
+    H, Wt = FAKE, ctypes.c_void_p(0x300000)
+
+    def call(hidden=H, n=4, ldh=64, weight=Wt, vocab=1000, ldw=64, d=64, targets=FAKE,
+             rows=None, m=4, tau=1.0, lp=FAKE, lse=None, ent=None, w=ws, wsb=big):
+        return f(hidden, n, ldh, weight, vocab, ldw, d, targets, rows, m, tau, lp, lse, ent, w,
+                 wsb, None)
+
+    assert call(n=-1) == INVALID
+    assert call(m=-1) == INVALID
+    assert call(vocab=0) == INVALID
+    assert call(d=0) == INVALID
+    assert call(d=72) == INVALID            # d > ldh
+    assert call(ldw=56) == INVALID          # d > ldw
+    for tau in (0.0, -2.0, float("inf"), float("nan")):
+        assert call(tau=tau) == INVALID
+    assert call(m=3) == INVALID             # dense call needs m == n_rows
+    assert call(n=0, rows=FAKE, m=3) == INVALID
+    assert call(hidden=None) == INVALID
+    assert call(weight=None) == INVALID
+    assert call(targets=None) == INVALID    # logprob needs targets
+    assert call(lp=None) == INVALID         # no output at all
+    # layout limits
+    assert call(hidden=ctypes.c_void_p(0x100008)) == UNSUPPORTED
+    assert call(d=60, ldh=64, ldw=64) == UNSUPPORTED
+    assert call(ldh=68, d=64) == UNSUPPORTED
+    assert call(ldh=1 << 22) == UNSUPPORTED
+    # workspace: required, large enough, aligned
+    assert call(w=None, wsb=0) == INVALID
+    assert b"workspace" in err()
+    assert call(wsb=4 * 1 * 16 - 1) == INVALID  # 4 rows x 1 segment
+    assert call(w=ctypes.c_void_p(0x200008)) == INVALID
+    # nothing to do: OK without touching any pointer
+    assert call(hidden=None, weight=None, targets=None, lp=None, m=0, n=0, w=None,
+                wsb=0) == OK
+    assert err() == b""

@@ -1,0 +1,215 @@
+"""GPU parity of the fused LM head (vwc_lmhead_logprob_fwd) against the fp64 oracle.
+
+Two input families:
+  * lattice inputs (hidden on multiples of 1/8, weight on multiples of 1/64): every
+    partial sum of every logit is exact in fp32 in any order, so the GPU's logits
+    equal the oracle's and logprob / lse / entropy must agree to 5e-5 absolute,
+    the bound of the plain logits path;
+  * Gaussian inputs (the named workloads): the fp32 accumulation of d bf16 products
+    moves a logit by at most about sqrt(d) * 2^-24 * A_j under a random-rounding
+    model (A_j = sum_k |h_k w_jk|); with a factor 4 on that standard deviation the
+    allowance is 5e-5 + 4 sqrt(d) 2^-24 (A_t + max_j A_j) / tau, the oracle's
+    err_scale output.
+Row sets are compared bit for bit: a row's reduction order depends only on
+(vocab, d).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocab_wide_cross_amd as vwc
+import workloads as W
+from gpu_util import DEV, assert_close_scalar, log
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def _dev_bf16(host: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(host).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def _np(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def _run(h, wt, tg, rows=None, tau=1.0, d=None, entropy=True):
+    hd, wd = _dev_bf16(h), _dev_bf16(wt)
+    td = torch.from_numpy(np.ascontiguousarray(tg, np.int32)).to(DEV)
+    rd = None if rows is None else torch.from_numpy(np.ascontiguousarray(rows, np.int32)).to(DEV)
+    want = ("logprob", "lse", "entropy") if entropy else ("logprob", "lse")
+    lp, ls, en = vwc.lmhead_logprob_fwd(hd, wd, td, rd, temperature=tau, want=want, d=d)
+    torch.cuda.synchronize()
+    return {"logprob": _np(lp), "lse": _np(ls), "entropy": _np(en)}
+
+
+def _compare(got, ref, atol, what):
+    errs = {}
+    for k in ("logprob", "lse", "entropy"):
+        if got.get(k) is None or k not in ref:
+            continue
+        tol = atol if np.isscalar(atol) else atol
+        errs[k] = assert_close_scalar(got[k], ref[k], f"{what} {k}", atol=tol)
+    return errs
+
+
+def _gauss_tol(w, ref):
+    return 5e-5 + 4.0 * math.sqrt(w.hidden) * U32 * ref["err_scale"]
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = W.get("lmhead_bf16_300x2000_d320")
+    wt = W.lmhead_weight(w)
+    return w, W.lmhead_hidden(w, weight=wt), wt, W.targets(w)
+
+
+@pytest.fixture(scope="module")
+def tiny_lattice():
+    w = W.scaled("lmhead_bf16_300x2000_d320", 300, 2000, lattice=True)
+    wt = W.lmhead_weight(w)
+    return w, W.lmhead_hidden(w, weight=wt), wt, W.targets(w)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+@pytest.mark.parametrize("ent", [True, False])
+def test_lattice_exact_logits(tiny_lattice, tau, ent):
+    w, h, wt, tg = tiny_lattice
+    log(f"lmhead lattice 300x2000 d320 tau={tau} entropy={ent}")
+    got = _run(h, wt, tg, tau=tau, entropy=ent)
+    ref = oracle.lmhead_forward(h, wt, tg, tau=tau)
+    errs = _compare(got, ref, 5e-5, "lattice")
+    log(f"  max errors {errs}")
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_gaussian_small(tiny, tau):
+    w, h, wt, tg = tiny
+    log(f"lmhead gaussian 300x2000 d320 tau={tau}")
+    got = _run(h, wt, tg, tau=tau)
+    ref = oracle.lmhead_forward(h, wt, tg, tau=tau, err_scale=True)
+    tol = _gauss_tol(w, ref)
+    for k in ("logprob", "lse", "entropy"):
+        err = np.abs(got[k].astype(np.float64) - ref[k])
+        assert (err <= tol).all(), f"{k}: max err {err.max():.3g}, allowance {tol.min():.3g}"
+        log(f"  {k}: max err {err.max():.3g} (allowance >= {tol.min():.3g})")
+
+
+# (m rows, vocab, d, ldh pad, ldw pad): one token tile or several, ragged vocabulary
+# tiles and segments (a wave's half of the last tile empty or partial), hidden
+# sizes below one stage and ragged in the last stage, NaN in the padding columns.
+SHAPES = [
+    (1, 1, 8, 0, 0),
+    (3, 129, 64, 8, 0),
+    (255, 256, 200, 0, 24),
+    (257, 1000, 328, 16, 8),
+    (64, 1025, 64, 0, 0),
+    (513, 4097, 136, 8, 8),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}_d{s[2]}" for s in SHAPES])
+def test_ragged_shapes_with_nan_padding(shape):
+    m, vocab, d, ph, pw = shape
+    w = W.scaled("lmhead_bf16_300x2000_d320", m, vocab, hidden=d, lattice=True)
+    log(f"lmhead ragged m={m} vocab={vocab} d={d} pad=({ph},{pw})")
+    wt = np.full((vocab, d + pw), 0x7FC0, np.uint16)
+    wt[:, :d] = W.lmhead_weight(w)
+    h = np.full((m, d + ph), 0x7FC0, np.uint16)
+    h[:, :d] = W.lmhead_hidden(w, weight=wt)
+    tg = W.targets(w)
+    got = _run(h, wt, tg, tau=0.7, d=d)
+    ref = oracle.lmhead_forward(h, wt, tg, tau=0.7, d=d)
+    _compare(got, ref, 5e-5, f"ragged {shape}")
+
+
+def test_row_sets_bitwise(tiny):
+    """A row gives the same bits whether it is computed with all rows or in a
+    compact, unordered row set with duplicates."""
+    w, h, wt, tg = tiny
+    log("lmhead row sets 300x2000")
+    dense = _run(h, wt, tg)
+    rows = np.array([299, 0, 17, 17, 256, 255, 3, 128, 299], np.int32)
+    comp = _run(h, wt, tg, rows=rows)
+    for k in ("logprob", "lse", "entropy"):
+        assert np.array_equal(comp[k].view(np.uint32), dense[k][rows].view(np.uint32)), k
+    one = _run(h, wt, tg, rows=np.array([128], np.int32))
+    for k in ("logprob", "lse", "entropy"):
+        assert one[k].view(np.uint32)[0] == dense[k].view(np.uint32)[128], k
+
+
+def test_bad_row_ids_and_targets(tiny):
+    w, h, wt, tg = tiny
+    log("lmhead bad ids")
+    tg2 = tg.copy()
+    tg2[5] = -1
+    tg2[6] = w.vocab
+    rows = np.array([4, 5, 6, -1, 300, 7], np.int32)
+    got = _run(h, wt, tg2, rows=rows)
+    assert np.isnan(got["logprob"][[1, 2, 3, 4]]).all()
+    assert np.isfinite(got["lse"][[0, 1, 2, 5]]).all()
+    assert np.isnan(got["lse"][[3, 4]]).all() and np.isnan(got["entropy"][[3, 4]]).all()
+    ok = np.array([0, 5])
+    ref = oracle.lmhead_forward(h, wt, tg2, rows=rows[ok], err_scale=True)
+    tol = _gauss_tol(w, ref)
+    assert (np.abs(got["logprob"][ok] - ref["logprob"]) <= tol).all()
+    # lse and entropy do not need the target, so the bad-target rows still match
+    ref2 = oracle.lmhead_forward(h, wt, None, rows=rows[[1, 2]], want=("lse", "entropy"),
+                                 err_scale=True)
+    for k in ("lse", "entropy"):
+        assert (np.abs(got[k][[1, 2]] - ref2[k]) <= _gauss_tol(w, ref2)).all()
+
+
+def test_empty_row_set(tiny):
+    w, h, wt, tg = tiny
+    out = vwc.lmhead_logprob_fwd(_dev_bf16(h), _dev_bf16(wt),
+                                 torch.from_numpy(tg).to(DEV),
+                                 torch.empty(0, dtype=torch.int32, device=DEV))
+    assert out[0].numel() == 0 and out[1].numel() == 0
+
+
+# ------------------------------------------------------------------ full size
+
+
+def _sample(m):
+    """Rows at tile edges and spread through the row set."""
+    s = {0, 1, 255, 256, m // 2, m - 257, m - 1}
+    s |= set(np.random.default_rng(17).choice(m, 9, replace=False).tolist())
+    return np.array(sorted(x for x in s if 0 <= x < m), np.int64)
+
+
+def _fullsize(w):
+    log(f"generating {w.name}")
+    wt = W.lmhead_weight(w)
+    h = W.lmhead_hidden(w, weight=wt)
+    tg = W.targets(w)
+    rows = W.row_index(w)
+    log(f"  weight {wt.shape}, hidden {h.shape}, {rows.size} kept rows")
+    got = _run(h, wt, tg, rows=rows)
+    log("  gpu done")
+    sel = _sample(rows.size)
+    ref = oracle.lmhead_forward(h, wt, tg, rows=rows[sel], err_scale=True)
+    log(f"  oracle done on {sel.size} rows")
+    return got, ref, sel
+
+
+def test_fullsize_lattice():
+    w = W.scaled("lmhead_bf16_16384x248320_d2560", 16384, 248320, lattice=True)
+    got, ref, sel = _fullsize(w)
+    errs = _compare({k: v[sel] for k, v in got.items()}, ref, 5e-5, "full lattice")
+    log(f"  max errors {errs}")
+
+
+def test_fullsize_gaussian():
+    w = W.get("lmhead_bf16_16384x248320_d2560")
+    got, ref, sel = _fullsize(w)
+    tol = _gauss_tol(w, ref)
+    for k in ("logprob", "lse", "entropy"):
+        err = np.abs(got[k][sel].astype(np.float64) - ref[k])
+        assert (err <= tol).all(), f"{k}: max err {err.max():.3g}, allowance {tol.min():.3g}"
+        log(f"  {k}: max err {err.max():.3g} (allowance >= {tol.min():.3g})")
+    assert np.isfinite(got["logprob"]).all() and (got["logprob"] <= 1e-6).all()

@@ -60,6 +60,9 @@ def _load() -> ctypes.CDLL:
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
+        "vwc_lmhead_workspace_bytes": ([i64, i64, i64], sz),
+        "vwc_lmhead_logprob_fwd": ([p, i64, i64, p, i64, i64, i64, p, p, i64, f32, p, p, p, p, sz,
+                                    p], i32),
         "vwc_status_string": ([i32], ctypes.c_char_p),
         "vwc_last_error": ([], ctypes.c_char_p),
         "vwc_abi_version": ([], i32),
@@ -366,3 +369,38 @@ def mask_to_index(mask, row_idx=None, count=None, stream=None):
     _check(_lib.vwc_mask_to_index(_ptr(mask), n, _ptr(row_idx), _ptr(count),
                                   _stream(stream, mask)))
     return row_idx, count
+
+
+def lmhead_workspace_bytes(rows: int, vocab: int, d: int) -> int:
+    return int(_lib.vwc_lmhead_workspace_bytes(rows, vocab, d))
+
+
+def lmhead_logprob_fwd(hidden, weight, targets=None, row_idx=None, temperature=1.0,
+                       logprob=None, lse=None, entropy=None, want=("logprob", "lse"), d=None,
+                       workspace=None, stream=None):
+    """Fused LM head: logprob / lse / entropy of hidden[row_idx] @ weight.T without
+    materialising the logits.  hidden [n_rows, >= d] and weight [vocab, >= d] are
+    bfloat16 with unit column stride; outputs are compact [m] float32."""
+    for t, name in ((hidden, "hidden"), (weight, "weight")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    n, kh, ldh = _rows_view(hidden)
+    v, kw, ldw = _rows_view(weight)
+    d = min(kh, kw) if d is None else int(d)
+    if targets is not None:
+        _i32(targets, "targets")
+    if row_idx is not None:
+        _i32(row_idx, "row_idx")
+    m = n if row_idx is None else row_idx.numel()
+    lp = _f32(m, hidden, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(m, hidden, lse) if (lse is not None or "lse" in want) else None
+    en = _f32(m, hidden, entropy) if (entropy is not None or "entropy" in want) else None
+    need = lmhead_workspace_bytes(m, v, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.vwc_lmhead_logprob_fwd(_ptr(hidden), n, ldh, _ptr(weight), v, ldw, d,
+                                       _ptr(targets), _ptr(row_idx), m, float(temperature),
+                                       _ptr(lp), _ptr(ls), _ptr(en), _ptr(workspace), wsb,
+                                       _stream(stream, hidden)))
+    return lp, ls, en

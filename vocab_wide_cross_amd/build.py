@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libvwc.so")
-SOURCES = ["vwc_kernels.hip", "vwc_api.cpp"]
+SOURCES = ["vwc_kernels.hip", "vwc_lmhead.hip", "vwc_api.cpp"]
 
 
 def hipcc() -> str:

@@ -462,6 +462,107 @@ vwc_status vwc_partial_combine(const vwc_partial *parts, int32_t k, int64_t rows
     return hip_status(vwc::launch_combine(p, stream), fn);
 }
 
+static int64_t lmhead_segments(int64_t vocab) {
+    const int64_t tiles = (vocab + vwc::kLmVoc - 1) / vwc::kLmVoc;
+    return (tiles + vwc::kLmSegTiles - 1) / vwc::kLmSegTiles;
+}
+
+// Workspace: the segment partials, then (16-byte aligned) the compacted
+// kept hidden rows.
+static size_t lmhead_partial_bytes(int64_t rows, int64_t vocab) {
+    return static_cast<size_t>(rows) * static_cast<size_t>(lmhead_segments(vocab)) *
+           sizeof(vwc_partial);
+}
+
+size_t vwc_lmhead_workspace_bytes(int64_t rows, int64_t vocab, int64_t d) {
+    if (rows <= 0 || vocab <= 0 || d <= 0) return 0;
+    const size_t gather = (static_cast<size_t>(rows) * static_cast<size_t>(d) * 2 + 15) / 16 * 16;
+    return lmhead_partial_bytes(rows, vocab) + gather;
+}
+
+vwc_status vwc_lmhead_logprob_fwd(const void *hidden, int64_t n_rows, int64_t ldh,
+                                  const void *weight, int64_t vocab, int64_t ldw, int64_t d,
+                                  const int32_t *targets, const int32_t *row_idx, int64_t m,
+                                  float temperature, float *logprob, float *lse, float *entropy,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "vwc_lmhead_logprob_fwd";
+    if (n_rows < 0 || m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: n_rows < 0 or m < 0", fn);
+    if (vocab <= 0) return fail(VWC_ERR_INVALID_ARG, "%s: vocab must be positive", fn);
+    if (d <= 0 || ldh < d || ldw < d)
+        return fail(VWC_ERR_INVALID_ARG, "%s: need 0 < d <= ldh and d <= ldw", fn);
+    if (!(temperature > 0.f) || !isfinite(temperature))
+        return fail(VWC_ERR_INVALID_ARG, "%s: temperature must be finite and > 0", fn);
+    if (m == 0) return ok();
+    if (!row_idx && m != n_rows)
+        return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
+    if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
+    if (!hidden || !weight) return fail(VWC_ERR_INVALID_ARG, "%s: hidden or weight is null", fn);
+    if (logprob && !targets) return fail(VWC_ERR_INVALID_ARG, "%s: targets is null", fn);
+    if (!logprob && !lse && !entropy)
+        return fail(VWC_ERR_INVALID_ARG, "%s: no output requested", fn);
+    if (reinterpret_cast<uintptr_t>(hidden) % 16 || reinterpret_cast<uintptr_t>(weight) % 16 ||
+        d % 8 || ldh % 8 || ldw % 8)
+        return fail(VWC_ERR_UNSUPPORTED,
+                    "%s: hidden and weight must be 16-byte aligned, d, ldh, ldw multiples of 8",
+                    fn);
+    // Tiles are addressed with 32-bit byte offsets: 256 rows of ldh or ldw
+    // elements must stay below 2^31 bytes.
+    if (vocab > INT32_MAX - vwc::kLmVoc || ldh >= (int64_t{1} << 22) ||
+        ldw >= (int64_t{1} << 22) || n_rows > INT64_MAX / 2 / ldh ||
+        vocab > INT64_MAX / 2 / ldw || m > INT64_MAX / 2 / d)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: operand too large", fn);
+    const int64_t nseg = lmhead_segments(vocab);
+    const int64_t ntb = (m + vwc::kLmTok - 1) / vwc::kLmTok;
+    if (ntb > INT32_MAX / nseg)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: %lld rows exceed one launch", fn,
+                    static_cast<long long>(m));
+    const size_t part_bytes = lmhead_partial_bytes(m, vocab);
+    const size_t need = row_idx ? vwc_lmhead_workspace_bytes(m, vocab, d) : part_bytes;
+    if (!workspace || workspace_bytes < need)
+        return fail(VWC_ERR_INVALID_ARG, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                    workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return fail(VWC_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+
+    vwc::LmPlan p{};
+    p.hidden = static_cast<const uint16_t *>(hidden);
+    p.ldh = ldh;
+    p.n_rows = n_rows;
+    if (row_idx) {  // keep the listed rows, in order, before the projection
+        uint16_t *compact = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + part_bytes);
+        hipError_t ge = vwc::launch_gather_rows(p.hidden, ldh, n_rows, row_idx, m,
+                                                static_cast<int32_t>(d), compact, stream);
+        if (ge != hipSuccess) return hip_status(ge, fn);
+        p.hidden = compact;
+        p.ldh = d;
+    }
+    p.weight = static_cast<const uint16_t *>(weight);
+    p.ldw = ldw;
+    p.vocab = static_cast<int32_t>(vocab);
+    p.d = static_cast<int32_t>(d);
+    p.targets = logprob ? targets : nullptr;
+    p.row_idx = row_idx;
+    p.m = m;
+    const double tau = static_cast<double>(temperature);
+    p.c = static_cast<float>(1.44269504088896340736 / tau);
+    p.ntb = static_cast<int>(ntb);
+    p.nvt = static_cast<int>((vocab + vwc::kLmVoc - 1) / vwc::kLmVoc);
+    p.nseg = static_cast<int>(nseg);
+    p.seg_part = static_cast<vwc_partial *>(workspace);
+    hipError_t e = vwc::launch_lmhead_fwd(p, entropy != nullptr, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    vwc::CombinePlan cp{};
+    cp.parts = p.seg_part;
+    cp.k = p.nseg;
+    cp.stride = m;
+    cp.rows = m;
+    cp.tau = tau;
+    cp.logprob = logprob;
+    cp.lse = lse;
+    cp.entropy = entropy;
+    return hip_status(vwc::launch_combine(cp, stream), fn);
+}
+
 vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,
                              hipStream_t stream) {
     const char *fn = "vwc_mask_to_index";

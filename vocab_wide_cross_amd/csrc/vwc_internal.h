@@ -126,6 +126,43 @@ struct TopkPlan {
     int64_t ld_grad;
 };
 
+// Fused LM head: logits of a tile of kept hidden rows against a tile of the
+// output-layer weight on MFMA, folded straight into lane states.
+constexpr int kLmTok = 256;        // hidden rows (tokens) per workgroup tile
+constexpr int kLmVoc = 256;        // vocabulary rows per tile
+#ifndef VWC_LM_K
+#define VWC_LM_K 64
+#endif
+constexpr int kLmK = VWC_LM_K;     // hidden columns per pipeline stage
+#ifndef VWC_LM_SEG_TILES
+#define VWC_LM_SEG_TILES 4
+#endif
+// Vocabulary tiles one workgroup folds into one partial; fixed, so the
+// reduction order of a row never depends on how many rows a call covers.
+constexpr int kLmSegTiles = VWC_LM_SEG_TILES;
+
+struct LmPlan {
+    const uint16_t *hidden;   // bf16 kept rows in output order: row i is output i
+    int64_t ldh;              // elements between those rows
+    int64_t n_rows;           // rows of the caller's hidden tensor (row ids are checked against it)
+    const uint16_t *weight;   // bf16 [vocab, ldw]
+    int64_t ldw;
+    int32_t vocab;
+    int32_t d;
+    const int32_t *targets;   // by row id; null: no target
+    const int32_t *row_idx;   // null: output i is row i
+    int64_t m;
+    float c;                  // log2(e) / tau rounded to float
+    int ntb;                  // token tiles: ceil(m / kLmTok)
+    int nvt;                  // vocabulary tiles: ceil(vocab / kLmVoc)
+    int nseg;                 // ceil(nvt / kLmSegTiles)
+    vwc_partial *seg_part;    // [nseg][m]
+};
+
+hipError_t launch_lmhead_fwd(const LmPlan &p, bool want_entropy, hipStream_t stream);
+hipError_t launch_gather_rows(const uint16_t *hidden, int64_t ldh, int64_t n_rows,
+                              const int32_t *row_idx, int64_t m, int32_t d, uint16_t *out,
+                              hipStream_t stream);
 hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream);
 hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream);
 hipError_t launch_topk_fixup(const TopkPlan &p, hipStream_t stream);

@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include "vwc_internal.h"
+#include "vwc_lane.h"
 
 namespace vwc {
 namespace {
@@ -47,7 +48,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr double kLn2 = 0.69314718055994530942;
 constexpr double kLog2e = 1.44269504088896340736;
 // A chunk whose sum of 2^u exceeds this re-centres K (u > 64 means the logit
 // is more than 64 * ln 2 = 44.4 nats above the reference).
@@ -147,17 +147,6 @@ template <int DT>
 __device__ __forceinline__ float load_element(const char *row, int64_t j) {
     return Unit<DT, false>::get(reinterpret_cast<const typename Unit<DT, false>::T *>(row)[j], 0);
 }
-
-// ---------------------------------------------------------------- lane state
-
-struct Lane {
-    float K;  // shift, log2 units; -inf until the first finite logit
-    float m;  // reference logit: K == fl(m * c)
-    float s;  // sum of 2^u, u = fl(x * c - K)
-    float w;  // sum of 2^u * u (terms with 2^u == 0 add 0)
-};
-
-__device__ __forceinline__ Lane lane_init() { return Lane{-INFINITY, -INFINITY, 0.f, 0.f}; }
 
 // Re-centre a lane on a chunk (units [0, nvalid) of v, still in registers)
 // and return the chunk's (sum, w) relative to the new K.  Rare: a new maximum
@@ -310,24 +299,6 @@ __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_
     }
 }
 
-// Merge lane state b into a (fixed, commutative rule: the larger K is kept).
-__device__ __forceinline__ void merge(Lane &a, const Lane &b) {
-    const bool swap = b.K > a.K;
-    const Lane &big = swap ? b : a;
-    const Lane &sml = swap ? a : b;
-    const float d = sml.K - big.K;  // <= 0 (NaN when both are empty)
-    const float r = __builtin_amdgcn_exp2f(d);
-    const bool has = sml.s != 0.f;  // true for NaN too, so NaN propagates
-    const float add_s = has ? r * sml.s : 0.f;
-    const float add_w = has ? r * __builtin_fmaf(d, sml.s, sml.w) : 0.f;
-    Lane o;
-    o.K = big.K;
-    o.m = (a.K == b.K) ? fmaxf(a.m, b.m) : big.m;
-    o.s = big.s + add_s;
-    o.w = big.w + add_w;
-    a = o;
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return bits_to_float(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
@@ -380,30 +351,6 @@ __device__ __forceinline__ Lane block_reduce(Lane L) {
 #pragma unroll
     for (int q = 1; q < kFwdBlock / 64; ++q) merge(acc, wave_state[q]);
     return acc;
-}
-
-// fp64 view of a partial.
-struct P64 {
-    double m, s, t, w;
-};
-
-// Lane state -> partial relative to its reference logit m (see vwc_partial).
-__device__ __forceinline__ P64 to_partial(const Lane &L, float c, double t) {
-    P64 p;
-    p.t = t;
-    if (!(L.s != 0.f)) {  // empty segment
-        p.m = -INFINITY;
-        p.s = 0.0;
-        p.w = 0.0;
-        return p;
-    }
-    // sum 2^{(x - m) c} = 2^rho * s with rho = K - m c, exact in fp64.
-    const double rho = static_cast<double>(L.K) - static_cast<double>(L.m) * static_cast<double>(c);
-    const double f = exp2(rho);
-    p.m = L.m;
-    p.s = static_cast<double>(L.s) * f;
-    p.w = kLn2 * f * (static_cast<double>(L.w) + rho * static_cast<double>(L.s));
-    return p;
 }
 
 // Merge partials in order (formulas in the vwc_partial comment).

@@ -1,0 +1,497 @@
+// vwc_lmhead.hip -- fused LM head for gfx950: the logits of the kept hidden
+// rows against the output-layer weight, computed on MFMA and folded straight
+// into log-sum-exp lane states, so no logit ever reaches HBM.
+//
+// Method (web pages, cited by title and section):
+//  * "[Bug] Training/log-prob forward materializes full-vocab fp32 logits over
+//    the entire packed sequence ...", maintainer comment: keep only the
+//    loss-mask rows of the final hidden state before the vocabulary
+//    projection, then compute log-probability and entropy on those rows.
+//  * "[RL][Performance] Avoid full-vocabulary TP gather for selected-token
+//    logprobs", "Alternatives considered": a fused LM-head / cross-entropy
+//    kernel.
+//  * "feat: Reduce reference model memory with with parallel logprob
+//    computation", "Implementation": per-shard max / sum of exponentials /
+//    owned target logit, merged once per row.  Here the shards are the
+//    vocabulary segments of one workgroup each.
+//
+// Design for gfx950:
+//  * One 256-thread workgroup owns a tile of 256 kept rows (tokens) and a
+//    segment of kLmSegTiles vocabulary tiles of 256 rows of the weight.  Its
+//    4 waves split the 256 x 256 logit tile 2 x 2; each wave holds a 128 x 128
+//    block as 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (256 fp32 per
+//    lane, in AGPRs).  The product is weight_tile x hidden_tile^T, so in every
+//    accumulator lane l holds 16 vocabulary rows of token l % 32.
+//  * The hidden dimension streams through LDS in stages of 64 columns, double
+//    buffered: the global loads of stage s + 1 are in flight while the MFMAs
+//    of stage s run, across vocabulary-tile boundaries too.  Both operands are
+//    K-contiguous rows, staged as 128-byte rows whose 16-byte chunks are
+//    XOR-swizzled so that the MFMA fragment reads (ds_read_b128) and the
+//    staging writes hit distinct banks.
+//  * After the last stage of a vocabulary tile each lane folds its 64 logits
+//    per token into the token's lane state (K, m, s, w) with one FMA and one
+//    v_exp_f32 per logit; lanes l and l ^ 32 and the two vocabulary halves
+//    merge at the end of the segment, and the workgroup writes one 16-byte
+//    partial per row.  The split-V combine merges a row's segment partials in
+//    segment order in fp64.
+//  * blockIdx runs over token tiles first, so the workgroups resident at once
+//    cover few vocabulary tiles: each weight tile is read from HBM about once
+//    and shared through L2 by every token tile; consecutive blockIdx values go
+//    to different XCDs, which gives each XCD 1/8 of the token tiles of the
+//    same vocabulary segments.
+#include <math.h>
+#include <stdint.h>
+
+#include "vwc_internal.h"
+#include "vwc_lane.h"
+
+namespace vwc {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kLmK * 2;               // one staged tile row
+constexpr int kTileBytes = kLmVoc * kRowBytes;    // one staged operand tile
+constexpr int kStageBytes = 2 * kTileBytes;       // weight tile + hidden tile
+constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per staged row
+constexpr int kRowsPerInst = 1024 / kRowBytes;    // rows one wave load instruction fills
+constexpr int kInstPerTile = 64 / kRowsPerInst;   // per wave and operand tile
+constexpr int kLoadsPerStage = 2 * kInstPerTile;  // per wave
+constexpr int kSteps = kLmK / 16;                 // MFMA k-steps per stage
+#ifdef VWC_LM_STAGES
+constexpr int kStages = VWC_LM_STAGES;            // LDS ring of stages
+#else
+constexpr int kStages = kLmK == 64 ? 2 : 4;
+#endif
+static_assert(kLmTok == kLmVoc, "the staging assumes square tiles");
+static_assert(kLmK == 32 || kLmK == 64, "stage widths of 64 or 128 bytes per row");
+static_assert(kStages >= 2 && kStages * kStageBytes <= 160 * 1024, "LDS ring too large");
+constexpr float kUFloor = -256.0f;
+
+// Chunk c (16 bytes) of staged row r sits at chunk position c ^ swz(r), so
+// that the rows one group of lanes reads in a cycle (one logical chunk of 8 or
+// 16 consecutive rows) land on distinct banks.  swz depends only on r % 16.
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (kChunks == 8)
+        return (r >> 1) & 7;
+    else
+        return ((r >> 1) ^ (r >> 2)) & 3;
+}
+
+// s_waitcnt vmcnt(n), other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `ahead` stages of this wave's loads are outstanding.
+__device__ __forceinline__ void wait_stages(int ahead) {
+    if (ahead <= 0) {
+        wait_vmcnt<0>();
+    } else if (ahead == 1) {
+        wait_vmcnt<kLoadsPerStage>();
+    } else if (ahead == 2) {
+        wait_vmcnt<2 * kLoadsPerStage>();
+    } else {
+        static_assert(kStages <= 5, "extend wait_stages");
+        wait_vmcnt<3 * kLoadsPerStage>();
+    }
+}
+
+__device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32); }
+
+// Fold the logits of token column j of the accumulators into lane state L.
+// Row (i, r) of the wave's 128 vocabulary rows is i * 32 + (r / 4) * 8 +
+// (l / 32) * 4 + r % 4; with MASK, rows at or past vlim (relative to the
+// lane's half) are outside the vocabulary and skipped.
+//
+// One pass with the lane's current shift K: u = x c - K, s += 2^u, w += 2^u u.
+// K is seeded from the lane's first logit and only moves (an exact-maximum
+// re-centre over the tile, rarely taken) when the tile's sum leaves
+// [0, 2^64] or turns NaN, as in the streaming forward.
+constexpr float kTileBound = 0x1p64f;
+
+template <bool MASK, bool ENT>
+__device__ __forceinline__ void fold_recentre(const f32x16 (&acc)[4][4], int j, float c, int vlim,
+                                              Lane &L, float &cs, float &cw) {
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (r & 3);
+            if (!MASK || row < vlim) cm = fmaxf(cm, acc[i][j][r]);
+        }
+    const float Kn = cm * c;
+    if (Kn > L.K) {
+        if (L.s != 0.f) {
+            const float d = L.K - Kn;
+            const float rr = __builtin_amdgcn_exp2f(d);
+            L.w = rr * __builtin_fmaf(d, L.s, L.w);
+            L.s = rr * L.s;
+        }
+        L.K = Kn;
+        L.m = cm;
+    }
+    cs = 0.f;
+    cw = 0.f;
+    if (L.K == -INFINITY) return;  // nothing finite in this lane yet
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (r & 3);
+            if (MASK && row >= vlim) continue;
+            const float u = __builtin_fmaf(acc[i][j][r], c, -L.K);
+            const float e = __builtin_amdgcn_exp2f(u);
+            cs += e;
+            if (ENT) cw = __builtin_fmaf(e, fmaxf(u, kUFloor), cw);
+        }
+}
+
+template <bool MASK, bool ENT>
+__device__ __forceinline__ void fold_column(const f32x16 (&acc)[4][4], int j, float c, int vlim,
+                                            Lane &L) {
+    if (L.K == -INFINITY && (!MASK || vlim > 0)) {  // seed with the lane's first logit
+        const float x0 = acc[0][j][0];
+        if (x0 > -INFINITY) {
+            L.m = x0;
+            L.K = x0 * c;
+        }
+    }
+    float s0 = 0.f, s1 = 0.f, w0 = 0.f, w1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (r & 3);
+            const float u = __builtin_fmaf(acc[i][j][r], c, -L.K);
+            float e = __builtin_amdgcn_exp2f(u);
+            if (MASK && row >= vlim) e = 0.f;
+            if (r & 1) {
+                s1 += e;
+                if (ENT) w1 = __builtin_fmaf(e, u, w1);
+            } else {
+                s0 += e;
+                if (ENT) w0 = __builtin_fmaf(e, u, w0);
+            }
+        }
+    }
+    float cs = s0 + s1;
+    float cw = w0 + w1;
+    // Re-centre when the tile needs a new shift, or when masked rows (u
+    // possibly infinite while the lane has no shift yet) or -inf logits left a
+    // NaN; NaN logits also land there and stay NaN through s.
+    if (!(cs <= kTileBound) || (ENT && cw != cw)) fold_recentre<MASK, ENT>(acc, j, c, vlim, L, cs, cw);
+    L.s += cs;
+    if (ENT) L.w += cw;
+}
+
+template <bool ENT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void lmhead_fwd_kernel(LmPlan p) {
+    __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;  // vocabulary half of the tile
+    const int wn = wave & 1;   // token half of the tile
+    const int tb = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.ntb));
+    const int seg = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.ntb));
+    const int vt0 = seg * kLmSegTiles;
+    const int vt1 = min(vt0 + kLmSegTiles, p.nvt);
+
+    // Staging role.  Stages go from global memory straight into LDS
+    // (buffer_load ... lds, 16 bytes per lane): one wave instruction fills
+    // 1 KiB, i.e. kRowsPerInst staged rows, lane L writing chunk position
+    // L % kChunks of row L / kChunks.  Wave w fills rows [64 w, 64 w + 64) of
+    // both tiles, kRowsPerInst per instruction q, so lane L fetches logical
+    // chunk cq[q] = (L % kChunks) ^ swz(row) of row 64 w + kRowsPerInst q +
+    // L / kChunks.
+    const int srow = wave * 64 + lane / kChunks;
+    int cq[kInstPerTile];
+    // Both operands come through buffer resources whose size stops at the last
+    // valid row (vocabulary rows of the weight tile, kept rows of the token
+    // tile), so rows past it read as zero; chunks past the hidden size are sent
+    // out of range too.  The token tile is row tb * 256 of p.hidden, which
+    // holds the kept rows in order (compacted beforehand when a row list is
+    // given).  Offsets stay below 256 * ld * 2 < 2^31.
+    uint32_t aoff[kInstPerTile], hoff[kInstPerTile];
+#pragma unroll
+    for (int q = 0; q < kInstPerTile; ++q) {
+        const int row = srow + kRowsPerInst * q;
+        cq[q] = (lane % kChunks) ^ swz(row);
+        aoff[q] = static_cast<uint32_t>(row * p.ldw * 2 + cq[q] * 16);
+        hoff[q] = static_cast<uint32_t>(row * p.ldh * 2 + cq[q] * 16);
+    }
+    const int trows = static_cast<int>(min(static_cast<int64_t>(kLmTok),
+                                           p.m - static_cast<int64_t>(tb) * kLmTok));
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.hidden + static_cast<int64_t>(tb) * kLmTok * p.ldh), 0,
+        static_cast<int>(trows * p.ldh * 2), 0x00020000);
+
+    // MFMA role: fragment rows and the swizzled chunk of each 16-column step.
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    const int a_off = (wm * 128 + fr) * kRowBytes;
+    const int b_off = kTileBytes + (wn * 128 + fr) * kRowBytes;
+    int koff[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) koff[s] = ((2 * s + fh) ^ swz(fr)) << 4;
+
+    // Targets of the lane's 4 token columns (-1: none, or outside the vocabulary).
+    int tg[4];
+    float tv[4];
+    Lane L[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t i = static_cast<int64_t>(tb) * kLmTok + wn * 128 + j * 32 + fr;
+        tg[j] = -1;
+        if (p.targets && i < p.m) {
+            const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+            if (r >= 0 && r < p.n_rows) {
+                const int32_t t = p.targets[r];
+                if (t >= 0 && t < p.vocab) tg[j] = t;
+            }
+        }
+        tv[j] = -INFINITY;
+        L[j] = lane_init();
+    }
+
+    // Stages run over (vocabulary tile, 32-column step) pairs, kStages in the
+    // ring.  The next stage to load is step lkt of the weight tile at lw, into
+    // ring slot lslot.
+    const int nk = (p.d + kLmK - 1) / kLmK;
+    const int nstage = (vt1 - vt0) * nk;
+    const int64_t wtile = static_cast<int64_t>(kLmVoc) * p.ldw;  // elements per weight tile
+    const uint16_t *lw = p.weight + vt0 * wtile;
+    int lrem = p.vocab - vt0 * kLmVoc;  // vocabulary rows from that tile on
+    int lkt = 0, lslot = 0, lg = 0;
+    char *const wlds = lds + wave * 64 * kRowBytes;  // this wave's rows of slot 0
+    auto load_next = [&]() {
+        const int k0 = lkt * kLmK;
+        char *A = wlds + lslot * kStageBytes;
+        char *B = A + kTileBytes;
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(lw), 0, min(lrem, kLmVoc) * static_cast<int>(p.ldw) * 2,
+            0x00020000);
+#pragma unroll
+        for (int q = 0; q < kInstPerTile; ++q) {
+            // Chunks past the hidden size get the top offset bit: out of range.
+            const uint32_t kb = static_cast<uint32_t>(k0 * 2) |
+                                (k0 + cq[q] * 8 < p.d ? 0u : 0x80000000u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, A + q * kRowsPerInst * kRowBytes, 16,
+                                                     aoff[q] + kb, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, B + q * kRowsPerInst * kRowBytes, 16,
+                                                     hoff[q] + kb, 0, 0, 0);
+        }
+        ++lg;
+        if (++lslot == kStages) lslot = 0;
+        if (++lkt == nk) {
+            lkt = 0;
+            lw += wtile;
+            lrem -= kLmVoc;
+        }
+    };
+    auto read_frags = [&](int slot, int s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+        const char *S = lds + slot * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = *reinterpret_cast<const bf16x8 *>(S + a_off + i * 32 * kRowBytes + koff[s]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b[j] = *reinterpret_cast<const bf16x8 *>(S + b_off + j * 32 * kRowBytes + koff[s]);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    bf16x8 fa[2][4], fb[2][4];
+
+    // Prologue: fill the ring, wait for stage 0.
+    for (int g = 0; g < kStages && g < nstage; ++g) load_next();
+    wait_stages(min(kStages, nstage) - 1);
+    __syncthreads();
+    if (nstage > 0) read_frags(0, 0, fa[0], fb[0]);
+
+    int g = 0;     // stage being computed
+    int slot = 0;  // its ring slot
+    for (int vt = vt0; vt < vt1; ++vt) {
+        for (int kt = 0; kt < nk; ++kt, ++g) {
+            const int nslot = slot + 1 == kStages ? 0 : slot + 1;
+            const bool more = g + 1 < nstage;
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                // Step s of stage g.  The fragments of the next step (step 0 of
+                // stage g + 1 after the last step, unless stage g ends the tile:
+                // they are read after the fold then) go out one by one between
+                // the first MFMAs.
+                const bool next_here = s + 1 < kSteps;
+                if (next_here)
+                    read_frags(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                else if (more && kt + 1 < nk)
+                    read_frags(nslot, 0, fa[0], fb[0]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
+                if (next_here) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (s == kSteps - 2) {
+                    // Every read of stage g's slot has been issued by now (the
+                    // last step's fragments were read during this step), and the
+                    // barrier waits for them; once this wave's loads of stage
+                    // g + 1 have landed, the barrier also makes that stage
+                    // visible to all.  Stage g's slot then takes stage g + kStages.
+                    if (more) wait_stages(min(nstage - 1, g + kStages - 1) - (g + 1));
+                    __syncthreads();
+                    if (lg < nstage) load_next();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            slot = nslot;
+        }
+
+        // Fold the tile's logits into the lane states (the next stages' loads
+        // are in flight meanwhile).
+        const int vbase = vt * kLmVoc + wm * 128;  // vocabulary id of the wave's row 0
+        // Target logits: the lane holding row tg - vbase of its token keeps it.
+        bool mine = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mine |= static_cast<unsigned>(tg[j] - vbase) < 128u;
+        if (__ballot(mine)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tl = tg[j] - vbase - fh * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (tl == i * 32 + (r >> 2) * 8 + (r & 3)) tv[j] = acc[i][j][r];
+            }
+        }
+        const int vlim = p.vocab - vbase - fh * 4;
+        if (vbase + 128 > p.vocab) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fold_column<true, ENT>(acc, j, p.c, vlim, L[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fold_column<false, ENT>(acc, j, p.c, vlim, L[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        if (g < nstage) read_frags(slot, 0, fa[0], fb[0]);
+    }
+
+    // Lanes l and l ^ 32 hold other rows of the same tokens.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const Lane o{shfl_xor32(L[j].K), shfl_xor32(L[j].m), shfl_xor32(L[j].s),
+                     shfl_xor32(L[j].w)};
+        merge(L[j], o);
+        tv[j] = fmaxf(tv[j], shfl_xor32(tv[j]));
+    }
+    // The two vocabulary halves meet in LDS (the stage buffers are free now).
+    float *fin = reinterpret_cast<float *>(lds);
+    if (wm == 1 && lane < 32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float *f = fin + ((wn * 4 + j) * 32 + lane) * 5;
+            f[0] = L[j].K;
+            f[1] = L[j].m;
+            f[2] = L[j].s;
+            f[3] = L[j].w;
+            f[4] = tv[j];
+        }
+    }
+    __syncthreads();
+    if (wm != 0 || lane >= 32) return;
+    const int64_t v_lo = static_cast<int64_t>(vt0) * kLmVoc;
+    const int64_t v_hi = min(static_cast<int64_t>(vt1) * kLmVoc, static_cast<int64_t>(p.vocab));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float *f = fin + ((wn * 4 + j) * 32 + lane) * 5;
+        merge(L[j], Lane{f[0], f[1], f[2], f[3]});
+        const float t_here = fmaxf(tv[j], f[4]);
+        const int64_t i = static_cast<int64_t>(tb) * kLmTok + wn * 128 + j * 32 + lane;
+        if (i >= p.m) continue;
+        const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+        vwc_partial out;
+        if (r < 0 || r >= p.n_rows) {  // row id outside the hidden rows
+            out = vwc_partial{NAN, NAN, NAN, NAN};
+        } else {
+            double t = -INFINITY;
+            if (p.targets) {
+                const int64_t tt = p.targets[r];
+                if (tt < 0 || tt >= p.vocab) {
+                    if (seg == 0) t = NAN;
+                } else if (tt >= v_lo && tt < v_hi) {
+                    t = t_here;
+                }
+            }
+            const P64 q = to_partial(L[j], p.c, t);
+            out = vwc_partial{static_cast<float>(q.m), static_cast<float>(q.s),
+                              static_cast<float>(q.t), static_cast<float>(q.w)};
+        }
+        p.seg_part[static_cast<int64_t>(seg) * p.m + i] = out;
+    }
+}
+
+// Kept rows of the hidden states, in row-list order, into a dense [m, d]
+// array (the pages' compaction at the hidden-state boundary).  Row ids outside
+// [0, n_rows) give zero rows; their outputs are written as NaN later.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *hidden, int64_t ldh,
+                                                          int64_t n_rows, const int32_t *row_idx,
+                                                          int64_t m, int32_t d, uint16_t *out) {
+    const int64_t chunks = d / 8;  // 16-byte chunks per row
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= m * chunks) return;
+    const int64_t i = t / chunks;
+    const int64_t c = t - i * chunks;
+    const int64_t r = row_idx[i];
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r >= 0 && r < n_rows) v = *reinterpret_cast<const u32x4 *>(hidden + r * ldh + c * 8);
+    *reinterpret_cast<u32x4 *>(out + i * d + c * 8) = v;
+}
+
+}  // namespace
+
+hipError_t launch_gather_rows(const uint16_t *hidden, int64_t ldh, int64_t n_rows,
+                              const int32_t *row_idx, int64_t m, int32_t d, uint16_t *out,
+                              hipStream_t stream) {
+    const int64_t work = m * (d / 8);
+    const dim3 grid(static_cast<unsigned>((work + 255) / 256));
+    hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, stream, hidden, ldh, n_rows,
+                       row_idx, m, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_lmhead_fwd(const LmPlan &p, bool want_entropy, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.ntb) * p.nseg));
+    const dim3 block(kThreads);
+    if (want_entropy)
+        hipLaunchKernelGGL(lmhead_fwd_kernel<true>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(lmhead_fwd_kernel<false>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace vwc

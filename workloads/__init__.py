@@ -69,6 +69,10 @@ class Workload:
     align_prob: float = 0.0        # LM head: rows whose hidden state leans toward the target's
     align_lo: float = 0.0          # weight row, raising the target logit by U(align_lo,
     align_hi: float = 0.0          # align_hi) on average
+    lattice: bool = False          # LM head: hidden entries on multiples of 1/8 in [-4, 4],
+                                   # weight entries on multiples of 1/64, so every partial
+                                   # sum of a logit (|x| < 2^15, multiples of 2^-9) is exact
+                                   # in fp32 whatever the summation order
 
     @property
     def esize(self) -> int:
@@ -305,6 +309,8 @@ def _weight_block_values(w: Workload, b: int) -> np.ndarray:
     n = min(_WEIGHT_BLOCK, w.vocab - j0)
     x = _gen(w, "weight", b).standard_normal((n, w.hidden), dtype=np.float32)
     x *= np.float32(_weight_sigma(w))
+    if w.lattice:
+        x = np.clip(np.round(x * 64.0), -127.0, 127.0).astype(np.float32) / np.float32(64.0)
     return x
 
 
@@ -362,6 +368,8 @@ def lmhead_hidden_rows(w: Workload, rows, ld: int | None = None,
                 wrow = (weight[tg[r], : w.hidden] if weight is not None
                         else lmhead_weight_rows(w, [tg[r]])[0])
                 x += alpha * bf16_bits_to_float32(wrow) / sw2d
+        if w.lattice:
+            x = np.clip(np.round(x * 8.0), -32.0, 32.0).astype(np.float32) / np.float32(8.0)
         out[i, : w.hidden] = float32_to_bf16_bits(x)
     return out
 

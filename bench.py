@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 DEFAULT_WORKLOAD = "spiked_bf16_8192x248320"
 
 
@@ -273,6 +274,101 @@ def bench_other(args, w, x):
     return out
 
 
+def lmhead_cpu_baseline(w, h, wt, tg, rows, seconds):
+    """The fp64 oracle on kept rows of the same inputs, one row at a time (its own
+    OpenMP over vocabulary columns), until `seconds` have passed."""
+    import numpy as np
+
+    import oracle
+
+    sel = np.random.default_rng(11).permutation(rows.size)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds and done < sel.size:
+        r = rows[sel[done: done + 1]]
+        oracle.lmhead_forward(h, wt, tg, rows=r)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} kept rows of {w.name} in random order (fp64 projection of each "
+                      f"row against all {w.vocab} weight rows, then logprob+lse+entropy), "
+                      f"{el:.1f} s of oracle time"}
+
+
+def bench_lmhead(args, w):
+    """Fused LM head: logprob / lse (and entropy) of the kept hidden rows without
+    logits.  Timed beside it, as context: torch's bf16 GEMM (hipBLASLt) writing the
+    bf16 logits followed by this library's forward over them."""
+    import numpy as np
+    import torch
+
+    import vocab_wide_cross_amd as vwc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    t0 = time.time()
+    wt_h = W.lmhead_weight(w)
+    h_h = W.lmhead_hidden(w, weight=wt_h)
+    tg_h = W.targets(w)
+    rows_h = W.row_index(w)
+    wt = torch.from_numpy(wt_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    h = torch.from_numpy(h_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    tg = torch.from_numpy(tg_h).to(dev)
+    rows = torch.from_numpy(rows_h).to(dev)
+    M, V, d = rows_h.size, w.vocab, w.hidden
+    ws = torch.empty(vwc.lmhead_workspace_bytes(M, V, d), dtype=torch.uint8, device=dev)
+    lp, lse, ent = (torch.empty(M, device=dev) for _ in range(3))
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    flops = 2.0 * M * V * d
+    passes = [
+        ("lmhead_fwd(logprob,lse)",
+         lambda: vwc.lmhead_logprob_fwd(h, wt, tg, rows, w.tau, logprob=lp, lse=lse,
+                                        workspace=ws, stream=stream), flops),
+        ("lmhead_fwd(logprob,lse,entropy)",
+         lambda: vwc.lmhead_logprob_fwd(h, wt, tg, rows, w.tau, logprob=lp, lse=lse,
+                                        entropy=ent, workspace=ws, stream=stream), flops),
+    ]
+    ms, wall = time_passes(passes, args.steps, args.warmup, stream)
+    per_pass = [{"pass": n, "ms": m, "tflops": f / (m * 1e-3) / 1e12,
+                 "frac": f / (m * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+                for (n, _, f), m in zip(passes, ms)]
+    # Context: the unfused route materialises bf16 logits [M, V] with hipBLASLt.
+    hc = h[rows.long()].contiguous()
+    logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    ws2 = torch.empty(max(vwc.workspace_bytes(M, V, logits.dtype), 1), dtype=torch.uint8,
+                      device=dev)
+    unf = [("gather+torch_bf16_gemm", lambda: torch.matmul(h[rows.long()], wt.T, out=logits), flops),
+           ("fwd_over_logits", lambda: vwc.selected_logprob_fwd(logits, tg[rows.long()], w.tau,
+                                                                logprob=lp, lse=lse, workspace=ws2,
+                                                                stream=stream), 0)]
+    ums, _ = time_passes(unf, max(3, args.steps // 4), 1, stream)
+    del logits, hc
+    out = {
+        "metric": f"kept rows/s of the fused LM head ({w.name})",
+        "value": M / (ms[0] * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms[0], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": w.name, "hidden_rows": w.n_rows, "kept_rows": M, "vocab": V,
+                   "hidden": d, "temperature": w.tau},
+        "passes": per_pass,
+        "roofline": {"bound": "mfma", "kernel": "lmhead_fwd_kernel",
+                     "achieved": flops / (ms[0] * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / (ms[0] * 1e-3) / 1e12 /
+                     MFMA_BF16_PEAK_TFLOPS, "traffic": None, "avg_launch_ms": ms[0],
+                     "flops_alg_per_launch": flops,
+                     "note": "launch = row gather + MFMA kernel + segment merge (HIP events)"},
+        "unfused_context": {"gemm_ms": ums[0], "gemm_tflops": flops / (ums[0] * 1e-3) / 1e12,
+                            "fwd_over_logits_ms": ums[1], "total_ms": ums[0] + ums[1],
+                            "logits_bytes": M * V * 2},
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = lmhead_cpu_baseline(w, h_h, wt_h, tg_h, rows_h, args.cpu_seconds)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -289,6 +385,9 @@ def main():
 
     dev = torch.device("cuda:0")
     w = W.get(args.workload)
+    if w.hidden > 0:
+        print(json.dumps(bench_lmhead(args, w)))
+        return
     esize = 2 if w.dtype == "bf16" else 4
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 

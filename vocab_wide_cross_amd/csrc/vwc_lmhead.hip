@@ -53,22 +53,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
+constexpr int kLmGroup = 4;                       // token tiles per group of the work order
 constexpr int kRowBytes = kLmK * 2;               // one staged tile row
 constexpr int kTileBytes = kLmVoc * kRowBytes;    // one staged operand tile
-constexpr int kStageBytes = 2 * kTileBytes;       // weight tile + hidden tile
 constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per staged row
 constexpr int kRowsPerInst = 1024 / kRowBytes;    // rows one wave load instruction fills
 constexpr int kInstPerTile = 64 / kRowsPerInst;   // per wave and operand tile
-constexpr int kLoadsPerStage = 2 * kInstPerTile;  // per wave
 constexpr int kSteps = kLmK / 16;                 // MFMA k-steps per stage
-#ifdef VWC_LM_STAGES
-constexpr int kStages = VWC_LM_STAGES;            // LDS ring of stages
-#else
-constexpr int kStages = kLmK == 64 ? 2 : 4;
-#endif
+constexpr int kWPerStep = kInstPerTile / kSteps;  // weight load instructions per k-step
+// LDS rings of operand tiles.  The weight tile of stage g + 2 streams in during
+// stage g, kWPerStep load instructions per k-step, into the unit stage g - 1
+// freed; the hidden tile of stage g + 2 goes out in stage g's last k-step, into
+// the unit stage g frees.  Spreading the loads keeps each wave's memory queue
+// short: a load that cannot issue would hold up the MFMAs behind it.
+constexpr int kWS = 3;
+constexpr int kHS = 2;
 static_assert(kLmTok == kLmVoc, "the staging assumes square tiles");
 static_assert(kLmK == 32 || kLmK == 64, "stage widths of 64 or 128 bytes per row");
-static_assert(kStages >= 2 && kStages * kStageBytes <= 160 * 1024, "LDS ring too large");
+static_assert(kWS >= kHS && (kWS + kHS) * kTileBytes <= 160 * 1024, "LDS rings too large");
 constexpr float kUFloor = -256.0f;
 
 // Chunk c (16 bytes) of staged row r sits at chunk position c ^ swz(r), so
@@ -88,21 +90,34 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most `ahead` stages of this wave's loads are outstanding.
-__device__ __forceinline__ void wait_stages(int ahead) {
-    if (ahead <= 0) {
-        wait_vmcnt<0>();
-    } else if (ahead == 1) {
-        wait_vmcnt<kLoadsPerStage>();
-    } else if (ahead == 2) {
-        wait_vmcnt<2 * kLoadsPerStage>();
-    } else {
-        static_assert(kStages <= 5, "extend wait_stages");
-        wait_vmcnt<3 * kLoadsPerStage>();
-    }
+__device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32); }
+
+// Workgroup barrier without the memory fences of __syncthreads(): the fences
+// would also wait for the LDS loads that are meant to stay in flight.  The
+// waves' own LDS reads are waited for first (lgkmcnt(0)), so no slot is
+// refilled under a read; the loads the barrier must cover are waited for
+// explicitly (vmcnt) before it.
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
 }
 
-__device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32); }
+// Scheduling of one k-step (16 MFMAs): one LDS read and an even share of NV
+// loads after each of the first 8 MFMAs, then the remaining 8 MFMAs.
+template <int Q, int NV>
+__device__ __forceinline__ void interleave_group() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    constexpr int nq = NV * (Q + 1) / 8 - NV * Q / 8;
+    if constexpr (nq > 0) __builtin_amdgcn_sched_group_barrier(0x020, nq, 0);  // loads
+    if constexpr (Q + 1 < 8) interleave_group<Q + 1, NV>();
+}
+
+template <int NV>
+__device__ __forceinline__ void interleave() {
+    interleave_group<0, NV>();
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+}
 
 // Fold the logits of token column j of the accumulators into lane state L.
 // Row (i, r) of the wave's 128 vocabulary rows is i * 32 + (r / 4) * 8 +
@@ -191,18 +206,37 @@ __device__ __forceinline__ void fold_column(const f32x16 (&acc)[4][4], int j, fl
     if (ENT) L.w += cw;
 }
 
-template <bool ENT>
+template <bool ENT, bool RAGGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void lmhead_fwd_kernel(LmPlan p) {
-    __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds[(kWS + kHS) * kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
     const int wm = wave >> 1;  // vocabulary half of the tile
     const int wn = wave & 1;   // token half of the tile
-    const int tb = static_cast<int>(blockIdx.x % static_cast<unsigned>(p.ntb));
-    const int seg = static_cast<int>(blockIdx.x / static_cast<unsigned>(p.ntb));
+    // Work order.  Consecutive workgroups go to the 8 XCDs in turn, and each
+    // XCD has its own L2, so XCD x (blockIdx % 8) takes one contiguous block of
+    // the work list; the list runs over groups of kLmGroup token tiles, and
+    // over the vocabulary segments inside a group.  The workgroups an XCD runs
+    // at once then share a few token tiles and a few weight tiles in its L2.
+    int tb, seg;
+    {
+        const int T = p.ntb * p.nseg;
+        const int b = static_cast<int>(blockIdx.x);
+        const int per = T / 8, rem = T % 8;  // XCDs below rem take per + 1 items
+        const int x = b % 8, r = b / 8;
+        const int v = r < per ? (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + r
+                              : x * (per + 1) + per;
+        const int G = min(kLmGroup, p.ntb);
+        const int grp = v / (G * p.nseg);
+        const int g0 = grp * G;
+        const int gs = min(G, p.ntb - g0);  // token tiles in this group
+        const int w = v - grp * G * p.nseg;
+        seg = w / gs;
+        tb = g0 + w % gs;
+    }
     const int vt0 = seg * kLmSegTiles;
     const int vt1 = min(vt0 + kLmSegTiles, p.nvt);
 
@@ -239,7 +273,7 @@ void lmhead_fwd_kernel(LmPlan p) {
     const int fr = lane & 31;
     const int fh = lane >> 5;
     const int a_off = (wm * 128 + fr) * kRowBytes;
-    const int b_off = kTileBytes + (wn * 128 + fr) * kRowBytes;
+    const int b_off = (wn * 128 + fr) * kRowBytes;
     int koff[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) koff[s] = ((2 * s + fh) ^ swz(fr)) << 4;
@@ -263,49 +297,53 @@ void lmhead_fwd_kernel(LmPlan p) {
         L[j] = lane_init();
     }
 
-    // Stages run over (vocabulary tile, 32-column step) pairs, kStages in the
-    // ring.  The next stage to load is step lkt of the weight tile at lw, into
-    // ring slot lslot.
+    // Stages run over (vocabulary tile, kLmK-column step) pairs.
     const int nk = (p.d + kLmK - 1) / kLmK;
     const int nstage = (vt1 - vt0) * nk;
+    // LDS: kWS weight units, then kHS hidden units, one operand tile each.
+    char *const wlds = lds + wave * 64 * kRowBytes;             // this wave's rows of unit 0
+    char *const hlds = wlds + kWS * kTileBytes;
     const int64_t wtile = static_cast<int64_t>(kLmVoc) * p.ldw;  // elements per weight tile
-    const uint16_t *lw = p.weight + vt0 * wtile;
-    int lrem = p.vocab - vt0 * kLmVoc;  // vocabulary rows from that tile on
-    int lkt = 0, lslot = 0, lg = 0;
-    char *const wlds = lds + wave * 64 * kRowBytes;  // this wave's rows of slot 0
-    auto load_next = [&]() {
-        const int k0 = lkt * kLmK;
-        char *A = wlds + lslot * kStageBytes;
-        char *B = A + kTileBytes;
-        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(lw), 0, min(lrem, kLmVoc) * static_cast<int>(p.ldw) * 2,
-            0x00020000);
+    // Issue the loads of one operand tile: step k0 of the tile at base `rsrc`,
+    // into LDS at `dst` (this wave's rows).  With a hidden size that is not a
+    // multiple of kLmK, chunks past it get the top offset bit, which sends them
+    // out of range (read as zero).
+    auto load_tile = [&](const __amdgpu_buffer_rsrc_t rsrc, const uint32_t (&off)[kInstPerTile],
+                         char *dst, int k0, int q0, int nq) {
+        const uint32_t kb = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
-        for (int q = 0; q < kInstPerTile; ++q) {
-            // Chunks past the hidden size get the top offset bit: out of range.
-            const uint32_t kb = static_cast<uint32_t>(k0 * 2) |
-                                (k0 + cq[q] * 8 < p.d ? 0u : 0x80000000u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, A + q * kRowsPerInst * kRowBytes, 16,
-                                                     aoff[q] + kb, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, B + q * kRowsPerInst * kRowBytes, 16,
-                                                     hoff[q] + kb, 0, 0, 0);
-        }
-        ++lg;
-        if (++lslot == kStages) lslot = 0;
-        if (++lkt == nk) {
-            lkt = 0;
-            lw += wtile;
-            lrem -= kLmVoc;
+        for (int q = q0; q < q0 + nq; ++q) {
+            uint32_t o = off[q] + kb;
+            if (RAGGED) o |= k0 + cq[q] * 8 < p.d ? 0u : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst + q * kRowsPerInst * kRowBytes, 16,
+                                                     o, 0, 0, 0);
         }
     };
-    auto read_frags = [&](int slot, int s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-        const char *S = lds + slot * kStageBytes;
+    // Weight tiles: a buffer resource per tile (rows of the tile inside the
+    // vocabulary).  A stage past the segment's last (its loads are issued to
+    // keep the loop free of branches) gets an empty range: no memory is read
+    // and the unit, which no later stage uses, receives zeros.
+    auto w_rsrc = [&](int vt, bool live) {
+        const int rows = live ? min(p.vocab - vt * kLmVoc, kLmVoc) : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(p.weight + (live ? vt * wtile : 0)), 0,
+            rows * static_cast<int>(p.ldw) * 2, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t hr_none = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.hidden), 0, 0, 0x00020000);
+    auto load_h = [&](int k, int u, bool live) {
+        load_tile(live ? hr : hr_none, hoff, hlds + u * kTileBytes, k * kLmK, 0, kInstPerTile);
+    };
+    // Fragments of k-step s from weight unit wu and hidden unit hu.
+    auto read_frags = [&](int wu, int hu, int s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+        const char *SA = lds + wu * kTileBytes;
+        const char *SB = lds + (kWS + hu) * kTileBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            a[i] = *reinterpret_cast<const bf16x8 *>(S + a_off + i * 32 * kRowBytes + koff[s]);
+            a[i] = *reinterpret_cast<const bf16x8 *>(SA + a_off + i * 32 * kRowBytes + koff[s]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            b[j] = *reinterpret_cast<const bf16x8 *>(S + b_off + j * 32 * kRowBytes + koff[s]);
+            b[j] = *reinterpret_cast<const bf16x8 *>(SB + b_off + j * 32 * kRowBytes + koff[s]);
     };
 
     f32x16 acc[4][4];
@@ -315,57 +353,83 @@ void lmhead_fwd_kernel(LmPlan p) {
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     bf16x8 fa[2][4], fb[2][4];
 
-    // Prologue: fill the ring, wait for stage 0.
-    for (int g = 0; g < kStages && g < nstage; ++g) load_next();
-    wait_stages(min(kStages, nstage) - 1);
+    // Prologue: stages 0 and 1 whole (hidden tile, then weight tile); wait for
+    // stage 0.  (hk) is the step of the next hidden load, (wt, wk) the tile and
+    // step of the next weight load.
+    int hk = 0, wk = 0, wt = vt0;
+    auto step_h = [&]() { hk = hk + 1 == nk ? 0 : hk + 1; };
+    auto step_w = [&]() {
+        const bool wrap = wk + 1 == nk;
+        wk = wrap ? 0 : wk + 1;
+        wt += wrap ? 1 : 0;
+    };
+    for (int i = 0; i < 2 && i < nstage; ++i) {
+        load_h(hk, i, true);
+        step_h();
+        load_tile(w_rsrc(wt, true), aoff, wlds + i * kTileBytes, wk * kLmK, 0, kInstPerTile);
+        step_w();
+    }
+    if (nstage > 1)
+        wait_vmcnt<2 * kInstPerTile>();
+    else
+        wait_vmcnt<0>();
     __syncthreads();
-    if (nstage > 0) read_frags(0, 0, fa[0], fb[0]);
+    if (nstage > 0) read_frags(0, 0, 0, fa[0], fb[0]);
 
-    int g = 0;     // stage being computed
-    int slot = 0;  // its ring slot
+    int g = 0;               // stage being computed
+    int wu = 0, hu = 0;      // its units
     for (int vt = vt0; vt < vt1; ++vt) {
         for (int kt = 0; kt < nk; ++kt, ++g) {
-            const int nslot = slot + 1 == kStages ? 0 : slot + 1;
+            const int nwu = wu + 1 == kWS ? 0 : wu + 1;
+            const int nhu = hu + 1 == kHS ? 0 : hu + 1;
             const bool more = g + 1 < nstage;
+            // The weight tile of stage g + 2, unit (g + 2) % 3 = the one after nwu.
+            const __amdgpu_buffer_rsrc_t wr = w_rsrc(wt, g + 2 < nstage);
+            char *const wdst = wlds + (nwu + 1 == kWS ? 0 : nwu + 1) * kTileBytes;
+            const int wk0 = wk * kLmK;
+            step_w();
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 // Step s of stage g.  The fragments of the next step (step 0 of
-                // stage g + 1 after the last step, unless stage g ends the tile:
-                // they are read after the fold then) go out one by one between
-                // the first MFMAs.
+                // stage g + 1 after the last step) and this step's share of the
+                // weight loads go out one by one between the MFMAs; in the last
+                // step, so do the hidden loads that refill stage g's unit.
+                // (After the last stage the reads touch units nobody refills.)
                 const bool next_here = s + 1 < kSteps;
+                const bool last = s + 1 == kSteps;
                 if (next_here)
-                    read_frags(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-                else if (more && kt + 1 < nk)
-                    read_frags(nslot, 0, fa[0], fb[0]);
+                    read_frags(wu, hu, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                else
+                    read_frags(nwu, nhu, 0, fa[0], fb[0]);
+                load_tile(wr, aoff, wdst, wk0, s * kWPerStep, kWPerStep);
+                if (last) {
+                    load_h(hk, hu, g + kHS < nstage);
+                    step_h();
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
-                if (next_here) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-                }
+                if (last)
+                    interleave<kWPerStep + kInstPerTile>();
+                else
+                    interleave<kWPerStep>();
                 __builtin_amdgcn_sched_barrier(0);
                 if (s == kSteps - 2) {
-                    // Every read of stage g's slot has been issued by now (the
-                    // last step's fragments were read during this step), and the
-                    // barrier waits for them; once this wave's loads of stage
-                    // g + 1 have landed, the barrier also makes that stage
-                    // visible to all.  Stage g's slot then takes stage g + kStages.
-                    if (more) wait_stages(min(nstage - 1, g + kStages - 1) - (g + 1));
-                    __syncthreads();
-                    if (lg < nstage) load_next();
+                    // Every read of stage g's units has been issued by now (the
+                    // last step's fragments were read during this step) and the
+                    // barrier waits for them.  Stage g + 1's tiles went out in
+                    // earlier stages; only this stage's weight loads (for stage
+                    // g + 2) may still be in flight.
+                    if (more) wait_vmcnt<kWPerStep * (kSteps - 1)>();
+                    block_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            slot = nslot;
+            wu = nwu;
+            hu = nhu;
         }
 
         // Fold the tile's logits into the lane states (the next stages' loads
@@ -398,8 +462,12 @@ void lmhead_fwd_kernel(LmPlan p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-        if (g < nstage) read_frags(slot, 0, fa[0], fb[0]);
     }
+
+    // The last loads (of stages past the segment) must land before the LDS is
+    // reused below.
+    wait_vmcnt<0>();
+    __syncthreads();
 
     // Lanes l and l ^ 32 hold other rows of the same tokens.
 #pragma unroll
@@ -487,10 +555,18 @@ hipError_t launch_gather_rows(const uint16_t *hidden, int64_t ldh, int64_t n_row
 hipError_t launch_lmhead_fwd(const LmPlan &p, bool want_entropy, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.ntb) * p.nseg));
     const dim3 block(kThreads);
-    if (want_entropy)
-        hipLaunchKernelGGL(lmhead_fwd_kernel<true>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(lmhead_fwd_kernel<false>, grid, block, 0, stream, p);
+    const bool ragged = p.d % kLmK != 0;
+    if (want_entropy) {
+        if (ragged)
+            hipLaunchKernelGGL((lmhead_fwd_kernel<true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((lmhead_fwd_kernel<true, false>), grid, block, 0, stream, p);
+    } else {
+        if (ragged)
+            hipLaunchKernelGGL((lmhead_fwd_kernel<false, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((lmhead_fwd_kernel<false, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -93,13 +93,13 @@ def cpu_baseline(w, seconds):
                       f"{elapsed:.1f} s of oracle time"}
 
 
-def recorded_traffic(kernel_key):
+def recorded_traffic(kernel_key, workload=DEFAULT_WORKLOAD, source="vwc_kernels.hip"):
     """Per-launch HBM bytes measured by rocprofv3 counters (see profiles/), valid only
     while the kernel source is the one they were measured on."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "traffic_spiked_bf16_8192x248320.json")
-    src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", "vwc_kernels.hip")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", source)
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -356,7 +356,10 @@ def bench_lmhead(args, w):
         "roofline": {"bound": "mfma", "kernel": "lmhead_fwd_kernel",
                      "achieved": flops / (ms[0] * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (ms[0] * 1e-3) / 1e12 /
-                     MFMA_BF16_PEAK_TFLOPS, "traffic": None, "avg_launch_ms": ms[0],
+                     MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(["lmhead_fwd_kernel<false, false>"], w.name,
+                                                 "vwc_lmhead.hip"),
+                     "avg_launch_ms": ms[0],
                      "flops_alg_per_launch": flops,
                      "note": "launch = row gather + MFMA kernel + segment merge (HIP events)"},
         "unfused_context": {"gemm_ms": ums[0], "gemm_tflops": flops / (ums[0] * 1e-3) / 1e12,

@@ -16,29 +16,32 @@
 //    vocabulary segments of one workgroup each.
 //
 // Design for gfx950:
+//  * The kept hidden rows are compacted first (gather_rows_kernel), so a tile
+//    of 256 of them is contiguous.
 //  * One 256-thread workgroup owns a tile of 256 kept rows (tokens) and a
 //    segment of kLmSegTiles vocabulary tiles of 256 rows of the weight.  Its
 //    4 waves split the 256 x 256 logit tile 2 x 2; each wave holds a 128 x 128
 //    block as 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (256 fp32 per
 //    lane, in AGPRs).  The product is weight_tile x hidden_tile^T, so in every
 //    accumulator lane l holds 16 vocabulary rows of token l % 32.
-//  * The hidden dimension streams through LDS in stages of 64 columns, double
-//    buffered: the global loads of stage s + 1 are in flight while the MFMAs
-//    of stage s run, across vocabulary-tile boundaries too.  Both operands are
-//    K-contiguous rows, staged as 128-byte rows whose 16-byte chunks are
-//    XOR-swizzled so that the MFMA fragment reads (ds_read_b128) and the
-//    staging writes hit distinct banks.
+//  * The hidden dimension streams through LDS in stages of kLmK columns.
+//    buffer_load ... lds writes every lane's 16 bytes straight into LDS, from
+//    a buffer resource per tile whose size stops at the last valid row, so
+//    rows past the vocabulary or past the kept rows read as zero.  Weight
+//    tiles use a 3-slot ring and stream in two stages ahead, a few load
+//    instructions per k-step; hidden tiles use a 2-slot ring.  Staged rows are
+//    128 bytes whose 16-byte chunks are XOR-swizzled, so the MFMA fragment
+//    reads (ds_read_b128) hit distinct banks.  One barrier per stage; the
+//    fragments of the next k-step are read between the MFMAs of this one.
 //  * After the last stage of a vocabulary tile each lane folds its 64 logits
 //    per token into the token's lane state (K, m, s, w) with one FMA and one
 //    v_exp_f32 per logit; lanes l and l ^ 32 and the two vocabulary halves
 //    merge at the end of the segment, and the workgroup writes one 16-byte
 //    partial per row.  The split-V combine merges a row's segment partials in
 //    segment order in fp64.
-//  * blockIdx runs over token tiles first, so the workgroups resident at once
-//    cover few vocabulary tiles: each weight tile is read from HBM about once
-//    and shared through L2 by every token tile; consecutive blockIdx values go
-//    to different XCDs, which gives each XCD 1/8 of the token tiles of the
-//    same vocabulary segments.
+//  * Workgroups go to the 8 XCDs in turn; each XCD takes a contiguous block
+//    of a work list grouped by a few token tiles, so the workgroups it runs at
+//    once share token and weight tiles in its L2.
 #include <math.h>
 #include <stdint.h>
 

@@ -93,19 +93,30 @@ def cpu_baseline(w, seconds):
                       f"{elapsed:.1f} s of oracle time"}
 
 
+def code_digest(path):
+    """SHA-256 of a C/HIP source with its comments and whitespace removed: it changes
+    with the code, not with its comments."""
+    import hashlib
+    import re
+
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def recorded_traffic(kernel_key, workload=DEFAULT_WORKLOAD, source="vwc_kernels.hip"):
     """Per-launch HBM bytes measured by rocprofv3 counters (see profiles/), valid only
-    while the kernel source is the one they were measured on."""
-    import hashlib
-
+    while the kernel code is the one they were measured on."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", source)
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = code_digest(src)
     except OSError:
         return None
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_code_digest") != digest:
         return None
     total = 0
     for k in kernel_key:

@@ -554,13 +554,13 @@ vwc_status vwc_lmhead_logprob_fwd(const void *hidden, int64_t n_rows, int64_t ld
     vwc::CombinePlan cp{};
     cp.parts = p.seg_part;
     cp.k = p.nseg;
-    cp.stride = m;
+    cp.stride = 1;
     cp.rows = m;
     cp.tau = tau;
     cp.logprob = logprob;
     cp.lse = lse;
     cp.entropy = entropy;
-    return hip_status(vwc::launch_combine(cp, stream), fn);
+    return hip_status(vwc::launch_combine_rows(cp, stream), fn);
 }
 
 vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,

@@ -156,7 +156,7 @@ struct LmPlan {
     int ntb;                  // token tiles: ceil(m / kLmTok)
     int nvt;                  // vocabulary tiles: ceil(vocab / kLmVoc)
     int nseg;                 // ceil(nvt / kLmSegTiles)
-    vwc_partial *seg_part;    // [nseg][m]
+    vwc_partial *seg_part;    // [m][nseg], row-major
 };
 
 hipError_t launch_lmhead_fwd(const LmPlan &p, bool want_entropy, hipStream_t stream);
@@ -168,6 +168,8 @@ hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream);
 hipError_t launch_topk_fixup(const TopkPlan &p, hipStream_t stream);
 hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream);
 hipError_t launch_combine(const CombinePlan &p, hipStream_t stream);
+// Row-major partials ([rows][k]), one wave per row (rows with many segments).
+hipError_t launch_combine_rows(const CombinePlan &p, hipStream_t stream);
 hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, int32_t *count,
                                 hipStream_t stream);
 

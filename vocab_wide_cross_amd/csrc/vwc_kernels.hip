@@ -490,6 +490,72 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(CombinePlan p) {
         write_final(g, p.tau, i, p.logprob, p.lse, p.entropy);
 }
 
+// One wave per row: merge k partials stored row-major ([rows][k], so a row's
+// partials are contiguous).  Each lane folds partials lane, lane + 64, ...
+// into a running fp64 (M, S, W) (rescaled whenever its reference rises), then
+// the 64 lane states merge over a fixed xor tree.  Used for rows with many
+// segments (the fused LM head), where one thread per row would serialise.
+constexpr int kCombineRowsBlock = 256;
+
+__device__ __forceinline__ void merge64(double &M, double &S, double &W, double m, double s,
+                                        double w, double tau) {
+    if (!(s != 0.0)) return;  // empty (NaN states are not empty and poison S)
+    if (m > M) {
+        if (S != 0.0) {
+            const double d = (M - m) / tau;
+            const double f = exp(d);
+            W = f * (W + d * S);
+            S = f * S;
+        }
+        M = m;
+    }
+    const double d = (m - M) / tau;
+    const double f = exp(d);
+    S += s * f;
+    W += f * (w + d * s);
+}
+
+__global__ __launch_bounds__(kCombineRowsBlock) void combine_rows_kernel(CombinePlan p) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * (kCombineRowsBlock / 64) +
+                      (threadIdx.x >> 6);
+    if (i >= p.rows) return;  // whole waves
+    const int lane = threadIdx.x & 63;
+    const vwc_partial *row = p.parts + i * p.k;
+    double M = -INFINITY, S = 0.0, W = 0.0, T = -INFINITY;
+    bool tnan = false;
+    for (int q = lane; q < p.k; q += 64) {
+        const vwc_partial v = row[q];
+        if (v.t != v.t)
+            tnan = true;
+        else if (v.t > T)
+            T = v.t;
+        merge64(M, S, W, v.m, v.s, v.w, p.tau);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double m = __shfl_xor(M, off), s = __shfl_xor(S, off), w = __shfl_xor(W, off);
+        const double t = __shfl_xor(T, off);
+        tnan |= __shfl_xor(static_cast<int>(tnan), off) != 0;
+        // Lane pairs merge in the same (lower-lane-first) order on both sides.
+        double Ma = M, Sa = S, Wa = W;
+        double Mb = m, Sb = s, Wb = w;
+        if (lane & off) {
+            Ma = m; Sa = s; Wa = w;
+            Mb = M; Sb = S; Wb = W;
+        }
+        merge64(Ma, Sa, Wa, Mb, Sb, Wb, p.tau);
+        M = Ma;
+        S = Sa;
+        W = Wa;
+        if (t > T) T = t;
+    }
+    if (lane != 0) return;
+    // An all-empty row keeps M = -inf and S = 0 (outputs -inf / NaN as in the
+    // per-thread merge).
+    const Merged g{M, S, W, tnan ? NAN : T};
+    write_final(g, p.tau, i, p.logprob, p.lse, p.entropy);
+}
+
 // ---------------------------------------------------------------- backward
 
 template <int GDT, int N>
@@ -890,6 +956,14 @@ hipError_t launch_combine(const CombinePlan &p, hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>((p.rows + kCombineBlock - 1) / kCombineBlock)),
         block(kCombineBlock);
     hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_rows(const CombinePlan &p, hipStream_t stream) {
+    constexpr int rows_per_block = kCombineRowsBlock / 64;
+    const dim3 grid(static_cast<uint32_t>((p.rows + rows_per_block - 1) / rows_per_block)),
+        block(kCombineRowsBlock);
+    hipLaunchKernelGGL(combine_rows_kernel, grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

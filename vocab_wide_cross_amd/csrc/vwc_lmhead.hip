@@ -522,7 +522,7 @@ void lmhead_fwd_kernel(LmPlan p) {
             out = vwc_partial{static_cast<float>(q.m), static_cast<float>(q.s),
                               static_cast<float>(q.t), static_cast<float>(q.w)};
         }
-        p.seg_part[static_cast<int64_t>(seg) * p.m + i] = out;
+        p.seg_part[i * p.nseg + seg] = out;  // row-major: a row's segments are contiguous
     }
 }
 

@@ -55,13 +55,21 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
+#ifndef VWC_LM_WAVES
+#define VWC_LM_WAVES 8
+#endif
+constexpr int kWaves = VWC_LM_WAVES;              // waves per workgroup: 4 or 8
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWN = kWaves / 2;                   // token groups (the 2 vocabulary halves
+                                                  // times kWN token groups = the waves)
+constexpr int kJ = kLmTok / kWN / 32;             // 32-token accumulator columns per wave
+constexpr int kRowsPerWave = kLmTok / kWaves;     // staged rows each wave loads per tile
 constexpr int kLmGroup = 4;                       // token tiles per group of the work order
 constexpr int kRowBytes = kLmK * 2;               // one staged tile row
 constexpr int kTileBytes = kLmVoc * kRowBytes;    // one staged operand tile
 constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per staged row
 constexpr int kRowsPerInst = 1024 / kRowBytes;    // rows one wave load instruction fills
-constexpr int kInstPerTile = 64 / kRowsPerInst;   // per wave and operand tile
+constexpr int kInstPerTile = kRowsPerWave / kRowsPerInst;  // per wave and operand tile
 constexpr int kSteps = kLmK / 16;                 // MFMA k-steps per stage
 constexpr int kWPerStep = kInstPerTile / kSteps;  // weight load instructions per k-step
 // LDS rings of operand tiles.  The weight tile of stage g + 2 streams in during
@@ -72,6 +80,7 @@ constexpr int kWPerStep = kInstPerTile / kSteps;  // weight load instructions pe
 constexpr int kWS = 3;
 constexpr int kHS = 2;
 static_assert(kLmTok == kLmVoc, "the staging assumes square tiles");
+static_assert(kWaves == 4 || kWaves == 8, "4 waves (1 per SIMD) or 8 (2 per SIMD)");
 static_assert(kLmK == 32 || kLmK == 64, "stage widths of 64 or 128 bytes per row");
 static_assert(kWS >= kHS && (kWS + kHS) * kTileBytes <= 160 * 1024, "LDS rings too large");
 constexpr float kUFloor = -256.0f;
@@ -105,21 +114,25 @@ __device__ __forceinline__ void block_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
-// Scheduling of one k-step (16 MFMAs): one LDS read and an even share of NV
-// loads after each of the first 8 MFMAs, then the remaining 8 MFMAs.
+// Scheduling of one k-step (4 kJ MFMAs, 4 + kJ fragment reads for the next
+// step): one LDS read and an even share of NV loads after each of the first
+// 4 + kJ MFMAs, then the remaining MFMAs.
+constexpr int kReads = 4 + kJ;
+constexpr int kMfmas = 4 * kJ;
+
 template <int Q, int NV>
 __device__ __forceinline__ void interleave_group() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    constexpr int nq = NV * (Q + 1) / 8 - NV * Q / 8;
+    constexpr int nq = NV * (Q + 1) / kReads - NV * Q / kReads;
     if constexpr (nq > 0) __builtin_amdgcn_sched_group_barrier(0x020, nq, 0);  // loads
-    if constexpr (Q + 1 < 8) interleave_group<Q + 1, NV>();
+    if constexpr (Q + 1 < kReads) interleave_group<Q + 1, NV>();
 }
 
 template <int NV>
 __device__ __forceinline__ void interleave() {
     interleave_group<0, NV>();
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if constexpr (kMfmas > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
 }
 
 // Fold the logits of token column j of the accumulators into lane state L.
@@ -134,7 +147,7 @@ __device__ __forceinline__ void interleave() {
 constexpr float kTileBound = 0x1p64f;
 
 template <bool MASK, bool ENT>
-__device__ __forceinline__ void fold_recentre(const f32x16 (&acc)[4][4], int j, float c, int vlim,
+__device__ __forceinline__ void fold_recentre(const f32x16 (&acc)[4][kJ], int j, float c, int vlim,
                                               Lane &L, float &cs, float &cw) {
     float cm = -INFINITY;
 #pragma unroll
@@ -172,7 +185,7 @@ __device__ __forceinline__ void fold_recentre(const f32x16 (&acc)[4][4], int j, 
 }
 
 template <bool MASK, bool ENT>
-__device__ __forceinline__ void fold_column(const f32x16 (&acc)[4][4], int j, float c, int vlim,
+__device__ __forceinline__ void fold_column(const f32x16 (&acc)[4][kJ], int j, float c, int vlim,
                                             Lane &L) {
     if (L.K == -INFINITY && (!MASK || vlim > 0)) {  // seed with the lane's first logit
         const float x0 = acc[0][j][0];
@@ -210,15 +223,16 @@ __device__ __forceinline__ void fold_column(const f32x16 (&acc)[4][4], int j, fl
 }
 
 template <bool ENT, bool RAGGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void lmhead_fwd_kernel(LmPlan p) {
     __shared__ __attribute__((aligned(16))) char lds[(kWS + kHS) * kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
-    const int wm = wave >> 1;  // vocabulary half of the tile
-    const int wn = wave & 1;   // token half of the tile
+    const int wm = wave / kWN;  // vocabulary half of the tile
+    const int wn = wave % kWN;  // token group of the tile
     // Work order.  Consecutive workgroups go to the 8 XCDs in turn, and each
     // XCD has its own L2, so XCD x (blockIdx % 8) takes one contiguous block of
     // the work list; the list runs over groups of kLmGroup token tiles, and
@@ -246,11 +260,11 @@ void lmhead_fwd_kernel(LmPlan p) {
     // Staging role.  Stages go from global memory straight into LDS
     // (buffer_load ... lds, 16 bytes per lane): one wave instruction fills
     // 1 KiB, i.e. kRowsPerInst staged rows, lane L writing chunk position
-    // L % kChunks of row L / kChunks.  Wave w fills rows [64 w, 64 w + 64) of
-    // both tiles, kRowsPerInst per instruction q, so lane L fetches logical
-    // chunk cq[q] = (L % kChunks) ^ swz(row) of row 64 w + kRowsPerInst q +
-    // L / kChunks.
-    const int srow = wave * 64 + lane / kChunks;
+    // L % kChunks of row L / kChunks.  Wave w fills kRowsPerWave rows of both
+    // tiles from row kRowsPerWave w on, kRowsPerInst per instruction q, so lane
+    // L fetches logical chunk cq[q] = (L % kChunks) ^ swz(row) of row
+    // kRowsPerWave w + kRowsPerInst q + L / kChunks.
+    const int srow = wave * kRowsPerWave + lane / kChunks;
     int cq[kInstPerTile];
     // Both operands come through buffer resources whose size stops at the last
     // valid row (vocabulary rows of the weight tile, kept rows of the token
@@ -276,18 +290,18 @@ void lmhead_fwd_kernel(LmPlan p) {
     const int fr = lane & 31;
     const int fh = lane >> 5;
     const int a_off = (wm * 128 + fr) * kRowBytes;
-    const int b_off = (wn * 128 + fr) * kRowBytes;
+    const int b_off = (wn * 32 * kJ + fr) * kRowBytes;
     int koff[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) koff[s] = ((2 * s + fh) ^ swz(fr)) << 4;
 
-    // Targets of the lane's 4 token columns (-1: none, or outside the vocabulary).
-    int tg[4];
-    float tv[4];
-    Lane L[4];
+    // Targets of the lane's kJ token columns (-1: none, or outside the vocabulary).
+    int tg[kJ];
+    float tv[kJ];
+    Lane L[kJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t i = static_cast<int64_t>(tb) * kLmTok + wn * 128 + j * 32 + fr;
+    for (int j = 0; j < kJ; ++j) {
+        const int64_t i = static_cast<int64_t>(tb) * kLmTok + wn * 32 * kJ + j * 32 + fr;
         tg[j] = -1;
         if (p.targets && i < p.m) {
             const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
@@ -304,7 +318,7 @@ void lmhead_fwd_kernel(LmPlan p) {
     const int nk = (p.d + kLmK - 1) / kLmK;
     const int nstage = (vt1 - vt0) * nk;
     // LDS: kWS weight units, then kHS hidden units, one operand tile each.
-    char *const wlds = lds + wave * 64 * kRowBytes;             // this wave's rows of unit 0
+    char *const wlds = lds + wave * kRowsPerWave * kRowBytes;   // this wave's rows of unit 0
     char *const hlds = wlds + kWS * kTileBytes;
     const int64_t wtile = static_cast<int64_t>(kLmVoc) * p.ldw;  // elements per weight tile
     // Issue the loads of one operand tile: step k0 of the tile at base `rsrc`,
@@ -338,23 +352,23 @@ void lmhead_fwd_kernel(LmPlan p) {
         load_tile(live ? hr : hr_none, hoff, hlds + u * kTileBytes, k * kLmK, 0, kInstPerTile);
     };
     // Fragments of k-step s from weight unit wu and hidden unit hu.
-    auto read_frags = [&](int wu, int hu, int s, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+    auto read_frags = [&](int wu, int hu, int s, bf16x8 (&a)[4], bf16x8 (&b)[kJ]) {
         const char *SA = lds + wu * kTileBytes;
         const char *SB = lds + (kWS + hu) * kTileBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             a[i] = *reinterpret_cast<const bf16x8 *>(SA + a_off + i * 32 * kRowBytes + koff[s]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kJ; ++j)
             b[j] = *reinterpret_cast<const bf16x8 *>(SB + b_off + j * 32 * kRowBytes + koff[s]);
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][kJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    bf16x8 fa[2][4], fb[2][4];
+        for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16{};
+    bf16x8 fa[2][4], fb[2][kJ];
 
     // Prologue: stages 0 and 1 whole (hidden tile, then weight tile); wait for
     // stage 0.  (hk) is the step of the next hidden load, (wt, wk) the tile and
@@ -412,7 +426,7 @@ void lmhead_fwd_kernel(LmPlan p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < kJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
                 if (last)
@@ -441,10 +455,10 @@ void lmhead_fwd_kernel(LmPlan p) {
         // Target logits: the lane holding row tg - vbase of its token keeps it.
         bool mine = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mine |= static_cast<unsigned>(tg[j] - vbase) < 128u;
+        for (int j = 0; j < kJ; ++j) mine |= static_cast<unsigned>(tg[j] - vbase) < 128u;
         if (__ballot(mine)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kJ; ++j) {
                 const int tl = tg[j] - vbase - fh * 4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -456,15 +470,15 @@ void lmhead_fwd_kernel(LmPlan p) {
         const int vlim = p.vocab - vbase - fh * 4;
         if (vbase + 128 > p.vocab) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fold_column<true, ENT>(acc, j, p.c, vlim, L[j]);
+            for (int j = 0; j < kJ; ++j) fold_column<true, ENT>(acc, j, p.c, vlim, L[j]);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fold_column<false, ENT>(acc, j, p.c, vlim, L[j]);
+            for (int j = 0; j < kJ; ++j) fold_column<false, ENT>(acc, j, p.c, vlim, L[j]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+            for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16{};
     }
 
     // The last loads (of stages past the segment) must land before the LDS is
@@ -474,7 +488,7 @@ void lmhead_fwd_kernel(LmPlan p) {
 
     // Lanes l and l ^ 32 hold other rows of the same tokens.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kJ; ++j) {
         const Lane o{shfl_xor32(L[j].K), shfl_xor32(L[j].m), shfl_xor32(L[j].s),
                      shfl_xor32(L[j].w)};
         merge(L[j], o);
@@ -484,8 +498,8 @@ void lmhead_fwd_kernel(LmPlan p) {
     float *fin = reinterpret_cast<float *>(lds);
     if (wm == 1 && lane < 32) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float *f = fin + ((wn * 4 + j) * 32 + lane) * 5;
+        for (int j = 0; j < kJ; ++j) {
+            float *f = fin + ((wn * kJ + j) * 32 + lane) * 5;
             f[0] = L[j].K;
             f[1] = L[j].m;
             f[2] = L[j].s;
@@ -498,11 +512,11 @@ void lmhead_fwd_kernel(LmPlan p) {
     const int64_t v_lo = static_cast<int64_t>(vt0) * kLmVoc;
     const int64_t v_hi = min(static_cast<int64_t>(vt1) * kLmVoc, static_cast<int64_t>(p.vocab));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float *f = fin + ((wn * 4 + j) * 32 + lane) * 5;
+    for (int j = 0; j < kJ; ++j) {
+        const float *f = fin + ((wn * kJ + j) * 32 + lane) * 5;
         merge(L[j], Lane{f[0], f[1], f[2], f[3]});
         const float t_here = fmaxf(tv[j], f[4]);
-        const int64_t i = static_cast<int64_t>(tb) * kLmTok + wn * 128 + j * 32 + lane;
+        const int64_t i = static_cast<int64_t>(tb) * kLmTok + wn * 32 * kJ + j * 32 + lane;
         if (i >= p.m) continue;
         const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
         vwc_partial out;

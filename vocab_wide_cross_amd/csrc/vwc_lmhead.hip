@@ -18,12 +18,13 @@
 // Design for gfx950:
 //  * The kept hidden rows are compacted first (gather_rows_kernel), so a tile
 //    of 256 of them is contiguous.
-//  * One 256-thread workgroup owns a tile of 256 kept rows (tokens) and a
+//  * One 512-thread workgroup owns a tile of 256 kept rows (tokens) and a
 //    segment of kLmSegTiles vocabulary tiles of 256 rows of the weight.  Its
-//    4 waves split the 256 x 256 logit tile 2 x 2; each wave holds a 128 x 128
-//    block as 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (256 fp32 per
-//    lane, in AGPRs).  The product is weight_tile x hidden_tile^T, so in every
-//    accumulator lane l holds 16 vocabulary rows of token l % 32.
+//    8 waves (2 per SIMD, so each hides the other's stalls) split the
+//    256 x 256 logit tile 2 x 4; each wave holds a 128 x 64 block as 4 x 2
+//    accumulators of v_mfma_f32_32x32x16_bf16 (128 fp32 per lane).  The
+//    product is weight_tile x hidden_tile^T, so in every accumulator lane l
+//    holds 16 vocabulary rows of token l % 32.
 //  * The hidden dimension streams through LDS in stages of kLmK columns.
 //    buffer_load ... lds writes every lane's 16 bytes straight into LDS, from
 //    a buffer resource per tile whose size stops at the last valid row, so
@@ -32,7 +33,7 @@
 //    instructions per k-step; hidden tiles use a 2-slot ring.  Staged rows are
 //    128 bytes whose 16-byte chunks are XOR-swizzled, so the MFMA fragment
 //    reads (ds_read_b128) hit distinct banks.  One barrier per stage; the
-//    fragments of the next k-step are read between the MFMAs of this one.
+//    fragments of the next k-step are read ahead of the MFMAs of this one.
 //  * After the last stage of a vocabulary tile each lane folds its 64 logits
 //    per token into the token's lane state (K, m, s, w) with one FMA and one
 //    v_exp_f32 per logit; lanes l and l ^ 32 and the two vocabulary halves
@@ -64,7 +65,10 @@ constexpr int kWN = kWaves / 2;                   // token groups (the 2 vocabul
                                                   // times kWN token groups = the waves)
 constexpr int kJ = kLmTok / kWN / 32;             // 32-token accumulator columns per wave
 constexpr int kRowsPerWave = kLmTok / kWaves;     // staged rows each wave loads per tile
-constexpr int kLmGroup = 4;                       // token tiles per group of the work order
+#ifndef VWC_LM_GROUP
+#define VWC_LM_GROUP 4
+#endif
+constexpr int kLmGroup = VWC_LM_GROUP;            // token tiles per group of the work order
 constexpr int kRowBytes = kLmK * 2;               // one staged tile row
 constexpr int kTileBytes = kLmVoc * kRowBytes;    // one staged operand tile
 constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per staged row
@@ -112,27 +116,6 @@ __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32);
 __device__ __forceinline__ void block_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
     __builtin_amdgcn_s_barrier();
-}
-
-// Scheduling of one k-step (4 kJ MFMAs, 4 + kJ fragment reads for the next
-// step): one LDS read and an even share of NV loads after each of the first
-// 4 + kJ MFMAs, then the remaining MFMAs.
-constexpr int kReads = 4 + kJ;
-constexpr int kMfmas = 4 * kJ;
-
-template <int Q, int NV>
-__device__ __forceinline__ void interleave_group() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    constexpr int nq = NV * (Q + 1) / kReads - NV * Q / kReads;
-    if constexpr (nq > 0) __builtin_amdgcn_sched_group_barrier(0x020, nq, 0);  // loads
-    if constexpr (Q + 1 < kReads) interleave_group<Q + 1, NV>();
-}
-
-template <int NV>
-__device__ __forceinline__ void interleave() {
-    interleave_group<0, NV>();
-    if constexpr (kMfmas > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kReads, 0);
 }
 
 // Fold the logits of token column j of the accumulators into lane state L.
@@ -409,9 +392,11 @@ void lmhead_fwd_kernel(LmPlan p) {
             for (int s = 0; s < kSteps; ++s) {
                 // Step s of stage g.  The fragments of the next step (step 0 of
                 // stage g + 1 after the last step) and this step's share of the
-                // weight loads go out one by one between the MFMAs; in the last
-                // step, so do the hidden loads that refill stage g's unit.
-                // (After the last stage the reads touch units nobody refills.)
+                // weight loads are issued ahead of the step's MFMAs; in the last
+                // step, so are the hidden loads that refill stage g's unit.  The
+                // fence keeps each step's group in order; the two waves of a
+                // SIMD interleave with each other.  (After the last stage the
+                // reads touch units nobody refills.)
                 const bool next_here = s + 1 < kSteps;
                 const bool last = s + 1 == kSteps;
                 if (next_here)
@@ -429,10 +414,6 @@ void lmhead_fwd_kernel(LmPlan p) {
                     for (int j = 0; j < kJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
-                if (last)
-                    interleave<kWPerStep + kInstPerTile>();
-                else
-                    interleave<kWPerStep>();
                 __builtin_amdgcn_sched_barrier(0);
                 if (s == kSteps - 2) {
                     // Every read of stage g's units has been issued by now (the

@@ -58,7 +58,9 @@
  *    m == 0 returns VWC_OK without a launch.  Data errors cannot be seen on
  *    the host: a target outside [0, vocab) gives logprob = NaN in that row
  *    (dense and `_rows`), and -infinity through the split-vocabulary calls
- *    when no slice owns it.  NaN logits propagate to that row's outputs.
+ *    when no slice owns it.  A row id outside [0, n_rows) gives NaN outputs
+ *    (a partial with NaN s, t and w) and reads nothing.  NaN logits propagate
+ *    to that row's outputs.
  *  - Detail for the last failure on the calling thread: vwc_last_error().
  */
 #ifndef VWC_H
@@ -113,9 +115,10 @@ typedef struct vwc_partial {
 } vwc_partial;
 
 /* Bytes of workspace the forward, entropy and partial calls need for `rows`
-   output rows of a `vocab`-wide row (or slice) of dtype dt: 16 bytes per row
-   per internal row segment, 0 when a row is handled by a single workgroup.
-   Never O(rows * vocab). */
+   output rows of a `vocab`-wide row (or slice) of dtype dt.  A row is cut into
+   ceil(vocab * e / 128 KiB) segments (e = 2 for bf16, 4 for fp32).  Rows of up
+   to 3 segments are reduced and merged inside one workgroup and need none;
+   longer rows need 16 bytes per row per segment.  Never O(rows * vocab). */
 size_t vwc_workspace_bytes(int64_t rows, int64_t vocab, vwc_dtype dt);
 
 /*

@@ -49,9 +49,16 @@ def test_workspace_bytes(lib):
     f = lib.vwc_workspace_bytes
     f.restype = ctypes.c_size_t
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
-    # bf16 rows of 248320 (485 KiB) are cut into 4 segments of <= 128 KiB
-    assert f(8192, 248320, BF16) == 8192 * 4 * 16
+    # Rows are cut into segments of <= 128 KiB.  Up to 3 segments, one workgroup
+    # reduces and merges a row: no workspace.  Longer rows take one workgroup per
+    # segment and 16 bytes per row and segment.
+    assert f(8192, 248320, BF16) == 8192 * 4 * 16   # 485 KiB: 4 segments
     assert f(8192, 248320, FP32) == 8192 * 8 * 16
+    assert f(4096, 151936, BF16) == 0               # 297 KiB: 3 segments
+    assert f(8192, 98304, FP32) == 0                # exactly 3 segments
+    assert f(8192, 98305, FP32) == 8192 * 4 * 16
+    assert f(16384, 62080, FP32) == 0               # 2 segments
+    assert f(3, 1 << 20, BF16) == 3 * 16 * 16
     assert f(64, 2048, FP32) == 0          # one segment: no workspace
     assert f(0, 248320, BF16) == 0
     assert f(10, 0, BF16) == 0
@@ -92,11 +99,11 @@ def test_forward_validation(lib):
     # misaligned for its dtype
     assert f(ctypes.c_void_p(0x100001), BF16, 4, 16, 16, FAKE, 1.0, FAKE, None, None, None, 0,
              None) == UNSUPPORTED
-    # workspace required for multi-segment rows, and must be large enough
-    assert f(FAKE, BF16, 4, 248320, 248320, FAKE, 1.0, FAKE, None, None, None, 0,
+    # workspace required for rows of more than 4 segments, and must be large enough
+    assert f(FAKE, FP32, 4, 248320, 248320, FAKE, 1.0, FAKE, None, None, None, 0,
              None) == INVALID
     assert b"workspace" in err()
-    assert f(FAKE, BF16, 4, 248320, 248320, FAKE, 1.0, FAKE, None, None, ws, 4 * 4 * 16 - 1,
+    assert f(FAKE, FP32, 4, 248320, 248320, FAKE, 1.0, FAKE, None, None, ws, 4 * 8 * 16 - 1,
              None) == INVALID
     # zero rows: OK, nothing launched (no GPU is touched here)
     assert f(None, BF16, 0, 16, 16, None, 1.0, None, None, None, None, 0, None) == OK

@@ -310,10 +310,13 @@ def test_split_vocab_rows_and_unowned_targets():
 # ------------------------------------------------------------------ edge values
 
 
-def test_out_of_range_targets_and_rows_give_nan():
-    w = W.scaled("spiked_bf16_8192x248320", 8, 1000)
+@pytest.mark.parametrize("vocab", [1000, 100000, 151936, 248320])
+def test_out_of_range_targets_and_rows_give_nan(vocab):
+    """One segment, two and three (merged inside the row's workgroup), four (a
+    workgroup per segment and a merge launch)."""
+    w = W.scaled("spiked_bf16_8192x248320", 8, vocab)
     x, t, _ = _host(w)
-    t[2], t[5] = -1, 1000
+    t[2], t[5] = -1, vocab
     xd, td = to_dev_logits(x), torch.from_numpy(t).to(DEV)
     lp, lse, _ = vwc.selected_logprob_fwd(xd, td)
     lpn = _np(lp)
@@ -330,6 +333,11 @@ def test_out_of_range_targets_and_rows_give_nan():
     for v in (lp, lse, ent):
         a = _np(v)
         assert np.isnan(a[1]) and np.isnan(a[2]) and np.isfinite(a[0]) and np.isfinite(a[3])
+    ref = oracle.forward(x, t, rows=np.array([0, 1]))
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        assert_close_scalar(_np(v)[[0, 3]], ref[k], k)
+    part = _np(vwc.vocab_partial(xd, 0, td, rows))
+    assert np.isnan(part[[1, 2]][:, 1:]).all() and np.isfinite(part[[0, 3]]).all()
 
 
 def test_masked_minus_inf_logits():

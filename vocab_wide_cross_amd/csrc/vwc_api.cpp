@@ -69,7 +69,7 @@ vwc_status check_logits(const char *fn, const void *logits, int dt, int64_t n_ro
 
 vwc_status check_workspace(const char *fn, int64_t rows, int64_t nseg, const void *ws,
                            size_t ws_bytes) {
-    if (nseg <= 1) return VWC_OK;
+    if (!vwc::fwd_needs_workspace(nseg)) return VWC_OK;
     const size_t need = static_cast<size_t>(rows) * static_cast<size_t>(nseg) * sizeof(vwc_partial);
     if (!ws || ws_bytes < need)
         return fail(VWC_ERR_INVALID_ARG, "%s: workspace needs %zu bytes, got %zu", fn, need,
@@ -134,7 +134,7 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
     p.logprob = logprob;
     p.lse = lse;
     p.entropy = entropy;
-    p.seg_part = nseg > 1 ? static_cast<vwc_partial *>(workspace) : nullptr;
+    p.seg_part = vwc::fwd_needs_workspace(nseg) ? static_cast<vwc_partial *>(workspace) : nullptr;
     p.partial_out = partial_out;
     return hip_status(vwc::launch_fwd(p, dt, stream), fn);
 }
@@ -228,7 +228,7 @@ extern "C" {
 size_t vwc_workspace_bytes(int64_t rows, int64_t vocab, vwc_dtype dt) {
     if (rows <= 0 || vocab <= 0 || !dtype_ok(dt)) return 0;
     const int64_t nseg = segments(vocab, dt, vwc::kFwdSegBytes);
-    if (nseg <= 1) return 0;
+    if (!vwc::fwd_needs_workspace(nseg)) return 0;
     return static_cast<size_t>(rows) * static_cast<size_t>(nseg) * sizeof(vwc_partial);
 }
 

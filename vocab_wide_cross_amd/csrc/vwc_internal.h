@@ -34,6 +34,25 @@ constexpr int kCombineBlock = 64;
 constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;
 
+// Rows of at most this many forward segments are reduced by one workgroup of
+// nseg * kFwdBlock threads that also merges the segment partials (no
+// workspace, no second launch); longer rows use one workgroup per segment and
+// a combine launch.  Both give the same bits.  1 turns the in-block merge off.
+// Timed on MI355X: three segments (768 threads, two workgroups per compute
+// unit) beat the two-launch form; four (1024 threads, one workgroup per
+// compute unit) lose 6 % on 248320-column bf16 rows to the lower occupancy.
+#ifndef VWC_FWD_INBLOCK_MAX
+#define VWC_FWD_INBLOCK_MAX 3
+#endif
+constexpr int kFwdMaxSegPerBlock = VWC_FWD_INBLOCK_MAX;
+static_assert(kFwdMaxSegPerBlock >= 1 && kFwdMaxSegPerBlock * VWC_FWD_BLOCK <= 1024,
+              "in-block merge exceeds the workgroup size limit");
+
+// Whether a forward over rows of nseg segments needs a workspace.
+constexpr bool fwd_needs_workspace(int64_t nseg) {
+    return nseg > 1 && nseg > kFwdMaxSegPerBlock;
+}
+
 enum TargetMode : int {
     kTargetNone = 0,   // entropy only
     kTargetFull = 1,   // targets index the full row; out of range -> NaN
@@ -59,7 +78,7 @@ struct FwdPlan {
     bool want_entropy;
     // Final outputs (nseg == 1 and !partial_out), compact [m]:
     float *logprob, *lse, *entropy;
-    // Segment partials, [nseg][m] (when nseg > 1) in workspace:
+    // Segment partials, [nseg][m] in workspace (when fwd_needs_workspace(nseg)):
     vwc_partial *seg_part;
     // Slice partial output [m] (vwc_vocab_partial):
     vwc_partial *partial_out;

@@ -243,7 +243,8 @@ __device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[
     if (W) L.w += cw;
 }
 
-// Stream units [u0, u1) of a row (lane l takes u0 + l, u0 + l + kFwdBlock, ...).
+// Stream units [u0, u1) of a row (thread `tid` of the segment's kFwdBlock
+// threads takes u0 + tid, u0 + tid + kFwdBlock, ...).
 // With prefetch on, the loads of chunk k+1 are issued before chunk k is folded,
 // so each wave keeps loads in flight while its ALU work runs.
 #ifndef VWC_FWD_PREFETCH
@@ -251,11 +252,11 @@ __device__ __forceinline__ void fold_chunk(const typename Unit<DT, VEC>::T (&v)[
 #endif
 template <int DT, bool VEC, int U, bool W>
 __device__ __forceinline__ void stream_units(const char *row, int32_t u0, int32_t u1, float c,
-                                             Lane &L) {
+                                             int32_t tid, Lane &L) {
     using Un = Unit<DT, VEC>;
     using T = typename Un::T;
     const T *p = reinterpret_cast<const T *>(row);
-    int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
+    int32_t b = u0 + tid;
 #if VWC_FWD_PREFETCH
     if (b + (U - 1) * kFwdBlock < u1) {
         T cur[U];
@@ -323,8 +324,11 @@ __device__ __forceinline__ void wave_step_swz(Lane &L) {
     merge(L, o);
 }
 
-// Reduce the lane states of a workgroup; the result is valid in thread 0.
-__device__ __forceinline__ Lane block_reduce(Lane L) {
+// Reduce the lane states of each group of kFwdBlock threads of a workgroup
+// (NG groups at most; `grp` is the caller's group); every thread of a group
+// gets its group's state.
+template <int NG>
+__device__ __forceinline__ Lane block_reduce(Lane L, int grp) {
     // Within a wave: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
     // row_mirror (all lanes of a row of 16 then hold the row's state), then a
     // swizzle exchanging rows 0<->1 and 2<->3 (xor 16 inside each 32-lane half).
@@ -343,13 +347,15 @@ __device__ __forceinline__ Lane block_reduce(Lane L) {
             bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.s), 0)),
             bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, L.w), 0))};
     merge(lo, hi);
-    __shared__ Lane wave_state[kFwdBlock / 64];
+    constexpr int kW = kFwdBlock / 64;
+    __shared__ Lane wave_state[NG * kW];
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) wave_state[wave] = lo;
     __syncthreads();
-    Lane acc = wave_state[0];
+    const Lane *g = wave_state + grp * kW;
+    Lane acc = g[0];
 #pragma unroll
-    for (int q = 1; q < kFwdBlock / 64; ++q) merge(acc, wave_state[q]);
+    for (int q = 1; q < kW; ++q) merge(acc, g[q]);
     return acc;
 }
 
@@ -400,20 +406,39 @@ __device__ __forceinline__ vwc_partial to_f32(const Merged &g) {
 
 // ---------------------------------------------------------------- forward
 
-template <int DT, bool VEC, bool W>
-__global__ __launch_bounds__(kFwdBlock) VWC_FWD_ATTR void fwd_segment_kernel(FwdPlan p) {
+// A row of nseg segments, each reduced by kFwdBlock threads into one partial.
+// Two launch shapes give the same bits:
+//   INBLOCK = false: one workgroup per (row, segment); with nseg > 1 the
+//     partials go to the workspace ([nseg][m]) and combine_kernel merges them;
+//   INBLOCK = true (2 <= nseg <= kFwdMaxSegPerBlock): one workgroup of
+//     nseg * kFwdBlock threads per row; group q reduces segment q, the groups'
+//     fp32 partials meet in LDS and thread 0 merges them with the combine's
+//     own code, in segment order.  No workspace, no second launch.
+// The in-block kernel asks the compiler for few enough registers that this many
+// waves share a SIMD (6: two workgroups of three segments per compute unit).
+#ifndef VWC_FWD_INBLOCK_WAVES
+#define VWC_FWD_INBLOCK_WAVES 6
+#endif
+template <int DT, bool VEC, bool W, bool INBLOCK>
+__global__ __launch_bounds__(INBLOCK ? kFwdBlock * kFwdMaxSegPerBlock : kFwdBlock,
+                              INBLOCK ? VWC_FWD_INBLOCK_WAVES : 1) VWC_FWD_ATTR
+    void fwd_segment_kernel(FwdPlan p) {
     using Un = Unit<DT, VEC>;
     constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
-    const int q = static_cast<int>(blockIdx.x - i * p.nseg);
+    const int32_t tid = static_cast<int32_t>(threadIdx.x) & (kFwdBlock - 1);
+    const int grp = INBLOCK ? static_cast<int>(threadIdx.x) / kFwdBlock : 0;
+    const int64_t i = INBLOCK ? static_cast<int64_t>(blockIdx.x)
+                              : static_cast<int64_t>(blockIdx.x) / p.nseg;
+    const int q = INBLOCK ? grp : static_cast<int>(blockIdx.x - i * p.nseg);
     const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
-    if (r < 0 || r >= p.n_rows) {  // row id outside the tensor: NaN, no reads
+    const bool bad = r < 0 || r >= p.n_rows;  // row id outside the tensor: NaN, no reads
+    if (!INBLOCK && bad) {
         if (threadIdx.x == 0) {
-            const vwc_partial bad{NAN, NAN, NAN, NAN};
+            const vwc_partial nan4{NAN, NAN, NAN, NAN};
             if (p.nseg > 1)
-                p.seg_part[static_cast<int64_t>(q) * p.m + i] = bad;
+                p.seg_part[static_cast<int64_t>(q) * p.m + i] = nan4;
             else if (p.partial_out)
-                p.partial_out[i] = bad;
+                p.partial_out[i] = nan4;
             else {
                 if (p.logprob && p.target_mode != kTargetNone) p.logprob[i] = NAN;
                 if (p.lse) p.lse[i] = NAN;
@@ -422,54 +447,78 @@ __global__ __launch_bounds__(kFwdBlock) VWC_FWD_ATTR void fwd_segment_kernel(Fwd
         }
         return;
     }
-    const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
 
-    const int32_t nunits = p.vocab / Un::N;  // whole units; the rest is the tail
-    const int32_t u0 = q * p.seg_units;
-    const int32_t u1 = min(u0 + p.seg_units, nunits);
-    const bool last = q == p.nseg - 1;
+    vwc_partial mine{NAN, NAN, NAN, NAN};
+    if (!bad) {  // uniform over the workgroup
+        const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
+        const int32_t nunits = p.vocab / Un::N;  // whole units; the rest is the tail
+        const int32_t u0 = q * p.seg_units;
+        const int32_t u1 = min(u0 + p.seg_units, nunits);
+        const bool last = q == p.nseg - 1;
 
-    Lane L = lane_init();
-    if (u0 < u1) stream_units<DT, VEC, kFwdU, W>(row, u0, u1, p.c, L);
-    if (VEC && last) {  // tail elements past the last whole vector
-        const int32_t j = nunits * Un::N + static_cast<int32_t>(threadIdx.x);
-        if (j < p.vocab) {
-            using Us = Unit<DT, false>;
-            typename Us::T v[1];
-            const typename Us::T *ptr = reinterpret_cast<const typename Us::T *>(row) + j;
-            v[0] = *ptr;
-            fold_chunk<DT, false, 1, W>(v, 1, p.c, L);
+        Lane L = lane_init();
+        if (u0 < u1) stream_units<DT, VEC, kFwdU, W>(row, u0, u1, p.c, tid, L);
+        if (VEC && last) {  // tail elements past the last whole vector
+            const int32_t j = nunits * Un::N + tid;
+            if (j < p.vocab) {
+                using Us = Unit<DT, false>;
+                typename Us::T v[1];
+                const typename Us::T *ptr = reinterpret_cast<const typename Us::T *>(row) + j;
+                v[0] = *ptr;
+                fold_chunk<DT, false, 1, W>(v, 1, p.c, L);
+            }
+        }
+        const Lane B = block_reduce<INBLOCK ? kFwdMaxSegPerBlock : 1>(L, grp);
+        if (!INBLOCK && threadIdx.x != 0) return;
+
+        if (tid == 0) {
+            // Target logit from the segment that owns its column.
+            double t = -INFINITY;
+            if (p.target_mode != kTargetNone) {
+                const int64_t tl = static_cast<int64_t>(p.targets[r]) - p.v_start;
+                const int64_t span = static_cast<int64_t>(p.seg_units) * Un::N;
+                const bool in_range = tl >= 0 && tl < p.vocab;
+                if (in_range) {
+                    const int64_t owner = min(tl / span, static_cast<int64_t>(p.nseg - 1));
+                    if (owner == q) t = load_element<DT>(row, tl);
+                } else if (p.target_mode == kTargetFull && q == 0) {
+                    t = NAN;
+                }
+            }
+            const P64 part = to_partial(B, p.c, t);
+            if (!INBLOCK && p.nseg == 1 && !p.partial_out) {
+                const Merged g = merge_partials([&](int) { return part; }, 1, p.tau);
+                write_final(g, p.tau, i, p.target_mode == kTargetNone ? nullptr : p.logprob,
+                            p.lse, p.entropy);
+                return;
+            }
+            mine = vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
+                               static_cast<float>(part.t), static_cast<float>(part.w)};
         }
     }
-    const Lane B = block_reduce(L);
+
+    if (!INBLOCK) {  // thread 0 of a (row, segment) workgroup
+        if (p.nseg > 1)
+            p.seg_part[static_cast<int64_t>(q) * p.m + i] = mine;
+        else
+            p.partial_out[i] = mine;
+        return;
+    }
+    __shared__ vwc_partial seg_parts[kFwdMaxSegPerBlock];
+    if (tid == 0) seg_parts[grp] = mine;
+    __syncthreads();
     if (threadIdx.x != 0) return;
-
-    // Target logit from the segment that owns its column.
-    double t = -INFINITY;
-    if (p.target_mode != kTargetNone) {
-        const int64_t tl = static_cast<int64_t>(p.targets[r]) - p.v_start;
-        const int64_t span = static_cast<int64_t>(p.seg_units) * Un::N;
-        const bool in_range = tl >= 0 && tl < p.vocab;
-        if (in_range) {
-            const int64_t owner = min(tl / span, static_cast<int64_t>(p.nseg - 1));
-            if (owner == q) t = load_element<DT>(row, tl);
-        } else if (p.target_mode == kTargetFull && q == 0) {
-            t = NAN;
-        }
-    }
-    const P64 part = to_partial(B, p.c, t);
-    if (p.nseg > 1) {
-        p.seg_part[static_cast<int64_t>(q) * p.m + i] =
-            vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
-                        static_cast<float>(part.t), static_cast<float>(part.w)};
-    } else if (p.partial_out) {
-        p.partial_out[i] = vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
-                                       static_cast<float>(part.t), static_cast<float>(part.w)};
-    } else {
-        const Merged g = merge_partials([&](int) { return part; }, 1, p.tau);
+    const Merged g = merge_partials(
+        [&](int k) {
+            const vwc_partial v = seg_parts[k];
+            return P64{v.m, v.s, v.t, v.w};
+        },
+        p.nseg, p.tau);
+    if (p.partial_out)
+        p.partial_out[i] = to_f32(g);
+    else
         write_final(g, p.tau, i, p.target_mode == kTargetNone ? nullptr : p.logprob, p.lse,
                     p.entropy);
-    }
 }
 
 // One thread per row: merge k partials ([k][stride]) in slice order.
@@ -898,20 +947,32 @@ __global__ __launch_bounds__(kScanBlock) void mask_to_index_kernel(const uint8_t
 
 // ---------------------------------------------------------------- launch helpers
 
-template <int DT>
-hipError_t launch_fwd_dt(const FwdPlan &p, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kFwdBlock);
+template <int DT, bool INBLOCK>
+void launch_fwd_shape(const FwdPlan &p, dim3 grid, dim3 block, hipStream_t s) {
     if (p.vector) {
         if (p.want_entropy)
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, true, INBLOCK>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, false, INBLOCK>), grid, block, 0, s,
+                               p);
     } else {
         if (p.want_entropy)
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, true, INBLOCK>), grid, block, 0, s,
+                               p);
         else
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, false, INBLOCK>), grid, block, 0, s,
+                               p);
     }
+}
+
+template <int DT>
+hipError_t launch_fwd_dt(const FwdPlan &p, hipStream_t s) {
+    if (p.nseg > 1 && !fwd_needs_workspace(p.nseg))
+        launch_fwd_shape<DT, true>(p, dim3(static_cast<uint32_t>(p.m)),
+                                   dim3(static_cast<uint32_t>(p.nseg * kFwdBlock)), s);
+    else
+        launch_fwd_shape<DT, false>(p, dim3(static_cast<uint32_t>(p.m * p.nseg)),
+                                    dim3(kFwdBlock), s);
     return hipGetLastError();
 }
 
@@ -938,7 +999,7 @@ hipError_t launch_bwd_dt(const BwdPlan &p, hipStream_t s) {
 hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream) {
     hipError_t e = dt == VWC_BF16 ? launch_fwd_dt<VWC_BF16>(p, stream)
                                   : launch_fwd_dt<VWC_FP32>(p, stream);
-    if (e != hipSuccess || p.nseg == 1) return e;
+    if (e != hipSuccess || !fwd_needs_workspace(p.nseg)) return e;
     CombinePlan c{};
     c.parts = p.seg_part;
     c.k = p.nseg;

@@ -213,6 +213,10 @@ def test_lmhead_validation(lib):
     assert call(d=60, ldh=64, ldw=64) == UNSUPPORTED
     assert call(ldh=68, d=64) == UNSUPPORTED
     assert call(ldh=1 << 22) == UNSUPPORTED
+    # kept rows whose gather would need more than 2^31 workgroups
+    wide = 1 << 21
+    assert call(n=1 << 31, rows=FAKE, m=1 << 31, d=wide, ldh=wide, ldw=wide) == UNSUPPORTED
+    assert b"gather" in err()
     # workspace: required, large enough, aligned
     assert call(w=None, wsb=0) == INVALID
     assert b"workspace" in err()

@@ -330,8 +330,9 @@ vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, i
  *           vocabulary entries, then the m kept rows compacted, m * d * 2
  *           bytes rounded up to 16); without row_idx the partials alone.
  * Layout limits (VWC_ERR_UNSUPPORTED otherwise): hidden and weight 16-byte
- * aligned, d, ldh and ldw multiples of 8, ldh and ldw below 2^22.  m > 0
- * needs n_rows >= 1.  A row id
+ * aligned, d, ldh and ldw multiples of 8, ldh and ldw below 2^22, m at most
+ * INT32_MAX (and m * d / 8 below 2^39 with row_idx).  m > 0 needs
+ * n_rows >= 1.  A row id
  * outside [0, n_rows) gives NaN outputs; a target outside [0, vocab) gives a
  * NaN logprob.  The reduction order of a row depends only on vocab and d,
  * so a row gives bit-identical results whatever row set it is computed in.

@@ -217,6 +217,7 @@ def test_lmhead_validation(lib):
     wide = 1 << 21
     assert call(n=1 << 31, rows=FAKE, m=1 << 31, d=wide, ldh=wide, ldw=wide) == UNSUPPORTED
     assert b"gather" in err()
+    assert call(n=1 << 31, m=1 << 31) == UNSUPPORTED   # more rows than one launch takes
     # workspace: required, large enough, aligned
     assert call(w=None, wsb=0) == INVALID
     assert b"workspace" in err()

@@ -516,7 +516,7 @@ vwc_status vwc_lmhead_logprob_fwd(const void *hidden, int64_t n_rows, int64_t ld
     // The row gather runs one thread per 16-byte chunk of the kept rows.
     if (row_idx && (m * (d / 8) + 255) / 256 > INT32_MAX)
         return fail(VWC_ERR_UNSUPPORTED, "%s: kept rows too large to gather in one launch", fn);
-    if (ntb > INT32_MAX / nseg)
+    if (m > INT32_MAX || ntb > INT32_MAX / nseg)
         return fail(VWC_ERR_UNSUPPORTED, "%s: %lld rows exceed one launch", fn,
                     static_cast<long long>(m));
     const size_t part_bytes = lmhead_partial_bytes(m, vocab);

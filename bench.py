@@ -74,23 +74,41 @@ def cpu_baseline(w, seconds):
         x[r0:r0 + blk.shape[0]] = blk
 
     W.fill_logits(w, sink, block_rows=256)
-    block = 128
-    rows_done, elapsed = 0, 0.0
-    while elapsed < seconds:
-        for r0 in range(0, w.n_rows, block):
-            rows = np.arange(r0, min(r0 + block, w.n_rows))
-            t0 = time.perf_counter()
-            oracle.forward(x[rows], t_all[rows])
-            oracle.backward(x[rows], t_all[rows], g_all[rows])
-            elapsed += time.perf_counter() - t0
-            rows_done += rows.size
-            if elapsed >= seconds:
-                break
-    return {"value": rows_done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{rows_done} rows of {w.name} in order, cycling over all {w.n_rows} rows "
-                      f"(fwd logprob+lse+entropy and the fp64 gradient of each row), "
-                      f"{elapsed:.1f} s of oracle time"}
+
+    def run(seconds, block):
+        rows_done, elapsed = 0, 0.0
+        while elapsed < seconds:
+            for r0 in range(0, w.n_rows, block):
+                rows = np.arange(r0, min(r0 + block, w.n_rows))
+                t0 = time.perf_counter()
+                oracle.forward(x[rows], t_all[rows])
+                oracle.backward(x[rows], t_all[rows], g_all[rows])
+                elapsed += time.perf_counter() - t0
+                rows_done += rows.size
+                if elapsed >= seconds:
+                    break
+        return rows_done, elapsed
+
+    rows_done, elapsed = run(seconds, 128)
+    out = {"value": rows_done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"{rows_done} rows of {w.name} in order, cycling over all {w.n_rows} rows "
+                     f"(fwd logprob+lse+entropy and the fp64 gradient of each row), "
+                     f"{elapsed:.1f} s of oracle time"}
+    out.update(single_core(lambda sec: run(sec, 8), seconds))
+    return out
+
+
+def single_core(run, seconds):
+    """The same oracle work on one thread, for a shorter time."""
+    import oracle
+
+    prev = oracle.set_num_threads(1)
+    try:
+        done, el = run(max(2.0, seconds / 3))
+    finally:
+        oracle.set_num_threads(prev)
+    return {"value_1core": done / el, "sample_1core": f"{done} rows on 1 thread, {el:.1f} s"}
 
 
 def code_digest(path):
@@ -126,9 +144,18 @@ def recorded_traffic(kernel_key, workload=DEFAULT_WORKLOAD, source="vwc_kernels.
     return total
 
 
+def ms_stats(samples):
+    """Mean, median and minimum of per-step event times (ms)."""
+    v = sorted(samples)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"ms": sum(v) / n, "ms_median": med, "ms_min": v[0]}
+
+
 def time_passes(passes, steps, warmup, stream):
-    """Run the passes in order `steps` times; per-pass average ms from HIP events
-    recorded on `stream`, and the wall-clock ms of one step."""
+    """Run the passes in order `steps` times; per-pass event times (ms, one list
+    per pass) from HIP events recorded on `stream`, and the wall-clock ms of one
+    step."""
     import torch
 
     for _ in range(warmup):
@@ -145,7 +172,7 @@ def time_passes(passes, steps, warmup, stream):
             ev[k][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - wall0) * 1e3 / steps
-    ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(len(passes))]
+    ms = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(passes))]
     return ms, wall
 
 
@@ -253,10 +280,14 @@ def bench_other(args, w, x):
         passes.append(("bwd", lambda: vwc.selected_logprob_bwd(x, t, lse, g, w.tau,
                                                                grad_logits=grad, stream=stream),
                        N * (2 * V * e + 12)))
-    ms, wall = time_passes(passes, args.steps, args.warmup, stream)
+    samples, wall = time_passes(passes, args.steps, args.warmup, stream)
     per_pass = []
-    for (name, _, b), m in zip(passes, ms):
-        per_pass.append({"pass": name, "ms": m, "bytes_alg": b,
+    ms = []
+    for (name, _, b), smp in zip(passes, samples):
+        st = ms_stats(smp)
+        m = st["ms"]
+        ms.append(m)
+        per_pass.append({"pass": name, **st, "bytes_alg": b,
                          "gbs_alg": b / (m * 1e-3) / 1e9,
                          "frac": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBS})
     total_b = sum(p[2] for p in passes)
@@ -276,12 +307,13 @@ def bench_other(args, w, x):
         sl, sls, sen = (torch.empty(N, device=dev) for _ in range(3))
         wsf = torch.empty(max(vwc.workspace_bytes(N, V, x.dtype), 1), dtype=torch.uint8,
                           device=dev)
-        ms1, _ = time_passes([("single", lambda: vwc.selected_logprob_fwd(
+        smp1, _ = time_passes([("single", lambda: vwc.selected_logprob_fwd(
             x, t, w.tau, logprob=sl, lse=sls, entropy=sen, workspace=wsf, stream=stream), 0)],
             args.steps, args.warmup, stream)
+        st1 = ms_stats(smp1[0])
         b1 = N * (V * e + 16)
-        out["single_pass_fwd"] = {"ms": ms1[0], "gbs_alg": b1 / (ms1[0] * 1e-3) / 1e9,
-                                  "frac": b1 / (ms1[0] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        out["single_pass_fwd"] = {**st1, "gbs_alg": b1 / (st1["ms"] * 1e-3) / 1e9,
+                                  "frac": b1 / (st1["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
     return out
 
 
@@ -293,16 +325,22 @@ def lmhead_cpu_baseline(w, h, wt, tg, rows, seconds):
     import oracle
 
     sel = np.random.default_rng(11).permutation(rows.size)
-    done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < seconds and done < sel.size:
-        r = rows[sel[done: done + 1]]
-        oracle.lmhead_forward(h, wt, tg, rows=r)
-        done += 1
-    el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{done} kept rows of {w.name} in random order (fp64 projection of each "
-                      f"row against all {w.vocab} weight rows, then logprob+lse+entropy), "
-                      f"{el:.1f} s of oracle time"}
+
+    def run(seconds):
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds and done < sel.size:
+            r = rows[sel[done: done + 1]]
+            oracle.lmhead_forward(h, wt, tg, rows=r)
+            done += 1
+        return done, time.perf_counter() - t0
+
+    done, el = run(seconds)
+    out = {"value": done / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{done} kept rows of {w.name} in random order (fp64 projection of each "
+                     f"row against all {w.vocab} weight rows, then logprob+lse+entropy), "
+                     f"{el:.1f} s of oracle time"}
+    out.update(single_core(run, seconds))
+    return out
 
 
 def bench_lmhead(args, w):
@@ -340,10 +378,12 @@ def bench_lmhead(args, w):
          lambda: vwc.lmhead_logprob_fwd(h, wt, tg, rows, w.tau, logprob=lp, lse=lse,
                                         entropy=ent, workspace=ws, stream=stream), flops),
     ]
-    ms, wall = time_passes(passes, args.steps, args.warmup, stream)
-    per_pass = [{"pass": n, "ms": m, "tflops": f / (m * 1e-3) / 1e12,
-                 "frac": f / (m * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-                for (n, _, f), m in zip(passes, ms)]
+    samples, wall = time_passes(passes, args.steps, args.warmup, stream)
+    stats = [ms_stats(smp) for smp in samples]
+    ms = [st["ms"] for st in stats]
+    per_pass = [{"pass": n, **st, "tflops": f / (st["ms"] * 1e-3) / 1e12,
+                 "frac": f / (st["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+                for (n, _, f), st in zip(passes, stats)]
     # Context: the unfused route materialises bf16 logits [M, V] with hipBLASLt.
     hc = h[rows.long()].contiguous()
     logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
@@ -353,7 +393,8 @@ def bench_lmhead(args, w):
            ("fwd_over_logits", lambda: vwc.selected_logprob_fwd(logits, tg[rows.long()], w.tau,
                                                                 logprob=lp, lse=lse, workspace=ws2,
                                                                 stream=stream), 0)]
-    ums, _ = time_passes(unf, max(3, args.steps // 4), 1, stream)
+    usmp, _ = time_passes(unf, max(3, args.steps // 4), 1, stream)
+    ums = [ms_stats(smp)["ms"] for smp in usmp]
     del logits, hc
     out = {
         "metric": f"kept rows/s of the fused LM head ({w.name})",
@@ -473,10 +514,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    fwd_st = ms_stats([e[0].elapsed_time(e[1]) for e in events])
+    bwd_st = ms_stats([e[1].elapsed_time(e[2]) for e in events])
+    fwd_avg = fwd_st["ms"]
+    bwd_avg = bwd_st["ms"]
     ms_per_step = wall * 1e3 / args.steps
     fwd_b, bwd_b = alg_bytes(w.n_rows, w.vocab, esize, esize, live, want_ent)
     fwd_e_b, _ = alg_bytes(w.n_rows, w.vocab, esize, esize, live, True)
@@ -490,7 +531,8 @@ def main():
                                  workspace=ws, stream=stream)
         ent_events[k][1].record(stream)
     torch.cuda.synchronize()
-    fwd_e_avg = sum(e[0].elapsed_time(e[1]) for e in ent_events) / args.steps
+    fwd_e_st = ms_stats([e[0].elapsed_time(e[1]) for e in ent_events])
+    fwd_e_avg = fwd_e_st["ms"]
 
     def gbs(b, ms):
         return b / (ms * 1e-3) / 1e9
@@ -502,7 +544,7 @@ def main():
         dom = ("bwd_segment_kernel", bwd_b, bwd_avg, ["bwd_segment_kernel<0, 0, true, false>"])
     else:
         dom = ("fwd_segment_kernel+combine_kernel", fwd_b, fwd_avg,
-               ["fwd_segment_kernel<0, true, false>", "combine_kernel"])
+               ["fwd_segment_kernel<0, true, false, false>", "combine_kernel"])
     traffic = recorded_traffic(dom[3]) if w.name == "spiked_bf16_8192x248320" else None
 
     result = {
@@ -522,13 +564,13 @@ def main():
                    "temperature": w.tau, "live_grad_rows": live,
                    "step": "fwd(logprob,lse" + (",entropy" if want_ent else "") +
                            ") + bwd(" + w.dtype + " grad)"},
-        "fwd": {"ms": fwd_avg, "tokens_per_s": w.n_rows / (fwd_avg * 1e-3),
+        "fwd": {**fwd_st, "tokens_per_s": w.n_rows / (fwd_avg * 1e-3),
                 "gbs_alg": gbs(fwd_b, fwd_avg), "frac": gbs(fwd_b, fwd_avg) / HBM_PEAK_GBS,
                 "bytes_alg": fwd_b},
-        "fwd_entropy": {"ms": fwd_e_avg, "tokens_per_s": w.n_rows / (fwd_e_avg * 1e-3),
+        "fwd_entropy": {**fwd_e_st, "tokens_per_s": w.n_rows / (fwd_e_avg * 1e-3),
                         "gbs_alg": gbs(fwd_e_b, fwd_e_avg),
                         "frac": gbs(fwd_e_b, fwd_e_avg) / HBM_PEAK_GBS, "bytes_alg": fwd_e_b},
-        "bwd": {"ms": bwd_avg, "tokens_per_s": w.n_rows / (bwd_avg * 1e-3),
+        "bwd": {**bwd_st, "tokens_per_s": w.n_rows / (bwd_avg * 1e-3),
                 "gbs_alg": gbs(bwd_b, bwd_avg), "frac": gbs(bwd_b, bwd_avg) / HBM_PEAK_GBS,
                 "bytes_alg": bwd_b},
         "fwd_bwd": {"ms": fwd_avg + bwd_avg,

@@ -82,6 +82,8 @@ def _load():
         lib.oracle_bf16_rne.restype = ctypes.c_uint16
         lib.oracle_bf16_rne_array.argtypes = [p, p, i64]
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         for f in ("oracle_forward", "oracle_backward", "oracle_backward_entropy",
                   "oracle_topk_kl_forward", "oracle_topk_kl_backward",
                   "oracle_slice_partial", "oracle_combine", "oracle_forward_vchunk",
@@ -286,6 +288,13 @@ def bf16_rne(v) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Run later oracle calls on n threads; returns the previous count."""
+    prev = num_threads()
+    _load().oracle_set_num_threads(int(n))
+    return prev
 
 
 def _lmhead_operands(hidden, weight, d):

@@ -201,6 +201,9 @@ void oracle_bf16_rne_array(const double *v, uint16_t *out, int64_t n);
 /* Number of OpenMP threads the oracle runs on. */
 int oracle_num_threads(void);
 
+/* Run later calls on n threads (n > 0; ignored otherwise). */
+void oracle_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

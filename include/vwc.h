@@ -260,7 +260,8 @@ vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
 
 /*
  * Gradient of sum_r g_r loss_r with respect to the student logits, in one
- * streaming pass plus a fix-up of the k payload columns per row (the page's
+ * streaming pass that also writes the k payload columns (rows on 16 bytes and
+ * k <= 256; otherwise a second launch rewrites those columns) (the page's
  * analytic form: q_j - p_j inside the top-k and q_j (P - Q)/(1 - Q) outside
  * for the tail objective; q_j P - p_j [j in T] for the truncated one, and 0
  * for a clamped truncated row or while the eps guard is active on the tail

@@ -158,3 +158,80 @@ def test_topk_kl_full_size_k128():
         del grad
     del x
     torch.cuda.empty_cache()
+
+
+def _bf16_round(a):
+    """float32 -> bf16 bits (round to nearest even) for building test logits."""
+    return oracle.bf16_rne(a.astype(np.float64))
+
+
+def _payload_columns(V, N, seg_col, k, rng):
+    """Columns that land on unit and segment edges: the first unit, a whole unit,
+    both sides of the first segment boundary, the last whole unit and the tail
+    past it; then distinct random columns up to k."""
+    tail0 = (V // N) * N
+    edge = [0, 1, N - 1, seg_col - 1, seg_col, seg_col + 1, tail0 - 1, V - 1, V - 2]
+    edge += list(range(4 * N, 5 * N))  # one whole unit
+    cols = list(dict.fromkeys(c for c in edge if 0 <= c < V))
+    rest = rng.permutation(np.setdiff1d(np.arange(V), cols))[: k - len(cols)]
+    return np.concatenate([cols, rest]).astype(np.int32)[:k]
+
+
+# (logits dtype, grad dtype, vocab, k, ld padding): the fused pass (rows on 16
+# bytes, k <= 256) with payload columns in the tail, on segment edges and filling
+# a unit, for each dtype pair; and the two cases that keep the separate payload
+# launch (k above the fused table's 256, rows not on 16 bytes).  The row stride
+# is the vocabulary rounded up to 8 (plus the padding); the columns past the
+# vocabulary hold NaN, in the logits and in the gradient buffer.
+LAYOUTS = [
+    ("bf16", "bf16", 151939, 64, 0),
+    ("bf16", "fp32", 151939, 40, 0),
+    ("fp32", "fp32", 70001, 32, 0),
+    ("fp32", "bf16", 70001, 32, 0),
+    ("bf16", "bf16", 151939, 300, 0),
+    ("bf16", "bf16", 151939, 64, 1),
+]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS, ids=[f"{a}-{b}-V{c}-k{d}-pad{e}" for a, b, c, d, e in LAYOUTS])
+@pytest.mark.parametrize("mode", MODES)
+def test_topk_kl_payload_layouts(layout, mode):
+    dt, gdt, V, K, pad = layout
+    n = 6
+    N = 8 if dt == "bf16" else 4
+    e = 2 if dt == "bf16" else 4
+    ld = (V + 7) // 8 * 8 + pad
+    nseg = -(-(V * e) // (256 * 1024))
+    seg_col = -(-(V // N) // nseg) * N  # first column of segment 1
+    rng = np.random.default_rng(31 + K + pad)
+    idx = np.stack([_payload_columns(V, N, seg_col, K, rng) for _ in range(n)])
+    w_ = rng.exponential(size=(n, K))
+    mass = rng.uniform(0.5, 0.98, size=(n, 1))
+    tlp = np.log(mass * w_ / w_.sum(1, keepdims=True)).astype(np.float32)
+    xf = np.full((n, ld), np.nan, np.float32)
+    xf[:, :V] = rng.standard_normal((n, V)) * 2.0
+    for r in range(n):  # student close to the teacher on the payload: cancellation
+        xf[r, idx[r]] = tlp[r] + 9.0 + rng.normal(0, 0.05, K).astype(np.float32)
+    x = _bf16_round(xf) if dt == "bf16" else xf
+    xv = np.ascontiguousarray(x[:, :V])
+    g = rng.uniform(-1, 1, n).astype(np.float32)
+    g[1] = 0.0
+    log(f"top-k KL payload layout {layout} mode={mode}")
+    xd = to_dev_logits(x)[:, :V]
+    idd, tld = torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV)
+    fwd = vwc.topk_kl_fwd(xd, idd, tld, mode)
+    ref_fwd = check_fwd(fwd, xv, idx, tlp, mode, 1.0)
+    gdtype = torch.bfloat16 if gdt == "bf16" else torch.float32
+    gbuf = torch.full((n, ld), float("nan"), dtype=gdtype, device=DEV)
+    grad = vwc.topk_kl_bwd(xd, idd, tld, fwd, torch.from_numpy(g).to(DEV), mode,
+                           grad_logits=gbuf[:, :V])
+    ref = oracle.topk_kl_backward(xv, idx, tlp, mode, g)
+    if gdt == "fp32":
+        err = np.abs(_np(grad).astype(np.float64) - ref).max()
+        assert err <= 1e-6, f"fp32 grad err {err}"
+    else:
+        bound = grad_bound(xv, idx, tlp, mode, 1.0, fwd, ref_fwd, g)
+        nb = check_bf16_grad(grad_bits(grad.contiguous()), ref, bound)
+        log(f"  {nb} elements beyond one bf16 step (within the bar)")
+    assert np.all(_np(grad[1].float()) == 0.0)
+    assert torch.isnan(gbuf[:, V:].float()).all()  # nothing written past the vocabulary

@@ -143,6 +143,10 @@ struct KlArgs {
     const float *P, *Q, *S;
     int mode;
     double eps;
+    const int32_t *idx;  // payload columns [n_rows][k] and teacher log-probs
+    const float *tlp;
+    int32_t k;
+    bool fused;          // set by backward_common: the payload columns were written too
 };
 
 vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n_rows,
@@ -151,7 +155,7 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
                            const float *entropy, const float *grad_logprob,
                            const float *grad_entropy, void *grad_logits, int grad_dt,
                            int64_t ld_grad, bool by_row_id, hipStream_t stream,
-                           const KlArgs *kl = nullptr) {
+                           KlArgs *kl = nullptr) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
     if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
@@ -218,6 +222,16 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     p.nseg = static_cast<int>(nseg);
     p.seg_units = static_cast<int32_t>((nunits + nseg - 1) / nseg);
     if (p.seg_units < 1) p.seg_units = 1;
+    if (kl) {
+        // The payload columns go into the same pass when the rows are 16-byte
+        // vectors and a segment's payload fits the in-LDS table; otherwise the
+        // caller runs the fix-up launch.
+        kl->fused = p.vector && kl->k <= vwc::kKlMaxK && p.seg_units <= vwc::kKlMaxSegUnits;
+        p.kl_fused = kl->fused;
+        p.kl_idx = kl->idx;
+        p.kl_tlp = kl->tlp;
+        p.kl_k = kl->k;
+    }
     return hip_status(vwc::launch_bwd(p, stream), fn);
 }
 
@@ -396,11 +410,12 @@ vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
     if (n_rows > 0 && (!student_mass || !teacher_mass || !topk_sum || !grad_loss))
         return fail(VWC_ERR_INVALID_ARG,
                     "%s: null student_mass, teacher_mass, topk_sum or grad_loss", fn);
-    KlArgs kl{teacher_mass, student_mass, topk_sum, static_cast<int>(mode), tail_mass_eps};
+    KlArgs kl{teacher_mass, student_mass, topk_sum, static_cast<int>(mode), tail_mass_eps,
+              topk_idx, teacher_logprob, k, false};
     st = backward_common(fn, logits, dt, n_rows, vocab, ld, nullptr, nullptr, n_rows, temperature,
                          lse, nullptr, grad_loss, nullptr, grad_logits, grad_dt, ld_grad, true,
                          stream, &kl);
-    if (st != VWC_OK || n_rows == 0) return st;
+    if (st != VWC_OK || n_rows == 0 || kl.fused) return st;
     vwc::TopkPlan p{};
     p.logits = logits;
     p.ld = ld;

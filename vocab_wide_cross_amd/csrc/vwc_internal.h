@@ -105,6 +105,13 @@ struct BwdPlan {
     const float *kl_P, *kl_Q, *kl_S;
     int kl_mode;
     double kl_eps;
+    // Fused payload columns (kl_fused): the k payload columns of each row
+    // (kl_idx, kl_tlp: [m][kl_k]) get beta q_j - kappa p_j in the same pass,
+    // so no fix-up launch follows.
+    bool kl_fused;
+    const int32_t *kl_idx;
+    const float *kl_tlp;
+    int32_t kl_k;
     void *grad;
     int64_t ld_grad;
     bool grad_by_row_id;      // true: gradient row = row id; false: = output index
@@ -112,6 +119,14 @@ struct BwdPlan {
     int32_t seg_units;
     bool vector;
 };
+
+// The fused top-k KL backward keeps a segment's payload columns in an LDS hash
+// table of kKlSlots entries, so it takes rows of at most kKlMaxK payload
+// columns (load factor <= 1/2), and each thread's units of a segment are
+// flagged in one 32-bit mask.
+constexpr int kKlSlots = 512;
+constexpr int kKlMaxK = kKlSlots / 2;
+constexpr int64_t kKlMaxSegUnits = 32 * static_cast<int64_t>(VWC_BWD_BLOCK);
 
 struct CombinePlan {
     const vwc_partial *parts;   // [k][stride]

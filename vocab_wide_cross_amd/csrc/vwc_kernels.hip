@@ -676,6 +676,58 @@ __device__ __forceinline__ KlCoef kl_coef(int mode, double eps, double P, double
     return c;
 }
 
+// Gradient of payload column n of a row whose student logit is x:
+// (beta q - kappa p_n) g / tau with q = exp(x / tau - lse), p_n = exp(a_n), in
+// fp64 (the two terms cancel when the student matches the teacher).
+__device__ __forceinline__ float kl_payload_grad(double x, double tau, double lse, double gt,
+                                                 const KlCoef &c, float tlp) {
+    const double q = exp(x / tau - lse);
+    const double pn = exp(static_cast<double>(tlp));
+    return static_cast<float>(gt * (c.beta * q - c.kappa * pn));
+}
+
+// The payload columns of one backward segment, in LDS.  An open-addressing
+// table keyed by the segment-relative 16-byte unit (the row's tail past its
+// last whole vector has a key of its own) holds which columns of the unit are
+// payload columns and their final gradients; the streaming pass overwrites
+// those lanes of the unit before its one store.  A per-thread mask marks the
+// thread's units that have an entry (bit `it`: unit u0 + thread + it * kBwdBlock),
+// so the common unit costs one bit test.
+struct KlSlot {
+    int32_t unit;   // -1: empty
+    uint32_t cols;  // bit k: column k of the unit is a payload column
+    float val[8];   // its gradient
+};
+constexpr int32_t kKlTailKey = 0x7fffffff;
+
+__device__ __forceinline__ uint32_t kl_hash(int32_t key) {
+    return (static_cast<uint32_t>(key) * 0x9E3779B1u) >> 23;  // 9 bits: kKlSlots = 512
+}
+static_assert(kKlSlots == 512, "kl_hash yields 9 bits");
+
+// Slot of `key`, or -1 when it is absent (a probe ends at an empty slot; the
+// table is at most half full).
+__device__ __forceinline__ int kl_find(const KlSlot *tab, int32_t key) {
+    uint32_t h = kl_hash(key);
+    for (int probe = 0; probe < kKlSlots; ++probe) {
+        const int32_t u = tab[h].unit;
+        if (u == key) return static_cast<int>(h);
+        if (u == -1) return -1;
+        h = (h + 1) & (kKlSlots - 1);
+    }
+    return -1;
+}
+
+template <int N>
+__device__ __forceinline__ void kl_patch(const KlSlot *tab, int32_t key, float (&o)[N]) {
+    const int h = kl_find(tab, key);
+    if (h < 0) return;
+    const uint32_t cols = tab[h].cols;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        if ((cols >> k) & 1u) o[k] = tab[h].val[k];
+}
+
 // Uniform per-row constants of the backward.
 struct RowGrad {
     float c;       // log2(e) / tau
@@ -718,9 +770,11 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
     }
 }
 
-// Gradient of segment q of output row i.
-template <int DT, int GDT, bool VEC, bool WH>
+// Gradient of segment q of output row i.  KLF: top-k KL with the payload
+// columns written in the same pass (16-byte units, no entropy term).
+template <int DT, int GDT, bool VEC, bool WH, bool KLF>
 __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
+    static_assert(!KLF || (VEC && !WH), "fused payload columns: vector rows, no entropy term");
     using Un = Unit<DT, VEC>;
     using T = typename Un::T;
     constexpr int N = Un::N;
@@ -776,6 +830,43 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     if (kl) R.gs = static_cast<float>(R.gt * klc.alpha);  // o = q (g alpha / tau)
     const T *src = reinterpret_cast<const T *>(row);
 
+    __shared__ KlSlot kl_tab[KLF ? kKlSlots : 1];
+    __shared__ uint32_t kl_lane[KLF ? kBwdBlock : 1];
+    uint32_t kl_mine = 0;  // bit it: this thread's unit u0 + tid + it * kBwdBlock has payload columns
+    if constexpr (KLF) {
+        const int tid = static_cast<int>(threadIdx.x);
+        for (int h = tid; h < kKlSlots; h += kBwdBlock) {
+            kl_tab[h].unit = -1;
+            kl_tab[h].cols = 0u;
+        }
+        kl_lane[tid] = 0u;
+        __syncthreads();
+        // This segment's payload columns: its whole vectors, and in the last
+        // segment the tail past them.
+        const int32_t vc0 = u0 * N, vc1 = u1 * N;
+        for (int n = tid; n < p.kl_k; n += kBwdBlock) {
+            const int32_t j = p.kl_idx[i * p.kl_k + n];
+            const bool vec_col = j >= vc0 && j < vc1;
+            const bool tail_col = last && j >= nunits * N && j < p.vocab;
+            if (!vec_col && !tail_col) continue;  // another segment's, or outside the row
+            const int32_t key = vec_col ? j / N - u0 : kKlTailKey;
+            const int kk = j % N;
+            const float val = kl_payload_grad(static_cast<double>(load_element<DT>(row, j)),
+                                              R.tau, R.lse, R.gt, klc, p.kl_tlp[i * p.kl_k + n]);
+            uint32_t h = kl_hash(key);
+            for (int probe = 0; probe < kKlSlots; ++probe) {  // at most half full: ends early
+                const int32_t old = atomicCAS(&kl_tab[h].unit, -1, key);
+                if (old == -1 || old == key) break;
+                h = (h + 1) & (kKlSlots - 1);
+            }
+            atomicOr(&kl_tab[h].cols, 1u << kk);
+            kl_tab[h].val[kk] = val;
+            if (vec_col) atomicOr(&kl_lane[key % kBwdBlock], 1u << (key / kBwdBlock));
+        }
+        __syncthreads();
+        kl_mine = kl_lane[tid];
+    }
+
     int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
     for (; b + (U - 1) * kBwdBlock < u1; b += U * kBwdBlock) {
         T v[U];
@@ -786,6 +877,8 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
             const int32_t unit = b + j * kBwdBlock;
             float o[N];
             unit_grad<DT, VEC, WH>(v[j], unit * N, R, o);
+            if (KLF && ((kl_mine >> ((unit - u0) / kBwdBlock)) & 1u))
+                kl_patch<N>(kl_tab, unit - u0, o);
             GradStore<GDT, N>::store(grow + static_cast<int64_t>(unit) * N * kGE, o);
         }
     }
@@ -793,6 +886,7 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         const T v = Un::load(src + b);
         float o[N];
         unit_grad<DT, VEC, WH>(v, b * N, R, o);
+        if (KLF && ((kl_mine >> ((b - u0) / kBwdBlock)) & 1u)) kl_patch<N>(kl_tab, b - u0, o);
         GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, o);
     }
     if (VEC && last) {
@@ -802,16 +896,21 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
             const typename Us::T v = reinterpret_cast<const typename Us::T *>(row)[j];
             float o[1];
             unit_grad<DT, false, WH>(v, j, R, o);
+            if constexpr (KLF) {  // column j - nunits * N (< N) of the tail
+                const int h = kl_find(kl_tab, kKlTailKey);
+                const int kk = static_cast<int>(threadIdx.x);
+                if (h >= 0 && ((kl_tab[h].cols >> kk) & 1u)) o[0] = kl_tab[h].val[kk];
+            }
             GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, o);
         }
     }
 }
 
 // One workgroup per (row, segment) item.
-template <int DT, int GDT, bool VEC, bool WH>
+template <int DT, int GDT, bool VEC, bool WH, bool KLF = false>
 __global__ __launch_bounds__(kBwdBlock) VWC_BWD_ATTR void bwd_segment_kernel(BwdPlan p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) / p.nseg;
-    bwd_item<DT, GDT, VEC, WH>(p, i, static_cast<int>(blockIdx.x - i * p.nseg));
+    bwd_item<DT, GDT, VEC, WH, KLF>(p, i, static_cast<int>(blockIdx.x - i * p.nseg));
 }
 
 // ---------------------------------------------------------------- top-k KL
@@ -882,9 +981,8 @@ __global__ __launch_bounds__(kTopkBlock) void topk_fixup_kernel(TopkPlan p) {
     for (int n = threadIdx.x; n < p.k; n += kTopkBlock) {
         const int32_t j = p.idx[r * p.k + n];
         if (j < 0 || j >= p.vocab) continue;
-        const double q = exp(static_cast<double>(load_element<DT>(row, j)) / p.tau - lse);
-        const double pn = exp(static_cast<double>(p.tlp[r * p.k + n]));
-        const float o[1] = {static_cast<float>(gt * (c.beta * q - c.kappa * pn))};
+        const float o[1] = {kl_payload_grad(static_cast<double>(load_element<DT>(row, j)), p.tau,
+                                            lse, gt, c, p.tlp[r * p.k + n])};
         GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * (GDT == VWC_BF16 ? 2 : 4), o);
     }
 }
@@ -980,7 +1078,10 @@ template <int DT, int GDT>
 hipError_t launch_bwd_dt(const BwdPlan &p, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.m * p.nseg)), block(kBwdBlock);
     const bool wh = p.grad_ent != nullptr;
-    if (p.vector) {
+    if (p.kl_fused) {  // the host checked: vector rows, no entropy term
+        hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true, false, true>), grid, block, 0, s,
+                           p);
+    } else if (p.vector) {
         if (wh)
             hipLaunchKernelGGL((bwd_segment_kernel<DT, GDT, true, true>), grid, block, 0, s, p);
         else

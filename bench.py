@@ -541,7 +541,7 @@ def main():
     # backward is one kernel; the forward is the segment kernel plus a small
     # merge kernel (its events bracket both).
     if bwd_avg >= fwd_avg:
-        dom = ("bwd_segment_kernel", bwd_b, bwd_avg, ["bwd_segment_kernel<0, 0, true, false>"])
+        dom = ("bwd_segment_kernel", bwd_b, bwd_avg, ["bwd_segment_kernel<0, 0, true, false, false>"])
     else:
         dom = ("fwd_segment_kernel+combine_kernel", fwd_b, fwd_avg,
                ["fwd_segment_kernel<0, true, false, false>", "combine_kernel"])

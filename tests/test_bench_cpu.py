@@ -44,7 +44,7 @@ def test_code_digest_ignores_comments_and_whitespace(tmp_path):
 def test_recorded_traffic_is_gated_by_the_code_digest():
     path = os.path.join(ROOT, "profiles", f"traffic_{bench.DEFAULT_WORKLOAD}.json")
     rec = json.load(open(path))
-    key = "bwd_segment_kernel<0, 0, true, false>"
+    key = "bwd_segment_kernel<0, 0, true, false, false>"
     src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", "vwc_kernels.hip")
     got = bench.recorded_traffic([key])
     if rec["kernel_code_digest"] == bench.code_digest(src):

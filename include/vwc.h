@@ -169,8 +169,15 @@ vwc_status vwc_entropy_rows(const void *logits, vwc_dtype dt, int64_t n_rows, in
  *  grad_logits   [n_rows, ld_grad] of grad_dt (ld_grad >= vocab); columns
  *                [vocab, ld_grad) are not touched.  Rows with g_r == 0 are
  *                written as +0.0 without reading their logits or lse.
- * grad_logits must not overlap logits (VWC_ERR_INVALID_ARG when the two
- * address ranges intersect).
+ * grad_logits either is exactly logits (same pointer, dtype and ld: the
+ * gradient replaces the logits in place, saving the second [rows, vocab]
+ * buffer) or does not overlap them (VWC_ERR_INVALID_ARG when the address
+ * ranges intersect otherwise).  In place, every element is read and then
+ * written by the same thread, so no row sees another row's gradient; the
+ * logits are gone afterwards.  The same rule holds for every backward call;
+ * in place the `_rows` calls need VWC_GRAD_SCATTER and distinct row ids, and
+ * vwc_topk_kl_bwd needs rows on 16 bytes and k <= 256 (VWC_ERR_UNSUPPORTED
+ * otherwise).
  */
 vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
                                     int64_t vocab, int64_t ld, const int32_t *targets,

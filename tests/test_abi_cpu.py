@@ -110,6 +110,11 @@ def test_forward_validation(lib):
     assert err() == b""
 
 
+def err_str(lib):
+    lib.vwc_last_error.restype = ctypes.c_char_p
+    return lib.vwc_last_error()
+
+
 def test_rows_and_backward_validation(lib):
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     fr = lib.vwc_selected_logprob_fwd_rows
@@ -126,15 +131,30 @@ def test_rows_and_backward_validation(lib):
     assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, g, BF16, 8, None) == INVALID
     assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, g, 5, 16, None) == INVALID
     assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, None, FAKE, g, BF16, 16, None) == INVALID
-    # gradient overlapping the logits
+    # gradient overlapping the logits without being exactly them (in place needs
+    # the same pointer, dtype and ld)
     assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, ctypes.c_void_p(0x100010), BF16, 16,
              None) == INVALID
+    assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, FAKE, FP32, 16, None) == INVALID
+    assert b(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, FAKE, BF16, 24, None) == INVALID
+    assert b"overlaps" in err_str(lib)
     br = lib.vwc_selected_logprob_bwd_rows
     br.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, i64, ctypes.c_float, p, p, p,
                    ctypes.c_int, i64, ctypes.c_int, p]
     assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 2, 1.0, FAKE, FAKE, g, BF16, 16, 9,
               None) == INVALID
     assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 0, 1.0, FAKE, FAKE, g, BF16, 16, 0, None) == OK
+    # in place, compact gradient rows (indexed by output, not row id) are refused
+    assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 2, 1.0, FAKE, FAKE, FAKE, BF16, 16, 0,
+              None) == INVALID
+    assert b"row id" in err_str(lib)
+    # in place, the top-k KL backward needs the single-pass payload (k <= 256)
+    kb = lib.vwc_topk_kl_bwd
+    kb.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, ctypes.c_int32, ctypes.c_int,
+                   ctypes.c_float, ctypes.c_float, p, p, p, p, p, p, ctypes.c_int, i64, p]
+    assert kb(FAKE, BF16, 4, 1000, 1000, FAKE, FAKE, 300, 1, 1e-6, 1.0, FAKE, FAKE, FAKE, FAKE,
+              FAKE, FAKE, BF16, 1000, None) == UNSUPPORTED
+    assert b"in-place top-k KL" in err_str(lib)
 
 
 def test_partial_combine_and_mask_validation(lib):

@@ -14,3 +14,4 @@ from ._binding import (  # noqa: F401
     partial_combine, selected_logprob_bwd, selected_logprob_bwd_rows, selected_logprob_fwd,
     selected_logprob_fwd_rows, topk_kl_bwd, topk_kl_fwd, vocab_partial, workspace_bytes,
 )
+from .autograd import selected_logprob  # noqa: F401,E402

@@ -1,0 +1,99 @@
+"""Differentiable selected-token log-probability (and entropy) over the C-ABI.
+
+The pages' user-facing form is an autograd function whose forward keeps the
+logits, the targets and the per-row logZ, and whose backward recomputes the
+softmax and writes (onehot - softmax) * grad_output into a gradient of the
+logits' dtype ("fix: chunk target logprobs without tensor parallelism",
+section "Changes"; "[megatron] feat: add memory-efficient chunked top-k KL
+computation", section "Design & Code Changes": keep the logits and an fp32
+logZ, recompute in the backward).  Here the forward and the backward are each
+one call into the library; this module only moves arguments.
+
+A row subset (the loss-mask rows, "[Bug] Training/log-prob forward
+materializes full-vocab fp32 logits ...", maintainer comment) is computed in
+compact form; its gradient is the full [rows, vocab] tensor with +0.0 on the
+rows outside the subset (written by the library, which reads no logits for
+them).  Duplicate row ids add their gradients.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _binding as B
+
+
+def _dense_rows(values, row_idx, n, like):
+    """Length-n vector with values[i] added at row_idx[i] (0 elsewhere)."""
+    out = torch.zeros(n, dtype=torch.float32, device=like.device)
+    if values is not None:
+        out.index_add_(0, row_idx.long(), values.float())
+    return out
+
+
+def _dense_copy(values, row_idx, n, like):
+    out = torch.zeros(n, dtype=torch.float32, device=like.device)
+    out.index_copy_(0, row_idx.long(), values)
+    return out
+
+
+class _SelectedLogprob(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, targets, temperature, row_idx, with_entropy, inplace_backward):
+        want = ("logprob", "lse", "entropy") if with_entropy else ("logprob", "lse")
+        if row_idx is None:
+            lp, lse, ent = B.selected_logprob_fwd(logits, targets, temperature, want=want)
+        else:
+            lp, lse, ent = B.selected_logprob_fwd_rows(logits, targets, row_idx, temperature,
+                                                       want=want)
+        ctx.temperature = temperature
+        ctx.with_entropy = with_entropy
+        ctx.inplace_backward = inplace_backward
+        ctx.has_rows = row_idx is not None
+        saved = [logits, targets, lse]
+        if with_entropy:
+            saved.append(ent)
+        if row_idx is not None:
+            saved.append(row_idx)
+        ctx.save_for_backward(*saved)
+        if with_entropy:
+            return lp, ent
+        return lp
+
+    @staticmethod
+    def backward(ctx, grad_lp, grad_ent=None):
+        saved = list(ctx.saved_tensors)
+        logits, targets, lse = saved[:3]
+        ent = saved[3] if ctx.with_entropy else None
+        row_idx = saved[-1] if ctx.has_rows else None
+        if grad_lp is None and grad_ent is None:
+            return None, None, None, None, None, None
+        n = logits.size(0)
+        if row_idx is not None:  # compact outputs -> every row, 0 outside the subset
+            grad_lp = _dense_rows(grad_lp, row_idx, n, logits) if grad_lp is not None else None
+            grad_ent = _dense_rows(grad_ent, row_idx, n, logits) if grad_ent is not None else None
+            lse = _dense_copy(lse, row_idx, n, logits)
+            if ent is not None:
+                ent = _dense_copy(ent, row_idx, n, logits)
+        out = logits if ctx.inplace_backward else None
+        if ent is not None and grad_ent is not None:
+            g = B.logprob_entropy_bwd(logits, targets, lse, ent, grad_lp.contiguous()
+                                      if grad_lp is not None else None, grad_ent.contiguous(),
+                                      ctx.temperature, grad_logits=out)
+        else:
+            g = B.selected_logprob_bwd(logits, targets, lse, grad_lp.contiguous(),
+                                       ctx.temperature, grad_logits=out)
+        return g, None, None, None, None, None
+
+
+def selected_logprob(logits, targets, temperature=1.0, row_idx=None, with_entropy=False,
+                     inplace_backward=False):
+    """logprob[i] = log_softmax(logits[r] / temperature)[targets[r]] for r = row_idx[i]
+    (every row when row_idx is None), differentiable with respect to `logits`.
+
+    with_entropy=True also returns the entropy of each row's softmax, and the
+    backward takes the gradients of both outputs in one pass.  With
+    inplace_backward=True the backward writes the gradient over `logits` itself
+    (no second [rows, vocab] buffer) and returns that tensor as the gradient; the
+    logits are gone afterwards."""
+    return _SelectedLogprob.apply(logits, targets, float(temperature), row_idx,
+                                  bool(with_entropy), bool(inplace_backward))

@@ -176,15 +176,24 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
         return fail(VWC_ERR_UNSUPPORTED, "%s: grad_logits not aligned to its dtype", fn);
     if (ld_grad > INT64_MAX / 16 / n_rows)
         return fail(VWC_ERR_UNSUPPORTED, "%s: gradient tensor too large", fn);
-    // The gradient must not overlap the logits it is computed from.
-    const int64_t grad_rows = by_row_id ? n_rows : m;
-    const uintptr_t x0 = reinterpret_cast<uintptr_t>(logits);
-    const uintptr_t x1 = x0 + static_cast<uintptr_t>(((n_rows - 1) * ld + vocab) * esize(dt));
-    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_logits);
-    const uintptr_t g1 =
-        g0 + static_cast<uintptr_t>(((grad_rows - 1) * ld_grad + vocab) * esize(grad_dt));
-    if (g0 < x1 && x0 < g1)
-        return fail(VWC_ERR_INVALID_ARG, "%s: grad_logits overlaps logits", fn);
+    // The gradient either replaces the logits exactly (same buffer, dtype and
+    // row stride, each row's gradient over that row: every element is read and
+    // written by the same thread) or does not overlap them at all.
+    const bool in_place = grad_logits == logits && grad_dt == dt && ld_grad == ld;
+    if (in_place) {
+        if (row_idx && !by_row_id)
+            return fail(VWC_ERR_INVALID_ARG,
+                        "%s: an in-place gradient needs gradient rows indexed by row id", fn);
+    } else {
+        const int64_t grad_rows = by_row_id ? n_rows : m;
+        const uintptr_t x0 = reinterpret_cast<uintptr_t>(logits);
+        const uintptr_t x1 = x0 + static_cast<uintptr_t>(((n_rows - 1) * ld + vocab) * esize(dt));
+        const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_logits);
+        const uintptr_t g1 =
+            g0 + static_cast<uintptr_t>(((grad_rows - 1) * ld_grad + vocab) * esize(grad_dt));
+        if (g0 < x1 && x0 < g1)
+            return fail(VWC_ERR_INVALID_ARG, "%s: grad_logits overlaps logits", fn);
+    }
 
     const int64_t nseg = segments(vocab, dt, vwc::kBwdSegBytes);
     if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;
@@ -227,6 +236,11 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
         // vectors and a segment's payload fits the in-LDS table; otherwise the
         // caller runs the fix-up launch.
         kl->fused = p.vector && kl->k <= vwc::kKlMaxK && p.seg_units <= vwc::kKlMaxSegUnits;
+        // The fix-up launch re-reads payload logits after the stream wrote them.
+        if (in_place && !kl->fused)
+            return fail(VWC_ERR_UNSUPPORTED,
+                        "%s: an in-place top-k KL gradient needs rows on 16 bytes and k <= %d",
+                        fn, vwc::kKlMaxK);
         p.kl_fused = kl->fused;
         p.kl_idx = kl->idx;
         p.kl_tlp = kl->tlp;

@@ -17,8 +17,8 @@ BF16, FP32 = 0, 1
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from vocab_wide_cross_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__._build_module().build()
     return ctypes.CDLL(LIB)
 
 

@@ -245,7 +245,7 @@ def test_grad_zero_rows_are_positive_zero(tiny):
 # ----------------------------------------------------------------------------- split-V
 
 
-@pytest.mark.parametrize("vchunk", [7, 64, 4096, 1000])
+@pytest.mark.parametrize("vchunk", [1, 2, 3, 5, 7, 8, 64, 1000, 4096])
 def test_vocab_chunks_match_single_pass(tiny, vchunk):
     """Vocabulary chunks merged by the shard combine reproduce the single pass
     (chunk sizes of the verl PR's small test: 7, 64, 4096)."""
@@ -285,13 +285,29 @@ def test_unowned_target_is_visible():
 
 
 def test_row_chunks_bitwise(tiny):
-    """Row chunking (chunk sizes 7, 64, 4096) changes nothing, bit for bit."""
+    """Row chunking changes nothing, bit for bit: the chunk sizes of the NeMo-RL
+    PR's tests (1, 2, 3, 5, 7, 8, 64) and of the verl PR's (7, 64, 4096)."""
     _, x, t, _ = tiny
     a = oracle.forward(x, t, row_chunk=4096)
-    for c in (7, 64, 1):
+    for c in (1, 2, 3, 5, 7, 8, 64):
         b = oracle.forward(x, t, row_chunk=c)
         for k in a:
             assert np.array_equal(a[k], b[k])
+
+
+def test_default_chunk_with_a_residual():
+    """1024 + 7 rows through the default chunk of 1024: the residual chunk of 7
+    gives the rows' single-row values, bit for bit (forward and gradient)."""
+    w = W.scaled("tiny_fp32_64x2048", 1031, 257)
+    x, t, g = W.all_logits(w), W.targets(w), W.grad_out(w)
+    a = oracle.forward(x, t, row_chunk=1024)
+    for r in (0, 1023, 1024, 1030):
+        b = oracle.forward(x[r:r + 1], t[r:r + 1], row_chunk=1)
+        for k in a:
+            assert a[k][r] == b[k][0]
+    gr = oracle.backward(x, t, g)
+    g1 = oracle.backward(x[1024:], t[1024:], g[1024:])
+    assert np.array_equal(gr[1024:], g1)
 
 
 def test_compact_rows_equal_dense_rows():

@@ -226,20 +226,31 @@ def test_empty_row_sets_are_noops():
     assert lp0.numel() == 0
 
 
-def test_row_chunks_are_bitwise_identical():
-    """Covering the rows in chunks of 7 / 64 / 4096 gives the same bits."""
-    w = W.scaled("spiked_bf16_8192x248320", 200, 70001)
-    x, t, _ = _host(w)
-    xd, td = to_dev_logits(x), torch.from_numpy(t).to(DEV)
-    full, _, fent = vwc.selected_logprob_fwd(xd, td, want=("logprob", "entropy"))
-    for chunk in (7, 64, 4096):
-        parts, ents = [], []
+@pytest.mark.parametrize("vocab", [70001, 248320])
+def test_row_chunks_are_bitwise_identical(vocab):
+    """Covering the rows in chunks of 1 / 7 / 64 / 4096 gives the same bits, through
+    row lists and through dense calls on row slices, forward and backward (rows of
+    2 segments merged in-block, and of 4 merged by a second launch)."""
+    w = W.scaled("spiked_bf16_8192x248320", 200, vocab)
+    x, t, g = _host(w)
+    xd, td, gd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    full, flse, fent = vwc.selected_logprob_fwd(xd, td, want=("logprob", "lse", "entropy"))
+    fgrad = vwc.selected_logprob_bwd(xd, td, flse, gd)
+    for chunk in (1, 7, 64, 4096):
+        parts, ents, dense = [], [], []
         for r0 in range(0, w.n_rows, chunk):
-            rows = torch.arange(r0, min(r0 + chunk, w.n_rows), dtype=torch.int32, device=DEV)
+            r1 = min(r0 + chunk, w.n_rows)
+            rows = torch.arange(r0, r1, dtype=torch.int32, device=DEV)
             lp, _, en = vwc.selected_logprob_fwd_rows(xd, td, rows, want=("logprob", "entropy"))
             parts.append(lp)
             ents.append(en)
+            dlp, dlse, _ = vwc.selected_logprob_fwd(xd[r0:r1], td[r0:r1])
+            dense.append(dlp)
+            if chunk == 64:
+                gr = vwc.selected_logprob_bwd(xd[r0:r1], td[r0:r1], dlse, gd[r0:r1])
+                assert torch.equal(gr.view(torch.int16), fgrad[r0:r1].view(torch.int16))
         assert torch.equal(torch.cat(parts), full) and torch.equal(torch.cat(ents), fent)
+        assert torch.equal(torch.cat(dense), full)
 
 
 def test_run_to_run_deterministic():

@@ -84,7 +84,11 @@ def _check(status: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if not t.is_cuda:  # a host address handed to a kernel would fault the GPU
+        raise ValueError("every tensor argument must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream, like: torch.Tensor):
@@ -118,10 +122,28 @@ def _f32(n, like, out):
     return out
 
 
-def _i32(t: torch.Tensor, name: str):
+def _i32(t: torch.Tensor, name: str, n: int | None = None):
     if t.dtype != torch.int32 or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous int32 tensor")
+    if n is not None and t.numel() < n:
+        raise ValueError(f"{name} needs at least {n} entries, got {t.numel()}")
     return t
+
+
+def _f32_in(t, n: int, name: str):
+    """A float32 input the kernels read n entries of (None passes through)."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of at least {n} entries")
+    return t
+
+
+def _grad_rows(g, rows: int, vocab: int):
+    gn, gv, gld = _rows_view(g)
+    if gn < rows or gv < vocab:
+        raise ValueError(f"grad_logits must be at least [{rows}, {vocab}]")
+    return gld
 
 
 def workspace_bytes(rows: int, vocab: int, dtype) -> int:
@@ -146,7 +168,7 @@ def selected_logprob_fwd(logits, targets, temperature=1.0, logprob=None, lse=Non
                          entropy=None, want=("logprob", "lse"), workspace=None, stream=None):
     """Dense forward; returns (logprob, lse, entropy), None for outputs not asked for."""
     n, v, ld = _rows_view(logits)
-    _i32(targets, "targets")
+    _i32(targets, "targets", n)
     lp = _f32(n, logits, logprob) if (logprob is not None or "logprob" in want) else None
     ls = _f32(n, logits, lse) if (lse is not None or "lse" in want) else None
     en = _f32(n, logits, entropy) if (entropy is not None or "entropy" in want) else None
@@ -161,7 +183,7 @@ def selected_logprob_fwd_rows(logits, targets, row_idx, temperature=1.0, logprob
                               entropy=None, want=("logprob", "lse"), workspace=None, stream=None):
     """Forward on rows row_idx; outputs are compact [m]."""
     n, v, ld = _rows_view(logits)
-    _i32(targets, "targets")
+    _i32(targets, "targets", n)
     _i32(row_idx, "row_idx")
     m = row_idx.numel()
     lp = _f32(m, logits, logprob) if (logprob is not None or "logprob" in want) else None
@@ -178,6 +200,7 @@ def selected_logprob_fwd_rows(logits, targets, row_idx, temperature=1.0, logprob
 def entropy(logits, temperature=1.0, out=None, lse=None, workspace=None, stream=None):
     n, v, ld = _rows_view(logits)
     en = _f32(n, logits, out)
+    lse = None if lse is None else _f32(n, logits, lse)
     ws, wsb = _workspace(n, v, logits, workspace)
     _check(_lib.vwc_entropy(_ptr(logits), _dtype(logits), n, v, ld, float(temperature), _ptr(en),
                             _ptr(lse), _ptr(ws), wsb, _stream(stream, logits)))
@@ -190,6 +213,7 @@ def entropy_rows(logits, row_idx, temperature=1.0, out=None, lse=None, workspace
     _i32(row_idx, "row_idx")
     m = row_idx.numel()
     en = _f32(m, logits, out)
+    lse = None if lse is None else _f32(m, logits, lse)
     ws, wsb = _workspace(m, v, logits, workspace)
     _check(_lib.vwc_entropy_rows(_ptr(logits), _dtype(logits), n, v, ld, _ptr(row_idx), m,
                                  float(temperature), _ptr(en), _ptr(lse), _ptr(ws), wsb,
@@ -208,11 +232,11 @@ def selected_logprob_bwd(logits, targets, lse, grad_logprob, temperature=1.0, gr
                          grad_dtype=None, stream=None):
     """Dense backward: grad_logits[r, j] = g_r ([j == t_r] - p_rj) / tau."""
     n, v, ld = _rows_view(logits)
-    _i32(targets, "targets")
+    _i32(targets, "targets", n)
+    _f32_in(lse, n, "lse")
+    _f32_in(grad_logprob, n, "grad_logprob")
     g = _grad_out(logits, n, grad_logits, grad_dtype)
-    gn, gv, gld = _rows_view(g)
-    if gn != n or gv < v:
-        raise ValueError("grad_logits must be [n_rows, >= vocab]")
+    gld = _grad_rows(g, n, v)
     _check(_lib.vwc_selected_logprob_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(targets),
                                          float(temperature), _ptr(lse), _ptr(grad_logprob),
                                          _ptr(g), _dtype(g), gld, _stream(stream, logits)))
@@ -223,15 +247,17 @@ def selected_logprob_bwd_rows(logits, targets, row_idx, lse, grad_logprob, tempe
                               grad_logits=None, grad_dtype=None, layout=VWC_GRAD_COMPACT,
                               stream=None):
     n, v, ld = _rows_view(logits)
-    _i32(targets, "targets")
+    _i32(targets, "targets", n)
     _i32(row_idx, "row_idx")
     m = row_idx.numel()
+    _f32_in(lse, m, "lse")
+    _f32_in(grad_logprob, m, "grad_logprob")
+    rows = m if layout == VWC_GRAD_COMPACT else n
     if grad_logits is None:
-        rows = m if layout == VWC_GRAD_COMPACT else n
         grad_logits = _grad_out(logits, rows, None, grad_dtype)
         if layout == VWC_GRAD_SCATTER:
             grad_logits.zero_()
-    _, gv, gld = _rows_view(grad_logits)
+    gld = _grad_rows(grad_logits, rows, v)
     _check(_lib.vwc_selected_logprob_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
                                               _ptr(targets), _ptr(row_idx), m,
                                               float(temperature), _ptr(lse), _ptr(grad_logprob),
@@ -245,11 +271,12 @@ def logprob_entropy_bwd(logits, targets, lse, entropy, grad_logprob=None, grad_e
     """Dense backward of sum_r g_r logprob_r + h_r entropy_r (g or h may be None)."""
     n, v, ld = _rows_view(logits)
     if targets is not None:
-        _i32(targets, "targets")
+        _i32(targets, "targets", n)
+    for t, name in ((lse, "lse"), (entropy, "entropy"), (grad_logprob, "grad_logprob"),
+                    (grad_entropy, "grad_entropy")):
+        _f32_in(t, n, name)
     g = _grad_out(logits, n, grad_logits, grad_dtype)
-    gn, gv, gld = _rows_view(g)
-    if gn != n or gv < v:
-        raise ValueError("grad_logits must be [n_rows, >= vocab]")
+    gld = _grad_rows(g, n, v)
     _check(_lib.vwc_logprob_entropy_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(targets),
                                         float(temperature), _ptr(lse), _ptr(entropy),
                                         _ptr(grad_logprob), _ptr(grad_entropy), _ptr(g), _dtype(g),
@@ -263,15 +290,18 @@ def logprob_entropy_bwd_rows(logits, targets, row_idx, lse, entropy, grad_logpro
     """Compact-row version of logprob_entropy_bwd (lse/entropy/gradients are [m])."""
     n, v, ld = _rows_view(logits)
     if targets is not None:
-        _i32(targets, "targets")
+        _i32(targets, "targets", n)
     _i32(row_idx, "row_idx")
     m = row_idx.numel()
+    for t, name in ((lse, "lse"), (entropy, "entropy"), (grad_logprob, "grad_logprob"),
+                    (grad_entropy, "grad_entropy")):
+        _f32_in(t, m, name)
+    rows = m if layout == VWC_GRAD_COMPACT else n
     if grad_logits is None:
-        rows = m if layout == VWC_GRAD_COMPACT else n
         grad_logits = _grad_out(logits, rows, None, grad_dtype)
         if layout == VWC_GRAD_SCATTER:
             grad_logits.zero_()
-    _, gv, gld = _rows_view(grad_logits)
+    gld = _grad_rows(grad_logits, rows, v)
     _check(_lib.vwc_logprob_entropy_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
                                              _ptr(targets), _ptr(row_idx), m, float(temperature),
                                              _ptr(lse), _ptr(entropy), _ptr(grad_logprob),
@@ -309,10 +339,14 @@ def topk_kl_bwd(logits, topk_idx, teacher_logprob, fwd, grad_loss, mode=VWC_KL_T
     dict topk_kl_fwd returned."""
     n, v, ld = _rows_view(logits)
     _i32(topk_idx, "topk_idx")
+    if topk_idx.dim() != 2 or topk_idx.size(0) != n or teacher_logprob.shape != topk_idx.shape:
+        raise ValueError("topk_idx and teacher_logprob must both be [n_rows, k]")
+    _f32_in(teacher_logprob, topk_idx.numel(), "teacher_logprob")
+    for name in ("lse", "student_mass", "teacher_mass", "topk_sum"):
+        _f32_in(fwd[name], n, name)
+    _f32_in(grad_loss, n, "grad_loss")
     g = _grad_out(logits, n, grad_logits, grad_dtype)
-    gn, gv, gld = _rows_view(g)
-    if gn != n or gv < v:
-        raise ValueError("grad_logits must be [n_rows, >= vocab]")
+    gld = _grad_rows(g, n, v)
     _check(_lib.vwc_topk_kl_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(topk_idx),
                                 _ptr(teacher_logprob), topk_idx.size(1), int(mode),
                                 float(tail_mass_eps), float(temperature), _ptr(fwd["lse"]),
@@ -327,12 +361,13 @@ def vocab_partial(logits_slice, v_start, targets=None, row_idx=None, temperature
     """Partial (m, s, t, w) of a vocabulary slice; returns a [m, 4] float32 tensor."""
     n, v, ld = _rows_view(logits_slice)
     if targets is not None:
-        _i32(targets, "targets")
+        _i32(targets, "targets", n)
     if row_idx is not None:
         _i32(row_idx, "row_idx")
     m = n if row_idx is None else row_idx.numel()
     if out is None:
         out = torch.empty((m, 4), dtype=torch.float32, device=logits_slice.device)
+    _f32_in(out, 4 * m, "out")
     ws, wsb = _workspace(m, v, logits_slice, workspace)
     _check(_lib.vwc_vocab_partial(_ptr(logits_slice), _dtype(logits_slice), n, v, ld, v_start,
                                   _ptr(targets), _ptr(row_idx), m, float(temperature), _ptr(out),
@@ -366,6 +401,8 @@ def mask_to_index(mask, row_idx=None, count=None, stream=None):
         row_idx = torch.empty(max(n, 1), dtype=torch.int32, device=mask.device)
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=mask.device)
+    _i32(row_idx, "row_idx", n)
+    _i32(count, "count", 1)
     _check(_lib.vwc_mask_to_index(_ptr(mask), n, _ptr(row_idx), _ptr(count),
                                   _stream(stream, mask)))
     return row_idx, count
@@ -388,7 +425,7 @@ def lmhead_logprob_fwd(hidden, weight, targets=None, row_idx=None, temperature=1
     v, kw, ldw = _rows_view(weight)
     d = min(kh, kw) if d is None else int(d)
     if targets is not None:
-        _i32(targets, "targets")
+        _i32(targets, "targets", n)
     if row_idx is not None:
         _i32(row_idx, "row_idx")
     m = n if row_idx is None else row_idx.numel()

@@ -76,17 +76,24 @@ constexpr int kRowsPerInst = 1024 / kRowBytes;    // rows one wave load instruct
 constexpr int kInstPerTile = kRowsPerWave / kRowsPerInst;  // per wave and operand tile
 constexpr int kSteps = kLmK / 16;                 // MFMA k-steps per stage
 constexpr int kWPerStep = kInstPerTile / kSteps;  // weight load instructions per k-step
-// LDS rings of operand tiles.  The weight tile of stage g + 2 streams in during
-// stage g, kWPerStep load instructions per k-step, into the unit stage g - 1
-// freed; the hidden tile of stage g + 2 goes out in stage g's last k-step, into
-// the unit stage g frees.  Spreading the loads keeps each wave's memory queue
-// short: a load that cannot issue would hold up the MFMAs behind it.
-constexpr int kWS = 3;
-constexpr int kHS = 2;
+// LDS rings of operand tiles, kDist stages deep.  The weight tile of stage
+// g + kDist streams in during stage g, kWPerStep load instructions per k-step,
+// into the unit stage g - 1 freed; the hidden tile of stage g + kDist goes out
+// in stage g's last k-step, into the unit stage g frees.  Spreading the loads
+// keeps each wave's memory queue short: a load that cannot issue would hold up
+// the MFMAs behind it.
+#ifndef VWC_LM_DIST
+#define VWC_LM_DIST 2
+#endif
+constexpr int kDist = VWC_LM_DIST;
+constexpr int kWS = kDist + 1;
+constexpr int kHS = kDist;
 static_assert(kLmTok == kLmVoc, "the staging assumes square tiles");
 static_assert(kWaves == 4 || kWaves == 8, "4 waves (1 per SIMD) or 8 (2 per SIMD)");
 static_assert(kLmK == 32 || kLmK == 64, "stage widths of 64 or 128 bytes per row");
-static_assert(kWS >= kHS && (kWS + kHS) * kTileBytes <= 160 * 1024, "LDS rings too large");
+static_assert(kDist >= 2 && (kWS + kHS) * kTileBytes <= 160 * 1024, "LDS rings too large");
+static_assert(kSteps >= 2 && kWPerStep * kSteps == kInstPerTile, "weight loads per k-step");
+static_assert((kDist - 1) * 2 * kInstPerTile < 64, "vmcnt range");
 constexpr float kUFloor = -256.0f;
 
 // Chunk c (16 bytes) of staged row r sits at chunk position c ^ swz(r), so
@@ -353,9 +360,11 @@ void lmhead_fwd_kernel(LmPlan p) {
         for (int j = 0; j < kJ; ++j) acc[i][j] = f32x16{};
     bf16x8 fa[2][4], fb[2][kJ];
 
-    // Prologue: stages 0 and 1 whole (hidden tile, then weight tile); wait for
-    // stage 0.  (hk) is the step of the next hidden load, (wt, wk) the tile and
-    // step of the next weight load.
+    // Prologue: stages 0 .. kDist - 1 whole (hidden tile, then weight tile; the
+    // ones past the last stage read nothing), then wait for stage 0.  Every
+    // stage issues the same loads, so the counts the waits rely on are exact.
+    // (hk) is the step of the next hidden load, (wt, wk) the tile and step of
+    // the next weight load.
     int hk = 0, wk = 0, wt = vt0;
     auto step_h = [&]() { hk = hk + 1 == nk ? 0 : hk + 1; };
     auto step_w = [&]() {
@@ -363,16 +372,15 @@ void lmhead_fwd_kernel(LmPlan p) {
         wk = wrap ? 0 : wk + 1;
         wt += wrap ? 1 : 0;
     };
-    for (int i = 0; i < 2 && i < nstage; ++i) {
-        load_h(hk, i, true);
+#pragma unroll
+    for (int i = 0; i < kDist; ++i) {
+        load_h(hk, i, i < nstage);
         step_h();
-        load_tile(w_rsrc(wt, true), aoff, wlds + i * kTileBytes, wk * kLmK, 0, kInstPerTile);
+        load_tile(w_rsrc(wt, i < nstage), aoff, wlds + i * kTileBytes, wk * kLmK, 0,
+                  kInstPerTile);
         step_w();
     }
-    if (nstage > 1)
-        wait_vmcnt<2 * kInstPerTile>();
-    else
-        wait_vmcnt<0>();
+    wait_vmcnt<(kDist - 1) * 2 * kInstPerTile>();
     __syncthreads();
     if (nstage > 0) read_frags(0, 0, 0, fa[0], fb[0]);
 
@@ -383,9 +391,10 @@ void lmhead_fwd_kernel(LmPlan p) {
             const int nwu = wu + 1 == kWS ? 0 : wu + 1;
             const int nhu = hu + 1 == kHS ? 0 : hu + 1;
             const bool more = g + 1 < nstage;
-            // The weight tile of stage g + 2, unit (g + 2) % 3 = the one after nwu.
-            const __amdgpu_buffer_rsrc_t wr = w_rsrc(wt, g + 2 < nstage);
-            char *const wdst = wlds + (nwu + 1 == kWS ? 0 : nwu + 1) * kTileBytes;
+            // The weight tile of stage g + kDist, unit (g + kDist) % kWS: the one
+            // before wu, which stage g - 1 used.
+            const __amdgpu_buffer_rsrc_t wr = w_rsrc(wt, g + kDist < nstage);
+            char *const wdst = wlds + (wu == 0 ? kWS - 1 : wu - 1) * kTileBytes;
             const int wk0 = wk * kLmK;
             step_w();
 #pragma unroll
@@ -419,9 +428,11 @@ void lmhead_fwd_kernel(LmPlan p) {
                     // Every read of stage g's units has been issued by now (the
                     // last step's fragments were read during this step) and the
                     // barrier waits for them.  Stage g + 1's tiles went out in
-                    // earlier stages; only this stage's weight loads (for stage
-                    // g + 2) may still be in flight.
-                    if (more) wait_vmcnt<kWPerStep * (kSteps - 1)>();
+                    // earlier stages; only the tiles of stages g + 2 .. g +
+                    // kDist - 1 and this stage's weight loads (for stage g +
+                    // kDist) may still be in flight.
+                    if (more)
+                        wait_vmcnt<(kDist - 2) * 2 * kInstPerTile + kWPerStep * (kSteps - 1)>();
                     block_barrier();
                     __builtin_amdgcn_sched_barrier(0);
                 }

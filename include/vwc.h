@@ -266,6 +266,21 @@ vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
                            hipStream_t stream);
 
 /*
+ * Top-k KL over the row set row_idx[0..m) (the loss-mask rows, as for the
+ * other `_rows` calls).  topk_idx and teacher_logprob are [m, k] (one payload
+ * per listed row, in list order); the outputs are float[m].  A row id outside
+ * [0, n_rows) gives NaN outputs for its entry.  Each listed row gets the bits
+ * of the dense call's row.  workspace: vwc_workspace_bytes(m, vocab, dt).
+ */
+vwc_status vwc_topk_kl_fwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                                int64_t ld, const int32_t *row_idx, int64_t m,
+                                const int32_t *topk_idx, const float *teacher_logprob, int32_t k,
+                                vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                                float *loss, float *student_mass, float *teacher_mass,
+                                float *topk_sum, float *lse, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Gradient of sum_r g_r loss_r with respect to the student logits, in one
  * streaming pass that also writes the k payload columns (rows on 16 bytes and
  * k <= 256; otherwise a second launch rewrites those columns) (the page's
@@ -283,6 +298,23 @@ vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
                            const float *lse, const float *student_mass, const float *teacher_mass,
                            const float *topk_sum, const float *grad_loss, void *grad_logits,
                            vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream);
+
+/*
+ * Backward over the row set row_idx[0..m): the payload, lse, student_mass,
+ * teacher_mass, topk_sum and grad_loss are the `_rows` forward's, indexed by
+ * list position.  layout as for vwc_selected_logprob_bwd_rows: gradient row i
+ * at row i of [m, ld_grad] (VWC_GRAD_COMPACT) or at row row_idx[i] of
+ * [n_rows, ld_grad] (VWC_GRAD_SCATTER, other rows untouched; duplicate ids
+ * race).  Rows with an id outside [0, n_rows) are not written.
+ */
+vwc_status vwc_topk_kl_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                                int64_t ld, const int32_t *row_idx, int64_t m,
+                                const int32_t *topk_idx, const float *teacher_logprob, int32_t k,
+                                vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                                const float *lse, const float *student_mass,
+                                const float *teacher_mass, const float *topk_sum,
+                                const float *grad_loss, void *grad_logits, vwc_dtype grad_dt,
+                                int64_t ld_grad, vwc_grad_layout layout, hipStream_t stream);
 
 /*
  * Partial of one vocabulary slice ([E] "Implementation", steps 1-3 in one

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
 
@@ -155,6 +155,24 @@ def test_rows_and_backward_validation(lib):
     assert kb(FAKE, BF16, 4, 1000, 1000, FAKE, FAKE, 300, 1, 1e-6, 1.0, FAKE, FAKE, FAKE, FAKE,
               FAKE, FAKE, BF16, 1000, None) == UNSUPPORTED
     assert b"in-place top-k KL" in err_str(lib)
+    # row-set top-k KL: a row list is required, the layout must be known
+    kfr = lib.vwc_topk_kl_fwd_rows
+    kfr.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i64, p, p, ctypes.c_int32, ctypes.c_int,
+                    ctypes.c_float, ctypes.c_float, p, p, p, p, p, p, ctypes.c_size_t, p]
+    assert kfr(FAKE, BF16, 4, 1000, 1000, None, 2, FAKE, FAKE, 8, 1, 1e-6, 1.0, None, None, None,
+               None, FAKE, None, 0, None) == INVALID
+    assert b"row_idx" in err_str(lib)
+    assert kfr(FAKE, BF16, 4, 1000, 1000, FAKE, 0, FAKE, FAKE, 8, 1, 1e-6, 1.0, None, None, None,
+               None, FAKE, None, 0, None) == OK          # empty row set
+    kbr = lib.vwc_topk_kl_bwd_rows
+    kbr.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i64, p, p, ctypes.c_int32, ctypes.c_int,
+                    ctypes.c_float, ctypes.c_float, p, p, p, p, p, p, ctypes.c_int, i64,
+                    ctypes.c_int, p]
+    assert kbr(FAKE, BF16, 4, 1000, 1000, FAKE, 2, FAKE, FAKE, 8, 1, 1e-6, 1.0, FAKE, FAKE, FAKE,
+               FAKE, FAKE, g, BF16, 1000, 7, None) == INVALID
+    assert b"layout" in err_str(lib)
+    assert kbr(FAKE, BF16, 4, 1000, 1000, FAKE, 2, FAKE, FAKE, 0, 1, 1e-6, 1.0, FAKE, FAKE, FAKE,
+               FAKE, FAKE, g, BF16, 1000, 0, None) == INVALID   # k = 0
 
 
 def test_partial_combine_and_mask_validation(lib):

@@ -235,3 +235,49 @@ def test_topk_kl_payload_layouts(layout, mode):
         log(f"  {nb} elements beyond one bf16 step (within the bar)")
     assert np.all(_np(grad[1].float()) == 0.0)
     assert torch.isnan(gbuf[:, V:].float()).all()  # nothing written past the vocabulary
+
+
+@pytest.mark.parametrize("k,pad", [(128, 0), (300, 0), (64, 1)],
+                         ids=["single-pass", "fix-up k300", "fix-up unaligned"])
+@pytest.mark.parametrize("mode", MODES)
+def test_topk_kl_rows_equal_dense_rows(k, pad, mode):
+    """The row-set calls give each listed row the dense call's bits: forward
+    outputs, and gradients in the compact and the scatter layouts (the fused
+    payload pass and both fix-up cases); bad row ids give NaN and no gradient."""
+    w = W.scaled("distill_bf16_4096x248320_k128", 16, 151936, topk=k)
+    x = W.all_logits(w)
+    idx, tlp = W.topk_payload(w)
+    g = np.random.default_rng(8).uniform(-1, 1, w.n_rows).astype(np.float32)
+    g[5] = 0.0
+    ld = 151936 + 8 * pad + pad
+    xh = np.zeros((w.n_rows, ld), np.uint16)
+    xh[:, :151936] = x
+    xd = to_dev_logits(xh)[:, :151936]
+    idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
+    dense = vwc.topk_kl_fwd(xd, idd, tld, mode)
+    dgrad = vwc.topk_kl_bwd(xd, idd, tld, dense, gd, mode)
+    rows = np.array([15, 0, 5, 9, 3], np.int32)
+    rl = torch.from_numpy(rows).to(DEV).long()
+    rd = torch.from_numpy(rows).to(DEV)
+    sub = vwc.topk_kl_fwd_rows(xd, rd, idd[rl].contiguous(), tld[rl].contiguous(), mode)
+    for key in dense:
+        assert torch.equal(sub[key], dense[key][rl]), key
+    comp = vwc.topk_kl_bwd_rows(xd, rd, idd[rl].contiguous(), tld[rl].contiguous(), sub,
+                                gd[rl].contiguous(), mode)
+    assert torch.equal(comp.view(torch.int16), dgrad[rl].view(torch.int16))
+    scat = torch.full_like(xd, float("nan"))
+    vwc.topk_kl_bwd_rows(xd, rd, idd[rl].contiguous(), tld[rl].contiguous(), sub,
+                         gd[rl].contiguous(), mode, grad_logits=scat,
+                         layout=vwc.VWC_GRAD_SCATTER)
+    assert torch.equal(scat[rl].view(torch.int16), dgrad[rl].view(torch.int16))
+    others = np.setdiff1d(np.arange(w.n_rows), rows)
+    assert torch.isnan(scat[others].float()).all()  # rows outside the list untouched
+    # a bad row id: NaN outputs, no gradient written
+    bad = torch.tensor([2, -1, 16], dtype=torch.int32, device=DEV)
+    bl = torch.tensor([2, 0, 0], device=DEV).long()
+    sb = vwc.topk_kl_fwd_rows(xd, bad, idd[bl].contiguous(), tld[bl].contiguous(), mode)
+    assert torch.isnan(sb["loss"][1:]).all() and torch.isfinite(sb["loss"][0])
+    cg = torch.full((3, 151936), 7.0, dtype=torch.bfloat16, device=DEV)
+    vwc.topk_kl_bwd_rows(xd, bad, idd[bl].contiguous(), tld[bl].contiguous(), sb,
+                         torch.ones(3, device=DEV), mode, grad_logits=cg)
+    assert (cg[1:].float() == 7.0).all()

@@ -57,6 +57,10 @@ def _load() -> ctypes.CDLL:
                              p, p, p, sz, p], i32),
         "vwc_topk_kl_bwd": ([p, i32, i64, i64, i64, p, p, ctypes.c_int32, i32, f32, f32, p, p, p,
                              p, p, p, i32, i64, p], i32),
+        "vwc_topk_kl_fwd_rows": ([p, i32, i64, i64, i64, p, i64, p, p, ctypes.c_int32, i32, f32,
+                                  f32, p, p, p, p, p, p, sz, p], i32),
+        "vwc_topk_kl_bwd_rows": ([p, i32, i64, i64, i64, p, i64, p, p, ctypes.c_int32, i32, f32,
+                                  f32, p, p, p, p, p, p, i32, i64, i32, p], i32),
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
@@ -354,6 +358,61 @@ def topk_kl_bwd(logits, topk_idx, teacher_logprob, fwd, grad_loss, mode=VWC_KL_T
                                 _ptr(fwd["topk_sum"]), _ptr(grad_loss), _ptr(g), _dtype(g), gld,
                                 _stream(stream, logits)))
     return g
+
+
+def topk_kl_fwd_rows(logits, row_idx, topk_idx, teacher_logprob, mode=VWC_KL_TAIL,
+                     tail_mass_eps=1e-6, temperature=1.0, workspace=None, stream=None):
+    """Top-k forward KL of the rows row_idx; topk_idx / teacher_logprob are [m, k] (one
+    payload per listed row); returns dict of float32 [m] tensors as topk_kl_fwd."""
+    n, v, ld = _rows_view(logits)
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    _i32(topk_idx, "topk_idx")
+    if topk_idx.dim() != 2 or topk_idx.size(0) != m or teacher_logprob.shape != topk_idx.shape:
+        raise ValueError("topk_idx and teacher_logprob must both be [m, k]")
+    _f32_in(teacher_logprob, topk_idx.numel(), "teacher_logprob")
+    k = topk_idx.size(1)
+    out = {name: torch.empty(m, dtype=torch.float32, device=logits.device)
+           for name in ("loss", "student_mass", "teacher_mass", "topk_sum", "lse")}
+    ws, wsb = _workspace(m, v, logits, workspace)
+    _check(_lib.vwc_topk_kl_fwd_rows(_ptr(logits), _dtype(logits), n, v, ld, _ptr(row_idx), m,
+                                     _ptr(topk_idx), _ptr(teacher_logprob), k, int(mode),
+                                     float(tail_mass_eps), float(temperature), _ptr(out["loss"]),
+                                     _ptr(out["student_mass"]), _ptr(out["teacher_mass"]),
+                                     _ptr(out["topk_sum"]), _ptr(out["lse"]), _ptr(ws), wsb,
+                                     _stream(stream, logits)))
+    return out
+
+
+def topk_kl_bwd_rows(logits, row_idx, topk_idx, teacher_logprob, fwd, grad_loss,
+                     mode=VWC_KL_TAIL, tail_mass_eps=1e-6, temperature=1.0, grad_logits=None,
+                     grad_dtype=None, layout=VWC_GRAD_COMPACT, stream=None):
+    """Gradient of sum_i grad_loss[i] * loss[i] over the rows row_idx; `fwd` is the dict
+    topk_kl_fwd_rows returned.  layout: compact [m, vocab] or scatter into [n_rows, vocab]."""
+    n, v, ld = _rows_view(logits)
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    _i32(topk_idx, "topk_idx")
+    if topk_idx.dim() != 2 or topk_idx.size(0) != m or teacher_logprob.shape != topk_idx.shape:
+        raise ValueError("topk_idx and teacher_logprob must both be [m, k]")
+    _f32_in(teacher_logprob, topk_idx.numel(), "teacher_logprob")
+    for name in ("lse", "student_mass", "teacher_mass", "topk_sum"):
+        _f32_in(fwd[name], m, name)
+    _f32_in(grad_loss, m, "grad_loss")
+    rows = m if layout == VWC_GRAD_COMPACT else n
+    if grad_logits is None:
+        grad_logits = _grad_out(logits, rows, None, grad_dtype)
+        if layout == VWC_GRAD_SCATTER:
+            grad_logits.zero_()
+    gld = _grad_rows(grad_logits, rows, v)
+    _check(_lib.vwc_topk_kl_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld, _ptr(row_idx), m,
+                                     _ptr(topk_idx), _ptr(teacher_logprob), topk_idx.size(1),
+                                     int(mode), float(tail_mass_eps), float(temperature),
+                                     _ptr(fwd["lse"]), _ptr(fwd["student_mass"]),
+                                     _ptr(fwd["teacher_mass"]), _ptr(fwd["topk_sum"]),
+                                     _ptr(grad_loss), _ptr(grad_logits), _dtype(grad_logits), gld,
+                                     layout, _stream(stream, logits)))
+    return grad_logits
 
 
 def vocab_partial(logits_slice, v_start, targets=None, row_idx=None, temperature=1.0, out=None,

@@ -373,22 +373,26 @@ static vwc_status check_topk(const char *fn, const int32_t *topk_idx, const floa
     return VWC_OK;
 }
 
-vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
-                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
-                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
-                           float *loss, float *student_mass, float *teacher_mass, float *topk_sum,
-                           float *lse, void *workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-    const char *fn = "vwc_topk_kl_fwd";
+// Shared bodies of the dense and row-set top-k KL calls: row_idx null means
+// output i is row i (m == n_rows); the payload and the per-row values are
+// indexed by output.
+static vwc_status topk_fwd_common(const char *fn, const void *logits, int dt, int64_t n_rows,
+                                  int64_t vocab, int64_t ld, const int32_t *row_idx, int64_t m,
+                                  const int32_t *topk_idx, const float *teacher_logprob,
+                                  int32_t k, int mode, float tail_mass_eps, float temperature,
+                                  float *loss, float *student_mass, float *teacher_mass,
+                                  float *topk_sum, float *lse, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
-    if ((st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps, n_rows)) !=
+    if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
+    if ((st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps, m)) !=
         VWC_OK)
         return st;
-    if (n_rows == 0) return ok();
+    if (m == 0) return ok();
     if (!lse) return fail(VWC_ERR_INVALID_ARG, "%s: lse is null", fn);
-    st = forward_common(fn, logits, dt, n_rows, vocab, ld, 0, nullptr, vwc::kTargetNone, nullptr,
-                        n_rows, temperature, nullptr, lse, nullptr, nullptr, workspace,
+    st = forward_common(fn, logits, dt, n_rows, vocab, ld, 0, nullptr, vwc::kTargetNone, row_idx,
+                        m, temperature, nullptr, lse, nullptr, nullptr, workspace,
                         workspace_bytes, stream);
     if (st != VWC_OK) return st;
     vwc::TopkPlan p{};
@@ -397,6 +401,8 @@ vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
     p.vocab = static_cast<int32_t>(vocab);
     p.dt = dt;
     p.n_rows = n_rows;
+    p.row_idx = row_idx;
+    p.m = m;
     p.idx = topk_idx;
     p.tlp = teacher_logprob;
     p.k = k;
@@ -411,25 +417,26 @@ vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
     return hip_status(vwc::launch_topk_fwd(p, stream), fn);
 }
 
-vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
-                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
-                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
-                           const float *lse, const float *student_mass, const float *teacher_mass,
-                           const float *topk_sum, const float *grad_loss, void *grad_logits,
-                           vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream) {
-    const char *fn = "vwc_topk_kl_bwd";
-    vwc_status st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps,
-                               n_rows);
+static vwc_status topk_bwd_common(const char *fn, const void *logits, int dt, int64_t n_rows,
+                                  int64_t vocab, int64_t ld, const int32_t *row_idx, int64_t m,
+                                  const int32_t *topk_idx, const float *teacher_logprob,
+                                  int32_t k, int mode, float tail_mass_eps, float temperature,
+                                  const float *lse, const float *student_mass,
+                                  const float *teacher_mass, const float *topk_sum,
+                                  const float *grad_loss, void *grad_logits, int grad_dt,
+                                  int64_t ld_grad, bool by_row_id, hipStream_t stream) {
+    if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
+    vwc_status st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps, m);
     if (st != VWC_OK) return st;
-    if (n_rows > 0 && (!student_mass || !teacher_mass || !topk_sum || !grad_loss))
+    if (m > 0 && (!student_mass || !teacher_mass || !topk_sum || !grad_loss))
         return fail(VWC_ERR_INVALID_ARG,
                     "%s: null student_mass, teacher_mass, topk_sum or grad_loss", fn);
-    KlArgs kl{teacher_mass, student_mass, topk_sum, static_cast<int>(mode), tail_mass_eps,
+    KlArgs kl{teacher_mass, student_mass, topk_sum, mode, tail_mass_eps,
               topk_idx, teacher_logprob, k, false};
-    st = backward_common(fn, logits, dt, n_rows, vocab, ld, nullptr, nullptr, n_rows, temperature,
-                         lse, nullptr, grad_loss, nullptr, grad_logits, grad_dt, ld_grad, true,
+    st = backward_common(fn, logits, dt, n_rows, vocab, ld, nullptr, row_idx, m, temperature, lse,
+                         nullptr, grad_loss, nullptr, grad_logits, grad_dt, ld_grad, by_row_id,
                          stream, &kl);
-    if (st != VWC_OK || n_rows == 0 || kl.fused) return st;
+    if (st != VWC_OK || m == 0 || kl.fused) return st;
     vwc::TopkPlan p{};
     p.logits = logits;
     p.ld = ld;
@@ -437,6 +444,9 @@ vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
     p.dt = dt;
     p.gdt = grad_dt;
     p.n_rows = n_rows;
+    p.row_idx = row_idx;
+    p.m = m;
+    p.grad_by_row_id = by_row_id;
     p.idx = topk_idx;
     p.tlp = teacher_logprob;
     p.k = k;
@@ -451,6 +461,63 @@ vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int
     p.grad = grad_logits;
     p.ld_grad = ld_grad;
     return hip_status(vwc::launch_topk_fixup(p, stream), fn);
+}
+
+vwc_status vwc_topk_kl_fwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                           float *loss, float *student_mass, float *teacher_mass, float *topk_sum,
+                           float *lse, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    return topk_fwd_common("vwc_topk_kl_fwd", logits, dt, n_rows, vocab, ld, nullptr, n_rows,
+                           topk_idx, teacher_logprob, k, mode, tail_mass_eps, temperature, loss,
+                           student_mass, teacher_mass, topk_sum, lse, workspace, workspace_bytes,
+                           stream);
+}
+
+vwc_status vwc_topk_kl_fwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                                int64_t ld, const int32_t *row_idx, int64_t m,
+                                const int32_t *topk_idx, const float *teacher_logprob, int32_t k,
+                                vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                                float *loss, float *student_mass, float *teacher_mass,
+                                float *topk_sum, float *lse, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "vwc_topk_kl_fwd_rows";
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    return topk_fwd_common(fn, logits, dt, n_rows, vocab, ld, row_idx, m, topk_idx,
+                           teacher_logprob, k, mode, tail_mass_eps, temperature, loss,
+                           student_mass, teacher_mass, topk_sum, lse, workspace, workspace_bytes,
+                           stream);
+}
+
+vwc_status vwc_topk_kl_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                           int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                           int32_t k, vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                           const float *lse, const float *student_mass, const float *teacher_mass,
+                           const float *topk_sum, const float *grad_loss, void *grad_logits,
+                           vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream) {
+    return topk_bwd_common("vwc_topk_kl_bwd", logits, dt, n_rows, vocab, ld, nullptr, n_rows,
+                           topk_idx, teacher_logprob, k, mode, tail_mass_eps, temperature, lse,
+                           student_mass, teacher_mass, topk_sum, grad_loss, grad_logits, grad_dt,
+                           ld_grad, true, stream);
+}
+
+vwc_status vwc_topk_kl_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                                int64_t ld, const int32_t *row_idx, int64_t m,
+                                const int32_t *topk_idx, const float *teacher_logprob, int32_t k,
+                                vwc_kl_mode mode, float tail_mass_eps, float temperature,
+                                const float *lse, const float *student_mass,
+                                const float *teacher_mass, const float *topk_sum,
+                                const float *grad_loss, void *grad_logits, vwc_dtype grad_dt,
+                                int64_t ld_grad, vwc_grad_layout layout, hipStream_t stream) {
+    const char *fn = "vwc_topk_kl_bwd_rows";
+    if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    return topk_bwd_common(fn, logits, dt, n_rows, vocab, ld, row_idx, m, topk_idx,
+                           teacher_logprob, k, mode, tail_mass_eps, temperature, lse,
+                           student_mass, teacher_mass, topk_sum, grad_loss, grad_logits, grad_dt,
+                           ld_grad, layout == VWC_GRAD_SCATTER, stream);
 }
 
 vwc_status vwc_vocab_partial(const void *logits_slice, vwc_dtype dt, int64_t n_rows,

@@ -138,26 +138,31 @@ struct CombinePlan {
     vwc_partial *partial_out;   // merge into partials instead of final outputs
 };
 
-// Top-k KL per-row pieces: gathers k student logits per row.
+// Top-k KL per-row pieces: gathers k student logits per output row.  Output
+// i is row row_idx[i] of the logits (row i when row_idx is null); the payload
+// and the per-row values are indexed by output.
 struct TopkPlan {
     const void *logits;
     int64_t ld;
     int32_t vocab;
     int dt, gdt;
     int64_t n_rows;
-    const int32_t *idx;        // [n_rows][k]
-    const float *tlp;          // [n_rows][k]
+    const int32_t *row_idx;    // [m] or null
+    int64_t m;                 // output rows
+    const int32_t *idx;        // [m][k]
+    const float *tlp;          // [m][k]
     int32_t k;
     int mode;
     double eps;
     double tau;
-    const float *lse;          // [n_rows]
+    const float *lse;          // [m]
     // forward outputs (nullable)
     float *loss, *Q, *P, *S;
     // backward (fix-up) inputs/outputs
     const float *inP, *inQ, *inS, *grad_loss;
     void *grad;
     int64_t ld_grad;
+    bool grad_by_row_id;       // gradient row = row id (scatter) or output index (compact)
 };
 
 // Fused LM head: logits of a tile of kept hidden rows against a tile of the

@@ -927,17 +927,27 @@ __device__ __forceinline__ double wave_sum(double v) {
 // S = sum p (a - log q) in fp64 (lane-strided, then a fixed butterfly).
 template <int DT>
 __global__ __launch_bounds__(kTopkBlock) void topk_fwd_kernel(TopkPlan p) {
-    const int64_t r = blockIdx.x;
+    const int64_t i = blockIdx.x;
+    const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+    if (r < 0 || r >= p.n_rows) {  // row id outside the logits: NaN outputs, no reads
+        if (threadIdx.x == 0) {
+            if (p.loss) p.loss[i] = NAN;
+            if (p.Q) p.Q[i] = NAN;
+            if (p.P) p.P[i] = NAN;
+            if (p.S) p.S[i] = NAN;
+        }
+        return;
+    }
     const char *row = static_cast<const char *>(p.logits) + r * p.ld * (DT == VWC_BF16 ? 2 : 4);
-    const double lse = static_cast<double>(p.lse[r]);
+    const double lse = static_cast<double>(p.lse[i]);
     double P = 0.0, Q = 0.0, S = 0.0, bad = 0.0;
     for (int n = threadIdx.x; n < p.k; n += kTopkBlock) {
-        const int32_t j = p.idx[r * p.k + n];
+        const int32_t j = p.idx[i * p.k + n];
         if (j < 0 || j >= p.vocab) {
             bad = 1.0;
             continue;
         }
-        const double a = static_cast<double>(p.tlp[r * p.k + n]);
+        const double a = static_cast<double>(p.tlp[i * p.k + n]);
         const double lq = static_cast<double>(load_element<DT>(row, j)) / p.tau - lse;
         const double pn = exp(a);
         P += pn;
@@ -958,31 +968,34 @@ __global__ __launch_bounds__(kTopkBlock) void topk_fwd_kernel(TopkPlan p) {
         L = S + (pt == 0.0 ? 0.0 : pt * (log(pt) - log(qt)));
     }
     if (bad != 0.0) L = P = Q = S = NAN;
-    if (p.loss) p.loss[r] = static_cast<float>(L);
-    if (p.Q) p.Q[r] = static_cast<float>(Q);
-    if (p.P) p.P[r] = static_cast<float>(P);
-    if (p.S) p.S[r] = static_cast<float>(S);
+    if (p.loss) p.loss[i] = static_cast<float>(L);
+    if (p.Q) p.Q[i] = static_cast<float>(Q);
+    if (p.P) p.P[i] = static_cast<float>(P);
+    if (p.S) p.S[i] = static_cast<float>(S);
 }
 
 // After the streaming backward wrote alpha q_j g / tau everywhere: overwrite
 // the k payload columns with (beta q_j - kappa p_j) g / tau.
 template <int DT, int GDT>
 __global__ __launch_bounds__(kTopkBlock) void topk_fixup_kernel(TopkPlan p) {
-    const int64_t r = blockIdx.x;
-    const float g = p.grad_loss[r];
+    const int64_t i = blockIdx.x;
+    const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+    if (r < 0 || r >= p.n_rows) return;  // the streaming pass wrote nothing for it either
+    const float g = p.grad_loss[i];
     if (g == 0.f) return;
-    const KlCoef c = kl_coef(p.mode, p.eps, static_cast<double>(p.inP[r]),
-                             static_cast<double>(p.inQ[r]), static_cast<double>(p.inS[r]));
+    const KlCoef c = kl_coef(p.mode, p.eps, static_cast<double>(p.inP[i]),
+                             static_cast<double>(p.inQ[i]), static_cast<double>(p.inS[i]));
     if (c.dead) return;
     const char *row = static_cast<const char *>(p.logits) + r * p.ld * (DT == VWC_BF16 ? 2 : 4);
-    char *grow = static_cast<char *>(p.grad) + r * p.ld_grad * (GDT == VWC_BF16 ? 2 : 4);
-    const double lse = static_cast<double>(p.lse[r]);
+    char *grow = static_cast<char *>(p.grad) +
+                 (p.grad_by_row_id ? r : i) * p.ld_grad * (GDT == VWC_BF16 ? 2 : 4);
+    const double lse = static_cast<double>(p.lse[i]);
     const double gt = static_cast<double>(g) / p.tau;
     for (int n = threadIdx.x; n < p.k; n += kTopkBlock) {
-        const int32_t j = p.idx[r * p.k + n];
+        const int32_t j = p.idx[i * p.k + n];
         if (j < 0 || j >= p.vocab) continue;
         const float o[1] = {kl_payload_grad(static_cast<double>(load_element<DT>(row, j)), p.tau,
-                                            lse, gt, c, p.tlp[r * p.k + n])};
+                                            lse, gt, c, p.tlp[i * p.k + n])};
         GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * (GDT == VWC_BF16 ? 2 : 4), o);
     }
 }
@@ -1138,7 +1151,7 @@ hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream) {
 }
 
 hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream) {
-    const dim3 grid(static_cast<uint32_t>(p.n_rows)), block(kTopkBlock);
+    const dim3 grid(static_cast<uint32_t>(p.m)), block(kTopkBlock);
     if (p.dt == VWC_BF16)
         hipLaunchKernelGGL(topk_fwd_kernel<VWC_BF16>, grid, block, 0, stream, p);
     else
@@ -1147,7 +1160,7 @@ hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream) {
 }
 
 hipError_t launch_topk_fixup(const TopkPlan &p, hipStream_t stream) {
-    const dim3 grid(static_cast<uint32_t>(p.n_rows)), block(kTopkBlock);
+    const dim3 grid(static_cast<uint32_t>(p.m)), block(kTopkBlock);
     if (p.dt == VWC_BF16) {
         if (p.gdt == VWC_BF16)
             hipLaunchKernelGGL((topk_fixup_kernel<VWC_BF16, VWC_BF16>), grid, block, 0, stream, p);

@@ -81,17 +81,23 @@ typedef enum vwc_status {
     VWC_OK = 0,
     VWC_ERR_INVALID_ARG = 1, /* a null required pointer, a negative size, ld < vocab, ... */
     VWC_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle (e.g. misaligned dtype) */
-    VWC_ERR_HIP = 3          /* a HIP launch failed; see vwc_last_error() */
+    VWC_ERR_HIP = 3,         /* a HIP launch failed; see vwc_last_error() */
+    VWC_STATUS_INT_RANGE_LO_ = -0x7fffffff - 1, /* (these two make every int a value */
+    VWC_STATUS_INT_RANGE_HI_ = 0x7fffffff       /*  of the type: callers pass ints) */
 } vwc_status;
 
 typedef enum vwc_dtype {
     VWC_BF16 = 0, /* bfloat16, stored as its 16-bit pattern */
-    VWC_FP32 = 1  /* IEEE binary32 */
+    VWC_FP32 = 1, /* IEEE binary32 */
+    VWC_DTYPE_INT_RANGE_LO_ = -0x7fffffff - 1, /* every int is a value; others are refused */
+    VWC_DTYPE_INT_RANGE_HI_ = 0x7fffffff
 } vwc_dtype;
 
 typedef enum vwc_grad_layout {
     VWC_GRAD_COMPACT = 0, /* gradient row i of a [m, ld_grad] buffer */
-    VWC_GRAD_SCATTER = 1  /* gradient row row_idx[i] of a [n_rows, ld_grad] buffer */
+    VWC_GRAD_SCATTER = 1, /* gradient row row_idx[i] of a [n_rows, ld_grad] buffer */
+    VWC_GRAD_LAYOUT_INT_RANGE_LO_ = -0x7fffffff - 1, /* every int is a value; others are refused */
+    VWC_GRAD_LAYOUT_INT_RANGE_HI_ = 0x7fffffff
 } vwc_grad_layout;
 
 /*
@@ -236,7 +242,9 @@ vwc_status vwc_logprob_entropy_bwd_rows(const void *logits, vwc_dtype dt, int64_
 
 typedef enum vwc_kl_mode {
     VWC_KL_TRUNCATED = 0, /* sum over the teacher top-k, clamped at 0 */
-    VWC_KL_TAIL = 1       /* K+1 categories: the top-k plus one aggregate tail */
+    VWC_KL_TAIL = 1,      /* K+1 categories: the top-k plus one aggregate tail */
+    VWC_KL_MODE_INT_RANGE_LO_ = -0x7fffffff - 1, /* every int is a value; others are refused */
+    VWC_KL_MODE_INT_RANGE_HI_ = 0x7fffffff
 } vwc_kl_mode;
 
 /*

@@ -56,7 +56,8 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        # ORACLE_LIB points the tests' mutation checks at a deliberately broken copy.
+        # ORACLE_LIB points the tests at another build: a deliberately broken copy
+        # (mutation checks) or a sanitizer-instrumented one.
         path = os.environ.get("ORACLE_LIB") or _LIB_PATH
         if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build(force=False)

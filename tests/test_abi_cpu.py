@@ -8,7 +8,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vwc.h")
-LIB = os.path.join(ROOT, "vocab_wide_cross_amd", "libvwc.so")
+# VWC_TEST_LIB points the checks at another build of the library (the
+# sanitizer test runs them against an instrumented copy).
+LIB = os.environ.get("VWC_TEST_LIB") or os.path.join(ROOT, "vocab_wide_cross_amd", "libvwc.so")
 
 OK, INVALID, UNSUPPORTED = 0, 1, 2
 BF16, FP32 = 0, 1

@@ -673,7 +673,7 @@ vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, i
 }
 
 const char *vwc_status_string(vwc_status status) {
-    switch (status) {
+    switch (static_cast<int>(status)) {
         case VWC_OK: return "ok";
         case VWC_ERR_INVALID_ARG: return "invalid argument";
         case VWC_ERR_UNSUPPORTED: return "unsupported";

@@ -126,6 +126,12 @@ def test_rows_and_backward_validation(lib):
     assert fr(FAKE, BF16, 8, 16, 16, FAKE, None, 3, 1.0, FAKE, None, None, None, 0, None) == INVALID
     assert fr(FAKE, BF16, 8, 16, 16, FAKE, FAKE, -1, 1.0, FAKE, None, None, None, 0, None) == INVALID
     assert fr(FAKE, BF16, 8, 16, 16, FAKE, FAKE, 0, 1.0, FAKE, None, None, None, 0, None) == OK
+    # a row list longer than one launch is refused before any size is computed from it
+    # (the workspace and gradient sizes would overflow 64 bits)
+    huge = 1 << 62
+    assert fr(FAKE, BF16, 8, 1 << 20, 1 << 20, FAKE, FAKE, huge, 1.0, FAKE, None, None, FAKE,
+              1 << 30, None) == UNSUPPORTED
+    assert b"exceed one launch" in err_str(lib)
     b = lib.vwc_selected_logprob_bwd
     b.argtypes = [p, ctypes.c_int, i64, i64, i64, p, ctypes.c_float, p, p, p, ctypes.c_int, i64, p]
     g = ctypes.c_void_p(0x900000)
@@ -146,6 +152,9 @@ def test_rows_and_backward_validation(lib):
     assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 2, 1.0, FAKE, FAKE, g, BF16, 16, 9,
               None) == INVALID
     assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 0, 1.0, FAKE, FAKE, g, BF16, 16, 0, None) == OK
+    assert br(FAKE, BF16, 4, 1 << 20, 1 << 20, FAKE, FAKE, huge, 1.0, FAKE, FAKE, g, BF16,
+              1 << 20, 0, None) == UNSUPPORTED     # compact gradient of 2^62 rows
+    assert b"exceed one launch" in err_str(lib)
     # in place, compact gradient rows (indexed by output, not row id) are refused
     assert br(FAKE, BF16, 4, 16, 16, FAKE, FAKE, 2, 1.0, FAKE, FAKE, FAKE, BF16, 16, 0,
               None) == INVALID

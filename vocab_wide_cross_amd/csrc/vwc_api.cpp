@@ -105,8 +105,8 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
     if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
 
     const int64_t nseg = segments(vocab, dt, vwc::kFwdSegBytes);
+    if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;  // first: bounds m for the sizes below
     if ((st = check_workspace(fn, m, nseg, workspace, workspace_bytes)) != VWC_OK) return st;
-    if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;
 
     vwc::FwdPlan p{};
     p.logits = logits;
@@ -174,7 +174,10 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
         return fail(VWC_ERR_INVALID_ARG, "%s: null lse or grad_logits", fn);
     if (reinterpret_cast<uintptr_t>(grad_logits) % esize(grad_dt) != 0)
         return fail(VWC_ERR_UNSUPPORTED, "%s: grad_logits not aligned to its dtype", fn);
-    if (ld_grad > INT64_MAX / 16 / n_rows)
+    const int64_t nseg = segments(vocab, dt, vwc::kBwdSegBytes);
+    if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;  // first: bounds m for the sizes below
+    const int64_t grad_rows = by_row_id ? n_rows : m;
+    if (ld_grad > INT64_MAX / 16 / grad_rows)
         return fail(VWC_ERR_UNSUPPORTED, "%s: gradient tensor too large", fn);
     // The gradient either replaces the logits exactly (same buffer, dtype and
     // row stride, each row's gradient over that row: every element is read and
@@ -185,7 +188,6 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
             return fail(VWC_ERR_INVALID_ARG,
                         "%s: an in-place gradient needs gradient rows indexed by row id", fn);
     } else {
-        const int64_t grad_rows = by_row_id ? n_rows : m;
         const uintptr_t x0 = reinterpret_cast<uintptr_t>(logits);
         const uintptr_t x1 = x0 + static_cast<uintptr_t>(((n_rows - 1) * ld + vocab) * esize(dt));
         const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_logits);
@@ -194,9 +196,6 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
         if (g0 < x1 && x0 < g1)
             return fail(VWC_ERR_INVALID_ARG, "%s: grad_logits overlaps logits", fn);
     }
-
-    const int64_t nseg = segments(vocab, dt, vwc::kBwdSegBytes);
-    if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;
 
     vwc::BwdPlan p{};
     p.logits = logits;

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Small shapes cover every row (several row segments, ragged tails, the
-element-by-element path for unaligned layouts, edge cases).  Bars: logprob /
+rows that do not start on 16 bytes, edge cases).  Bars: logprob /
 lse / entropy abs err <= 5e-5; fp32 gradient abs err <= 1e-6; bf16 gradient
 within one bf16 step of the oracle rounded to bf16; the computed row set equal
 to the oracle's, bit for bit.
@@ -119,8 +119,10 @@ def test_fp32_grad_from_bf16_and_bf16_grad_from_fp32():
 
 
 @pytest.mark.parametrize("vocab,ld", [(20011, 20011), (20011, 20013), (4096, 4100), (70001, 70003)])
-def test_unaligned_rows_take_element_path(vocab, ld):
-    """Rows that do not start on 16 bytes (odd ld) use the element-by-element path."""
+def test_unaligned_rows_odd_stride(vocab, ld):
+    """Rows that do not start on 16 bytes (odd ld): the forward streams vectors from
+    each row's first 16-byte boundary; the backward, whose gradient rows here have
+    another stride (another phase), goes element by element."""
     w = W.scaled("spiked_bf16_8192x248320", 24, vocab)
     x = W.logits_rows(w, np.arange(w.n_rows), ld=ld)
     t, g = W.targets(w), W.grad_out(w)

@@ -50,6 +50,23 @@ bool rows_aligned16(const void *p, int64_t ld, int64_t e) {
     return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * e) % 16 == 0);
 }
 
+// The backward streams 16-byte vectors of each logits row from its first
+// 16-byte boundary on (`head` elements in) and stores each vector's gradient
+// with one store, so that boundary must fall on a 16-byte boundary of the
+// row's gradient too.  It does when every row has the same phase on both
+// sides (row strides of whole 16-byte multiples and matching bases), or when
+// both sides shift by the same bytes from row to row (equal element size and
+// stride, the gradient row indexed like the logits row, equal base phase).
+bool vector_rows(const void *x, int64_t ld, int64_t e, const void *g, int64_t ld_grad,
+                 int64_t ge, bool same_row) {
+    const uintptr_t bx = reinterpret_cast<uintptr_t>(x), bg = reinterpret_cast<uintptr_t>(g);
+    if ((ld * e) % 16 == 0 && (ld_grad * ge) % 16 == 0) {
+        const uintptr_t head = ((16 - bx % 16) % 16) / static_cast<uintptr_t>(e);
+        return (bg + head * static_cast<uintptr_t>(ge)) % 16 == 0;
+    }
+    return same_row && e == ge && ld == ld_grad && bx % 16 == bg % 16;
+}
+
 // Common checks of a logits operand.
 vwc_status check_logits(const char *fn, const void *logits, int dt, int64_t n_rows, int64_t vocab,
                         int64_t ld, float temperature) {
@@ -124,9 +141,8 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
     if (target_mode == vwc::kTargetSlice && !targets) p.target_mode = vwc::kTargetNone;
     p.tau = static_cast<double>(temperature);
     p.c = static_cast<float>(1.44269504088896340736 / p.tau);
-    p.vector = rows_aligned16(logits, ld, esize(dt));
-    const int64_t unit = p.vector ? 16 / esize(dt) : 1;
-    const int64_t nunits = vocab / unit;
+    // Every row streams 16-byte vectors from its first 16-byte boundary on.
+    const int64_t nunits = vocab / (16 / esize(dt));
     p.nseg = static_cast<int>(nseg);
     p.seg_units = static_cast<int32_t>((nunits + nseg - 1) / nseg);
     if (p.seg_units < 1) p.seg_units = 1;
@@ -223,8 +239,10 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     p.grad = grad_logits;
     p.ld_grad = ld_grad;
     p.grad_by_row_id = by_row_id;
-    p.vector = rows_aligned16(logits, ld, esize(dt)) &&
-               rows_aligned16(grad_logits, ld_grad, esize(grad_dt));
+    const bool aligned = rows_aligned16(logits, ld, esize(dt)) &&
+                         rows_aligned16(grad_logits, ld_grad, esize(grad_dt));
+    p.vector = vector_rows(logits, ld, esize(dt), grad_logits, ld_grad, esize(grad_dt),
+                           !row_idx || by_row_id);
     const int64_t unit = p.vector ? 16 / esize(dt) : 1;
     const int64_t nunits = vocab / unit;
     p.nseg = static_cast<int>(nseg);
@@ -234,7 +252,7 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
         // The payload columns go into the same pass when the rows are 16-byte
         // vectors and a segment's payload fits the in-LDS table; otherwise the
         // caller runs the fix-up launch.
-        kl->fused = p.vector && kl->k <= vwc::kKlMaxK && p.seg_units <= vwc::kKlMaxSegUnits;
+        kl->fused = aligned && kl->k <= vwc::kKlMaxK && p.seg_units <= vwc::kKlMaxSegUnits;
         // The fix-up launch re-reads payload logits after the stream wrote them.
         if (in_place && !kl->fused)
             return fail(VWC_ERR_UNSUPPORTED,

@@ -73,8 +73,8 @@ struct FwdPlan {
     float c;                  // log2(e) / tau rounded to float
     double tau;               // the float temperature widened
     int nseg;                 // segments per row
-    int32_t seg_units;        // load units (16-byte vectors, or elements) per segment
-    bool vector;              // 16-byte vector path
+    int32_t seg_units;        // 16-byte load units per segment (rows stream from their
+                              // first 16-byte boundary; the edges go element-wise)
     bool want_entropy;
     // Final outputs (nseg == 1 and !partial_out), compact [m]:
     float *logprob, *lse, *entropy;
@@ -117,7 +117,8 @@ struct BwdPlan {
     bool grad_by_row_id;      // true: gradient row = row id; false: = output index
     int nseg;
     int32_t seg_units;
-    bool vector;
+    bool vector;              // 16-byte units from each row's first 16-byte boundary
+                              // (else one element per unit)
 };
 
 // The fused top-k KL backward keeps a segment's payload columns in an LDS hash

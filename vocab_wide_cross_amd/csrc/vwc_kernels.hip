@@ -148,6 +148,24 @@ __device__ __forceinline__ float load_element(const char *row, int64_t j) {
     return Unit<DT, false>::get(reinterpret_cast<const typename Unit<DT, false>::T *>(row)[j], 0);
 }
 
+// Elements of a row before its first 16-byte boundary (the row starts on an
+// element boundary), at most the row's length.
+template <int64_t kE>
+__device__ __forceinline__ int32_t row_head(const void *row, int32_t vocab) {
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row)) & 15u;
+    return min(static_cast<int32_t>(((16u - mis) & 15u) / kE), vocab);
+}
+
+// Column of edge element `k` of a row whose whole vectors cover columns
+// [head, head + body): the head columns first, then the tail past the body;
+// -1 past the last edge element.
+__device__ __forceinline__ int32_t edge_column(int32_t head, int32_t body, int32_t vocab,
+                                               int32_t k) {
+    if (k < head) return k;
+    const int32_t j = head + body + (k - head);
+    return j < vocab ? j : -1;
+}
+
 // Re-centre a lane on a chunk (units [0, nvalid) of v, still in registers)
 // and return the chunk's (sum, w) relative to the new K.  Rare: a new maximum
 // far above the reference, or NaN/-inf data.
@@ -451,20 +469,23 @@ __global__ __launch_bounds__(INBLOCK ? kFwdBlock * kFwdMaxSegPerBlock : kFwdBloc
     vwc_partial mine{NAN, NAN, NAN, NAN};
     if (!bad) {  // uniform over the workgroup
         const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
-        const int32_t nunits = p.vocab / Un::N;  // whole units; the rest is the tail
+        // The whole vectors start at the row's first 16-byte boundary, `head`
+        // elements in (0 when the row starts on one); the elements before it
+        // and past the last whole vector are the row's edges.
+        const int32_t head = VEC ? row_head<kE>(row, p.vocab) : 0;
+        const int32_t nunits = (p.vocab - head) / Un::N;
         const int32_t u0 = q * p.seg_units;
         const int32_t u1 = min(u0 + p.seg_units, nunits);
         const bool last = q == p.nseg - 1;
 
         Lane L = lane_init();
-        if (u0 < u1) stream_units<DT, VEC, kFwdU, W>(row, u0, u1, p.c, tid, L);
-        if (VEC && last) {  // tail elements past the last whole vector
-            const int32_t j = nunits * Un::N + tid;
-            if (j < p.vocab) {
+        if (u0 < u1) stream_units<DT, VEC, kFwdU, W>(row + head * kE, u0, u1, p.c, tid, L);
+        if (VEC && last) {  // the edge elements, one per thread
+            const int32_t j = edge_column(head, nunits * Un::N, p.vocab, tid);
+            if (j >= 0) {
                 using Us = Unit<DT, false>;
                 typename Us::T v[1];
-                const typename Us::T *ptr = reinterpret_cast<const typename Us::T *>(row) + j;
-                v[0] = *ptr;
+                v[0] = reinterpret_cast<const typename Us::T *>(row)[j];
                 fold_chunk<DT, false, 1, W>(v, 1, p.c, L);
             }
         }
@@ -785,8 +806,13 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     if (r < 0 || r >= p.n_rows) return;  // row id outside the tensor: nothing is written
     const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
     char *grow = static_cast<char *>(p.grad) + (p.grad_by_row_id ? r : i) * p.ld_grad * kGE;
-
-    const int32_t nunits = p.vocab / N;
+    // Whole vectors from the row's first 16-byte boundary on (the host checked
+    // that it falls on a vector boundary of the gradient row too; the fused
+    // top-k KL path takes rows that start on one); the edges go element-wise.
+    const int32_t head = (VEC && !KLF) ? row_head<kE>(row, p.vocab) : 0;
+    const char *vrow = row + head * kE;
+    char *vgrow = grow + head * kGE;
+    const int32_t nunits = (p.vocab - head) / N;
     const int32_t u0 = q * p.seg_units;
     const int32_t u1 = min(u0 + p.seg_units, nunits);
     const bool last = q == p.nseg - 1;
@@ -804,10 +830,11 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
 #pragma unroll
         for (int k = 0; k < N; ++k) z[k] = 0.f;
         for (int32_t b = u0 + static_cast<int32_t>(threadIdx.x); b < u1; b += kBwdBlock)
-            GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, z);
+            GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(b) * N * kGE, z);
         if (VEC && last) {
-            const int32_t j = nunits * N + static_cast<int32_t>(threadIdx.x);
-            if (j < p.vocab) {
+            const int32_t j = edge_column(head, nunits * N, p.vocab,
+                                          static_cast<int32_t>(threadIdx.x));
+            if (j >= 0) {
                 float z1[1] = {0.f};
                 GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, z1);
             }
@@ -828,7 +855,7 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     R.b = static_cast<float>(R.hs * kLn2);
     R.t = (g != 0.f && !kl) ? p.targets[r] : -1;
     if (kl) R.gs = static_cast<float>(R.gt * klc.alpha);  // o = q (g alpha / tau)
-    const T *src = reinterpret_cast<const T *>(row);
+    const T *src = reinterpret_cast<const T *>(vrow);
 
     __shared__ KlSlot kl_tab[KLF ? kKlSlots : 1];
     __shared__ uint32_t kl_lane[KLF ? kBwdBlock : 1];
@@ -876,22 +903,22 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         for (int j = 0; j < U; ++j) {
             const int32_t unit = b + j * kBwdBlock;
             float o[N];
-            unit_grad<DT, VEC, WH>(v[j], unit * N, R, o);
+            unit_grad<DT, VEC, WH>(v[j], head + unit * N, R, o);
             if (KLF && ((kl_mine >> ((unit - u0) / kBwdBlock)) & 1u))
                 kl_patch<N>(kl_tab, unit - u0, o);
-            GradStore<GDT, N>::store(grow + static_cast<int64_t>(unit) * N * kGE, o);
+            GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(unit) * N * kGE, o);
         }
     }
     for (; b < u1; b += kBwdBlock) {
         const T v = Un::load(src + b);
         float o[N];
-        unit_grad<DT, VEC, WH>(v, b * N, R, o);
+        unit_grad<DT, VEC, WH>(v, head + b * N, R, o);
         if (KLF && ((kl_mine >> ((b - u0) / kBwdBlock)) & 1u)) kl_patch<N>(kl_tab, b - u0, o);
-        GradStore<GDT, N>::store(grow + static_cast<int64_t>(b) * N * kGE, o);
+        GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(b) * N * kGE, o);
     }
     if (VEC && last) {
-        const int32_t j = nunits * N + static_cast<int32_t>(threadIdx.x);
-        if (j < p.vocab) {
+        const int32_t j = edge_column(head, nunits * N, p.vocab, static_cast<int32_t>(threadIdx.x));
+        if (j >= 0) {
             using Us = Unit<DT, false>;
             const typename Us::T v = reinterpret_cast<const typename Us::T *>(row)[j];
             float o[1];
@@ -1058,22 +1085,13 @@ __global__ __launch_bounds__(kScanBlock) void mask_to_index_kernel(const uint8_t
 
 // ---------------------------------------------------------------- launch helpers
 
+// Every row streams 16-byte vectors from its first 16-byte boundary on.
 template <int DT, bool INBLOCK>
 void launch_fwd_shape(const FwdPlan &p, dim3 grid, dim3 block, hipStream_t s) {
-    if (p.vector) {
-        if (p.want_entropy)
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, true, INBLOCK>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, true, false, INBLOCK>), grid, block, 0, s,
-                               p);
-    } else {
-        if (p.want_entropy)
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, true, INBLOCK>), grid, block, 0, s,
-                               p);
-        else
-            hipLaunchKernelGGL((fwd_segment_kernel<DT, false, false, INBLOCK>), grid, block, 0, s,
-                               p);
-    }
+    if (p.want_entropy)
+        hipLaunchKernelGGL((fwd_segment_kernel<DT, true, true, INBLOCK>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_segment_kernel<DT, true, false, INBLOCK>), grid, block, 0, s, p);
 }
 
 template <int DT>

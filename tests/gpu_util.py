@@ -67,3 +67,22 @@ def assert_bf16_grad(got_bits, ref_grad64, what, oracle):
     d = bf16_ulp_distance(got_bits, ref_bits)
     assert d.max() <= 1, f"{what}: bf16 gradient {d.max()} steps from the rounded oracle"
     return int(d.max())
+
+
+def place_rows(host: np.ndarray, off: int):
+    """Device copy of host rows [n, ld] inside a flat allocation, starting `off`
+    elements in (so every row may start off 16 bytes); returns (flat, [n, ld] view)."""
+    n, ld = host.shape
+    dt = torch.bfloat16 if host.dtype == np.uint16 else torch.float32
+    flat = torch.zeros(n * ld + off + 64, dtype=dt, device=DEV)
+    view = flat[off:off + n * ld].view(n, ld)
+    view.copy_(to_dev_logits(host))
+    return flat, view
+
+
+def like_layout(view: torch.Tensor, dtype=None) -> torch.Tensor:
+    """A zeroed [n, ld] buffer with the view's stride and element offset."""
+    n, ld = view.shape
+    off = view.storage_offset()
+    flat = torch.zeros(n * ld + off + 64, dtype=dtype or view.dtype, device=DEV)
+    return flat[off:off + n * ld].view(n, ld)

@@ -17,33 +17,14 @@ import torch
 import oracle
 import vocab_wide_cross_amd as vwc
 import workloads as W
-from gpu_util import DEV, assert_bf16_grad, assert_close_scalar, grad_bits, log
+from gpu_util import (DEV, assert_bf16_grad, assert_close_scalar, grad_bits, like_layout, log,
+                      place_rows)
 
 pytestmark = pytest.mark.gpu
 
 
 def _np(t):
     return t.detach().cpu().numpy()
-
-
-def _placed(host, off):
-    """Device copy of host rows [n, ld] inside a flat allocation, starting `off`
-    elements in; returns (flat buffer, [n, ld] view)."""
-    n, ld = host.shape
-    dt = torch.bfloat16 if host.dtype == np.uint16 else torch.float32
-    flat = torch.zeros(n * ld + off + 64, dtype=dt, device=DEV)
-    src = torch.from_numpy(host.view(np.int16) if dt == torch.bfloat16 else host).to(DEV)
-    view = flat[off:off + n * ld].view(n, ld)
-    view.copy_(src.view(dt) if dt == torch.bfloat16 else src)
-    return flat, view
-
-
-def _like(view, dtype=None):
-    """An empty gradient buffer with the view's layout (same stride and phase)."""
-    n, ld = view.shape
-    off = view.storage_offset()
-    flat = torch.zeros(n * ld + off + 64, dtype=dtype or view.dtype, device=DEV)
-    return flat[off:off + n * ld].view(n, ld)
 
 
 def _check_grad(got, ref, what):
@@ -74,7 +55,7 @@ def test_forward_and_backward(dtype, vocab, ld, off):
     w = W.scaled(name, n, vocab)
     x = W.logits_rows(w, np.arange(n), ld=ld)
     t, g = W.targets(w), W.grad_out(w)
-    flat, xv = _placed(x, off)
+    flat, xv = place_rows(x, off)
     xd = xv[:, :vocab]
     td, gd = torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
     log(f"{dtype} V={vocab} ld={ld} offset={off}: forward")
@@ -85,7 +66,7 @@ def test_forward_and_backward(dtype, vocab, ld, off):
     gref = oracle.backward(x, t, g, vocab=vocab)
 
     log("  backward, gradient in the logits' layout")
-    gsame = _like(xv)[:, :vocab]
+    gsame = like_layout(xv)[:, :vocab]
     vwc.selected_logprob_bwd(xd, td, lse, gd, grad_logits=gsame)
     _check_grad(gsame, gref, "same layout")
     log("  backward, gradient rows with another stride")
@@ -94,7 +75,7 @@ def test_forward_and_backward(dtype, vocab, ld, off):
     _check_grad(gother, gref, "other stride")
     log("  backward, other gradient dtype")
     gdt = torch.float32 if dtype == "bf16" else torch.bfloat16
-    gcast = _like(xv, gdt)[:, :vocab]
+    gcast = like_layout(xv, gdt)[:, :vocab]
     vwc.selected_logprob_bwd(xd, td, lse, gd, grad_logits=gcast)
     # (an fp32 gradient from bf16 logits: lse is an fp32 input, so p carries its
     # rounding; 1e-6 absolute still holds)
@@ -103,7 +84,7 @@ def test_forward_and_backward(dtype, vocab, ld, off):
     h = W.grad_out(W.scaled(name, n, vocab + 1))
     hd = torch.from_numpy(h).to(DEV)
     gent = vwc.logprob_entropy_bwd(xd, td, lse, ent, grad_logprob=gd, grad_entropy=hd)
-    flat2, xv2 = _placed(x, off)
+    flat2, xv2 = place_rows(x, off)
     xin = xv2[:, :vocab]
     gin = vwc.logprob_entropy_bwd(xin, td, lse, ent, grad_logprob=gd, grad_entropy=hd,
                                   grad_logits=xin)
@@ -129,7 +110,7 @@ def test_row_sets(dtype, vocab, ld, off):
     w = W.scaled(name, n, vocab)
     x = W.logits_rows(w, np.arange(n), ld=ld)
     t, g = W.targets(w), W.grad_out(w)
-    _, xv = _placed(x, off)
+    _, xv = place_rows(x, off)
     xd = xv[:, :vocab]
     td = torch.from_numpy(t).to(DEV)
     rows = np.array([3, 0, 17, 31, 8, 9, 22], dtype=np.int32)
@@ -141,7 +122,7 @@ def test_row_sets(dtype, vocab, ld, off):
         assert_close_scalar(_np(v), ref[k], k)
     gref = oracle.backward(x, t, g[rows], rows=rows, vocab=vocab)
     # scatter into the logits' layout: gradient row = row id, vector path
-    gs = _like(xv)[:, :vocab]
+    gs = like_layout(xv)[:, :vocab]
     vwc.selected_logprob_bwd_rows(xd, td, idx, lse, gr, grad_logits=gs,
                                   layout=vwc.VWC_GRAD_SCATTER)
     _check_grad(gs[idx.long()], gref, "scatter")

@@ -24,7 +24,10 @@ constexpr int kCombineBlock = 64;
 // elements is cut into ceil(vocab * e / kFwdSegBytes) segments, a function of
 // (vocab, dtype) only, so a row's reduction order never depends on how many
 // rows a call covers.  The backward has no reduction; its segment size only
-// sets the work per workgroup.  Sizes were chosen by timing on MI355X.
+// sets the work per workgroup.  bf16 rows are cut into ceil(vocab * 2 /
+// kBwdSegBytes) pieces; fp32 rows into the whole number of kBwdSegBytes / 2
+// pieces nearest to their size (at least one), i.e. pieces of about 85 to
+// 192 KiB.  Sizes and rules were chosen by timing on MI355X.
 #ifndef VWC_FWD_SEG_BYTES
 #define VWC_FWD_SEG_BYTES (128 * 1024)
 #endif

@@ -40,9 +40,13 @@
  *    synchronize the host.  Results are ready when the stream reaches them.
  *  - Logits are row-major: element (r, j) sits at logits + (r * ld + j) * e,
  *    e = 2 (bf16) or 4 (fp32), 0 <= j < vocab <= ld.  The logits pointer must
- *    be aligned to e bytes.  Rows whose start is 16-byte aligned (aligned base
- *    and ld * e a multiple of 16) take the 16-byte vector path; other layouts
- *    are computed element by element (correct, slower).
+ *    be aligned to e bytes; rows may start anywhere else.  Every row is read
+ *    in 16-byte vectors from its first 16-byte boundary on, the few elements
+ *    before it and past the last whole vector one by one.  A backward keeps
+ *    16-byte stores when each row's boundary is also one of its gradient row
+ *    (same layout, in place, or both strides whole multiples of 16 bytes with
+ *    matching bases) and otherwise writes element by element (same results,
+ *    slower).
  *  - logprob / lse / entropy are float32, one per output row.  Gradients are
  *    written in grad_dt (bf16 rounded to nearest-even, or fp32).
  *  - Row sets: the dense calls cover rows 0..n_rows-1.  The `_rows` calls

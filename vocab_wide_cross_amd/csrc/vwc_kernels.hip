@@ -19,7 +19,8 @@
 //  * One 256-thread workgroup streams one segment (<= 128 KiB) of one row.
 //    Consecutive lanes read consecutive 16-byte vectors, so every wave load
 //    instruction covers 1 KiB of contiguous HBM; each lane keeps U loads in
-//    flight.
+//    flight.  The vectors start at the row's first 16-byte boundary; the few
+//    elements before it and past the last whole vector go one per thread.
 //  * Each lane keeps (K, s, w) in fp32 registers: K is a shift in log2
 //    units, s = sum 2^u and w = sum 2^u * u with u = x * c - K, c = log2(e)/tau
 //    (one FMA and one v_exp_f32 per element).  K only moves when a chunk's sum
@@ -29,10 +30,16 @@
 //    relative to the K it was accumulated with, so the lag costs no accuracy.
 //  * Lane states merge through DPP (quad_perm, row mirrors) and ds_swizzle
 //    within the wave, then through LDS across the 4 waves, in a fixed order.
-//  * Rows longer than one segment write one 16-byte partial per segment; a
-//    second small kernel merges them in segment order in fp64 (the pages'
-//    shard merge).  The epilogue arithmetic (partials, merge, log) is fp64,
-//    once per row.
+//  * Rows of 2-3 segments are reduced by one workgroup of 256 threads per
+//    segment, whose partials merge in LDS; longer rows write one 16-byte
+//    partial per segment and a second small kernel merges them.  Both merge
+//    in segment order in fp64 with the same code (the pages' shard merge), so
+//    the two shapes give the same bits.  The epilogue arithmetic (partials,
+//    merge, log) is fp64, once per row.
+//  * The backward streams each row once more: one 1024-thread workgroup per
+//    segment reads 16-byte vectors and writes each one's gradient with one
+//    non-temporal 16-byte store; rows without loss are written as +0.0
+//    without being read.
 #include <math.h>
 #include <stdint.h>
 

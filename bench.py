@@ -537,6 +537,24 @@ def main():
     def gbs(b, ms):
         return b / (ms * 1e-3) / 1e9
 
+    # The same step as one call (vwc_selected_logprob_fwd_bwd): the loss weight
+    # is known up front here, so each row is read once and kept on chip between
+    # the reduction and the gradient.  Timed on its own; not the step above.
+    fused_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        vwc.selected_logprob_fwd_bwd(x, targets, grad_out, w.tau, logprob=lp, lse=lse,
+                                     grad_logits=grad, workspace=ws, stream=stream)
+    for k in range(args.steps):
+        fused_ev[k][0].record(stream)
+        vwc.selected_logprob_fwd_bwd(x, targets, grad_out, w.tau, logprob=lp, lse=lse,
+                                     grad_logits=grad, workspace=ws, stream=stream)
+        fused_ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    fused_st = ms_stats([e[0].elapsed_time(e[1]) for e in fused_ev])
+    # one read of the logits, grad_out and targets; logprob, lse and the gradient written
+    fused_b = w.n_rows * (w.vocab * esize + 8) + w.n_rows * (8 + w.vocab * esize)
+
     # Dominant kernel: the launch with the longest average duration.  The
     # backward is one kernel; the forward is the segment kernel plus a small
     # merge kernel (its events bracket both).
@@ -577,6 +595,11 @@ def main():
                     "tokens_per_s": w.n_rows / ((fwd_avg + bwd_avg) * 1e-3),
                     "gbs_alg": gbs(fwd_b + bwd_b, fwd_avg + bwd_avg),
                     "frac": gbs(fwd_b + bwd_b, fwd_avg + bwd_avg) / HBM_PEAK_GBS},
+        "fused_fwd_bwd": {**fused_st, "tokens_per_s": w.n_rows / (fused_st["ms"] * 1e-3),
+                          "gbs_alg": gbs(fused_b, fused_st["ms"]),
+                          "frac": gbs(fused_b, fused_st["ms"]) / HBM_PEAK_GBS,
+                          "bytes_alg": fused_b,
+                          "note": "one call, loss weight known before the forward"},
         "roofline": {"bound": "hbm", "kernel": dom[0],
                      "achieved": gbs(dom[1], dom[2]), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs(dom[1], dom[2]) / HBM_PEAK_GBS, "traffic": traffic,

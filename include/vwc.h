@@ -196,6 +196,32 @@ vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_
                                     vwc_dtype grad_dt, int64_t ld_grad, hipStream_t stream);
 
 /*
+ * Forward and backward in one call, for a loss whose per-row weight g_r is
+ * known before the forward (a fixed-weight loss: token-mean cross-entropy, a
+ * policy-gradient step whose importance ratio is still 1).  The results are
+ * those of vwc_selected_logprob_fwd followed by vwc_selected_logprob_bwd with
+ * the lse it wrote ([B] "Changes": the gradient (onehot - softmax) * g in the
+ * logits' dtype; [C] "Design & Code Changes": from the logits and the fp32
+ * logZ).  lse (float[n_rows]) is required; logprob and entropy are nullable.
+ * The other arguments are as in those two calls, and grad_logits follows the
+ * same in-place rule.  When a row fits on chip (at most 31744 16-byte vectors:
+ * 253952 bf16 or 126976 fp32 columns) and the gradient has the logits' dtype
+ * and 16-byte phase, one workgroup per row reads the row once, reduces it,
+ * and writes the gradient from the held values (HBM traffic: one read and one
+ * write of the rows instead of two reads and one write).  Otherwise the two
+ * calls run in turn (`workspace` as for the forward).  Each row's lse and
+ * entropy may differ from the separate forward's in the last bits (another
+ * reduction order); every result meets the same bounds.
+ */
+vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                        int64_t vocab, int64_t ld, const int32_t *targets,
+                                        float temperature, const float *grad_logprob,
+                                        float *logprob, float *lse, float *entropy,
+                                        void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/*
  * Backward over the compact row set row_idx[0..m).  lse and grad_logprob are
  * float[m] (compact, as the `_rows` forward writes them).  layout selects
  * where gradient row i goes: VWC_GRAD_COMPACT -> row i of [m, ld_grad];

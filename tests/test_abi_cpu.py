@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
 
@@ -184,6 +184,30 @@ def test_rows_and_backward_validation(lib):
     assert b"layout" in err_str(lib)
     assert kbr(FAKE, BF16, 4, 1000, 1000, FAKE, 2, FAKE, FAKE, 0, 1, 1e-6, 1.0, FAKE, FAKE, FAKE,
                FAKE, FAKE, g, BF16, 1000, 0, None) == INVALID   # k = 0
+
+
+def test_fused_forward_backward_validation(lib):
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.vwc_selected_logprob_fwd_bwd
+    f.argtypes = [p, ctypes.c_int, i64, i64, i64, p, ctypes.c_float, p, p, p, p, p, ctypes.c_int,
+                  i64, p, ctypes.c_size_t, p]
+    f.restype = ctypes.c_int
+    g = ctypes.c_void_p(0x900000)
+    # lse is required (it is both an output and the backward's saved logZ)
+    assert f(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, FAKE, None, None, g, BF16, 16, None, 0,
+             None) == INVALID
+    assert b"lse" in err_str(lib)
+    # a gradient that overlaps the logits without being them
+    assert f(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, None, FAKE, None,
+             ctypes.c_void_p(0x100010), BF16, 16, None, 0, None) == INVALID
+    assert b"overlaps" in err_str(lib)
+    # no rows: nothing to do; bad temperature and ld as for the other calls
+    assert f(FAKE, BF16, 0, 16, 16, None, 1.0, None, None, None, None, None, BF16, 16, None, 0,
+             None) == OK
+    assert f(FAKE, BF16, 4, 16, 16, FAKE, 0.0, FAKE, None, FAKE, None, g, BF16, 16, None, 0,
+             None) == INVALID
+    assert f(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, None, FAKE, None, g, BF16, 8, None, 0,
+             None) == INVALID
 
 
 def test_partial_combine_and_mask_validation(lib):

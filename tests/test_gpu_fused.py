@@ -1,0 +1,129 @@
+"""vwc_selected_logprob_fwd_bwd (forward and backward in one call, the loss
+weight known up front) against the fp64 oracle and against the two separate
+calls.
+
+Rows that fit on chip take the one-workgroup-per-row kernel; wider rows, a
+gradient of another dtype or another 16-byte phase take the two calls.  Bars
+as in the other parity tests.  The gradient must also equal, bit for bit,
+what the separate backward writes from the lse this call produced (both use
+the same per-element code), in place or not.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocab_wide_cross_amd as vwc
+import workloads as W
+from gpu_util import (DEV, assert_bf16_grad, assert_close_scalar, grad_bits, like_layout, log,
+                      place_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+def _check_grad(got, ref, what):
+    if got.dtype == torch.bfloat16:
+        assert_bf16_grad(grad_bits(got), ref, what, oracle)
+    else:
+        err = np.abs(_np(got).astype(np.float64) - ref).max()
+        assert err <= 1e-6, f"{what}: fp32 gradient error {err:.3g}"
+
+
+CASES = [
+    # dtype, vocab, ld, offset, tau, n
+    ("bf16", 248320, 248320, 0, 1.0, 24),   # the default step's rows: on chip
+    ("bf16", 248321, 248321, 0, 1.0, 16),   # odd stride: every row its own phase
+    ("bf16", 253952, 253952, 0, 0.7, 8),    # the widest row that fits
+    ("bf16", 253953, 253953, 0, 1.0, 8),    # one column wider: the two calls
+    ("bf16", 151936, 151936, 3, 1.0, 24),   # base 6 bytes in
+    ("bf16", 32000, 32000, 0, 0.7, 40),
+    ("bf16", 5, 5, 1, 1.0, 40),             # shorter than a vector
+    ("fp32", 70001, 70004, 1, 0.7, 24),
+    ("fp32", 126976, 126976, 0, 1.0, 8),    # the widest fp32 row that fits
+    ("fp32", 248320, 248320, 0, 1.0, 8),    # the two calls
+]
+
+
+@pytest.mark.parametrize("dtype,vocab,ld,off,tau,n", CASES)
+def test_fused_against_oracle_and_separate_calls(dtype, vocab, ld, off, tau, n):
+    name = "spiked_bf16_8192x248320" if dtype == "bf16" else "tiny_fp32_64x2048"
+    w = W.scaled(name, n, vocab, tau=tau)
+    x = W.logits_rows(w, np.arange(n), ld=ld)
+    t, g = W.targets(w), W.grad_out(w)
+    _, xv = place_rows(x, off)
+    xd = xv[:, :vocab]
+    td, gd = torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    log(f"{dtype} V={vocab} ld={ld} offset={off} tau={tau}: fused call")
+    gbuf = like_layout(xv)[:, :vocab]
+    lp, lse, ent, grad = vwc.selected_logprob_fwd_bwd(
+        xd, td, gd, w.tau, want=("logprob", "lse", "entropy"), grad_logits=gbuf)
+    ref = oracle.forward(x, t, tau=w.tau, vocab=vocab)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        assert_close_scalar(_np(v), ref[k], k)
+    gref = oracle.backward(x, t, g, tau=w.tau, vocab=vocab)
+    _check_grad(grad, gref, "fused gradient")
+    # the separate backward from the same lse writes the same bits
+    gsep = vwc.selected_logprob_bwd(xd, td, lse, gd, w.tau, grad_logits=like_layout(xv)[:, :vocab])
+    assert torch.equal(_bits(grad), _bits(gsep))
+    # and the separate forward agrees with this lse to the same bound
+    slp, slse, sent = vwc.selected_logprob_fwd(xd, td, w.tau, want=("logprob", "lse", "entropy"))
+    for a, b in ((lp, slp), (lse, slse), (ent, sent)):
+        assert np.abs(_np(a).astype(np.float64) - _np(b)).max() <= 1e-4
+    # in place: the gradient replaces the logits, same bits
+    _, xv2 = place_rows(x, off)
+    xin = xv2[:, :vocab]
+    lp2, lse2, _, gin = vwc.selected_logprob_fwd_bwd(xin, td, gd, w.tau, grad_logits=xin)
+    assert gin.data_ptr() == xin.data_ptr()
+    assert torch.equal(_bits(lse2), _bits(lse)) and torch.equal(_bits(lp2), _bits(lp))
+    assert torch.equal(_bits(gin), _bits(grad))
+
+
+def test_fused_other_gradient_dtype_and_default_buffer():
+    """A gradient of another dtype takes the two calls; a fresh contiguous buffer
+    (the binding's default) keeps the rows' phase and the on-chip path."""
+    w = W.scaled("spiked_bf16_8192x248320", 16, 50257)
+    x, t, g = W.all_logits(w), W.targets(w), W.grad_out(w)
+    xd = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    td, gd = torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    gref = oracle.backward(x, t, g)
+    lp, lse, _, g32 = vwc.selected_logprob_fwd_bwd(xd, td, gd, grad_dtype=torch.float32)
+    assert g32.dtype == torch.float32
+    # lse is an fp32 input of the backward, so p carries its rounding: 1e-6 absolute holds
+    assert np.abs(_np(g32).astype(np.float64) - gref).max() <= 1e-6
+    _, _, _, gb = vwc.selected_logprob_fwd_bwd(xd, td, gd)
+    assert_bf16_grad(grad_bits(gb), gref, "default buffer", oracle)
+    assert_close_scalar(_np(lp), oracle.forward(x, t)["logprob"], "logprob")
+
+
+def test_fused_full_size_sampled_rows():
+    """The default step's full shape, in the launch the bench times; sampled rows
+    against the oracle, every row against the separate calls."""
+    w = W.get("spiked_bf16_8192x248320")
+    from gpu_util import upload_workload
+    xd = upload_workload(w)
+    t, g = W.targets(w), W.grad_out(w)
+    td, gd = torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    lp, lse, ent, grad = vwc.selected_logprob_fwd_bwd(xd, td, gd,
+                                                      want=("logprob", "lse", "entropy"))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 777, 4095, 4096, 8190, 8191])
+    x = W.logits_rows(w, rows)
+    ref = oracle.forward(x, t[rows])
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        assert_close_scalar(_np(v)[rows], ref[k], k)
+    gref = oracle.backward(x, t[rows], g[rows])
+    assert_bf16_grad(grad_bits(grad[torch.from_numpy(rows).to(DEV)]), gref, "sampled rows",
+                     oracle)
+    gsep = vwc.selected_logprob_bwd(xd, td, lse, gd)
+    assert torch.equal(_bits(grad), _bits(gsep))
+    slp, slse, _ = vwc.selected_logprob_fwd(xd, td)
+    assert np.abs(_np(slse).astype(np.float64) - _np(lse)).max() <= 1e-4
+    assert np.abs(_np(slp).astype(np.float64) - _np(lp)).max() <= 1e-4

@@ -48,6 +48,8 @@ def _load() -> ctypes.CDLL:
         "vwc_entropy": ([p, i32, i64, i64, i64, f32, p, p, p, sz, p], i32),
         "vwc_entropy_rows": ([p, i32, i64, i64, i64, p, i64, f32, p, p, p, sz, p], i32),
         "vwc_selected_logprob_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, i32, i64, p], i32),
+        "vwc_selected_logprob_fwd_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64,
+                                          p, sz, p], i32),
         "vwc_selected_logprob_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, i32,
                                            i64, i32, p], i32),
         "vwc_logprob_entropy_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64, p], i32),
@@ -245,6 +247,29 @@ def selected_logprob_bwd(logits, targets, lse, grad_logprob, temperature=1.0, gr
                                          float(temperature), _ptr(lse), _ptr(grad_logprob),
                                          _ptr(g), _dtype(g), gld, _stream(stream, logits)))
     return g
+
+
+def selected_logprob_fwd_bwd(logits, targets, grad_logprob, temperature=1.0, logprob=None,
+                             lse=None, entropy=None, want=("logprob", "lse"), grad_logits=None,
+                             grad_dtype=None, workspace=None, stream=None):
+    """Forward and backward in one call for a loss weight grad_logprob known up front;
+    returns (logprob, lse, entropy, grad_logits), None for outputs not asked for (lse is
+    always produced)."""
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets", n)
+    _f32_in(grad_logprob, n, "grad_logprob")
+    lp = _f32(n, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(n, logits, lse)
+    en = _f32(n, logits, entropy) if (entropy is not None or "entropy" in want) else None
+    g = _grad_out(logits, n, grad_logits, grad_dtype)
+    gld = _grad_rows(g, n, v)
+    ws, wsb = _workspace(n, v, logits, workspace)
+    _check(_lib.vwc_selected_logprob_fwd_bwd(_ptr(logits), _dtype(logits), n, v, ld,
+                                             _ptr(targets), float(temperature),
+                                             _ptr(grad_logprob), _ptr(lp), _ptr(ls), _ptr(en),
+                                             _ptr(g), _dtype(g), gld, _ptr(ws), wsb,
+                                             _stream(stream, logits)))
+    return lp, ls, en, g
 
 
 def selected_logprob_bwd_rows(logits, targets, row_idx, lse, grad_logprob, temperature=1.0,

@@ -166,6 +166,28 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
     return hip_status(vwc::launch_fwd(p, dt, stream), fn);
 }
 
+// The gradient buffer [grad_rows, ld_grad] of grad_dt: aligned, addressable,
+// and either exactly the logits (same pointer, dtype and row stride: each
+// element is read and then written by the same thread) or disjoint from them.
+vwc_status check_grad_buffer(const char *fn, const void *logits, int dt, int64_t n_rows,
+                             int64_t vocab, int64_t ld, const void *grad_logits, int grad_dt,
+                             int64_t ld_grad, int64_t grad_rows, bool *in_place) {
+    if (reinterpret_cast<uintptr_t>(grad_logits) % esize(grad_dt) != 0)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: grad_logits not aligned to its dtype", fn);
+    if (ld_grad > INT64_MAX / 16 / grad_rows)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: gradient tensor too large", fn);
+    *in_place = grad_logits == logits && grad_dt == dt && ld_grad == ld;
+    if (*in_place) return VWC_OK;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(logits);
+    const uintptr_t x1 = x0 + static_cast<uintptr_t>(((n_rows - 1) * ld + vocab) * esize(dt));
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_logits);
+    const uintptr_t g1 =
+        g0 + static_cast<uintptr_t>(((grad_rows - 1) * ld_grad + vocab) * esize(grad_dt));
+    if (g0 < x1 && x0 < g1)
+        return fail(VWC_ERR_INVALID_ARG, "%s: grad_logits overlaps logits", fn);
+    return VWC_OK;
+}
+
 struct KlArgs {
     const float *P, *Q, *S;
     int mode;
@@ -199,30 +221,16 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     if (grad_entropy && !entropy) return fail(VWC_ERR_INVALID_ARG, "%s: entropy is null", fn);
     if (!lse || !grad_logits)
         return fail(VWC_ERR_INVALID_ARG, "%s: null lse or grad_logits", fn);
-    if (reinterpret_cast<uintptr_t>(grad_logits) % esize(grad_dt) != 0)
-        return fail(VWC_ERR_UNSUPPORTED, "%s: grad_logits not aligned to its dtype", fn);
     const int64_t nseg = bwd_segments(vocab, dt);
     if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;  // first: bounds m for the sizes below
     const int64_t grad_rows = by_row_id ? n_rows : m;
-    if (ld_grad > INT64_MAX / 16 / grad_rows)
-        return fail(VWC_ERR_UNSUPPORTED, "%s: gradient tensor too large", fn);
-    // The gradient either replaces the logits exactly (same buffer, dtype and
-    // row stride, each row's gradient over that row: every element is read and
-    // written by the same thread) or does not overlap them at all.
-    const bool in_place = grad_logits == logits && grad_dt == dt && ld_grad == ld;
-    if (in_place) {
-        if (row_idx && !by_row_id)
-            return fail(VWC_ERR_INVALID_ARG,
-                        "%s: an in-place gradient needs gradient rows indexed by row id", fn);
-    } else {
-        const uintptr_t x0 = reinterpret_cast<uintptr_t>(logits);
-        const uintptr_t x1 = x0 + static_cast<uintptr_t>(((n_rows - 1) * ld + vocab) * esize(dt));
-        const uintptr_t g0 = reinterpret_cast<uintptr_t>(grad_logits);
-        const uintptr_t g1 =
-            g0 + static_cast<uintptr_t>(((grad_rows - 1) * ld_grad + vocab) * esize(grad_dt));
-        if (g0 < x1 && x0 < g1)
-            return fail(VWC_ERR_INVALID_ARG, "%s: grad_logits overlaps logits", fn);
-    }
+    bool in_place = false;
+    st = check_grad_buffer(fn, logits, dt, n_rows, vocab, ld, grad_logits, grad_dt, ld_grad,
+                           grad_rows, &in_place);
+    if (st != VWC_OK) return st;
+    if (in_place && row_idx && !by_row_id)
+        return fail(VWC_ERR_INVALID_ARG,
+                    "%s: an in-place gradient needs gradient rows indexed by row id", fn);
 
     vwc::BwdPlan p{};
     p.logits = logits;
@@ -341,6 +349,60 @@ vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_
     return backward_common("vwc_selected_logprob_bwd", logits, dt, n_rows, vocab, ld, targets,
                            nullptr, n_rows, temperature, lse, nullptr, grad_logprob, nullptr,
                            grad_logits, grad_dt, ld_grad, true, stream);
+}
+
+vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                        int64_t vocab, int64_t ld, const int32_t *targets,
+                                        float temperature, const float *grad_logprob,
+                                        float *logprob, float *lse, float *entropy,
+                                        void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    const char *fn = "vwc_selected_logprob_fwd_bwd";
+    vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
+    if (st != VWC_OK) return st;
+    if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
+    if (ld_grad < vocab) return fail(VWC_ERR_INVALID_ARG, "%s: ld_grad < vocab", fn);
+    if (n_rows == 0) return ok();
+    if (!targets || !grad_logprob || !lse || !grad_logits)
+        return fail(VWC_ERR_INVALID_ARG, "%s: null targets, grad_logprob, lse or grad_logits",
+                    fn);
+    const int64_t e = esize(dt);
+    bool in_place = false;
+    if (n_rows > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    st = check_grad_buffer(fn, logits, dt, n_rows, vocab, ld, grad_logits, grad_dt, ld_grad,
+                           n_rows, &in_place);
+    if (st != VWC_OK) return st;
+    // One workgroup holds a whole row on chip when it fits and the gradient
+    // rows share the logits' dtype and 16-byte phase; otherwise the forward
+    // and the backward run as their own calls (same results, one more read).
+    const bool fused = grad_dt == dt && vocab / (16 / e) <= vwc::kFusedMaxUnits &&
+                       vector_rows(logits, ld, e, grad_logits, ld_grad, e, true);
+    if (!fused) {
+        st = forward_common(fn, logits, dt, n_rows, vocab, ld, 0, targets, vwc::kTargetFull,
+                            nullptr, n_rows, temperature, logprob, lse, entropy, nullptr,
+                            workspace, workspace_bytes, stream);
+        if (st != VWC_OK) return st;
+        return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, nullptr, n_rows,
+                               temperature, lse, nullptr, grad_logprob, nullptr, grad_logits,
+                               grad_dt, ld_grad, true, stream);
+    }
+    vwc::FusedPlan p{};
+    p.logits = logits;
+    p.ld = ld;
+    p.vocab = static_cast<int32_t>(vocab);
+    p.dt = dt;
+    p.targets = targets;
+    p.m = n_rows;
+    p.tau = static_cast<double>(temperature);
+    p.c = static_cast<float>(1.44269504088896340736 / p.tau);
+    p.grad_out = grad_logprob;
+    p.logprob = logprob;
+    p.lse = lse;
+    p.entropy = entropy;
+    p.grad = grad_logits;
+    p.ld_grad = ld_grad;
+    return hip_status(vwc::launch_fused(p, stream), fn);
 }
 
 vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,

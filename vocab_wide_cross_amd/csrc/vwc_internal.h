@@ -124,6 +124,30 @@ struct BwdPlan {
                               // (else one element per unit)
 };
 
+// Forward and backward of one row in one workgroup, the row held on chip
+// between them (grad_out known before the forward).  Rows of at most
+// kFusedMaxUnits 16-byte units, the gradient in the logits' dtype with rows on
+// the same 16-byte phase (the host checks; other calls take fwd + bwd).
+constexpr int kFusedBlock = 1024;
+constexpr int kFusedLds = 9;    // units per thread staged in LDS (144 KiB)
+constexpr int kFusedReg = 22;   // units per thread held in registers
+constexpr int64_t kFusedMaxUnits = static_cast<int64_t>(kFusedLds + kFusedReg) * kFusedBlock;
+
+struct FusedPlan {
+    const void *logits;
+    int64_t ld;
+    int32_t vocab;
+    int dt;                   // logits and gradient dtype
+    const int32_t *targets;   // [m]
+    int64_t m;                // rows
+    float c;                  // log2(e) / tau rounded to float
+    double tau;
+    const float *grad_out;    // [m]
+    float *logprob, *lse, *entropy;  // [m]; lse non-null, the others nullable
+    void *grad;
+    int64_t ld_grad;
+};
+
 // The fused top-k KL backward keeps a segment's payload columns in an LDS hash
 // table of kKlSlots entries, so it takes rows of at most kKlMaxK payload
 // columns (load factor <= 1/2), and each thread's units of a segment are
@@ -210,6 +234,7 @@ hipError_t launch_fwd(const FwdPlan &p, int dt, hipStream_t stream);
 hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream);
 hipError_t launch_topk_fixup(const TopkPlan &p, hipStream_t stream);
 hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream);
+hipError_t launch_fused(const FusedPlan &p, hipStream_t stream);
 hipError_t launch_combine(const CombinePlan &p, hipStream_t stream);
 // Row-major partials ([rows][k]), one wave per row (rows with many segments).
 hipError_t launch_combine_rows(const CombinePlan &p, hipStream_t stream);

@@ -1034,6 +1034,158 @@ __global__ __launch_bounds__(kTopkBlock) void topk_fixup_kernel(TopkPlan p) {
     }
 }
 
+// ---------------------------------------------------------------- fused forward + backward
+
+// One 1024-thread workgroup per row (one per compute unit: the row fills its
+// LDS and most of its registers), the whole row kept on chip between the
+// reduction and the gradient.  Unit u = tid + k * 1024 (16 bytes from the
+// row's first 16-byte boundary) sits in LDS for k < kFusedLds (staged by
+// buffer_load ... lds) and in registers after that.  Phase 1 reads the row once
+// and reduces it (four groups of 256 threads, their partials merged in fp64 as
+// in the segmented forward); thread 0 writes logprob / lse / entropy and
+// shares the fp32 lse; phase 2 computes every gradient element from the held
+// values with the backward's own per-unit code and writes it.  Every read of
+// the row ends before the barrier that starts phase 2, so the gradient may
+// replace the logits.
+template <int DT, bool W>
+__global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
+    using Un = Unit<DT, true>;
+    using T = typename Un::T;
+    using Us = Unit<DT, false>;
+    constexpr int N = Un::N;
+    constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
+    constexpr int kGroups = kFusedBlock / kFwdBlock;
+    constexpr int kStride = kFusedBlock * 16;  // bytes between a thread's units
+    __shared__ __attribute__((aligned(16))) char stage[kFusedLds * kStride];
+    __shared__ vwc_partial group_part[kGroups];
+    __shared__ float row_lse;
+
+    const int64_t i = blockIdx.x;
+    const int32_t tid = static_cast<int32_t>(threadIdx.x);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const char *row = static_cast<const char *>(p.logits) + i * p.ld * kE;
+    char *grow = static_cast<char *>(p.grad) + i * p.ld_grad * kE;
+    const int32_t head = row_head<kE>(row, p.vocab);
+    const int32_t nunits = (p.vocab - head) / N;
+    // This thread's units: tid + k * kFusedBlock; the LDS ones (k < kFusedLds)
+    // and the register ones (k = kFusedLds + kr, kr < nreg) that lie in the row.
+    const int32_t nreg = min(max((nunits - tid - kFusedLds * kFusedBlock + kFusedBlock - 1) /
+                                     kFusedBlock, 0), kFusedReg);
+    const char *vrow = row + head * kE + tid * 16;  // this thread's unit 0
+    char *vgrow = grow + head * kE + tid * 16;
+    const float g = p.grad_out[i];
+    const int32_t t = p.targets[i];
+
+    // Phase 1: the LDS units through the DMA path (a buffer resource that ends
+    // at the row's last whole vector, so units past it read as zero: the whole
+    // offset goes in the per-lane offset, which the range check covers), then
+    // the register units, the row's edge element of this thread and the target.
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(row + head * kE), 0, nunits * 16, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < kFusedLds; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, stage + k * kStride + wave * 64 * 16, 16,
+            static_cast<uint32_t>(tid * 16 + k * kStride), 0, 0, 0);
+    T v[kFusedReg];
+#pragma unroll
+    for (int kr = 0; kr < kFusedReg; ++kr) {
+        v[kr] = T{};
+        if (kr < nreg)
+            v[kr] = Un::load(reinterpret_cast<const T *>(vrow + (kFusedLds + kr) * kStride));
+    }
+    const int32_t edge = edge_column(head, nunits * N, p.vocab, tid);
+    typename Us::T ev[1] = {typename Us::T{}};
+    if (edge >= 0) ev[0] = reinterpret_cast<const typename Us::T *>(row)[edge];
+    double tx = -INFINITY;  // the target logit (group 0's partial carries it)
+    if (tid == 0) tx = (t >= 0 && t < p.vocab) ? static_cast<double>(load_element<DT>(row, t)) : NAN;
+
+    Lane L = lane_init();
+    // Fold the register units in short chunks (few unpacked values live at a
+    // time while every unit stays held for phase 2).
+    constexpr int kChunk = 2;
+    static_assert(kFusedReg % kChunk == 0, "whole chunks of register units");
+#pragma unroll
+    for (int k0 = 0; k0 < kFusedReg; k0 += kChunk) {
+        const int nv = min(max(nreg - k0, 0), kChunk);
+        if (nv > 0)
+            fold_chunk<DT, true, kChunk, W>(*reinterpret_cast<const T(*)[kChunk]>(&v[k0]), nv,
+                                            p.c, L);
+    }
+    // vmcnt(0): this wave's LDS units have landed (each thread reads back only
+    // what its own wave's loads wrote; the barrier also keeps the compiler
+    // from moving the LDS reads above the wait).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+#pragma unroll 1
+    for (int k = 0; k < kFusedLds; ++k) {
+        if (tid + k * kFusedBlock >= nunits) break;
+        const T x[1] = {*reinterpret_cast<const T *>(stage + k * kStride + tid * 16)};
+        fold_chunk<DT, true, 1, W>(x, 1, p.c, L);
+    }
+    if (edge >= 0) fold_chunk<DT, false, 1, W>(ev, 1, p.c, L);
+
+    const int grp = tid / kFwdBlock;
+    const Lane B = block_reduce<kGroups>(L, grp);
+    if ((tid & (kFwdBlock - 1)) == 0) {
+        const P64 part = to_partial(B, p.c, grp == 0 ? tx : -INFINITY);
+        group_part[grp] = vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
+                                      static_cast<float>(part.t), static_cast<float>(part.w)};
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const Merged mg = merge_partials(
+            [&](int q) {
+                const vwc_partial a = group_part[q];
+                return P64{a.m, a.s, a.t, a.w};
+            },
+            kGroups, p.tau);
+        write_final(mg, p.tau, i, p.logprob, p.lse, W ? p.entropy : nullptr);
+        row_lse = static_cast<float>(mg.M / p.tau + log(mg.S));  // the value lse[i] holds
+    }
+    __syncthreads();
+
+    // Phase 2: the gradient, as the backward computes it from the saved fp32 lse.
+    RowGrad R;
+    R.c = p.c;
+    R.tau = p.tau;
+    R.gt = static_cast<double>(g) / p.tau;
+    R.gs = static_cast<float>(-R.gt);
+    R.lse = static_cast<double>(row_lse);
+    R.B = static_cast<float>(R.lse * kLog2e);
+    R.hs = 0.0;
+    R.H = 0.0;
+    R.a = 0.f;
+    R.b = 0.f;
+    R.t = t;
+    const bool zero = g == 0.f;  // a row without loss: +0.0, nothing computed
+    auto emit = [&](const T &x, int32_t u, char *dst) {
+        float o[N];
+        if (zero) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) o[k] = 0.f;
+        } else {
+            unit_grad<DT, true, false>(x, head + u * N, R, o);
+        }
+        GradStore<DT, N>::store(dst, o);
+    };
+#pragma unroll
+    for (int kr = 0; kr < kFusedReg; ++kr)
+        if (kr < nreg)
+            emit(v[kr], tid + (kFusedLds + kr) * kFusedBlock, vgrow + (kFusedLds + kr) * kStride);
+#pragma unroll 1
+    for (int k = 0; k < kFusedLds; ++k) {
+        const int32_t u = tid + k * kFusedBlock;
+        if (u >= nunits) break;
+        emit(*reinterpret_cast<const T *>(stage + k * kStride + tid * 16), u, vgrow + k * kStride);
+    }
+    if (edge >= 0) {
+        float o[1] = {0.f};
+        if (!zero) unit_grad<DT, false, false>(ev[0], edge, R, o);
+        GradStore<DT, 1>::store(grow + static_cast<int64_t>(edge) * kE, o);
+    }
+}
+
 // ---------------------------------------------------------------- mask -> index
 
 constexpr int kScanBlock = 1024;
@@ -1173,6 +1325,23 @@ hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream) {
                                  : launch_bwd_dt<VWC_BF16, VWC_FP32>(p, stream);
     return p.gdt == VWC_BF16 ? launch_bwd_dt<VWC_FP32, VWC_BF16>(p, stream)
                              : launch_bwd_dt<VWC_FP32, VWC_FP32>(p, stream);
+}
+
+hipError_t launch_fused(const FusedPlan &p, hipStream_t stream) {
+    const dim3 grid(static_cast<uint32_t>(p.m)), block(kFusedBlock);
+    const bool w = p.entropy != nullptr;
+    if (p.dt == VWC_BF16) {
+        if (w)
+            hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, false>), grid, block, 0, stream, p);
+    } else {
+        if (w)
+            hipLaunchKernelGGL((fused_row_kernel<VWC_FP32, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fused_row_kernel<VWC_FP32, false>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_fwd(const TopkPlan &p, hipStream_t stream) {

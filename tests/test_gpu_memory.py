@@ -85,6 +85,13 @@ def test_inplace_backward_allocates_nothing(inputs):
     assert grew <= SLACK
 
 
+def test_one_call_forward_backward_allocates_only_its_outputs(inputs):
+    logits, targets, grad_out = inputs
+    grew, outs = _peak_growth(lambda: vwc.selected_logprob_fwd_bwd(logits, targets, grad_out))
+    log(f"fwd+bwd in one call: grew {grew} B")
+    assert grew <= _bytes(*outs) + vwc.workspace_bytes(N, V, torch.bfloat16) + SLACK
+
+
 def test_entropy_gradient_allocates_only_the_gradient(inputs):
     logits, targets, grad_out = inputs
     _, lse, ent = vwc.selected_logprob_fwd(logits, targets, want=("lse", "entropy"))

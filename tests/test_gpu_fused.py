@@ -127,3 +127,35 @@ def test_fused_full_size_sampled_rows():
     slp, slse, _ = vwc.selected_logprob_fwd(xd, td)
     assert np.abs(_np(slse).astype(np.float64) - _np(lse)).max() <= 1e-4
     assert np.abs(_np(slp).astype(np.float64) - _np(lp)).max() <= 1e-4
+
+
+def test_fused_special_values():
+    """-inf logits (masked entries, whole leading stretches of them), a NaN
+    logit, an out-of-range target: the one call agrees with the two calls."""
+    w = W.scaled("tiny_fp32_64x2048", 16, 3001)
+    x, t, g = W.all_logits(w), W.targets(w), W.grad_out(w)
+    rng = np.random.default_rng(5)
+    mask = rng.random(x.shape) < 0.3
+    mask[:, :300] = True
+    mask[np.arange(16), t] = False
+    x = x.copy()
+    x[mask] = -np.inf
+    x[7, 2000] = np.nan
+    t = t.copy()
+    t[9] = 3001  # outside the row: NaN logprob, as in the forward
+    xd = torch.from_numpy(x).to(DEV)
+    td, gd = torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    lp, lse, ent, grad = vwc.selected_logprob_fwd_bwd(xd, td, gd,
+                                                      want=("logprob", "lse", "entropy"))
+    slp, slse, sent = vwc.selected_logprob_fwd(xd, td, want=("logprob", "lse", "entropy"))
+    for a, b in ((lp, slp), (lse, slse), (ent, sent)):
+        a, b = _np(a).astype(np.float64), _np(b).astype(np.float64)
+        assert np.array_equal(np.isnan(a), np.isnan(b))
+        ok = ~np.isnan(a)
+        assert np.abs(a[ok] - b[ok]).max() <= 1e-4
+    assert np.isnan(_np(lp)[7]) and np.isnan(_np(lp)[9]) and np.isfinite(_np(lse)[9])
+    gsep = vwc.selected_logprob_bwd(xd, td, lse, gd)
+    assert torch.equal(_bits(grad), _bits(gsep))
+    rows = np.array([r for r in range(16) if r not in (7, 9)])
+    gref = oracle.backward(x[rows], t[rows], g[rows])
+    assert np.abs(_np(grad)[rows].astype(np.float64) - gref).max() <= 1e-6

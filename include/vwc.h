@@ -222,6 +222,27 @@ vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_
                                         hipStream_t stream);
 
 /*
+ * The same over the row set row_idx[0..m) ([D] maintainer comment: compute on
+ * the loss-mask rows only): grad_logprob, logprob, lse and entropy are compact
+ * float[m]; targets are indexed by row id; layout places the gradient as in
+ * vwc_selected_logprob_bwd_rows (VWC_GRAD_SCATTER: rows row_idx[i] of
+ * [n_rows, ld_grad], other rows untouched, duplicate ids race; in place needs
+ * scatter and distinct ids).  Row ids outside [0, n_rows) give NaN outputs and
+ * no gradient.  A compact gradient keeps the on-chip path only when every row
+ * has the same 16-byte phase as its gradient row (strides of whole 16-byte
+ * multiples); otherwise the two `_rows` calls run.
+ */
+vwc_status vwc_selected_logprob_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                             int64_t vocab, int64_t ld, const int32_t *targets,
+                                             const int32_t *row_idx, int64_t m,
+                                             float temperature, const float *grad_logprob,
+                                             float *logprob, float *lse, float *entropy,
+                                             void *grad_logits, vwc_dtype grad_dt,
+                                             int64_t ld_grad, vwc_grad_layout layout,
+                                             void *workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+
+/*
  * Backward over the compact row set row_idx[0..m).  lse and grad_logprob are
  * float[m] (compact, as the `_rows` forward writes them).  layout selects
  * where gradient row i goes: VWC_GRAD_COMPACT -> row i of [m, ld_grad];

@@ -159,3 +159,47 @@ def test_fused_special_values():
     rows = np.array([r for r in range(16) if r not in (7, 9)])
     gref = oracle.backward(x[rows], t[rows], g[rows])
     assert np.abs(_np(grad)[rows].astype(np.float64) - gref).max() <= 1e-6
+
+
+@pytest.mark.parametrize("dtype,vocab,ld,off", [("bf16", 248320, 248320, 0),
+                                                ("bf16", 20011, 20011, 0),
+                                                ("fp32", 7001, 7004, 1)])
+def test_fused_row_sets(dtype, vocab, ld, off):
+    """Compact and scatter gradients over a row list (with a bad id), against the
+    oracle and, bit for bit, against the separate `_rows` backward from the same lse."""
+    name = "spiked_bf16_8192x248320" if dtype == "bf16" else "tiny_fp32_64x2048"
+    n = 24
+    w = W.scaled(name, n, vocab)
+    x = W.logits_rows(w, np.arange(n), ld=ld)
+    t = W.targets(w)
+    _, xv = place_rows(x, off)
+    xd = xv[:, :vocab]
+    td = torch.from_numpy(t).to(DEV)
+    rows = np.array([5, 0, 23, 11, 17, 2, 8], dtype=np.int32)
+    gr = W.grad_out(W.scaled(name, rows.size, vocab))
+    gr[1] = 0.0
+    idx, grd = torch.from_numpy(rows).to(DEV), torch.from_numpy(gr).to(DEV)
+    ref = oracle.forward(x, t, rows=rows, vocab=vocab)
+    gref = oracle.backward(x, t, gr, rows=rows, vocab=vocab)
+    for layout in (vwc.VWC_GRAD_SCATTER, vwc.VWC_GRAD_COMPACT):
+        gbuf = like_layout(xv)[:, :vocab] if layout == vwc.VWC_GRAD_SCATTER else None
+        lp, lse, ent, grad = vwc.selected_logprob_fwd_bwd_rows(
+            xd, td, idx, grd, want=("logprob", "lse", "entropy"), grad_logits=gbuf,
+            layout=layout)
+        for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+            assert_close_scalar(_np(v), ref[k], k)
+        got = grad[idx.long()] if layout == vwc.VWC_GRAD_SCATTER else grad
+        _check_grad(got, gref, f"rows, layout {layout}")
+        sep = vwc.selected_logprob_bwd_rows(
+            xd, td, idx, lse, grd, layout=layout,
+            grad_logits=like_layout(xv)[:, :vocab] if layout == vwc.VWC_GRAD_SCATTER else None)
+        assert torch.equal(_bits(grad), _bits(sep))
+        if layout == vwc.VWC_GRAD_SCATTER:
+            others = torch.from_numpy(np.setdiff1d(np.arange(n), rows)).to(DEV).long()
+            assert torch.count_nonzero(grad[others]) == 0
+    # a row id outside the tensor: NaN outputs, and its gradient row stays untouched
+    bad = torch.tensor([3, n + 4], dtype=torch.int32, device=DEV)
+    gb = torch.full((2, vocab), 7.0, dtype=xd.dtype, device=DEV)
+    lp, lse, _, gb = vwc.selected_logprob_fwd_bwd_rows(xd, td, bad, grd[:2], grad_logits=gb)
+    assert np.isnan(_np(lp)[1]) and np.isnan(_np(lse)[1]) and np.isfinite(_np(lse)[0])
+    assert torch.all(gb[1] == 7.0)

@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
         "vwc_selected_logprob_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, i32, i64, p], i32),
         "vwc_selected_logprob_fwd_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64,
                                           p, sz, p], i32),
+        "vwc_selected_logprob_fwd_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, p,
+                                               i32, i64, i32, p, sz, p], i32),
         "vwc_selected_logprob_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, i32,
                                            i64, i32, p], i32),
         "vwc_logprob_entropy_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64, p], i32),
@@ -270,6 +272,37 @@ def selected_logprob_fwd_bwd(logits, targets, grad_logprob, temperature=1.0, log
                                              _ptr(g), _dtype(g), gld, _ptr(ws), wsb,
                                              _stream(stream, logits)))
     return lp, ls, en, g
+
+
+def selected_logprob_fwd_bwd_rows(logits, targets, row_idx, grad_logprob, temperature=1.0,
+                                  logprob=None, lse=None, entropy=None, want=("logprob", "lse"),
+                                  grad_logits=None, grad_dtype=None, layout=VWC_GRAD_COMPACT,
+                                  workspace=None, stream=None):
+    """The one-call forward + backward over a row set; outputs and grad_logprob compact [m];
+    returns (logprob, lse, entropy, grad_logits)."""
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets", n)
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    _f32_in(grad_logprob, m, "grad_logprob")
+    lp = _f32(m, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(m, logits, lse)
+    en = _f32(m, logits, entropy) if (entropy is not None or "entropy" in want) else None
+    rows = m if layout == VWC_GRAD_COMPACT else n
+    if grad_logits is None:
+        grad_logits = _grad_out(logits, rows, None, grad_dtype)
+        if layout == VWC_GRAD_SCATTER:
+            grad_logits.zero_()
+    gld = _grad_rows(grad_logits, rows, v)
+    ws, wsb = _workspace(m, v, logits, workspace)
+    _check(_lib.vwc_selected_logprob_fwd_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
+                                                  _ptr(targets), _ptr(row_idx), m,
+                                                  float(temperature), _ptr(grad_logprob),
+                                                  _ptr(lp), _ptr(ls), _ptr(en),
+                                                  _ptr(grad_logits), _dtype(grad_logits), gld,
+                                                  layout, _ptr(ws), wsb,
+                                                  _stream(stream, logits)))
+    return lp, ls, en, grad_logits
 
 
 def selected_logprob_bwd_rows(logits, targets, row_idx, lse, grad_logprob, temperature=1.0,

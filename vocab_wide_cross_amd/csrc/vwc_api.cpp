@@ -351,41 +351,51 @@ vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_
                            grad_logits, grad_dt, ld_grad, true, stream);
 }
 
-vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
-                                        int64_t vocab, int64_t ld, const int32_t *targets,
-                                        float temperature, const float *grad_logprob,
-                                        float *logprob, float *lse, float *entropy,
-                                        void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
-                                        void *workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
-    const char *fn = "vwc_selected_logprob_fwd_bwd";
+// Shared body of the one-call forward + backward, dense (row_idx null) or over
+// a row set (outputs and grad_logprob compact [m]; the gradient row is the row
+// id with by_row_id, else the output index).
+static vwc_status fwd_bwd_common(const char *fn, const void *logits, int dt, int64_t n_rows,
+                                 int64_t vocab, int64_t ld, const int32_t *targets,
+                                 const int32_t *row_idx, int64_t m, float temperature,
+                                 const float *grad_logprob, float *logprob, float *lse,
+                                 float *entropy, void *grad_logits, int grad_dt, int64_t ld_grad,
+                                 bool by_row_id, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
     if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
     if (ld_grad < vocab) return fail(VWC_ERR_INVALID_ARG, "%s: ld_grad < vocab", fn);
-    if (n_rows == 0) return ok();
+    if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
+    if (m == 0) return ok();
+    if (!row_idx && m != n_rows)
+        return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
+    if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
     if (!targets || !grad_logprob || !lse || !grad_logits)
         return fail(VWC_ERR_INVALID_ARG, "%s: null targets, grad_logprob, lse or grad_logits",
                     fn);
+    if (m > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
     const int64_t e = esize(dt);
     bool in_place = false;
-    if (n_rows > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
     st = check_grad_buffer(fn, logits, dt, n_rows, vocab, ld, grad_logits, grad_dt, ld_grad,
-                           n_rows, &in_place);
+                           by_row_id ? n_rows : m, &in_place);
     if (st != VWC_OK) return st;
-    // One workgroup holds a whole row on chip when it fits and the gradient
-    // rows share the logits' dtype and 16-byte phase; otherwise the forward
-    // and the backward run as their own calls (same results, one more read).
+    if (in_place && row_idx && !by_row_id)
+        return fail(VWC_ERR_INVALID_ARG,
+                    "%s: an in-place gradient needs gradient rows indexed by row id", fn);
+    // One workgroup holds a whole row on chip when it fits and each gradient
+    // row shares its logits row's dtype and 16-byte phase; otherwise the
+    // forward and the backward run as their own calls (same results, one more
+    // read of the rows).
     const bool fused = grad_dt == dt && vocab / (16 / e) <= vwc::kFusedMaxUnits &&
-                       vector_rows(logits, ld, e, grad_logits, ld_grad, e, true);
+                       vector_rows(logits, ld, e, grad_logits, ld_grad, e, !row_idx || by_row_id);
     if (!fused) {
         st = forward_common(fn, logits, dt, n_rows, vocab, ld, 0, targets, vwc::kTargetFull,
-                            nullptr, n_rows, temperature, logprob, lse, entropy, nullptr,
-                            workspace, workspace_bytes, stream);
+                            row_idx, m, temperature, logprob, lse, entropy, nullptr, workspace,
+                            workspace_bytes, stream);
         if (st != VWC_OK) return st;
-        return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, nullptr, n_rows,
+        return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m,
                                temperature, lse, nullptr, grad_logprob, nullptr, grad_logits,
-                               grad_dt, ld_grad, true, stream);
+                               grad_dt, ld_grad, by_row_id, stream);
     }
     vwc::FusedPlan p{};
     p.logits = logits;
@@ -393,7 +403,9 @@ vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_
     p.vocab = static_cast<int32_t>(vocab);
     p.dt = dt;
     p.targets = targets;
-    p.m = n_rows;
+    p.row_idx = row_idx;
+    p.n_rows = n_rows;
+    p.m = m;
     p.tau = static_cast<double>(temperature);
     p.c = static_cast<float>(1.44269504088896340736 / p.tau);
     p.grad_out = grad_logprob;
@@ -402,7 +414,39 @@ vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_
     p.entropy = entropy;
     p.grad = grad_logits;
     p.ld_grad = ld_grad;
+    p.grad_by_row_id = by_row_id;
     return hip_status(vwc::launch_fused(p, stream), fn);
+}
+
+vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                        int64_t vocab, int64_t ld, const int32_t *targets,
+                                        float temperature, const float *grad_logprob,
+                                        float *logprob, float *lse, float *entropy,
+                                        void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    return fwd_bwd_common("vwc_selected_logprob_fwd_bwd", logits, dt, n_rows, vocab, ld, targets,
+                          nullptr, n_rows, temperature, grad_logprob, logprob, lse, entropy,
+                          grad_logits, grad_dt, ld_grad, true, workspace, workspace_bytes,
+                          stream);
+}
+
+vwc_status vwc_selected_logprob_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                             int64_t vocab, int64_t ld, const int32_t *targets,
+                                             const int32_t *row_idx, int64_t m,
+                                             float temperature, const float *grad_logprob,
+                                             float *logprob, float *lse, float *entropy,
+                                             void *grad_logits, vwc_dtype grad_dt,
+                                             int64_t ld_grad, vwc_grad_layout layout,
+                                             void *workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+    const char *fn = "vwc_selected_logprob_fwd_bwd_rows";
+    if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    return fwd_bwd_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
+                          grad_logprob, logprob, lse, entropy, grad_logits, grad_dt, ld_grad,
+                          layout == VWC_GRAD_SCATTER, workspace, workspace_bytes, stream);
 }
 
 vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,

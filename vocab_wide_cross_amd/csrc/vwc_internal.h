@@ -138,14 +138,17 @@ struct FusedPlan {
     int64_t ld;
     int32_t vocab;
     int dt;                   // logits and gradient dtype
-    const int32_t *targets;   // [m]
-    int64_t m;                // rows
+    const int32_t *targets;   // by row id
+    const int32_t *row_idx;   // null: output i is row i
+    int64_t n_rows;           // rows of the tensor (row ids are checked against it)
+    int64_t m;                // output rows
     float c;                  // log2(e) / tau rounded to float
     double tau;
     const float *grad_out;    // [m]
     float *logprob, *lse, *entropy;  // [m]; lse non-null, the others nullable
     void *grad;
     int64_t ld_grad;
+    bool grad_by_row_id;      // gradient row = row id (dense, scatter) or output index
 };
 
 // The fused top-k KL backward keeps a segment's payload columns in an LDS hash

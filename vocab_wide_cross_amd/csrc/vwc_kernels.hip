@@ -1060,11 +1060,20 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     __shared__ vwc_partial group_part[kGroups];
     __shared__ float row_lse;
 
-    const int64_t i = blockIdx.x;
+    const int64_t i = blockIdx.x;  // output row
     const int32_t tid = static_cast<int32_t>(threadIdx.x);
+    const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
+    if (r < 0 || r >= p.n_rows) {  // row id outside the tensor: NaN outputs, nothing written
+        if (tid == 0) {
+            if (p.logprob) p.logprob[i] = NAN;
+            p.lse[i] = NAN;
+            if (W && p.entropy) p.entropy[i] = NAN;
+        }
+        return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const char *row = static_cast<const char *>(p.logits) + i * p.ld * kE;
-    char *grow = static_cast<char *>(p.grad) + i * p.ld_grad * kE;
+    const char *row = static_cast<const char *>(p.logits) + r * p.ld * kE;
+    char *grow = static_cast<char *>(p.grad) + (p.grad_by_row_id ? r : i) * p.ld_grad * kE;
     const int32_t head = row_head<kE>(row, p.vocab);
     const int32_t nunits = (p.vocab - head) / N;
     // This thread's units: tid + k * kFusedBlock; the LDS ones (k < kFusedLds)
@@ -1074,7 +1083,7 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     const char *vrow = row + head * kE + tid * 16;  // this thread's unit 0
     char *vgrow = grow + head * kE + tid * 16;
     const float g = p.grad_out[i];
-    const int32_t t = p.targets[i];
+    const int32_t t = p.targets[r];
 
     // Phase 1: the LDS units through the DMA path (a buffer resource that ends
     // at the row's last whole vector, so units past it read as zero: the whole

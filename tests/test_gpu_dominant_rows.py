@@ -1,0 +1,180 @@
+"""GPU parity on rows where one non-target column holds nearly all the mass.
+
+With uniform targets, a confident model puts p_j -> 1 on a column that is
+usually not the target, so the backward's p_j = exp(x_j/tau - lse) multiplies
+the error of its exponent straight into the gradient.  The backward reads the
+fp32 logZ the forward saved ("[megatron] feat: add memory-efficient chunked
+top-k KL computation", "Design & Code Changes"), so an error of
+|g|/tau * p_j * |lse32 - lse| is inherent; everything the kernel adds on top
+must stay below a few fp32 roundings of p_j.
+
+Rows: a dominant non-target logit D with |D/tau| in [16, 64] (both signs), the
+rest D - tau * (margin + N(0, 1)) with margin ~ U(0, 30), so p_dominant runs
+from about 1e-3 to 1 - 1e-10.  Bars, elementwise:
+  fp32 gradient: |err| <= max(1e-6, |g|/tau * p_j * (|lse32 - lse| + 2^-21));
+  bf16 gradient: within one bf16 step of the oracle rounded to bf16;
+  entropy gradient (fp32): max(1e-6, p_j/tau * (A (|d lse| + 2^-20) + |h| |d H|))
+    with A = |g| + |h| (|log p_j| + |H| + 1), d lse / d H the forward's errors.
+Paths: the separate backward (dense, compact and scatter row sets), the one-call
+forward + backward (dense and row set, equal bit for bit to the separate
+backward from the same lse) and the entropy-gradient backward.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocab_wide_cross_amd as vwc
+import workloads as W
+from gpu_util import DEV, assert_bf16_grad, grad_bits, log, to_dev_logits
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def dominant_rows(n, vocab, tau, seed, dtype="fp32"):
+    """Logits [n, vocab], targets, the dominant column of each row, grad_out."""
+    rng = np.random.default_rng(seed)
+    tau32 = float(np.float32(tau))
+    sign = np.where(np.arange(n) % 4 == 3, -1.0, 1.0)
+    D = sign * rng.uniform(16, 64, n) * tau32
+    margin = rng.uniform(0, 30, n)
+    margin[:4] = [0.0, 2.0, 25.0, 30.0]
+    x = (D - tau32 * margin)[:, None] + tau32 * rng.standard_normal((n, vocab))
+    dom = rng.integers(0, vocab, n)
+    x[np.arange(n), dom] = D
+    t = rng.integers(0, vocab, n)
+    t = np.where(t == dom, (t + 1) % vocab, t).astype(np.int32)
+    g = rng.uniform(-1, 1, n).astype(np.float32)
+    g[5] = 0.0
+    x32 = x.astype(np.float32)
+    if dtype == "bf16":
+        return W.float32_to_bf16_bits(x32), t, dom, g
+    return x32, t, dom, g
+
+
+def _as_f64(x):
+    return (W.bf16_bits_to_float32(x) if x.dtype == np.uint16 else x).astype(np.float64)
+
+
+def fp32_grad_bar(x, t, g, tau, lse_gpu, rows=None):
+    """max(1e-6, |g|/tau p_j (|lse32 - lse| + 2^-21)) per element."""
+    xr = x if rows is None else x[rows]
+    tr = t if rows is None else t[rows]
+    tau32 = float(np.float32(tau))
+    f = oracle.forward(xr, tr, tau=tau)
+    p = np.exp(_as_f64(xr) / tau32 - f["lse"][:, None])
+    d_lse = np.abs(lse_gpu.astype(np.float64) - f["lse"])
+    bound = np.abs(g.astype(np.float64))[:, None] / tau32 * p * (d_lse[:, None] + 2.0 ** -21)
+    return np.maximum(1e-6, bound), p
+
+
+def check_fp32(got, ref, bar, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = err > bar
+    assert not bad.any(), (f"{what}: {bad.sum()} elements beyond the bar, worst "
+                           f"{np.max(err[bad] / bar[bad]):.3g}x")
+    return float(err.max())
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_dense_fp32_logits_fp32_grad(tau):
+    x, t, dom, g = dominant_rows(48, 4099, tau, 31)
+    xd, td, gd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    _, lse, _ = vwc.selected_logprob_fwd(xd, td, tau)
+    got = _np(vwc.selected_logprob_bwd(xd, td, lse, gd, tau))
+    ref = oracle.backward(x, t, g, tau=tau)
+    bar, p = fp32_grad_bar(x, t, g, tau, _np(lse))
+    err = check_fp32(got, ref, bar, f"fp32 dense tau={tau}")
+    assert p[np.arange(48), dom].max() > 1 - 1e-8
+    log(f"dominant rows fp32 tau={tau}: max err {err:.3g}")
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_dense_bf16_logits_both_grad_dtypes(tau):
+    """bf16 rows of 151936 columns (three forward segments, two backward segments)."""
+    x, t, dom, g = dominant_rows(24, 151936, tau, 32, "bf16")
+    xd, td, gd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    _, lse, _ = vwc.selected_logprob_fwd(xd, td, tau)
+    ref = oracle.backward(x, t, g, tau=tau)
+    g32 = _np(vwc.selected_logprob_bwd(xd, td, lse, gd, tau, grad_dtype=torch.float32))
+    bar, _ = fp32_grad_bar(x, t, g, tau, _np(lse))
+    check_fp32(g32, ref, bar, f"bf16 -> fp32 grad tau={tau}")
+    gb = vwc.selected_logprob_bwd(xd, td, lse, gd, tau)
+    assert_bf16_grad(grad_bits(gb), ref, f"bf16 grad tau={tau}", oracle)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_row_set_compact_and_scatter(tau):
+    x, t, _, g = dominant_rows(40, 20011, tau, 33, "bf16")
+    idx = np.array([0, 1, 2, 3, 6, 9, 10, 17, 22, 23, 31, 38], dtype=np.int32)
+    xd, td = to_dev_logits(x), torch.from_numpy(t).to(DEV)
+    idd = torch.from_numpy(idx).to(DEV)
+    gc = torch.from_numpy(g[idx]).to(DEV)
+    _, lse, _ = vwc.selected_logprob_fwd_rows(xd, td, idd, tau)
+    ref = oracle.backward(x, t, g[idx], tau=tau, rows=idx)
+    bar, _ = fp32_grad_bar(x, t, g[idx], tau, _np(lse), rows=idx)
+    comp = vwc.selected_logprob_bwd_rows(xd, td, idd, lse, gc, tau, grad_dtype=torch.float32)
+    check_fp32(_np(comp), ref, bar, "compact fp32")
+    scat = torch.zeros((40, 20011), dtype=torch.float32, device=DEV)
+    vwc.selected_logprob_bwd_rows(xd, td, idd, lse, gc, tau, grad_logits=scat,
+                                  layout=vwc.VWC_GRAD_SCATTER)
+    assert torch.equal(scat[idd.long()], comp)
+    compb = vwc.selected_logprob_bwd_rows(xd, td, idd, lse, gc, tau)
+    assert_bf16_grad(grad_bits(compb), ref, "compact bf16", oracle)
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+@pytest.mark.parametrize("dtype,vocab", [("fp32", 4099), ("bf16", 151936)])
+def test_one_call_forward_backward(tau, dtype, vocab):
+    """The one-call kernel: its gradient equals the separate backward's from the same
+    lse bit for bit, and meets the bars above."""
+    n = 24
+    x, t, _, g = dominant_rows(n, vocab, tau, 34, dtype)
+    xd, td, gd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    _, lse, _, grad = vwc.selected_logprob_fwd_bwd(xd, td, gd, tau)
+    sep = vwc.selected_logprob_bwd(xd, td, lse, gd, tau)
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(grad.view(bits), sep.view(bits))
+    ref = oracle.backward(x, t, g, tau=tau)
+    if dtype == "fp32":
+        bar, _ = fp32_grad_bar(x, t, g, tau, _np(lse))
+        check_fp32(_np(grad), ref, bar, f"one-call fp32 tau={tau}")
+    else:
+        assert_bf16_grad(grad_bits(grad), ref, f"one-call bf16 tau={tau}", oracle)
+    # Over a row set, compact and scatter.
+    idx = np.arange(1, n, 3, dtype=np.int32)
+    idd = torch.from_numpy(idx).to(DEV)
+    gc = torch.from_numpy(g[idx]).to(DEV)
+    _, lse_r, _, comp = vwc.selected_logprob_fwd_bwd_rows(xd, td, idd, gc, tau)
+    assert torch.equal(lse_r, lse[idd.long()])
+    assert torch.equal(comp.view(bits), grad[idd.long()].view(bits))
+    scat = torch.zeros_like(grad)
+    vwc.selected_logprob_fwd_bwd_rows(xd, td, idd, gc, tau, grad_logits=scat,
+                                      layout=vwc.VWC_GRAD_SCATTER)
+    assert torch.equal(scat[idd.long()].view(bits), comp.view(bits))
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_entropy_gradient_fp32(tau):
+    x, t, _, g = dominant_rows(48, 4099, tau, 35)
+    rng = np.random.default_rng(36)
+    h = rng.uniform(-1, 1, 48).astype(np.float32)
+    h[7] = 0.0
+    xd, td = to_dev_logits(x), torch.from_numpy(t).to(DEV)
+    gd, hd = torch.from_numpy(g).to(DEV), torch.from_numpy(h).to(DEV)
+    _, lse, ent = vwc.selected_logprob_fwd(xd, td, tau, want=("lse", "entropy"))
+    got = _np(vwc.logprob_entropy_bwd(xd, td, lse, ent, gd, hd, tau))
+    ref = oracle.backward_entropy(x, t, g, h, tau=tau)
+    f = oracle.forward(x, t, tau=tau)
+    tau32 = float(np.float32(tau))
+    p = np.exp(x.astype(np.float64) / tau32 - f["lse"][:, None])
+    d_lse = np.abs(_np(lse).astype(np.float64) - f["lse"])[:, None]
+    d_h = np.abs(_np(ent).astype(np.float64) - f["entropy"])[:, None]
+    ha = np.abs(h.astype(np.float64))[:, None]
+    A = np.abs(g.astype(np.float64))[:, None] + ha * (np.abs(np.log(p)) + f["entropy"][:, None] + 1)
+    bar = np.maximum(1e-6, p / tau32 * (A * (d_lse + 2.0 ** -20) + ha * d_h))
+    check_fp32(got, ref, bar, f"entropy grad fp32 tau={tau}")

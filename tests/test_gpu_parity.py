@@ -64,8 +64,12 @@ def test_bf16_forward_backward_shapes(vocab):
         assert_close_scalar(_np(v), ref[k], f"{k} V={vocab}")
     gref = oracle.backward(x, t, g)
     if vocab == 1:
-        # The gradient is exactly 0; the backward sees it through the fp32 lse
-        # the forward saved, so it can be off by |g| times lse's rounding.
+        # The exact gradient is 0 and lse = x / tau.  The forward folds the one
+        # term as 2^r with r = x c - fl(x c), the rounding residual of its shift,
+        # through the hardware's approximate exp2 (about 1 ulp), and undoes r in
+        # fp64; so the sum is 1 + e with |e| <= about 2^-22 and the saved lse may
+        # sit up to 2|e| from x / tau.  The backward's -expm1(x/tau - lse) turns
+        # that into |grad| <= |g| / tau * 2^-21.
         gg = _np(grad.float())[:, 0].astype(np.float64)
         assert np.all(np.abs(gg) <= np.abs(g) * 2.0 ** -20)
     else:

@@ -243,7 +243,9 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     p.n_rows = n_rows;
     p.m = m;
     p.tau = static_cast<double>(temperature);
-    p.c = static_cast<float>(1.44269504088896340736 / p.tau);
+    const vwc::ScaleSplit cs = vwc::split_scale(p.tau);
+    p.c_hi = cs.hi;
+    p.c_lo = cs.lo;
     p.lse = lse;
     p.grad_out = grad_logprob;
     p.entropy = entropy;
@@ -408,6 +410,9 @@ static vwc_status fwd_bwd_common(const char *fn, const void *logits, int dt, int
     p.m = m;
     p.tau = static_cast<double>(temperature);
     p.c = static_cast<float>(1.44269504088896340736 / p.tau);
+    const vwc::ScaleSplit cs = vwc::split_scale(p.tau);
+    p.gc_hi = cs.hi;
+    p.gc_lo = cs.lo;
     p.grad_out = grad_logprob;
     p.logprob = logprob;
     p.lse = lse;

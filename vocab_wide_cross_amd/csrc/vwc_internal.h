@@ -1,6 +1,7 @@
 // vwc_internal.h -- launch plans shared by the C-ABI layer and the kernels.
 #pragma once
 
+#include <math.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -97,7 +98,7 @@ struct BwdPlan {
     const int32_t *row_idx;   // null: dense
     int64_t n_rows;
     int64_t m;
-    float c;
+    float c_hi, c_lo;         // log2(e) / tau as a float pair (split_scale)
     double tau;
     const float *lse;         // [m]
     const float *grad_out;    // [m] incoming d/d logprob, or null (0)
@@ -124,6 +125,22 @@ struct BwdPlan {
                               // (else one element per unit)
 };
 
+// log2(e) / tau as a float pair for the backward's exponent u = x c - B:
+// hi is rounded down and lo = c - hi > 0 in float, so x hi + x lo carries c to
+// about 2^-48 relative, and a -inf logit gives -inf in both products (never
+// -inf + inf).  A lo of exactly 0 becomes a negligible positive value.
+struct ScaleSplit {
+    float hi, lo;
+};
+inline ScaleSplit split_scale(double tau) {
+    const double c = 1.44269504088896340736 / tau;
+    float hi = static_cast<float>(c);
+    if (static_cast<double>(hi) > c) hi = nextafterf(hi, 0.f);
+    float lo = static_cast<float>(c - static_cast<double>(hi));
+    if (!(lo > 0.f)) lo = hi * 0x1p-60f;
+    return ScaleSplit{hi, lo};
+}
+
 // Forward and backward of one row in one workgroup, the row held on chip
 // between them (grad_out known before the forward).  Rows of at most
 // kFusedMaxUnits 16-byte units, the gradient in the logits' dtype with rows on
@@ -142,7 +159,8 @@ struct FusedPlan {
     const int32_t *row_idx;   // null: output i is row i
     int64_t n_rows;           // rows of the tensor (row ids are checked against it)
     int64_t m;                // output rows
-    float c;                  // log2(e) / tau rounded to float
+    float c;                  // log2(e) / tau rounded to float (the reduction)
+    float gc_hi, gc_lo;       // log2(e) / tau as a float pair (the gradient; split_scale)
     double tau;
     const float *grad_out;    // [m]
     float *logprob, *lse, *entropy;  // [m]; lse non-null, the others nullable

@@ -758,10 +758,10 @@ __device__ __forceinline__ void kl_patch(const KlSlot *tab, int32_t key, float (
 
 // Uniform per-row constants of the backward.
 struct RowGrad {
-    float c;       // log2(e) / tau
-    float B;       // lse * log2(e), rounded to float
-    float gs;      // -g / tau
-    float a, b;    // entropy gradient: o = p * (a + b u) with u = x c - B
+    float c_hi, c_lo;  // log2(e) / tau as a float pair
+    float B;       // lse * log2(e), the float nearest to its fp64 value
+    float gs;      // 2^-B_lo times the factor of p: -g / tau (top-k KL: alpha g / tau)
+    float a, b;    // entropy gradient: o = p' (a + b u'), both times 2^-B_lo
     double gt;     // g / tau
     double hs;     // -h / tau
     double H;      // the saved entropy, widened
@@ -770,10 +770,41 @@ struct RowGrad {
     int32_t t;     // target column (-1: no logprob term)
 };
 
-// Gradient of one unit.  Logprob only: o_k = gs p_k with p_k = exp2(x_k c - B)
+// Row constants from the saved fp32 lse.  The probability is
+// p_j = 2^(x_j c - B) with c = log2(e)/tau and B = lse log2(e).  Held as single
+// floats, c and B would move the exponent by |x| ulp(c)/2 + ulp(B)/2, which is
+// several 1e-6 at |lse| of 16 to 64 and becomes the same absolute error in a
+// gradient where p_j -> 1.  So the kernel computes u' = (x c_hi - B_hi) + x c_lo
+// = x c - B + B_lo, accurate to about ulp(u'), and the factor 2^-B_lo that
+// p' = 2^u' carries in excess goes into the per-row factors, once per row in
+// fp64.  `coef` is the factor of p before that: -g/tau, or alpha g/tau.
+__device__ __forceinline__ RowGrad row_grad(float c_hi, float c_lo, double tau, float lse,
+                                            float g, float h, double H, double coef) {
+    RowGrad R;
+    R.c_hi = c_hi;
+    R.c_lo = c_lo;
+    R.tau = tau;
+    R.gt = static_cast<double>(g) / tau;
+    R.lse = static_cast<double>(lse);
+    const double B = R.lse * kLog2e;
+    R.B = static_cast<float>(B);
+    // Non-finite lse: no split (u' = x c - B as before, inf / NaN propagate).
+    const double B_lo = isfinite(R.B) ? B - static_cast<double>(R.B) : 0.0;
+    const double f = exp2(-B_lo);
+    R.hs = -static_cast<double>(h) / tau;
+    R.H = H;
+    R.gs = static_cast<float>(coef * f);
+    // o = p (a + b u) with u = u' - B_lo, a = -(g + h H)/tau, b = -h ln2/tau.
+    const double a = -R.gt + R.hs * H, b = R.hs * kLn2;
+    R.a = static_cast<float>(f * (a - b * B_lo));
+    R.b = static_cast<float>(f * b);
+    R.t = -1;
+    return R;
+}
+
+// Gradient of one unit.  Logprob only: o_k = gs p'_k with p'_k = 2^u'_k
 // (exp2f keeps denormal results).  With the entropy term (WH):
-//   o_k = p_k (-g/tau - h/tau (z_k - lse + H)) = p_k (a + b u_k),
-// u_k = x_k c - B = (z_k - lse) log2(e), a = -(g + h H)/tau, b = -h ln2/tau.
+//   o_k = p_k (-g/tau - h/tau (z_k - lse + H)) = p'_k (a + b u'_k).
 // The target column adds g/tau (1 - p_t), computed as -expm1(x_t/tau - lse) in
 // fp64 so that p_t -> 1 does not cancel.
 template <int DT, bool VEC, bool WH>
@@ -782,7 +813,8 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
     using Un = Unit<DT, VEC>;
 #pragma unroll
     for (int k = 0; k < Un::N; ++k) {
-        const float u = __builtin_fmaf(Un::get(v, k), R.c, -R.B);
+        const float x = Un::get(v, k);
+        const float u = __builtin_fmaf(x, R.c_lo, __builtin_fmaf(x, R.c_hi, -R.B));
         const float pk = exp2f(u);
         o[k] = WH ? pk * __builtin_fmaf(R.b, u, R.a) : pk * R.gs;
     }
@@ -849,19 +881,11 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         return;
     }
 
-    RowGrad R;
-    R.c = p.c;
-    R.tau = p.tau;
-    R.gt = static_cast<double>(g) / p.tau;
-    R.gs = static_cast<float>(-R.gt);
-    R.lse = static_cast<double>(p.lse[i]);
-    R.B = static_cast<float>(R.lse * kLog2e);
-    R.hs = -static_cast<double>(h) / p.tau;
-    R.H = WH ? static_cast<double>(p.entropy[i]) : 0.0;
-    R.a = static_cast<float>(-R.gt + R.hs * R.H);
-    R.b = static_cast<float>(R.hs * kLn2);
+    const double gt = static_cast<double>(g) / p.tau;
+    RowGrad R = row_grad(p.c_hi, p.c_lo, p.tau, p.lse[i], g, h,
+                         WH ? static_cast<double>(p.entropy[i]) : 0.0,
+                         kl ? gt * klc.alpha : -gt);  // top-k KL: o = q (g alpha / tau)
     R.t = (g != 0.f && !kl) ? p.targets[r] : -1;
-    if (kl) R.gs = static_cast<float>(R.gt * klc.alpha);  // o = q (g alpha / tau)
     const T *src = reinterpret_cast<const T *>(vrow);
 
     __shared__ KlSlot kl_tab[KLF ? kKlSlots : 1];
@@ -1155,17 +1179,8 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     __syncthreads();
 
     // Phase 2: the gradient, as the backward computes it from the saved fp32 lse.
-    RowGrad R;
-    R.c = p.c;
-    R.tau = p.tau;
-    R.gt = static_cast<double>(g) / p.tau;
-    R.gs = static_cast<float>(-R.gt);
-    R.lse = static_cast<double>(row_lse);
-    R.B = static_cast<float>(R.lse * kLog2e);
-    R.hs = 0.0;
-    R.H = 0.0;
-    R.a = 0.f;
-    R.b = 0.f;
+    RowGrad R = row_grad(p.gc_hi, p.gc_lo, p.tau, row_lse, g, 0.f, 0.0,
+                         -static_cast<double>(g) / p.tau);
     R.t = t;
     const bool zero = g == 0.f;  // a row without loss: +0.0, nothing computed
     auto emit = [&](const T &x, int32_t u, char *dst) {

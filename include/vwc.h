@@ -35,7 +35,8 @@
  * Conventions for every entry point:
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except
  *    where stated.  The library allocates nothing, keeps no pointer after the
- *    call returns and holds no state between calls.
+ *    call returns and holds no state between calls; the one exception is the
+ *    fixed scratch array of vwc_selected_logprob_fwd_noalloc.
  *  - Calls are asynchronous on `stream` (0 = the null stream) and never
  *    synchronize the host.  Results are ready when the stream reaches them.
  *  - Logits are row-major: element (r, j) sits at logits + (r * ld + j) * e,
@@ -146,6 +147,29 @@ vwc_status vwc_selected_logprob_fwd(const void *logits, vwc_dtype dt, int64_t n_
                                     float temperature, float *logprob, float *lse,
                                     float *entropy, void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/*
+ * vwc_selected_logprob_fwd without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Results are bit-identical to
+ * vwc_selected_logprob_fwd.  Rows whose forward needs segment partials
+ * (vwc_workspace_bytes(n_rows, vocab, dt) > 0) keep them in a device array of
+ * VWC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up on the first such call on
+ * a device, with that device current).  A call needing more returns
+ * VWC_ERR_UNSUPPORTED before any launch: at most 65536 bf16 rows of 248320
+ * columns (4 segments of 16 bytes each per row) or 32768 such fp32 rows per
+ * call.  The call allocates nothing, never calls hipMalloc/hipFree, and needs
+ * no clearing of the array (each call writes every partial it reads).  Calls
+ * that overlap on one GPU (several streams or host threads) share that array
+ * and race: serialise them.  Other arguments as vwc_selected_logprob_fwd.
+ */
+#define VWC_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+vwc_status vwc_selected_logprob_fwd_noalloc(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                            int64_t vocab, int64_t ld, const int32_t *targets,
+                                            float temperature, float *logprob, float *lse,
+                                            float *entropy, hipStream_t stream);
 
 /*
  * Forward over the compact row set row_idx[0..m) ([D] maintainer comment).

@@ -43,6 +43,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "vwc_workspace_bytes": ([i64, i64, i32], sz),
         "vwc_selected_logprob_fwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, sz, p], i32),
+        "vwc_selected_logprob_fwd_noalloc": ([p, i32, i64, i64, i64, p, f32, p, p, p, p], i32),
         "vwc_selected_logprob_fwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, sz,
                                            p], i32),
         "vwc_entropy": ([p, i32, i64, i64, i64, f32, p, p, p, sz, p], i32),
@@ -184,6 +185,21 @@ def selected_logprob_fwd(logits, targets, temperature=1.0, logprob=None, lse=Non
     _check(_lib.vwc_selected_logprob_fwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(targets),
                                          float(temperature), _ptr(lp), _ptr(ls), _ptr(en),
                                          _ptr(ws), wsb, _stream(stream, logits)))
+    return lp, ls, en
+
+
+def selected_logprob_fwd_noalloc(logits, targets, temperature=1.0, logprob=None, lse=None,
+                                 entropy=None, want=("logprob", "lse"), stream=None):
+    """selected_logprob_fwd without a workspace: the library's fixed per-GPU scratch
+    array holds the segment partials (outputs are still allocated here when None)."""
+    n, v, ld = _rows_view(logits)
+    _i32(targets, "targets", n)
+    lp = _f32(n, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(n, logits, lse) if (lse is not None or "lse" in want) else None
+    en = _f32(n, logits, entropy) if (entropy is not None or "entropy" in want) else None
+    _check(_lib.vwc_selected_logprob_fwd_noalloc(_ptr(logits), _dtype(logits), n, v, ld,
+                                                 _ptr(targets), float(temperature), _ptr(lp),
+                                                 _ptr(ls), _ptr(en), _stream(stream, logits)))
     return lp, ls, en
 
 

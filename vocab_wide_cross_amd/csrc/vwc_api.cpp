@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "vwc.h"
@@ -34,6 +36,39 @@ vwc_status ok() {
 vwc_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return ok();
     return fail(VWC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The allocation-free forward's segment partials: one array per GPU in this
+// library's code object, held until the process ends.  Host code uses the
+// per-device address from hipGetSymbolAddress, never the array's name.
+static __device__ __align__(256) unsigned char scratch[VWC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+vwc_status scratch_address(const char *fn, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(VWC_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(VWC_ERR_UNSUPPORTED, "%s: device ordinal %d beyond %d", fn, dev, kMaxDevices);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(VWC_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn,
+                            hipGetErrorString(e));
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return VWC_OK;
 }
 
 bool dtype_ok(int dt) { return dt == VWC_BF16 || dt == VWC_FP32; }
@@ -119,7 +154,8 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
                           int64_t vocab, int64_t ld, int64_t v_start, const int32_t *targets,
                           int target_mode, const int32_t *row_idx, int64_t m, float temperature,
                           float *logprob, float *lse, float *entropy, vwc_partial *partial_out,
-                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                          void *workspace, size_t workspace_bytes, hipStream_t stream,
+                          bool use_scratch = false) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
     if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
@@ -134,6 +170,21 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
 
     const int64_t nseg = segments(vocab, dt, vwc::kFwdSegBytes);
     if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;  // first: bounds m for the sizes below
+    if (use_scratch && vwc::fwd_needs_workspace(nseg)) {
+        // Every partial the merge reads is written by the same call, so the
+        // array needs no clearing.  Its address is the first HIP call.
+        const size_t need =
+            static_cast<size_t>(m) * static_cast<size_t>(nseg) * sizeof(vwc_partial);
+        if (need > VWC_NOALLOC_SCRATCH_BYTES)
+            return fail(VWC_ERR_UNSUPPORTED,
+                        "%s: %lld rows of %lld segments need %zu bytes of scratch; the "
+                        "library holds %zu per GPU (use vwc_selected_logprob_fwd with a "
+                        "workspace, or fewer rows per call)",
+                        fn, static_cast<long long>(m), static_cast<long long>(nseg), need,
+                        static_cast<size_t>(VWC_NOALLOC_SCRATCH_BYTES));
+        if ((st = scratch_address(fn, &workspace)) != VWC_OK) return st;
+        workspace_bytes = VWC_NOALLOC_SCRATCH_BYTES;
+    }
     if ((st = check_workspace(fn, m, nseg, workspace, workspace_bytes)) != VWC_OK) return st;
 
     vwc::FwdPlan p{};
@@ -306,6 +357,15 @@ vwc_status vwc_selected_logprob_fwd(const void *logits, vwc_dtype dt, int64_t n_
     return forward_common("vwc_selected_logprob_fwd", logits, dt, n_rows, vocab, ld, 0, targets,
                           vwc::kTargetFull, nullptr, n_rows, temperature, logprob, lse, entropy,
                           nullptr, workspace, workspace_bytes, stream);
+}
+
+vwc_status vwc_selected_logprob_fwd_noalloc(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                            int64_t vocab, int64_t ld, const int32_t *targets,
+                                            float temperature, float *logprob, float *lse,
+                                            float *entropy, hipStream_t stream) {
+    return forward_common("vwc_selected_logprob_fwd_noalloc", logits, dt, n_rows, vocab, ld, 0,
+                          targets, vwc::kTargetFull, nullptr, n_rows, temperature, logprob, lse,
+                          entropy, nullptr, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 vwc_status vwc_selected_logprob_fwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,

@@ -58,6 +58,18 @@ def alg_bytes(n_rows, vocab, esize, gsize, live_rows, entropy):
     return fwd, bwd
 
 
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, seconds):
     """Time the fp64 oracle (forward + gradient) over rows of the same workload:
     passes over all rows, in blocks of 128, until `seconds` of oracle time."""
@@ -90,8 +102,12 @@ def cpu_baseline(w, seconds):
         return rows_done, elapsed
 
     rows_done, elapsed = run(seconds, 128)
+    # Input bytes the oracle consumes per row: the logits row (read by the
+    # forward and again by the gradient, counted once) plus target and g.
+    row_bytes = w.vocab * w.esize + 8
     out = {"value": rows_done / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
-           "kind": "oracle",
+           "kind": "oracle", "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+           "input_gbs": rows_done * row_bytes / elapsed / 1e9,
            "sample": f"{rows_done} rows of {w.name} in order, cycling over all {w.n_rows} rows "
                      f"(fwd logprob+lse+entropy and the fp64 gradient of each row), "
                      f"{elapsed:.1f} s of oracle time"}
@@ -111,27 +127,42 @@ def single_core(run, seconds):
     return {"value_1core": done / el, "sample_1core": f"{done} rows on 1 thread, {el:.1f} s"}
 
 
-def code_digest(path):
-    """SHA-256 of a C/HIP source with its comments and whitespace removed: it changes
-    with the code, not with its comments."""
+# Sources that fix a kernel's code or launch geometry (segment sizes, block
+# shapes, the host's segment choice, the lane arithmetic).
+TRAFFIC_SOURCES = {
+    "vwc_kernels.hip": ["vwc_kernels.hip", "vwc_internal.h", "vwc_lane.h", "vwc_api.cpp"],
+    "vwc_lmhead.hip": ["vwc_lmhead.hip", "vwc_internal.h", "vwc_lane.h", "vwc_api.cpp"],
+}
+
+
+def code_digest(paths):
+    """SHA-256 over C/HIP sources with their comments and whitespace removed: it
+    changes with the code, not with its comments."""
     import hashlib
     import re
 
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = re.sub(r"\s+", " ", text).strip()
-    return hashlib.sha256(text.encode()).hexdigest()
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = re.sub(r"\s+", " ", text).strip()
+        h.update(text.encode() + b"\0")
+    return h.hexdigest()
+
+
+def traffic_digest(source="vwc_kernels.hip"):
+    csrc = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc")
+    return code_digest([os.path.join(csrc, f) for f in TRAFFIC_SOURCES[source]])
 
 
 def recorded_traffic(kernel_key, workload=DEFAULT_WORKLOAD, source="vwc_kernels.hip"):
     """Per-launch HBM bytes measured by rocprofv3 counters (see profiles/), valid only
-    while the kernel code is the one they were measured on."""
+    while the kernel code and launch geometry are the ones they were measured on."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", source)
     try:
         rec = json.load(open(path))
-        digest = code_digest(src)
+        digest = traffic_digest(source)
     except OSError:
         return None
     if rec.get("kernel_code_digest") != digest:
@@ -336,6 +367,9 @@ def lmhead_cpu_baseline(w, h, wt, tg, rows, seconds):
 
     done, el = run(seconds)
     out = {"value": done / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+           # operand bytes one kept row needs: its hidden row and the whole weight
+           "input_gbs": done * (w.hidden * 2 + w.vocab * w.hidden * 2) / el / 1e9,
            "sample": f"{done} kept rows of {w.name} in random order (fp64 projection of each "
                      f"row against all {w.vocab} weight rows, then logprob+lse+entropy), "
                      f"{el:.1f} s of oracle time"}
@@ -420,7 +454,14 @@ def bench_lmhead(args, w):
     }
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = lmhead_cpu_baseline(w, h_h, wt_h, tg_h, rows_h, args.cpu_seconds)
+        cpu = lmhead_cpu_baseline(w, h_h, wt_h, tg_h, rows_h, args.cpu_seconds)
+        cpu["gpu_over_oracle"] = out["value"] / cpu["value"]
+        out["cpu_baseline"] = cpu
+    import hashlib
+    out["inputs_sha256"] = {"hidden": hashlib.sha256(h_h.tobytes()).hexdigest(),
+                            "weight": hashlib.sha256(wt_h.tobytes()).hexdigest(),
+                            "targets": hashlib.sha256(tg_h.tobytes()).hexdigest(),
+                            "row_idx": hashlib.sha256(rows_h.tobytes()).hexdigest()}
     return out
 
 
@@ -457,23 +498,35 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
         return
 
-    # Inputs, generated on the host in row blocks and left resident in HBM.
+    # Inputs, generated on the host in row blocks (in row order) and left
+    # resident in HBM; SHA-256 of each buffer's bytes as uploaded.
+    import hashlib
+
     t0 = time.time()
     x = torch.empty((w.n_rows, w.vocab), dtype=dt, device=dev)
+    x_hash = hashlib.sha256()
 
     def sink(r0, blk):
+        x_hash.update(np.ascontiguousarray(blk).data)
         src = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
             else torch.from_numpy(blk)
         x[r0:r0 + blk.shape[0]].copy_(src.to(dev))
 
     W.fill_logits(w, sink, block_rows=512)
+    t_host = W.targets(w)
+    g_host = W.grad_out(w)
+    inputs_sha256 = {"logits": x_hash.hexdigest(),
+                     "targets": hashlib.sha256(t_host.tobytes()).hexdigest(),
+                     "grad_out": hashlib.sha256(g_host.tobytes()).hexdigest()}
+    if w.mask != "none":
+        inputs_sha256["loss_mask"] = hashlib.sha256(W.loss_mask(w).tobytes()).hexdigest()
     if w.name != DEFAULT_WORKLOAD:
         torch.cuda.synchronize()
         print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-        print(json.dumps(bench_other(args, w, x)))
+        out = bench_other(args, w, x)
+        out["inputs_sha256"] = inputs_sha256
+        print(json.dumps(out))
         return
-    t_host = W.targets(w)
-    g_host = W.grad_out(w)
     targets = torch.from_numpy(t_host).to(dev)
     grad_out = torch.from_numpy(g_host).to(dev)
     live = int((g_host != 0).sum())
@@ -605,9 +658,14 @@ def main():
                      "frac": gbs(dom[1], dom[2]) / HBM_PEAK_GBS, "traffic": traffic,
                      "avg_launch_ms": dom[2], "bytes_alg_per_launch": dom[1]},
     }
+    result["inputs_sha256"] = inputs_sha256
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        # GPU step throughput over the oracle's, both in rows/s of the same work
+        # (forward + gradient of each row).
+        cpu["gpu_over_oracle"] = result["value"] / cpu["value"]
+        result["cpu_baseline"] = cpu
     print(json.dumps(result))
 
 

@@ -64,6 +64,16 @@ static int check_targets(const int32_t *targets, const int32_t *rows, int64_t m,
  *   M = max z_j;  S = sum exp(z_j - M);  LSE = M + log S.
  * Two passes, columns in ascending order.
  */
+/* exp(z - M), with exp(-inf) = 0 even when M is -inf too (a row or slice of
+   -inf logits: masked vocabulary entries have probability 0). */
+static double exp_shifted(double z, double M) {
+    return z == -INFINITY ? 0.0 : exp(z - M);
+}
+
+/* p * a for a term of probability p: 0 when p is 0, whatever a is (the limit
+   0 log 0 = 0 of -p log p; a is -inf there).  NaN p stays NaN. */
+static double p_times(double p, double a) { return p == 0.0 ? 0.0 : p * a; }
+
 static void row_max_sum(const void *logits, int dtype, int64_t ld, int64_t row,
                         int64_t c0, int64_t n, double tau, double *M_out,
                         double *S_out) {
@@ -75,7 +85,7 @@ static void row_max_sum(const void *logits, int dtype, int64_t ld, int64_t row,
     double S = 0.0;
     for (int64_t j = 0; j < n; ++j) {
         double z = logit_at(logits, dtype, ld, row, c0 + j) / tau;
-        S += exp(z - M);
+        S += exp_shifted(z, M);
     }
     *M_out = M;
     *S_out = S;
@@ -87,8 +97,8 @@ static double row_entropy(const void *logits, int dtype, int64_t ld,
     double H = 0.0;
     for (int64_t j = 0; j < vocab; ++j) {
         double z = logit_at(logits, dtype, ld, row, j) / tau;
-        double p = exp(z - LSE);
-        H -= p * (z - LSE);
+        double p = exp_shifted(z, LSE);
+        H -= p_times(p, z - LSE);
     }
     return H;
 }
@@ -199,10 +209,10 @@ int oracle_backward_entropy(const void *logits, int dtype, int64_t n_rows,
         int64_t t = grad_logprob ? targets[r] : -1;
         for (int64_t j = 0; j < vocab; ++j) {
             double z = logit_at(logits, dtype, ld, r, j) / tau;
-            double p = exp(z - LSE);
+            double p = exp_shifted(z, LSE);
             double onehot = (j == t) ? 1.0 : 0.0;
             /* d logprob / dz_j = onehot_j - p_j;  dH / dz_j = -p_j (z_j - LSE + H). */
-            gi[j] = (g * (onehot - p) - h * p * (z - LSE + H)) / tau;
+            gi[j] = (g * (onehot - p) - h * p_times(p, z - LSE + H)) / tau;
         }
     }
     return 0;
@@ -349,7 +359,7 @@ int oracle_slice_partial(const void *logits_slice, int dtype, int64_t n_rows,
         double W = 0.0;
         for (int64_t j = 0; j < v_local; ++j) {
             double z = logit_at(logits_slice, dtype, ld, r, j) / tau;
-            W += exp(z - M) * (z - M);
+            W += p_times(exp_shifted(z, M), z - M);
         }
         pm[i] = M;
         ps[i] = S;
@@ -380,12 +390,14 @@ int oracle_combine(int64_t k, int64_t m, const double *pm, const double *ps,
         /* Sum of exp(z - M): each slice's sum rescaled from its own max. */
         double S = 0.0, W = 0.0, T = -INFINITY;
         for (int64_t q = 0; q < k; ++q) {
+            if (pt && pt[q * m + i] > T) T = pt[q * m + i];
+            /* A slice whose logits are all -inf has S = 0 and adds nothing. */
+            if (ps[q * m + i] == 0.0) continue;
             double d = pm[q * m + i] - M;
             double f = exp(d);
             S += ps[q * m + i] * f;
             /* sum exp(z - M)(z - M) = sum exp(z - M_q) e^d ((z - M_q) + d) */
             W += f * (pw[q * m + i] + d * ps[q * m + i]);
-            if (pt && pt[q * m + i] > T) T = pt[q * m + i];
         }
         double LSE = M + log(S);
         if (lse) lse[i] = LSE;

@@ -45,15 +45,29 @@ def test_recorded_traffic_is_gated_by_the_code_digest():
     path = os.path.join(ROOT, "profiles", f"traffic_{bench.DEFAULT_WORKLOAD}.json")
     rec = json.load(open(path))
     key = "bwd_segment_kernel<0, 0, true, false, false>"
-    src = os.path.join(ROOT, "vocab_wide_cross_amd", "csrc", "vwc_kernels.hip")
     got = bench.recorded_traffic([key])
-    if rec["kernel_code_digest"] == bench.code_digest(src):
+    if rec["kernel_code_digest"] == bench.traffic_digest("vwc_kernels.hip"):
         assert got == rec["per_launch_bytes"][key]["total"]
     else:
         assert got is None
     assert bench.recorded_traffic(["no_such_kernel"]) is None
-    # the digest of another source never matches
-    assert bench.recorded_traffic([key], source="vwc_api.cpp") is None
+    # the digest of another kernel's sources never matches
+    assert bench.recorded_traffic([key], source="vwc_lmhead.hip") is None
+
+
+def test_traffic_digest_covers_launch_geometry(tmp_path):
+    """A change to any file that sets a kernel's code or launch shape (segment
+    sizes, block sizes, the host's segment choice) changes the digest."""
+    for src in ("vwc_kernels.hip", "vwc_lmhead.hip"):
+        assert {"vwc_internal.h", "vwc_lane.h", "vwc_api.cpp"} <= set(bench.TRAFFIC_SOURCES[src])
+    files = []
+    for k in range(3):
+        f = tmp_path / f"f{k}.h"
+        f.write_text(f"constexpr int a{k} = {k};")
+        files.append(str(f))
+    d0 = bench.code_digest(files)
+    (tmp_path / "f2.h").write_text("constexpr int a2 = 7;")
+    assert bench.code_digest(files) != d0
 
 
 def test_more_than_one_gpu_is_refused():

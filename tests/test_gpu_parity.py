@@ -373,15 +373,26 @@ def test_masked_minus_inf_logits():
     lp, lse, ent = vwc.selected_logprob_fwd(xd, td, want=("logprob", "lse", "entropy"))
     grad = vwc.selected_logprob_bwd(xd, td, lse, gd)
     ref = oracle.forward(x, t)
-    assert_close_scalar(_np(lp), ref["logprob"], "lp")
-    assert_close_scalar(_np(lse), ref["lse"], "lse")
-    # oracle: -p log p of a zero-probability entry is 0 * inf; take the finite ones
-    xm = np.where(mask, 0.0, x.astype(np.float64))
-    p = np.where(mask, 0.0, np.exp(xm - ref["lse"][:, None]))
-    h = -(p * np.where(mask, 0.0, xm - ref["lse"][:, None])).sum(axis=1)
-    assert_close_scalar(_np(ent), h, "entropy")
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        assert_close_scalar(_np(v), ref[k], k)
     gref = oracle.backward(x, t, g)
     assert np.abs(_np(grad).astype(np.float64) - gref).max() <= 1e-6
+    # the entropy gradient: exactly 0 at the -inf columns (0 log 0 = 0)
+    h = np.random.default_rng(4).uniform(-1, 1, 16).astype(np.float32)
+    both = _np(vwc.logprob_entropy_bwd(xd, td, lse, ent, gd, torch.from_numpy(h).to(DEV)))
+    assert np.all(both[mask] == 0.0) and np.all(np.isfinite(both))
+    eref = oracle.backward_entropy(x, t, g, h)
+    assert np.abs(both.astype(np.float64) - eref).max() <= 1e-6
+    # split vocabulary: the slice [0, 300) is -inf (but for a target there) and
+    # adds nothing
+    cuts = [0, 300, 1700, 3001]
+    parts = torch.stack([vwc.vocab_partial(xd[:, a:b], a, td, None) for a, b in
+                         zip(cuts[:-1], cuts[1:])])
+    empty = t >= 300
+    assert empty.any() and np.all(_np(parts[0])[empty, 1] == 0.0)
+    lp2, lse2, ent2 = vwc.partial_combine(parts, 1.0, want=("logprob", "lse", "entropy"))
+    for k, v in (("logprob", lp2), ("lse", lse2), ("entropy", ent2)):
+        assert_close_scalar(_np(v), ref[k], f"split {k}")
 
 
 def test_nan_logit_poisons_only_its_row():

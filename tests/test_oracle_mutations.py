@@ -12,7 +12,7 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 # (name, original text, mutated text, pin tests to run)
 MUTATIONS = [
-    ("entropy sign", "H -= p * (z - LSE);", "H += p * (z - LSE);", "entropy"),
+    ("entropy sign", "H -= p_times(p, z - LSE);", "H += p_times(p, z - LSE);", "entropy"),
     ("tau dropped on the target", "double zt = logit_at(logits, dtype, ld, r, targets[r]) / tau;",
      "double zt = logit_at(logits, dtype, ld, r, targets[r]);", "logprob or temperature"),
     ("max dropped from LSE", "double LSE = M + log(S);\n            if (lse) lse[i] = LSE;",
@@ -31,8 +31,16 @@ MUTATIONS = [
      "uint32_t w = ((uint32_t)bits) << 15;", "sampled_rows"),
     ("target read by output index", "double zt = logit_at(logits, dtype, ld, r, targets[r]) / tau;",
      "double zt = logit_at(logits, dtype, ld, r, targets[i]) / tau;", "compact or chunks or errors"),
-    ("entropy gradient sign of H", "gi[j] = (g * (onehot - p) - h * p * (z - LSE + H)) / tau;",
-     "gi[j] = (g * (onehot - p) - h * p * (z - LSE - H)) / tau;", "entropy_grad"),
+    ("entropy gradient sign of H",
+     "gi[j] = (g * (onehot - p) - h * p_times(p, z - LSE + H)) / tau;",
+     "gi[j] = (g * (onehot - p) - h * p_times(p, z - LSE - H)) / tau;", "entropy_grad"),
+    # 0 log 0 = 0 for -inf logits (masked vocabulary entries)
+    ("zero-probability term kept as 0 * inf", "return p == 0.0 ? 0.0 : p * a;", "return p * a;",
+     "minus_inf"),
+    ("exp of -inf minus -inf", "return z == -INFINITY ? 0.0 : exp(z - M);",
+     "return exp(z - M);", "minus_inf"),
+    ("combine keeps an empty slice", "if (ps[q * m + i] == 0.0) continue;", "/* kept */",
+     "minus_inf"),
     ("tail mass from the student", "double pt = P < 1.0 ? 1.0 - P : 0.0;",
      "double pt = Q < 1.0 ? 1.0 - Q : 0.0;", "topk"),
     ("truncated clamp dropped", "if (L < 0.0) L = 0.0; /* clamp_min(0) of the truncated objective */",

@@ -157,6 +157,73 @@ def test_entropy_brute_force_and_library(tiny):
         np.testing.assert_allclose(o["entropy"], cat, rtol=0, atol=1e-12)
 
 
+def _minus_inf_rows(seed=21, n=6, V=777):
+    """Rows with -inf entries (masked vocabulary), one row with whole runs of them."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, V)).astype(np.float32) * 2
+    mask = rng.random((n, V)) < 0.3
+    mask[1, :400] = True
+    t = rng.integers(0, V, n).astype(np.int32)
+    mask[np.arange(n), t] = False
+    x[mask] = -np.inf
+    return x, t, mask
+
+
+def test_entropy_with_minus_inf_entries():
+    """A -inf logit has probability 0 and adds 0 log 0 = 0 to the entropy: the
+    oracle equals torch fp64 Categorical (which clamps -inf logits) and itself on
+    the row with those columns removed; logprob and lse are unchanged too."""
+    x, t, mask = _minus_inf_rows()
+    for tau in (1.0, 0.7):
+        o = oracle.forward(x, t, tau=tau)
+        z = torch.from_numpy(x).double() / float(np.float32(tau))
+        cat = torch.distributions.Categorical(logits=z).entropy().numpy()
+        np.testing.assert_allclose(o["entropy"], cat, rtol=0, atol=1e-12)
+        for r in range(x.shape[0]):
+            keep = ~mask[r]
+            tr = np.array([int(keep[:t[r]].sum())], np.int32)
+            ref = oracle.forward(x[r:r + 1, keep], tr, tau=tau)
+            for k in ("logprob", "lse", "entropy"):
+                assert abs(o[k][r] - ref[k][0]) <= 1e-12, (r, k)
+
+
+def test_entropy_grad_with_minus_inf_entries():
+    """d(g lp + h H)/dx with -inf logits: exactly 0 at those columns and, at the
+    others, the gradient of the row with them removed; torch fp64 autograd of
+    log_softmax and Categorical entropy agrees."""
+    x, t, mask = _minus_inf_rows(22)
+    rng = np.random.default_rng(23)
+    g = rng.uniform(-1, 1, x.shape[0]).astype(np.float32)
+    h = rng.uniform(-1, 1, x.shape[0]).astype(np.float32)
+    tau = 0.7
+    gr = oracle.backward_entropy(x, t, g, h, tau=tau)
+    assert np.all(gr[mask] == 0.0) and np.all(np.isfinite(gr))
+    for r in range(x.shape[0]):
+        keep = ~mask[r]
+        tr = np.array([int(keep[:t[r]].sum())], np.int32)
+        ref = oracle.backward_entropy(x[r:r + 1, keep], tr, g[r:r + 1], h[r:r + 1], tau=tau)
+        np.testing.assert_allclose(gr[r, keep], ref[0], rtol=0, atol=1e-14)
+    xt = torch.from_numpy(x).double().requires_grad_(True)
+    z = xt / float(np.float32(tau))
+    lp = torch.log_softmax(z, dim=1)[torch.arange(x.shape[0]), torch.from_numpy(t).long()]
+    H = torch.distributions.Categorical(logits=z).entropy()
+    (lp * torch.from_numpy(g).double() + H * torch.from_numpy(h).double()).sum().backward()
+    np.testing.assert_allclose(gr, xt.grad.numpy(), rtol=0, atol=1e-14)
+
+
+def test_slice_of_minus_inf_adds_nothing():
+    """A vocabulary slice whose logits are all -inf has sum 0 and adds nothing to
+    the merge: slicing reproduces the single pass, entropy included."""
+    x, t, _ = _minus_inf_rows(24, V=600)
+    x[:, 200:400] = -np.inf
+    t = np.where((t >= 200) & (t < 400), t - 200, t).astype(np.int32)
+    o = oracle.forward(x, t, tau=0.7)
+    for vchunk in (200, 100, 7):
+        v = oracle.forward_vchunk(x, t, 0.7, vchunk)
+        for k in ("logprob", "lse", "entropy"):
+            np.testing.assert_allclose(v[k], o[k], rtol=1e-12, atol=1e-12)
+
+
 def test_entropy_one_dominant_entry():
     x = np.zeros((1, 4096), np.float32)
     x[0, 123] = 1000.0

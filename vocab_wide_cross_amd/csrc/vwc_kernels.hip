@@ -384,6 +384,48 @@ __device__ __forceinline__ Lane block_reduce(Lane L, int grp) {
     return acc;
 }
 
+// Lane states of a whole wave reduced the cheap way: the largest shift K and
+// reference m first (maxima through DPP and ds_swizzle; K = fl(m c) is monotone
+// in m, so the two maxima belong together), then every lane's sums rescaled to
+// that K and added over the same exchange tree.  Empty lanes (s = 0) add 0; NaN
+// sums propagate.  Every lane gets the wave's state.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) { return fmaxf(v, dpp<CTRL>(v)); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) { return v + dpp<CTRL>(v); }
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = dpp_max<0xB1>(v);
+    v = dpp_max<0x4E>(v);
+    v = dpp_max<0x141>(v);
+    v = dpp_max<0x140>(v);
+    v = fmaxf(v, swz<0x401F>(v));
+    return fmaxf(bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)),
+                 bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x141>(v);
+    v = dpp_add<0x140>(v);
+    v = v + swz<0x401F>(v);
+    return bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+           bits_to_float(__builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+}
+
+__device__ __forceinline__ Lane wave_reduce_rescaled(const Lane &L) {
+    Lane o;
+    o.K = wave_max(L.K);
+    o.m = wave_max(L.m);
+    const float d = L.K - o.K;  // <= 0
+    const float r = __builtin_amdgcn_exp2f(d);
+    const bool has = L.s != 0.f;  // true for NaN too
+    o.s = wave_sum(has ? r * L.s : 0.f);
+    o.w = wave_sum(has ? r * __builtin_fmaf(d, L.s, L.w) : 0.f);
+    return o;
+}
+
 // Merge partials in order (formulas in the vwc_partial comment).
 struct Merged {
     double M, S, W, T;
@@ -802,21 +844,46 @@ __device__ __forceinline__ RowGrad row_grad(float c_hi, float c_lo, double tau, 
     return R;
 }
 
-// Gradient of one unit.  Logprob only: o_k = gs p'_k with p'_k = 2^u'_k
-// (exp2f keeps denormal results).  With the entropy term (WH):
+// Gradient of one unit.  Logprob only: o_k = gs p'_k with p'_k = 2^u'_k.
+// With the entropy term (WH):
 //   o_k = p_k (-g/tau - h/tau (z_k - lse + H)) = p'_k (a + b u'_k).
 // The target column adds g/tau (1 - p_t), computed as -expm1(x_t/tau - lse) in
 // fp64 so that p_t -> 1 does not cancel.
-template <int DT, bool VEC, bool WH>
+// v_exp_f32 flushes results below 2^-126, which exp2f rescales at five more
+// instructions per element.  With FAST, a unit whose exponents all lie at or
+// above -126 (nearly every unit) takes the bare instruction, which gives
+// exp2f's bits there, and a unit with a smaller one (or NaN) takes exp2f: the
+// same results for fewer VALU cycles, at the cost of a branch per unit.  The
+// one-call kernel, whose compute phases run between its memory phases, uses
+// it; the streaming backward, bound by memory, runs faster without the branch.
+template <int DT, bool VEC, bool WH, bool FAST = false>
 __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, int32_t col0,
                                           const RowGrad &R, float (&o)[Unit<DT, VEC>::N]) {
     using Un = Unit<DT, VEC>;
+    float u[Un::N];
 #pragma unroll
     for (int k = 0; k < Un::N; ++k) {
         const float x = Un::get(v, k);
-        const float u = __builtin_fmaf(x, R.c_lo, __builtin_fmaf(x, R.c_hi, -R.B));
-        const float pk = exp2f(u);
-        o[k] = WH ? pk * __builtin_fmaf(R.b, u, R.a) : pk * R.gs;
+        u[k] = __builtin_fmaf(x, R.c_lo, __builtin_fmaf(x, R.c_hi, -R.B));
+    }
+    float umin = u[0];
+#pragma unroll
+    for (int k = 1; k < Un::N; ++k) umin = fminf(umin, u[k]);
+    if (FAST && __builtin_expect(umin >= -126.f, 1)) {
+#pragma unroll
+        for (int k = 0; k < Un::N; ++k) {
+            const float pk = __builtin_amdgcn_exp2f(u[k]);
+            o[k] = WH ? pk * __builtin_fmaf(R.b, u[k], R.a) : pk * R.gs;
+        }
+    } else {
+        // Here u may be -inf (a -inf logit): its p is 0, and the entropy factor
+        // takes max(u, -256) so that the term is 0, not 0 * inf (2^-256 is 0 in
+        // fp32, so no finite term changes).
+#pragma unroll
+        for (int k = 0; k < Un::N; ++k) {
+            const float pk = exp2f(u[k]);
+            o[k] = WH ? pk * __builtin_fmaf(R.b, fmaxf(u[k], kUFloor), R.a) : pk * R.gs;
+        }
     }
     if (static_cast<uint32_t>(R.t - col0) < static_cast<uint32_t>(Un::N)) {
 #pragma unroll
@@ -824,7 +891,8 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
             if (col0 + k == R.t) {
                 const double d = static_cast<double>(Un::get(v, k)) / R.tau - R.lse;
                 double ot = R.gt * -expm1(d);
-                if (WH) ot += R.hs * exp(d) * (d + R.H);
+                const double pt = exp(d);
+                if (WH && pt != 0.0) ot += R.hs * pt * (d + R.H);
                 o[k] = static_cast<float>(ot);
             }
     }
@@ -1078,11 +1146,11 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     using Us = Unit<DT, false>;
     constexpr int N = Un::N;
     constexpr int64_t kE = DT == VWC_BF16 ? 2 : 4;
-    constexpr int kGroups = kFusedBlock / kFwdBlock;
     constexpr int kStride = kFusedBlock * 16;  // bytes between a thread's units
     __shared__ __attribute__((aligned(16))) char stage[kFusedLds * kStride];
-    __shared__ vwc_partial group_part[kGroups];
-    __shared__ float row_lse;
+    __shared__ Lane wave_state[kFusedBlock / 64];
+    __shared__ double row_gt;
+    __shared__ float row_lse, row_B, row_gs;
 
     const int64_t i = blockIdx.x;  // output row
     const int32_t tid = static_cast<int32_t>(threadIdx.x);
@@ -1104,17 +1172,25 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     // and the register ones (k = kFusedLds + kr, kr < nreg) that lie in the row.
     const int32_t nreg = min(max((nunits - tid - kFusedLds * kFusedBlock + kFusedBlock - 1) /
                                      kFusedBlock, 0), kFusedReg);
-    const char *vrow = row + head * kE + tid * 16;  // this thread's unit 0
-    char *vgrow = grow + head * kE + tid * 16;
-    const float g = p.grad_out[i];
-    const int32_t t = p.targets[r];
+    char *vgrow = grow + head * kE + tid * 16;  // this thread's unit 0 of the gradient
 
-    // Phase 1: the LDS units through the DMA path (a buffer resource that ends
-    // at the row's last whole vector, so units past it read as zero: the whole
-    // offset goes in the per-lane offset, which the range check covers), then
-    // the register units, the row's edge element of this thread and the target.
+    // Phase 1.  This thread's edge element is read first, then the LDS units
+    // through the DMA path and the register units through plain buffer loads,
+    // both from one buffer resource that ends at the row's last whole vector:
+    // units past it read as zero (the whole offset sits in the per-lane offset,
+    // which the range check covers), so every wave issues the same loads in the
+    // same order.  Only then come the loss weight, the target id and the target
+    // logit, whose dependent round trips would otherwise delay the row's
+    // loads.  Loads complete in order, so once at most kFusedReg + 1 are
+    // outstanding the wave's LDS units have landed, and they are folded while
+    // the register units still arrive.  Each thread reads back only what its
+    // own wave's loads wrote.  The edge and target loads are unconditional
+    // (clamped to the row) so that no branch makes the compiler wait for them.
+    const int32_t edge = edge_column(head, nunits * N, p.vocab, tid);
+    typename Us::T ev[1] = {reinterpret_cast<const typename Us::T *>(row)[max(edge, 0)]};
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(row + head * kE), 0, nunits * 16, 0x00020000);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kFusedLds; ++k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1122,20 +1198,32 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
             static_cast<uint32_t>(tid * 16 + k * kStride), 0, 0, 0);
     T v[kFusedReg];
 #pragma unroll
-    for (int kr = 0; kr < kFusedReg; ++kr) {
-        v[kr] = T{};
-        if (kr < nreg)
-            v[kr] = Un::load(reinterpret_cast<const T *>(vrow + (kFusedLds + kr) * kStride));
-    }
-    const int32_t edge = edge_column(head, nunits * N, p.vocab, tid);
-    typename Us::T ev[1] = {typename Us::T{}};
-    if (edge >= 0) ev[0] = reinterpret_cast<const typename Us::T *>(row)[edge];
-    double tx = -INFINITY;  // the target logit (group 0's partial carries it)
-    if (tid == 0) tx = (t >= 0 && t < p.vocab) ? static_cast<double>(load_element<DT>(row, t)) : NAN;
+    for (int kr = 0; kr < kFusedReg; ++kr)  // cache policy: non-temporal
+        v[kr] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rsrc, static_cast<uint32_t>(tid * 16 + (kFusedLds + kr) * kStride),
+                                          0, 2));
+    __builtin_amdgcn_sched_barrier(0);
+    const float g = p.grad_out[i];
+    const int32_t t = p.targets[r];
+    const bool t_ok = t >= 0 && t < p.vocab;
+    const typename Us::T t_raw = reinterpret_cast<const typename Us::T *>(row)[t_ok ? t : 0];
+    __builtin_amdgcn_sched_barrier(0);
+    // s_waitcnt vmcnt(kFusedReg + 1) (6-bit count: low 4 bits at [3:0], high 2
+    // at [15:14]; expcnt and lgkmcnt not waited on).
+    constexpr int kAfterLds = kFusedReg + 1;
+    static_assert(kAfterLds < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt(((kAfterLds >> 4) << 14) | 0x0F70 | (kAfterLds & 15));
+    __builtin_amdgcn_sched_barrier(0);
 
     Lane L = lane_init();
-    // Fold the register units in short chunks (few unpacked values live at a
-    // time while every unit stays held for phase 2).
+#pragma unroll 1
+    for (int k = 0; k < kFusedLds; ++k) {
+        if (tid + k * kFusedBlock >= nunits) break;
+        const T x[1] = {*reinterpret_cast<const T *>(stage + k * kStride + tid * 16)};
+        fold_chunk<DT, true, 1, W>(x, 1, p.c, L);
+    }
+    // The register units in short chunks (few unpacked values live at a time
+    // while every unit stays held for phase 2).
     constexpr int kChunk = 2;
     static_assert(kFusedReg % kChunk == 0, "whole chunks of register units");
 #pragma unroll
@@ -1145,42 +1233,49 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
             fold_chunk<DT, true, kChunk, W>(*reinterpret_cast<const T(*)[kChunk]>(&v[k0]), nv,
                                             p.c, L);
     }
-    // vmcnt(0): this wave's LDS units have landed (each thread reads back only
-    // what its own wave's loads wrote; the barrier also keeps the compiler
-    // from moving the LDS reads above the wait).
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-#pragma unroll 1
-    for (int k = 0; k < kFusedLds; ++k) {
-        if (tid + k * kFusedBlock >= nunits) break;
-        const T x[1] = {*reinterpret_cast<const T *>(stage + k * kStride + tid * 16)};
-        fold_chunk<DT, true, 1, W>(x, 1, p.c, L);
-    }
     if (edge >= 0) fold_chunk<DT, false, 1, W>(ev, 1, p.c, L);
 
-    const int grp = tid / kFwdBlock;
-    const Lane B = block_reduce<kGroups>(L, grp);
-    if ((tid & (kFwdBlock - 1)) == 0) {
-        const P64 part = to_partial(B, p.c, grp == 0 ? tx : -INFINITY);
-        group_part[grp] = vwc_partial{static_cast<float>(part.m), static_cast<float>(part.s),
-                                      static_cast<float>(part.t), static_cast<float>(part.w)};
-    }
+    // The row's state: each wave's lanes, then the 16 wave states (lanes 0-15
+    // of wave 0), reduced by rescaling to the largest shift (fp32); thread 0
+    // turns it into the row's outputs in fp64 as the segment forward does for
+    // one segment, and the gradient's per-row constants (computed once, shared
+    // through LDS).
+    const Lane Wv = wave_reduce_rescaled(L);
+    if ((tid & 63) == 0) wave_state[wave] = Wv;
     __syncthreads();
-    if (tid == 0) {
-        const Merged mg = merge_partials(
-            [&](int q) {
-                const vwc_partial a = group_part[q];
-                return P64{a.m, a.s, a.t, a.w};
-            },
-            kGroups, p.tau);
-        write_final(mg, p.tau, i, p.logprob, p.lse, W ? p.entropy : nullptr);
-        row_lse = static_cast<float>(mg.M / p.tau + log(mg.S));  // the value lse[i] holds
+    if (wave == 0) {
+        const Lane Lw = (tid < kFusedBlock / 64) ? wave_state[tid] : lane_init();
+        const Lane Rw = wave_reduce_rescaled(Lw);
+        if (tid == 0) {
+            const double tx = !t_ok ? NAN : static_cast<double>(Us::get(t_raw, 0));
+            const P64 part = to_partial(Rw, p.c, tx);
+            const Merged mg = merge_partials([&](int) { return part; }, 1, p.tau);
+            write_final(mg, p.tau, i, p.logprob, p.lse, W ? p.entropy : nullptr);
+            const float lse32 = static_cast<float>(mg.M / p.tau + log(mg.S));  // lse[i]
+            const RowGrad R0 = row_grad(p.gc_hi, p.gc_lo, p.tau, lse32, g, 0.f, 0.0,
+                                        -static_cast<double>(g) / p.tau);
+            row_lse = lse32;
+            row_B = R0.B;
+            row_gs = R0.gs;
+            row_gt = R0.gt;
+        }
     }
     __syncthreads();
 
-    // Phase 2: the gradient, as the backward computes it from the saved fp32 lse.
-    RowGrad R = row_grad(p.gc_hi, p.gc_lo, p.tau, row_lse, g, 0.f, 0.0,
-                         -static_cast<double>(g) / p.tau);
+    // Phase 2: the gradient, as the backward computes it from the saved fp32 lse
+    // (the row constants row_grad gives for it).
+    RowGrad R;
+    R.c_hi = p.gc_hi;
+    R.c_lo = p.gc_lo;
+    R.B = row_B;
+    R.gs = row_gs;
+    R.a = 0.f;
+    R.b = 0.f;
+    R.gt = row_gt;
+    R.hs = 0.0;
+    R.H = 0.0;
+    R.lse = static_cast<double>(row_lse);
+    R.tau = p.tau;
     R.t = t;
     const bool zero = g == 0.f;  // a row without loss: +0.0, nothing computed
     auto emit = [&](const T &x, int32_t u, char *dst) {
@@ -1189,7 +1284,7 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
 #pragma unroll
             for (int k = 0; k < N; ++k) o[k] = 0.f;
         } else {
-            unit_grad<DT, true, false>(x, head + u * N, R, o);
+            unit_grad<DT, true, false, true>(x, head + u * N, R, o);
         }
         GradStore<DT, N>::store(dst, o);
     };
@@ -1197,15 +1292,20 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     for (int kr = 0; kr < kFusedReg; ++kr)
         if (kr < nreg)
             emit(v[kr], tid + (kFusedLds + kr) * kFusedBlock, vgrow + (kFusedLds + kr) * kStride);
-#pragma unroll 1
+    // The register units are spent, so the LDS units are all read up front
+    // (slots past the row hold zeros and are not stored).
+    T xl[kFusedLds];
+#pragma unroll
+    for (int k = 0; k < kFusedLds; ++k)
+        xl[k] = *reinterpret_cast<const T *>(stage + k * kStride + tid * 16);
+#pragma unroll
     for (int k = 0; k < kFusedLds; ++k) {
         const int32_t u = tid + k * kFusedBlock;
-        if (u >= nunits) break;
-        emit(*reinterpret_cast<const T *>(stage + k * kStride + tid * 16), u, vgrow + k * kStride);
+        if (u < nunits) emit(xl[k], u, vgrow + k * kStride);
     }
     if (edge >= 0) {
         float o[1] = {0.f};
-        if (!zero) unit_grad<DT, false, false>(ev[0], edge, R, o);
+        if (!zero) unit_grad<DT, false, false, true>(ev[0], edge, R, o);
         GradStore<DT, 1>::store(grow + static_cast<int64_t>(edge) * kE, o);
     }
 }

@@ -22,16 +22,25 @@ def to_dev_logits(host: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(host).to(DEV)
 
 
-def upload_workload(w: W.Workload, ld: int | None = None, block_rows: int = 512) -> torch.Tensor:
-    """Generate every row on the host in blocks and copy it into one device tensor."""
+def upload_workload(w: W.Workload, ld: int | None = None, block_rows: int = 512,
+                    keep_rows=None):
+    """Generate every row on the host in blocks and copy it into one device tensor.
+    With keep_rows (ascending row ids, or True for all), also return a host copy
+    of those rows: (device tensor, host array [len(keep_rows), ld])."""
     ld = w.vocab if ld is None else ld
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     t = torch.empty((w.n_rows, ld), dtype=dt, device=DEV)
+    if keep_rows is True:
+        keep_rows = np.arange(w.n_rows)
+    host = None if keep_rows is None else np.empty((len(keep_rows), ld), dtype=w.np_dtype)
     t0 = time.time()
     last = [t0]
 
     def sink(r0, blk):
         t[r0:r0 + blk.shape[0]].copy_(to_dev_logits(blk))
+        if host is not None:
+            a, b = np.searchsorted(keep_rows, [r0, r0 + blk.shape[0]])
+            host[a:b] = blk[keep_rows[a:b] - r0]
         if time.time() - last[0] > 10:
             last[0] = time.time()
             log(f"  {w.name}: {r0 + blk.shape[0]} of {w.n_rows} rows uploaded")
@@ -39,7 +48,33 @@ def upload_workload(w: W.Workload, ld: int | None = None, block_rows: int = 512)
     W.fill_logits(w, sink, block_rows=block_rows, ld=ld)
     torch.cuda.synchronize()
     log(f"uploaded {w.name} [{w.n_rows}, {ld}] {w.dtype} in {time.time() - t0:.1f}s")
-    return t
+    return t if host is None else (t, host)
+
+
+def check_grad_rows(grad, grad_rows, x_host, t_rows, g_rows, what, oracle, tau=1.0,
+                    block=256):
+    """Every listed gradient row against the oracle, in blocks of rows: bf16 within
+    one step of the rounded oracle, fp32 within 1e-6.  grad_rows index `grad`;
+    x_host / t_rows / g_rows hold the same rows' logits, targets and incoming
+    gradients.  Returns the largest bf16 step count (or fp32 error)."""
+    worst = 0.0
+    t0 = time.time()
+    for a in range(0, len(grad_rows), block):
+        b = min(a + block, len(grad_rows))
+        gi = torch.from_numpy(np.asarray(grad_rows[a:b], dtype=np.int64)).to(DEV)
+        ref = oracle.backward(x_host[a:b], t_rows[a:b], g_rows[a:b], tau=tau)
+        got = grad[gi]
+        if got.dtype == torch.bfloat16:
+            worst = max(worst, assert_bf16_grad(grad_bits(got), ref, f"{what} rows {a}-{b}",
+                                                oracle))
+        else:
+            err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+            assert err <= 1e-6, f"{what} rows {a}-{b}: fp32 grad err {err}"
+            worst = max(worst, float(err))
+        if time.time() - t0 > 10:
+            t0 = time.time()
+            log(f"  {what}: {b} of {len(grad_rows)} gradient rows checked")
+    return worst
 
 
 def grad_bits(t: torch.Tensor) -> np.ndarray:

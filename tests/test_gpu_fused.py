@@ -103,30 +103,33 @@ def test_fused_other_gradient_dtype_and_default_buffer():
     assert_close_scalar(_np(lp), oracle.forward(x, t)["logprob"], "logprob")
 
 
-def test_fused_full_size_sampled_rows():
-    """The default step's full shape, in the launch the bench times; sampled rows
-    against the oracle, every row against the separate calls."""
+def test_fused_full_size_every_row():
+    """The default step's full shape, in the launch the bench times: every row's
+    outputs and every live row's gradient against the oracle, and every row
+    against the separate calls."""
     w = W.get("spiked_bf16_8192x248320")
-    from gpu_util import upload_workload
-    xd = upload_workload(w)
+    from gpu_util import check_grad_rows, upload_workload
+    xd, x = upload_workload(w, keep_rows=True)
     t, g = W.targets(w), W.grad_out(w)
     td, gd = torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
     lp, lse, ent, grad = vwc.selected_logprob_fwd_bwd(xd, td, gd,
                                                       want=("logprob", "lse", "entropy"))
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 777, 4095, 4096, 8190, 8191])
-    x = W.logits_rows(w, rows)
-    ref = oracle.forward(x, t[rows])
-    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
-        assert_close_scalar(_np(v)[rows], ref[k], k)
-    gref = oracle.backward(x, t[rows], g[rows])
-    assert_bf16_grad(grad_bits(grad[torch.from_numpy(rows).to(DEV)]), gref, "sampled rows",
-                     oracle)
     gsep = vwc.selected_logprob_bwd(xd, td, lse, gd)
     assert torch.equal(_bits(grad), _bits(gsep))
+    del gsep
     slp, slse, _ = vwc.selected_logprob_fwd(xd, td)
     assert np.abs(_np(slse).astype(np.float64) - _np(lse)).max() <= 1e-4
     assert np.abs(_np(slp).astype(np.float64) - _np(lp)).max() <= 1e-4
+    ref = oracle.forward(x, t)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        e = assert_close_scalar(_np(v), ref[k], k)
+        log(f"one call {k}: max err {e:.3g} over all {w.n_rows} rows")
+    zero = np.flatnonzero(g == 0)
+    assert torch.all(grad[torch.from_numpy(zero).to(DEV)].view(torch.int16) == 0)
+    live = np.flatnonzero(g != 0)
+    steps = check_grad_rows(grad, live, x[live], t[live], g[live], "one-call grad", oracle)
+    log(f"one call grad: all {live.size} live rows within {steps} bf16 step(s)")
 
 
 def test_fused_special_values():

@@ -434,6 +434,23 @@ vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, i
                              hipStream_t stream);
 
 /*
+ * The same for long masks (the packed and context-parallel sequences of [B]
+ * "Verification" and [D] "Bug Description" run to 64k-160k tokens and more),
+ * spread over the whole GPU: the mask is cut into tiles of 4096 entries, each
+ * tile's nonzeros are counted, one workgroup turns the counts into offsets, and
+ * every tile writes its ids from its offset; the ids equal the one-workgroup
+ * call's.  Masks of at most 65536 entries take the one-workgroup scan (one
+ * launch) and need no workspace; longer ones need
+ * vwc_mask_to_index_workspace_bytes(n) bytes (4 per tile), 4-byte aligned,
+ * whose contents on entry do not matter.  Other arguments as
+ * vwc_mask_to_index.
+ */
+size_t vwc_mask_to_index_workspace_bytes(int64_t n);
+
+vwc_status vwc_mask_to_index_ws(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Fused LM head ([D] maintainer comment: keep the loss-mask rows of the final
  * hidden state before the vocabulary projection and compute log-prob and
  * entropy on those rows only; [A] "Alternatives considered": a fused

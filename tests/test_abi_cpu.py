@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
 
@@ -230,6 +230,20 @@ def test_partial_combine_and_mask_validation(lib):
     assert mk(FAKE, 2 ** 31, FAKE, FAKE, None) == INVALID
     assert mk(FAKE, 4, FAKE, None, None) == INVALID
     assert mk(None, 4, FAKE, FAKE, None) == INVALID
+    # the tiled scan: 4 bytes per tile of 4096 entries past 65536 entries
+    wb = lib.vwc_mask_to_index_workspace_bytes
+    wb.argtypes = [i64]
+    wb.restype = ctypes.c_size_t
+    assert wb(0) == 0 and wb(65536) == 0
+    assert wb(65537) == 17 * 4 and wb(160000) == 40 * 4 and wb(1 << 20) == 256 * 4
+    mw = lib.vwc_mask_to_index_ws
+    mw.argtypes = [p, i64, p, p, p, ctypes.c_size_t, p]
+    assert mw(FAKE, -1, FAKE, FAKE, FAKE, 1024, None) == INVALID
+    assert mw(FAKE, 2 ** 31, FAKE, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert mw(FAKE, 1 << 20, FAKE, None, FAKE, 1024, None) == INVALID
+    assert mw(FAKE, 1 << 20, FAKE, FAKE, None, 0, None) == INVALID          # no workspace
+    assert mw(FAKE, 1 << 20, FAKE, FAKE, FAKE, 256 * 4 - 1, None) == INVALID  # too small
+    assert mw(FAKE, 1 << 20, FAKE, FAKE, ctypes.c_void_p(0x100002), 1024, None) == INVALID
 
 
 def _lmhead(lib):

@@ -172,6 +172,53 @@ def test_mask_to_index_matches_nonzero():
     assert c == 8192 and np.array_equal(_np(idx[:c]), W.row_index(w))
 
 
+@pytest.mark.parametrize("n", [65537, 160000, 160003, 1 << 20, 1000003])
+def test_long_mask_to_index_tiled_and_one_group(n):
+    """Long masks (packed and context-parallel sequences): the tiled scan over the
+    whole GPU and the one-workgroup scan both give numpy's nonzero, bit for bit,
+    for sparse, dense, full and empty masks and a mask that starts off 16 bytes."""
+    rng = np.random.default_rng(n)
+    for p in (0.0, 0.01, 0.5, 1.0):
+        mask = (rng.random(n + 1) < p).astype(np.uint8)
+        mask[rng.integers(0, n, 3)] = 9 if p > 0 else 0
+        want = np.flatnonzero(mask[:n]).astype(np.int32)
+        md = torch.from_numpy(mask).to(DEV)
+        for view in (md[:n], md[1:]):  # the second starts off 16 bytes
+            w = want if view.data_ptr() == md.data_ptr() else \
+                np.flatnonzero(mask[1:]).astype(np.int32)
+            for one_group in (False, True):
+                idx, cnt = vwc.mask_to_index(view, one_group=one_group)
+                c = int(cnt.item())
+                assert c == w.size, (p, one_group, c, w.size)
+                assert np.array_equal(_np(idx[:c]), w), (p, one_group)
+    log(f"mask_to_index n={n}: tiled and one-group scans equal nonzero()")
+
+
+def test_long_mask_to_index_graph_replays():
+    """The tiled scan (three launches and a workspace) captured once and replayed
+    on new masks gives the eager ids every time."""
+    n = 1 << 20
+    mask = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    idx = torch.empty(n, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(vwc.mask_to_index_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    mask.copy_((torch.rand(n, device=DEV, generator=gen) < 0.3).to(torch.uint8))
+    vwc.mask_to_index(mask, idx, cnt, workspace=ws)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vwc.mask_to_index(mask, idx, cnt, workspace=ws)
+    for rep in range(3):
+        mask.copy_((torch.rand(n, device=DEV, generator=gen) < 0.1 + 0.3 * rep).to(torch.uint8))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = np.flatnonzero(_np(mask)).astype(np.int32)
+        c = int(cnt.item())
+        assert c == want.size and np.array_equal(_np(idx[:c]), want), rep
+
+
 def test_compact_rows_forward_and_entropy():
     w = W.scaled("masked_bf16_4096x151936", 160, 151936)
     x, t, _ = _host(w)

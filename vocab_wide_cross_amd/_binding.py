@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
+        "vwc_mask_to_index_workspace_bytes": ([i64], sz),
+        "vwc_mask_to_index_ws": ([p, i64, p, p, p, sz, p], i32),
         "vwc_lmhead_workspace_bytes": ([i64, i64, i64], sz),
         "vwc_lmhead_logprob_fwd": ([p, i64, i64, p, i64, i64, i64, p, p, i64, f32, p, p, p, p, sz,
                                     p], i32),
@@ -523,8 +525,15 @@ def partial_combine(parts, temperature=1.0, logprob=None, lse=None, entropy=None
     return lp, ls, en
 
 
-def mask_to_index(mask, row_idx=None, count=None, stream=None):
-    """Ascending int32 ids of the nonzero entries of a uint8/bool mask (device count)."""
+def mask_to_index_workspace_bytes(n: int) -> int:
+    return int(_lib.vwc_mask_to_index_workspace_bytes(n))
+
+
+def mask_to_index(mask, row_idx=None, count=None, workspace=None, one_group=False, stream=None):
+    """Ascending int32 ids of the nonzero entries of a uint8/bool mask (device count).
+    Long masks take the tiled scan over the whole GPU (vwc_mask_to_index_ws, with a
+    workspace allocated here when none is passed); one_group=True forces the
+    one-workgroup call (vwc_mask_to_index)."""
     if mask.dtype == torch.bool:
         mask = mask.view(torch.uint8)
     if mask.dtype != torch.uint8 or not mask.is_contiguous():
@@ -536,8 +545,16 @@ def mask_to_index(mask, row_idx=None, count=None, stream=None):
         count = torch.empty(1, dtype=torch.int32, device=mask.device)
     _i32(row_idx, "row_idx", n)
     _i32(count, "count", 1)
-    _check(_lib.vwc_mask_to_index(_ptr(mask), n, _ptr(row_idx), _ptr(count),
-                                  _stream(stream, mask)))
+    if one_group:
+        _check(_lib.vwc_mask_to_index(_ptr(mask), n, _ptr(row_idx), _ptr(count),
+                                      _stream(stream, mask)))
+        return row_idx, count
+    need = mask_to_index_workspace_bytes(n)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=mask.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.vwc_mask_to_index_ws(_ptr(mask), n, _ptr(row_idx), _ptr(count), _ptr(workspace),
+                                     wsb, _stream(stream, mask)))
     return row_idx, count
 
 

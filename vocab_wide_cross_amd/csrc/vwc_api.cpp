@@ -871,6 +871,35 @@ vwc_status vwc_mask_to_index(const uint8_t *mask, int64_t n, int32_t *row_idx, i
     return hip_status(vwc::launch_mask_to_index(mask, n, row_idx, count, stream), fn);
 }
 
+// Masks up to this length take the one-workgroup scan (one launch, no
+// workspace); longer ones the tiled scan.
+constexpr int64_t kMaskOneGroupMax = 65536;
+
+size_t vwc_mask_to_index_workspace_bytes(int64_t n) {
+    if (n <= kMaskOneGroupMax) return 0;
+    return static_cast<size_t>(vwc::mask_tiles(n)) * sizeof(int32_t);
+}
+
+vwc_status vwc_mask_to_index_ws(const uint8_t *mask, int64_t n, int32_t *row_idx, int32_t *count,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "vwc_mask_to_index_ws";
+    if (n < 0 || n > INT32_MAX) return fail(VWC_ERR_INVALID_ARG, "%s: n outside [0, 2^31)", fn);
+    if (!count) return fail(VWC_ERR_INVALID_ARG, "%s: count is null", fn);
+    if (n > 0 && (!mask || !row_idx))
+        return fail(VWC_ERR_INVALID_ARG, "%s: null mask or row_idx", fn);
+    const size_t need = vwc_mask_to_index_workspace_bytes(n);
+    if (need == 0)
+        return hip_status(vwc::launch_mask_to_index(mask, n, row_idx, count, stream), fn);
+    if (!workspace || workspace_bytes < need)
+        return fail(VWC_ERR_INVALID_ARG, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                    workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+        return fail(VWC_ERR_INVALID_ARG, "%s: workspace must be 4-byte aligned", fn);
+    return hip_status(vwc::launch_mask_to_index_tiled(mask, n, row_idx, count,
+                                                      static_cast<int32_t *>(workspace), stream),
+                      fn);
+}
+
 const char *vwc_status_string(vwc_status status) {
     switch (static_cast<int>(status)) {
         case VWC_OK: return "ok";

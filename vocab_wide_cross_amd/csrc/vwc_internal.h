@@ -261,5 +261,9 @@ hipError_t launch_combine(const CombinePlan &p, hipStream_t stream);
 hipError_t launch_combine_rows(const CombinePlan &p, hipStream_t stream);
 hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, int32_t *count,
                                 hipStream_t stream);
+// Tiles of the multi-workgroup scan (one int32 of workspace each).
+int64_t mask_tiles(int64_t n);
+hipError_t launch_mask_to_index_tiled(const uint8_t *mask, int64_t n, int32_t *idx,
+                                      int32_t *count, int32_t *tiles, hipStream_t stream);
 
 }  // namespace vwc

@@ -1366,6 +1366,114 @@ __global__ __launch_bounds__(kScanBlock) void mask_to_index_kernel(const uint8_t
     if (threadIdx.x == 0) *count = carry;
 }
 
+// Long masks: three launches over tiles of kTileItems entries.  Each tile's
+// nonzero count goes to the workspace, one workgroup turns the counts into
+// exclusive offsets (and the total), then every tile writes its ascending ids
+// from its offset.  The same ids as the one-workgroup scan, in parallel over
+// the tiles.
+constexpr int kTileBlock = 256;
+constexpr int kTileItems = kTileBlock * kScanItems;  // 4096
+
+// Bits k of the returned word: entry b + k of the mask is nonzero (k < 16).
+__device__ __forceinline__ uint32_t mask_bits(const uint8_t *mask, int64_t n, int64_t b,
+                                              bool aligned) {
+    uint32_t bits = 0;
+    if (aligned && b + kScanItems <= n) {
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(mask + b);
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k)
+            if ((q[k >> 2] >> (8 * (k & 3))) & 0xffu) bits |= 1u << k;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kScanItems; ++k)
+            if (b + k < n && mask[b + k] != 0) bits |= 1u << k;
+    }
+    return bits;
+}
+
+// Exclusive prefix of v over the workgroup's threads (kTileBlock of them) and
+// the workgroup's total.
+__device__ __forceinline__ int32_t tile_exclusive_scan(int32_t v, int32_t *total) {
+    __shared__ int32_t wave_tot[kTileBlock / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTileBlock / 64; ++w) {
+        if (w < wave) off += wave_tot[w];
+        tot += wave_tot[w];
+    }
+    *total = tot;
+    return off + x - v;
+}
+
+__global__ __launch_bounds__(kTileBlock) void mask_tile_count_kernel(const uint8_t *mask,
+                                                                     int64_t n, int32_t *tiles) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(mask) & 15) == 0;
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kTileItems +
+                      static_cast<int64_t>(threadIdx.x) * kScanItems;
+    int32_t tot;
+    tile_exclusive_scan(__builtin_popcount(mask_bits(mask, n, b, aligned)), &tot);
+    if (threadIdx.x == 0) tiles[blockIdx.x] = tot;
+}
+
+// One workgroup: tiles[0..ntiles) -> exclusive offsets, *count = the total.
+__global__ __launch_bounds__(kScanBlock) void mask_tile_scan_kernel(int32_t *tiles,
+                                                                    int64_t ntiles,
+                                                                    int32_t *count) {
+    __shared__ int32_t wave_tot[kScanBlock / 64];
+    __shared__ int32_t wave_off[kScanBlock / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < ntiles; base += kScanBlock) {
+        const int64_t k = base + threadIdx.x;
+        const int32_t c = k < ntiles ? tiles[k] : 0;
+        int32_t x = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wave_tot[wave] = x;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t acc = 0;
+            for (int w = 0; w < kScanBlock / 64; ++w) {
+                wave_off[w] = acc;
+                acc += wave_tot[w];
+            }
+            wave_tot[0] = acc;
+        }
+        __syncthreads();
+        if (k < ntiles) tiles[k] = carry + wave_off[wave] + x - c;
+        carry += wave_tot[0];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *count = carry;
+}
+
+__global__ __launch_bounds__(kTileBlock) void mask_tile_write_kernel(const uint8_t *mask,
+                                                                     int64_t n,
+                                                                     const int32_t *tiles,
+                                                                     int32_t *idx) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(mask) & 15) == 0;
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kTileItems +
+                      static_cast<int64_t>(threadIdx.x) * kScanItems;
+    const uint32_t bits = mask_bits(mask, n, b, aligned);
+    int32_t tot;
+    int32_t off = tiles[blockIdx.x] + tile_exclusive_scan(__builtin_popcount(bits), &tot);
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k)
+        if (bits & (1u << k)) idx[off++] = static_cast<int32_t>(b + k);
+}
+
 // ---------------------------------------------------------------- launch helpers
 
 // Every row streams 16-byte vectors from its first 16-byte boundary on.
@@ -1497,6 +1605,25 @@ hipError_t launch_mask_to_index(const uint8_t *mask, int64_t n, int32_t *idx, in
                                 hipStream_t stream) {
     hipLaunchKernelGGL(mask_to_index_kernel, dim3(1), dim3(kScanBlock), 0, stream, mask, n, idx,
                        count);
+    return hipGetLastError();
+}
+
+int64_t mask_tiles(int64_t n) { return (n + kTileItems - 1) / kTileItems; }
+
+hipError_t launch_mask_to_index_tiled(const uint8_t *mask, int64_t n, int32_t *idx,
+                                      int32_t *count, int32_t *tiles, hipStream_t stream) {
+    const int64_t nt = mask_tiles(n);
+    if (nt == 0) {  // empty mask: the count only
+        hipLaunchKernelGGL(mask_tile_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, tiles,
+                           nt, count);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(mask_tile_count_kernel, dim3(static_cast<uint32_t>(nt)), dim3(kTileBlock),
+                       0, stream, mask, n, tiles);
+    hipLaunchKernelGGL(mask_tile_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, tiles, nt,
+                       count);
+    hipLaunchKernelGGL(mask_tile_write_kernel, dim3(static_cast<uint32_t>(nt)),
+                       dim3(kTileBlock), 0, stream, mask, n, tiles, idx);
     return hipGetLastError();
 }
 

@@ -45,6 +45,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of the logits' size (for counter scaling)")
+    ap.add_argument("--lmhead-order", default="",
+                    help="LM-head workloads, for counter runs: instead of timing, run one call per "
+                         "letter in this order, E with the entropy output, L without (e.g. ELLELEEL)")
     return ap.parse_args()
 
 
@@ -465,6 +468,36 @@ def bench_lmhead(args, w):
     return out
 
 
+def lmhead_order(args, w):
+    """One LM-head call per letter of args.lmhead_order (E: logprob, lse and entropy;
+    L: logprob and lse), each synchronized, on the workload's inputs; for counter
+    runs that attribute per-launch figures to an instance and a position."""
+    import numpy as np
+    import torch
+
+    import vocab_wide_cross_amd as vwc
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wt_h = W.lmhead_weight(w)
+    h_h = W.lmhead_hidden(w, weight=wt_h)
+    wt = torch.from_numpy(wt_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    h = torch.from_numpy(h_h.view(np.int16)).to(dev).view(torch.bfloat16)
+    tg = torch.from_numpy(W.targets(w)).to(dev)
+    rows = torch.from_numpy(W.row_index(w)).to(dev)
+    M = rows.numel()
+    ws = torch.empty(vwc.lmhead_workspace_bytes(M, w.vocab, w.hidden), dtype=torch.uint8,
+                     device=dev)
+    lp, lse, ent = (torch.empty(M, device=dev) for _ in range(3))
+    for k, e in enumerate(args.lmhead_order):
+        if e not in "EL":
+            raise SystemExit(f"--lmhead-order takes E and L, not {e!r}")
+        vwc.lmhead_logprob_fwd(h, wt, tg, rows, w.tau, logprob=lp, lse=lse,
+                               entropy=ent if e == "E" else None, workspace=ws)
+        torch.cuda.synchronize()
+    print(json.dumps({"lmhead_order": args.lmhead_order, "workload": w.name}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -482,6 +515,9 @@ def main():
     dev = torch.device("cuda:0")
     w = W.get(args.workload)
     if w.hidden > 0:
+        if args.lmhead_order:
+            lmhead_order(args, w)
+            return
         print(json.dumps(bench_lmhead(args, w)))
         return
     esize = 2 if w.dtype == "bf16" else 4

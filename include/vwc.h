@@ -271,8 +271,9 @@ vwc_status vwc_selected_logprob_fwd_bwd_rows(const void *logits, vwc_dtype dt, i
  * float[m] (compact, as the `_rows` forward writes them).  layout selects
  * where gradient row i goes: VWC_GRAD_COMPACT -> row i of [m, ld_grad];
  * VWC_GRAD_SCATTER -> row row_idx[i] of [n_rows, ld_grad], other rows
- * untouched (the caller clears them; [D] "values outside the selected loss
- * mask").  With VWC_GRAD_SCATTER, duplicate row ids race.
+ * untouched (the caller clears them: [D] maintainer comment, the results of
+ * rows off the loss mask are left to the caller).  With VWC_GRAD_SCATTER,
+ * duplicate row ids race.
  */
 vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
                                          int64_t vocab, int64_t ld, const int32_t *targets,

@@ -448,13 +448,6 @@ int oracle_forward_vchunk(const void *logits, int dtype, int64_t n_rows,
     return rc;
 }
 
-/*
- * Nearest bf16 to v, ties to even, straight from the double (no detour through
- * float, which would round twice).  bf16 has fp32's exponent range and 8
- * significant bits; below 2^-126 its spacing is the fixed 2^-133.  Dividing by
- * the spacing is exact (a power of two), rint() rounds to nearest-even in the
- * default rounding mode, and the product is exactly representable in float.
- */
 /* ------------------------------------------------------------ LM head */
 
 static int lmhead_args_ok(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
@@ -548,6 +541,13 @@ int oracle_lmhead_forward(const uint16_t *hidden, int64_t n_rows, int64_t ldh,
     return rc;
 }
 
+/*
+ * Nearest bf16 to v, ties to even, straight from the double (no detour through
+ * float, which would round twice).  bf16 has fp32's exponent range and 8
+ * significant bits; below 2^-126 its spacing is the fixed 2^-133.  Dividing by
+ * the spacing is exact (a power of two), rint() rounds to nearest-even in the
+ * default rounding mode, and the product is exactly representable in float.
+ */
 uint16_t oracle_bf16_rne(double v) {
     if (isnan(v)) return 0x7FC0;
     if (isinf(v)) return v > 0 ? 0x7F80 : 0xFF80;

@@ -45,6 +45,10 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of the logits' size (for counter scaling)")
+    ap.add_argument("--row-sweep", action="store_true",
+                    help="loss-mask workloads: also time the compact forward on leading parts of "
+                         "the row list (64 rows up to all), with a straight-line fit of time "
+                         "against rows")
     ap.add_argument("--lmhead-order", default="",
                     help="LM-head workloads, for counter runs: instead of timing, run one call per "
                          "letter in this order, E with the entropy output, L without (e.g. ELLELEEL)")
@@ -210,6 +214,50 @@ def time_passes(passes, steps, warmup, stream):
     return ms, wall
 
 
+def row_sweep(args, w, x, t, idx, stream):
+    """The compact forward (logprob, lse, entropy) on the first m entries of the
+    row list, for m from 64 up to all of them, and a least-squares line through
+    the points of 512 rows and more: its slope is the streaming rate, its
+    intercept the time a launch spends outside steady streaming (start-up and
+    the drain of its last rows)."""
+    import torch
+
+    import vocab_wide_cross_amd as vwc
+
+    M = int(idx.numel())
+    e = 2 if w.dtype == "bf16" else 4
+    sizes = sorted({m for m in (64, 128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096) if m < M}
+                   | {M})
+    lp, lse, ent = (torch.empty(M, device=x.device) for _ in range(3))
+    ws = torch.empty(max(vwc.workspace_bytes(M, w.vocab, x.dtype), 1), dtype=torch.uint8,
+                     device=x.device)
+    passes = [(f"fwd_rows[{m}]",
+               (lambda m=m: vwc.selected_logprob_fwd_rows(
+                   x, t, idx[:m], w.tau, logprob=lp[:m], lse=lse[:m], entropy=ent[:m],
+                   workspace=ws, stream=stream)), m * (w.vocab * e + 20)) for m in sizes]
+    samples, _ = time_passes(passes, args.steps, args.warmup, stream)
+    pts = []
+    for (name, _, b), smp, m in zip(passes, samples, sizes):
+        st = ms_stats(smp)
+        pts.append({"rows": m, **st, "frac": b / (st["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    fit = [p for p in pts if p["rows"] >= 512]
+    out = {"points": pts}
+    if len(fit) >= 2:
+        slope, icpt = fit_line([p["rows"] for p in fit], [p["ms"] for p in fit])
+        row_bytes = w.vocab * e + 20
+        out["fit"] = {"intercept_us": icpt * 1e3, "us_per_row": slope * 1e3,
+                      "streaming_frac": row_bytes / (slope * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
+def fit_line(xs, ys):
+    """Least-squares slope and intercept of ys against xs (at least two distinct xs)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sum((a - mx) ** 2 for a in xs)
+    return slope, my - slope * mx
+
+
 def bench_other(args, w, x):
     """The other workloads' passes: compacted rows (loss-mask index list),
     packed compact forward + backward, split-vocabulary partials + merge."""
@@ -337,6 +385,8 @@ def bench_other(args, w, x):
         "all_passes": {"ms": total_ms, "gbs_alg": total_b / (total_ms * 1e-3) / 1e9,
                        "frac": total_b / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
+    if args.row_sweep and w.mask != "none":
+        out["row_sweep"] = row_sweep(args, w, x, t, idx, stream)
     if w.n_slices > 1:
         sl, sls, sen = (torch.empty(N, device=dev) for _ in range(3))
         wsf = torch.empty(max(vwc.workspace_bytes(N, V, x.dtype), 1), dtype=torch.uint8,

@@ -85,3 +85,12 @@ def test_cpu_baseline_reports_all_threads_and_one():
     assert "1 thread" in out["sample_1core"]
     import oracle
     assert oracle.num_threads() == out["cores"]  # the thread count is restored
+
+
+def test_fit_line_recovers_a_line():
+    xs = [512, 1024, 1536, 2001]
+    slope, icpt = bench.fit_line(xs, [0.008 + 4.35e-5 * x for x in xs])
+    assert abs(slope - 4.35e-5) < 1e-12 and abs(icpt - 0.008) < 1e-9
+    # noise-free points off the line pull it by the least-squares amount
+    slope, icpt = bench.fit_line([0, 1, 2], [0.0, 1.0, 0.0])
+    assert slope == 0.0 and abs(icpt - 1.0 / 3.0) < 1e-15

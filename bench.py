@@ -482,7 +482,17 @@ def bench_lmhead(args, w):
                                                                 stream=stream), 0)]
     usmp, _ = time_passes(unf, max(3, args.steps // 4), 1, stream)
     ums = [ms_stats(smp)["ms"] for smp in usmp]
-    del logits, hc
+    del logits, hc, ws2
+    # The box's practical bf16 rate: hipBLASLt on a large square product (the
+    # MFMA peak assumes a clock that dense MFMA work does not hold).
+    sq = 16384
+    a_sq = torch.randn((sq, sq), device=dev).to(torch.bfloat16)
+    b_sq = torch.randn((sq, sq), device=dev).to(torch.bfloat16)
+    c_sq = torch.empty((sq, sq), dtype=torch.bfloat16, device=dev)
+    ssmp, _ = time_passes([("square", lambda: torch.matmul(a_sq, b_sq, out=c_sq), 0)],
+                          max(3, args.steps // 4), 1, stream)
+    sq_ms = ms_stats(ssmp[0])["ms"]
+    del a_sq, b_sq, c_sq
     out = {
         "metric": f"kept rows/s of the fused LM head ({w.name})",
         "value": M / (ms[0] * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -504,6 +514,10 @@ def bench_lmhead(args, w):
         "unfused_context": {"gemm_ms": ums[0], "gemm_tflops": flops / (ums[0] * 1e-3) / 1e12,
                             "fwd_over_logits_ms": ums[1], "total_ms": ums[0] + ums[1],
                             "logits_bytes": M * V * 2},
+        "square_gemm_context": {"shape": [sq, sq, sq], "ms": sq_ms,
+                                "tflops": 2.0 * sq ** 3 / (sq_ms * 1e-3) / 1e12,
+                                "lmhead_over_square": (flops / (ms[0] * 1e-3)) /
+                                                      (2.0 * sq ** 3 / (sq_ms * 1e-3))},
     }
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

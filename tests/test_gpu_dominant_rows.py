@@ -178,3 +178,54 @@ def test_entropy_gradient_fp32(tau):
     A = np.abs(g.astype(np.float64))[:, None] + ha * (np.abs(np.log(p)) + f["entropy"][:, None] + 1)
     bar = np.maximum(1e-6, p / tau32 * (A * (d_lse + 2.0 ** -20) + ha * d_h))
     check_fp32(got, ref, bar, f"entropy grad fp32 tau={tau}")
+
+
+def _large_rows(tau, seed):
+    """bf16 rows whose lse * log2(e) lies on both sides of 4096 (the bound below
+    which a bf16 gradient takes the exponent without the float pair's low part):
+    a top value `base` held by 1-3 columns, the rest 1-3 bf16 steps below it."""
+    rng = np.random.default_rng(seed)
+    tau32 = float(np.float32(tau))
+    lse_edge = 4096.0 / np.log2(np.e)  # lse where |B| = 4096
+    bases = []
+    for z in (lse_edge - 30, lse_edge - 6, lse_edge + 6, lse_edge + 30, 2 * lse_edge):
+        for sgn in (1.0, -1.0):
+            bases.append(sgn * z * tau32)
+    n, vocab = len(bases), 4099
+    x = np.empty((n, vocab), dtype=np.float32)
+    t = rng.integers(0, vocab, n).astype(np.int32)
+    for i, b in enumerate(bases):
+        b16 = W.bf16_bits_to_float32(W.float32_to_bf16_bits(np.array([b], dtype=np.float32)))[0]
+        step = np.spacing(np.float32(abs(b16))) * 65536.0  # one bf16 step at |b|
+        row = b16 - step * rng.integers(1, 4, vocab)
+        top = rng.choice(vocab, size=1 + i % 3, replace=False)
+        row[top] = b16
+        if i % 2 == 0:
+            row[t[i]] = b16  # the target among the top columns
+        x[i] = row
+    g = rng.uniform(-1, 1, n).astype(np.float32)
+    return W.float32_to_bf16_bits(x), t, g
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_bf16_rows_around_the_exponent_pair_bound(tau):
+    x, t, g = _large_rows(tau, 37)
+    xd, td, gd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    _, lse, _ = vwc.selected_logprob_fwd(xd, td, tau)
+    B = np.abs(_np(lse).astype(np.float64)) * np.log2(np.e)
+    assert (B < 4096).sum() >= 4 and (B > 4096).sum() >= 4
+    ref = oracle.backward(x, t, g, tau=tau)
+    gb = vwc.selected_logprob_bwd(xd, td, lse, gd, tau)
+    assert_bf16_grad(grad_bits(gb), ref, f"bf16 grad, large rows, tau={tau}", oracle)
+    g32 = _np(vwc.selected_logprob_bwd(xd, td, lse, gd, tau, grad_dtype=torch.float32))
+    bar, _ = fp32_grad_bar(x, t, g, tau, _np(lse))
+    check_fp32(g32, ref, bar, f"fp32 grad, large rows, tau={tau}")
+    _, lse1, _, grad = vwc.selected_logprob_fwd_bwd(xd, td, gd, tau)
+    sep = vwc.selected_logprob_bwd(xd, td, lse1, gd, tau)
+    assert torch.equal(grad.view(torch.int16), sep.view(torch.int16))
+    assert_bf16_grad(grad_bits(grad), ref, f"one-call bf16, large rows, tau={tau}", oracle)
+    # in place (the rows past the bound re-read their units before storing them)
+    xin = to_dev_logits(x)
+    _, lse2, _, gin = vwc.selected_logprob_fwd_bwd(xin, td, gd, tau, grad_logits=xin)
+    assert gin.data_ptr() == xin.data_ptr()
+    assert torch.equal(lse2, lse1) and torch.equal(gin.view(torch.int16), grad.view(torch.int16))

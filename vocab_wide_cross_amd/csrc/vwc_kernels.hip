@@ -41,6 +41,7 @@
 //    non-temporal 16-byte store; rows without loss are written as +0.0
 //    without being read.
 #include <math.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "vwc_internal.h"
@@ -844,19 +845,37 @@ __device__ __forceinline__ RowGrad row_grad(float c_hi, float c_lo, double tau, 
     return R;
 }
 
+// Whether a row's exponent needs the float pair.  An fp32 gradient always
+// does.  A bf16 gradient is rounded to 8 bits, and dropping x c_lo moves
+// u' by at most |x| c_lo < |x| c 2^-23; every element above 2^-126 has
+// |x| c <= |B| + 126, so for |B| < 4096 that is below 3.5e-4 relative in p,
+// a tenth of a bf16 step: such rows take x c_hi - B alone (one FMA less per
+// element), others (and non-finite B) keep the pair.
+__device__ __forceinline__ bool exponent_pair(bool fp32_grad, float B) {
+    return fp32_grad || !(fabsf(B) < 4096.f);
+}
+
 // Gradient of one unit.  Logprob only: o_k = gs p'_k with p'_k = 2^u'_k.
 // With the entropy term (WH):
 //   o_k = p_k (-g/tau - h/tau (z_k - lse + H)) = p'_k (a + b u'_k).
 // The target column adds g/tau (1 - p_t), computed as -expm1(x_t/tau - lse) in
 // fp64 so that p_t -> 1 does not cancel.
 // v_exp_f32 flushes results below 2^-126, which exp2f rescales at five more
-// instructions per element.  With FAST, a unit whose exponents all lie at or
-// above -126 (nearly every unit) takes the bare instruction, which gives
-// exp2f's bits there, and a unit with a smaller one (or NaN) takes exp2f: the
-// same results for fewer VALU cycles, at the cost of a branch per unit.  The
-// one-call kernel, whose compute phases run between its memory phases, uses
-// it; the streaming backward, bound by memory, runs faster without the branch.
-template <int DT, bool VEC, bool WH, bool FAST = false>
+// instructions per element.  EXP picks how p' is evaluated:
+//   kExpRescale: exp2f everywhere;
+//   kExpPerUnit: a unit whose exponents all lie at or above -126 (nearly every
+//     unit) takes the bare instruction, which gives exp2f's bits there, and a
+//     unit with a smaller one (or NaN) takes exp2f: the same results for fewer
+//     VALU cycles, at the cost of a branch per unit;
+//   kExpBare: the caller has shown that every exponent lies at or above -126.
+// The streaming backward, bound by memory, runs fastest with kExpRescale; the
+// one-call kernel, whose compute phases run between its memory phases, decides
+// once per thread.  PAIR: the exponent with the float pair (x c_hi - B) + x c_lo,
+// else x c_hi - B alone (see exponent_pair).  TGT: add the target column's
+// one-hot term here (callers that write that element themselves pass false).
+constexpr int kExpRescale = 0, kExpPerUnit = 1, kExpBare = 2;
+
+template <int DT, bool VEC, bool WH, int EXP = kExpRescale, bool PAIR = true, bool TGT = true>
 __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, int32_t col0,
                                           const RowGrad &R, float (&o)[Unit<DT, VEC>::N]) {
     using Un = Unit<DT, VEC>;
@@ -864,12 +883,13 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
 #pragma unroll
     for (int k = 0; k < Un::N; ++k) {
         const float x = Un::get(v, k);
-        u[k] = __builtin_fmaf(x, R.c_lo, __builtin_fmaf(x, R.c_hi, -R.B));
+        u[k] = PAIR ? __builtin_fmaf(x, R.c_lo, __builtin_fmaf(x, R.c_hi, -R.B))
+                    : __builtin_fmaf(x, R.c_hi, -R.B);
     }
     float umin = u[0];
 #pragma unroll
     for (int k = 1; k < Un::N; ++k) umin = fminf(umin, u[k]);
-    if (FAST && __builtin_expect(umin >= -126.f, 1)) {
+    if (EXP == kExpBare || (EXP == kExpPerUnit && __builtin_expect(umin >= -126.f, 1))) {
 #pragma unroll
         for (int k = 0; k < Un::N; ++k) {
             const float pk = __builtin_amdgcn_exp2f(u[k]);
@@ -885,7 +905,7 @@ __device__ __forceinline__ void unit_grad(const typename Unit<DT, VEC>::T &v, in
             o[k] = WH ? pk * __builtin_fmaf(R.b, fmaxf(u[k], kUFloor), R.a) : pk * R.gs;
         }
     }
-    if (static_cast<uint32_t>(R.t - col0) < static_cast<uint32_t>(Un::N)) {
+    if (TGT && static_cast<uint32_t>(R.t - col0) < static_cast<uint32_t>(Un::N)) {
 #pragma unroll
         for (int k = 0; k < Un::N; ++k)
             if (col0 + k == R.t) {
@@ -993,43 +1013,53 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         kl_mine = kl_lane[tid];
     }
 
-    int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
-    for (; b + (U - 1) * kBwdBlock < u1; b += U * kBwdBlock) {
-        T v[U];
+    auto stream = [&](auto pair_tag) {
+        constexpr bool kPair = decltype(pair_tag)::value;
+        int32_t b = u0 + static_cast<int32_t>(threadIdx.x);
+        for (; b + (U - 1) * kBwdBlock < u1; b += U * kBwdBlock) {
+            T v[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) v[j] = Un::load(src + b + j * kBwdBlock);
+            for (int j = 0; j < U; ++j) v[j] = Un::load(src + b + j * kBwdBlock);
+            // All U loads go out before any arithmetic (the scheduler may
+            // otherwise start unpacking after the first and hold the rest back).
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const int32_t unit = b + j * kBwdBlock;
-            float o[N];
-            unit_grad<DT, VEC, WH>(v[j], head + unit * N, R, o);
-            if (KLF && ((kl_mine >> ((unit - u0) / kBwdBlock)) & 1u))
-                kl_patch<N>(kl_tab, unit - u0, o);
-            GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(unit) * N * kGE, o);
-        }
-    }
-    for (; b < u1; b += kBwdBlock) {
-        const T v = Un::load(src + b);
-        float o[N];
-        unit_grad<DT, VEC, WH>(v, head + b * N, R, o);
-        if (KLF && ((kl_mine >> ((b - u0) / kBwdBlock)) & 1u)) kl_patch<N>(kl_tab, b - u0, o);
-        GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(b) * N * kGE, o);
-    }
-    if (VEC && last) {
-        const int32_t j = edge_column(head, nunits * N, p.vocab, static_cast<int32_t>(threadIdx.x));
-        if (j >= 0) {
-            using Us = Unit<DT, false>;
-            const typename Us::T v = reinterpret_cast<const typename Us::T *>(row)[j];
-            float o[1];
-            unit_grad<DT, false, WH>(v, j, R, o);
-            if constexpr (KLF) {  // column j - nunits * N (< N) of the tail
-                const int h = kl_find(kl_tab, kKlTailKey);
-                const int kk = static_cast<int>(threadIdx.x);
-                if (h >= 0 && ((kl_tab[h].cols >> kk) & 1u)) o[0] = kl_tab[h].val[kk];
+            for (int j = 0; j < U; ++j) {
+                const int32_t unit = b + j * kBwdBlock;
+                float o[N];
+                unit_grad<DT, VEC, WH, kExpRescale, kPair>(v[j], head + unit * N, R, o);
+                if (KLF && ((kl_mine >> ((unit - u0) / kBwdBlock)) & 1u))
+                    kl_patch<N>(kl_tab, unit - u0, o);
+                GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(unit) * N * kGE, o);
             }
-            GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, o);
         }
-    }
+        for (; b < u1; b += kBwdBlock) {
+            const T v = Un::load(src + b);
+            float o[N];
+            unit_grad<DT, VEC, WH, kExpRescale, kPair>(v, head + b * N, R, o);
+            if (KLF && ((kl_mine >> ((b - u0) / kBwdBlock)) & 1u)) kl_patch<N>(kl_tab, b - u0, o);
+            GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(b) * N * kGE, o);
+        }
+        if (VEC && last) {
+            const int32_t j = edge_column(head, nunits * N, p.vocab, static_cast<int32_t>(threadIdx.x));
+            if (j >= 0) {
+                using Us = Unit<DT, false>;
+                const typename Us::T v = reinterpret_cast<const typename Us::T *>(row)[j];
+                float o[1];
+                unit_grad<DT, false, WH, kExpRescale, kPair>(v, j, R, o);
+                if constexpr (KLF) {  // column j - nunits * N (< N) of the tail
+                    const int h = kl_find(kl_tab, kKlTailKey);
+                    const int kk = static_cast<int>(threadIdx.x);
+                    if (h >= 0 && ((kl_tab[h].cols >> kk) & 1u)) o[0] = kl_tab[h].val[kk];
+                }
+                GradStore<GDT, 1>::store(grow + static_cast<int64_t>(j) * kGE, o);
+            }
+        }
+    };
+    if (GDT == VWC_FP32 || exponent_pair(false, R.B))
+        stream(std::true_type{});
+    else if constexpr (GDT != VWC_FP32)
+        stream(std::false_type{});
 }
 
 // One workgroup per (row, segment) item.
@@ -1216,11 +1246,17 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     __builtin_amdgcn_sched_barrier(0);
 
     Lane L = lane_init();
+    float xmin = INFINITY;  // this thread's smallest whole-vector logit (NaN ignored)
+    auto unit_min = [&](const T &x) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) xmin = fminf(xmin, Un::get(x, k));
+    };
 #pragma unroll 1
     for (int k = 0; k < kFusedLds; ++k) {
         if (tid + k * kFusedBlock >= nunits) break;
         const T x[1] = {*reinterpret_cast<const T *>(stage + k * kStride + tid * 16)};
         fold_chunk<DT, true, 1, W>(x, 1, p.c, L);
+        unit_min(x[0]);
     }
     // The register units in short chunks (few unpacked values live at a time
     // while every unit stays held for phase 2).
@@ -1229,9 +1265,13 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
 #pragma unroll
     for (int k0 = 0; k0 < kFusedReg; k0 += kChunk) {
         const int nv = min(max(nreg - k0, 0), kChunk);
-        if (nv > 0)
+        if (nv > 0) {
             fold_chunk<DT, true, kChunk, W>(*reinterpret_cast<const T(*)[kChunk]>(&v[k0]), nv,
                                             p.c, L);
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j)
+                if (j < nv) unit_min(v[k0 + j]);
+        }
     }
     if (edge >= 0) fold_chunk<DT, false, 1, W>(ev, 1, p.c, L);
 
@@ -1278,34 +1318,92 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     R.tau = p.tau;
     R.t = t;
     const bool zero = g == 0.f;  // a row without loss: +0.0, nothing computed
-    auto emit = [&](const T &x, int32_t u, char *dst) {
-        float o[N];
-        if (zero) {
+    // p' = 2^u' with u' increasing in x, so the thread's smallest logit gives
+    // its smallest exponent: when that one lies at or above -126 every unit of
+    // the thread takes the bare exp2 (exp2f's bits there), else every unit takes
+    // exp2f, one decision per thread instead of one per unit.  The units are
+    // stored without the target column's one-hot term; the thread that owns that
+    // column writes its element afterwards.
+    auto phase2 = [&](auto pair_tag, auto bare_tag) {
+        constexpr bool kPair = decltype(pair_tag)::value;
+        constexpr int kExp = decltype(bare_tag)::value ? kExpBare : kExpRescale;
+        auto emit = [&](const T &x, int32_t u, char *dst) {
+            float o[N];
+            if (zero) {
 #pragma unroll
-            for (int k = 0; k < N; ++k) o[k] = 0.f;
-        } else {
-            unit_grad<DT, true, false, true>(x, head + u * N, R, o);
+                for (int k = 0; k < N; ++k) o[k] = 0.f;
+            } else {
+                unit_grad<DT, true, false, kExp, kPair, false>(x, head + u * N, R, o);
+            }
+            GradStore<DT, N>::store(dst, o);
+        };
+#pragma unroll
+        for (int kr = 0; kr < kFusedReg; ++kr)
+            if (kr < nreg)
+                emit(v[kr], tid + (kFusedLds + kr) * kFusedBlock, vgrow + (kFusedLds + kr) * kStride);
+        // The register units are spent, so the LDS units are all read up front
+        // (slots past the row hold zeros and are not stored).
+        T xl[kFusedLds];
+#pragma unroll
+        for (int k = 0; k < kFusedLds; ++k)
+            xl[k] = *reinterpret_cast<const T *>(stage + k * kStride + tid * 16);
+#pragma unroll
+        for (int k = 0; k < kFusedLds; ++k) {
+            const int32_t u = tid + k * kFusedBlock;
+            if (u < nunits) emit(xl[k], u, vgrow + k * kStride);
         }
-        GradStore<DT, N>::store(dst, o);
     };
+    const bool pair = exponent_pair(DT == VWC_FP32, R.B);
+    const float umin = pair ? __builtin_fmaf(xmin, R.c_lo, __builtin_fmaf(xmin, R.c_hi, -R.B))
+                            : __builtin_fmaf(xmin, R.c_hi, -R.B);
+    if constexpr (DT == VWC_FP32) {
+        if (umin >= -126.f)
+            phase2(std::true_type{}, std::true_type{});
+        else
+            phase2(std::true_type{}, std::false_type{});
+    } else if (!pair) {
+        if (umin >= -126.f)
+            phase2(std::false_type{}, std::true_type{});
+        else
+            phase2(std::false_type{}, std::false_type{});
+    } else {
+        // A row whose exponent keeps the float pair (|B| >= 4096, far outside any
+        // trained model's logits) re-reads its units from memory in a plain loop
+        // instead of a third unrolled copy of the above: each unit is read before
+        // this thread stores it, and no other thread touches it, so an in-place
+        // gradient is still safe.  exp2f's bits equal the bare exp2 where both apply.
+        const T *src = reinterpret_cast<const T *>(row + head * kE);
+#pragma unroll 1
+        for (int k = 0; k < kFusedLds + kFusedReg; ++k) {
+            const int32_t u = tid + k * kFusedBlock;
+            if (u >= nunits) break;
+            float o[N];
+            if (zero) {
 #pragma unroll
-    for (int kr = 0; kr < kFusedReg; ++kr)
-        if (kr < nreg)
-            emit(v[kr], tid + (kFusedLds + kr) * kFusedBlock, vgrow + (kFusedLds + kr) * kStride);
-    // The register units are spent, so the LDS units are all read up front
-    // (slots past the row hold zeros and are not stored).
-    T xl[kFusedLds];
-#pragma unroll
-    for (int k = 0; k < kFusedLds; ++k)
-        xl[k] = *reinterpret_cast<const T *>(stage + k * kStride + tid * 16);
-#pragma unroll
-    for (int k = 0; k < kFusedLds; ++k) {
-        const int32_t u = tid + k * kFusedBlock;
-        if (u < nunits) emit(xl[k], u, vgrow + k * kStride);
+                for (int e = 0; e < N; ++e) o[e] = 0.f;
+            } else {
+                unit_grad<DT, true, false, kExpRescale, true, false>(Un::load(src + u), head + u * N, R, o);
+            }
+            GradStore<DT, N>::store(vgrow + k * kStride, o);
+        }
+    }
+    // The target column, when it lies in the whole vectors: its unit went out
+    // above from this thread; this later store from the same thread replaces
+    // the element with the one-hot term included.
+    const int32_t tcol = t_ok ? t - head : -1;
+    if (!zero && tcol >= 0 && tcol < nunits * N && (tcol / N) % kFusedBlock == tid) {
+        const double d = static_cast<double>(Us::get(t_raw, 0)) / R.tau - R.lse;
+        float o[1] = {static_cast<float>(R.gt * -expm1(d))};
+        GradStore<DT, 1>::store(grow + static_cast<int64_t>(t) * kE, o);
     }
     if (edge >= 0) {
         float o[1] = {0.f};
-        if (!zero) unit_grad<DT, false, false, true>(ev[0], edge, R, o);
+        if (!zero) {
+            if (pair)
+                unit_grad<DT, false, false, kExpPerUnit, true>(ev[0], edge, R, o);
+            else
+                unit_grad<DT, false, false, kExpPerUnit, false>(ev[0], edge, R, o);
+        }
         GradStore<DT, 1>::store(grow + static_cast<int64_t>(edge) * kE, o);
     }
 }

@@ -332,6 +332,13 @@ def bench_other(args, w, x):
                        lambda: vwc.topk_kl_bwd(x, idx, tlp, fwd, g, vwc.VWC_KL_TAIL,
                                                grad_logits=grad, stream=stream),
                        N * (2 * V * e + K * (8 + 2 * e) + 20)))
+        # The same forward + backward as one call (the loss weight known up front):
+        # one read of the logits and the payload, one write of the gradient.
+        passes.append(("topk_kl_fwd_bwd(tail, K=%d, one call)" % K,
+                       lambda: vwc.topk_kl_fwd_bwd(x, idx, tlp, g, vwc.VWC_KL_TAIL,
+                                                   temperature=float(w.tau), grad_logits=grad,
+                                                   workspace=ws, stream=stream),
+                       N * (2 * V * e + K * (8 + e) + 24)))
     elif w.n_slices > 1:
         k, vl = w.n_slices, V // w.n_slices
         parts = torch.empty((k, N, 4), dtype=torch.float32, device=dev)

@@ -401,6 +401,35 @@ vwc_status vwc_topk_kl_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows
                                 int64_t ld_grad, vwc_grad_layout layout, hipStream_t stream);
 
 /*
+ * Top-k KL forward and backward in one call, for a distillation loss whose
+ * per-row weight g_r (grad_loss, float[n_rows]) is known before the forward,
+ * e.g. a token mean.  The results are those of vwc_topk_kl_fwd followed by
+ * vwc_topk_kl_bwd with the lse, student_mass, teacher_mass and topk_sum it
+ * wrote (the chunked top-k KL of "[megatron] feat: add memory-efficient
+ * chunked top-k KL computation": keep the logits and the per-row logZ,
+ * recompute the student softmax in the backward).  lse, student_mass,
+ * teacher_mass and topk_sum (float[n_rows]) are required, loss is nullable;
+ * the payload, mode, tail_mass_eps and the in-place rule are as in those two
+ * calls.  When a row fits on chip (as for vwc_selected_logprob_fwd_bwd), the
+ * gradient has the logits' dtype and 16-byte phase, and k <= 256, one
+ * workgroup per row reads the row once, reduces it, sums the payload, and
+ * writes the gradient (payload columns included) from the held values: one
+ * read and one write of the rows instead of two reads and one write.
+ * Otherwise the two calls run in turn (`workspace` as for vwc_topk_kl_fwd).
+ * lse, student_mass, teacher_mass, topk_sum and loss may differ from the
+ * separate forward's in the last bits (another reduction order); every
+ * result meets the same bounds, and the gradient is the separate backward's
+ * from these outputs.
+ */
+vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                               int32_t k, vwc_kl_mode mode, float tail_mass_eps,
+                               float temperature, const float *grad_loss, float *loss,
+                               float *student_mass, float *teacher_mass, float *topk_sum,
+                               float *lse, void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Partial of one vocabulary slice ([E] "Implementation", steps 1-3 in one
  * pass).  logits_slice points at global column v_start of row 0; the slice is
  * columns [0, v_local) of each row, rows ld elements apart.  targets hold

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 26
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
 
@@ -208,6 +208,34 @@ def test_fused_forward_backward_validation(lib):
              None) == INVALID
     assert f(FAKE, BF16, 4, 16, 16, FAKE, 1.0, FAKE, None, FAKE, None, g, BF16, 8, None, 0,
              None) == INVALID
+
+
+def test_topk_kl_one_call_validation(lib):
+    p, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    f = lib.vwc_topk_kl_fwd_bwd
+    f.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, ctypes.c_int32, ctypes.c_int, f32, f32, p,
+                  p, p, p, p, p, p, ctypes.c_int, i64, p, ctypes.c_size_t, p]
+    f.restype = ctypes.c_int
+    g = ctypes.c_void_p(0x900000)
+
+    def call(n=4, k=8, mode=1, eps=1e-6, tau=1.0, gl=FAKE, Q=FAKE, P=FAKE, S=FAKE, lse=FAKE,
+             grad=g, gdt=BF16, ldg=1000):
+        return f(FAKE, BF16, n, 1000, 1000, FAKE, FAKE, k, mode, eps, tau, gl, None, Q, P, S,
+                 lse, grad, gdt, ldg, None, 0, None)
+
+    assert call(n=0) == OK                                  # no rows
+    for kw in ({"lse": None}, {"Q": None}, {"P": None}, {"S": None}, {"gl": None},
+               {"grad": None}):
+        assert call(**kw) == INVALID, kw                    # every output but the loss required
+    assert b"null grad_loss" in err_str(lib)
+    assert call(k=0) == INVALID and call(k=1001) == INVALID  # k in [1, vocab]
+    assert call(mode=5) == INVALID
+    assert call(eps=0.0) == INVALID                         # the tail guard must lie in (0, 1)
+    assert call(tau=0.0) == INVALID
+    assert call(ldg=999) == INVALID
+    # in place without the single-pass payload (k > 256) runs nothing
+    assert call(k=300, grad=FAKE) == UNSUPPORTED
+    assert b"in-place top-k KL" in err_str(lib)
 
 
 def test_partial_combine_and_mask_validation(lib):

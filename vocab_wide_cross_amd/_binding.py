@@ -66,6 +66,8 @@ def _load() -> ctypes.CDLL:
                                   f32, p, p, p, p, p, p, sz, p], i32),
         "vwc_topk_kl_bwd_rows": ([p, i32, i64, i64, i64, p, i64, p, p, ctypes.c_int32, i32, f32,
                                   f32, p, p, p, p, p, p, i32, i64, i32, p], i32),
+        "vwc_topk_kl_fwd_bwd": ([p, i32, i64, i64, i64, p, p, ctypes.c_int32, i32, f32, f32, p,
+                                 p, p, p, p, p, p, i32, i64, p, sz, p], i32),
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
@@ -434,6 +436,32 @@ def topk_kl_bwd(logits, topk_idx, teacher_logprob, fwd, grad_loss, mode=VWC_KL_T
                                 _ptr(fwd["topk_sum"]), _ptr(grad_loss), _ptr(g), _dtype(g), gld,
                                 _stream(stream, logits)))
     return g
+
+
+def topk_kl_fwd_bwd(logits, topk_idx, teacher_logprob, grad_loss, mode=VWC_KL_TAIL,
+                    tail_mass_eps=1e-6, temperature=1.0, grad_logits=None, grad_dtype=None,
+                    workspace=None, stream=None):
+    """Top-k KL forward and backward in one call for a loss weight grad_loss known up front;
+    returns (dict of float32 [n_rows] tensors as topk_kl_fwd, grad_logits)."""
+    n, v, ld = _rows_view(logits)
+    _i32(topk_idx, "topk_idx")
+    if topk_idx.dim() != 2 or topk_idx.size(0) != n or teacher_logprob.shape != topk_idx.shape:
+        raise ValueError("topk_idx and teacher_logprob must both be [n_rows, k]")
+    _f32_in(teacher_logprob, topk_idx.numel(), "teacher_logprob")
+    _f32_in(grad_loss, n, "grad_loss")
+    out = {name: torch.empty(n, dtype=torch.float32, device=logits.device)
+           for name in ("loss", "student_mass", "teacher_mass", "topk_sum", "lse")}
+    g = _grad_out(logits, n, grad_logits, grad_dtype)
+    gld = _grad_rows(g, n, v)
+    ws, wsb = _workspace(n, v, logits, workspace)
+    _check(_lib.vwc_topk_kl_fwd_bwd(_ptr(logits), _dtype(logits), n, v, ld, _ptr(topk_idx),
+                                    _ptr(teacher_logprob), topk_idx.size(1), int(mode),
+                                    float(tail_mass_eps), float(temperature), _ptr(grad_loss),
+                                    _ptr(out["loss"]), _ptr(out["student_mass"]),
+                                    _ptr(out["teacher_mass"]), _ptr(out["topk_sum"]),
+                                    _ptr(out["lse"]), _ptr(g), _dtype(g), gld, _ptr(ws), wsb,
+                                    _stream(stream, logits)))
+    return out, g
 
 
 def topk_kl_fwd_rows(logits, row_idx, topk_idx, teacher_logprob, mode=VWC_KL_TAIL,

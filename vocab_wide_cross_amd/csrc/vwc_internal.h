@@ -167,6 +167,15 @@ struct FusedPlan {
     void *grad;
     int64_t ld_grad;
     bool grad_by_row_id;      // gradient row = row id (dense, scatter) or output index
+    // Top-k KL instead of the target's logprob (kl_idx non-null): the payload
+    // [m][kl_k] (student columns, teacher log-probs), the objective, and its
+    // outputs ([m]; loss nullable); grad_out is then the loss weight.
+    const int32_t *kl_idx;
+    const float *kl_tlp;
+    int32_t kl_k;
+    int kl_mode;
+    double kl_eps;
+    float *kl_loss, *kl_P, *kl_Q, *kl_S;
 };
 
 // The fused top-k KL backward keeps a segment's payload columns in an LDS hash

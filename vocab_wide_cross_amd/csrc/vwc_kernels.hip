@@ -750,11 +750,16 @@ __device__ __forceinline__ KlCoef kl_coef(int mode, double eps, double P, double
 // Gradient of payload column n of a row whose student logit is x:
 // (beta q - kappa p_n) g / tau with q = exp(x / tau - lse), p_n = exp(a_n), in
 // fp64 (the two terms cancel when the student matches the teacher).
+__device__ __forceinline__ float kl_payload_value(double q, double pn, double gt, double beta,
+                                                  double kappa) {
+    return static_cast<float>(gt * (beta * q - kappa * pn));
+}
+
 __device__ __forceinline__ float kl_payload_grad(double x, double tau, double lse, double gt,
                                                  const KlCoef &c, float tlp) {
     const double q = exp(x / tau - lse);
     const double pn = exp(static_cast<double>(tlp));
-    return static_cast<float>(gt * (c.beta * q - c.kappa * pn));
+    return kl_payload_value(q, pn, gt, c.beta, c.kappa);
 }
 
 // The payload columns of one backward segment, in LDS.  An open-addressing
@@ -1169,8 +1174,24 @@ __global__ __launch_bounds__(kTopkBlock) void topk_fixup_kernel(TopkPlan p) {
 // values with the backward's own per-unit code and writes it.  Every read of
 // the row ends before the barrier that starts phase 2, so the gradient may
 // replace the logits.
-template <int DT, bool W>
+//
+// KL: the same row pass for the top-k KL objective instead of the target's
+// logprob (the tail-aware / truncated objective of "[megatron] feat: add
+// memory-efficient chunked top-k KL computation", with the per-row weight
+// known up front).  Each thread below k also loads one payload entry: its
+// column id and teacher log-prob first (parked in LDS once the row's loads
+// are out, so that no register holds them through the fold), the student
+// logit at that column after the row, as the logprob mode loads the target's.  Once the row's lse is known, those
+// threads sum P, Q and S (a fixed butterfly per wave, then the waves in
+// order), thread 0 writes P, Q and S and turns their float values into the
+// gradient's coefficients exactly as the separate backward reads them, and
+// every payload thread computes its column's gradient and files it, in LDS,
+// under the thread that stores that column's unit, which writes it after the
+// unit (same thread, later store).  The loss, which the gradient does not
+// need, is written at the end.
+template <int DT, bool W, bool KL = false>
 __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
+    static_assert(!(KL && W), "the top-k KL call writes no entropy");
     using Un = Unit<DT, true>;
     using T = typename Un::T;
     using Us = Unit<DT, false>;
@@ -1181,15 +1202,35 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     __shared__ Lane wave_state[kFusedBlock / 64];
     __shared__ double row_gt;
     __shared__ float row_lse, row_B, row_gs;
+    // KL: the waves' payload sums (P, Q, S, bad), the row's coefficients, the
+    // payload gradients and, per thread, the list of those its units hold.
+    constexpr int kKlN = KL ? kKlMaxK : 1;
+    constexpr int kKlTid0 = 64;  // payload entry n is thread kKlTid0 + n (waves 1-4)
+    constexpr int kKlWaves = kKlMaxK / 64;
+    static_assert(!KL || kKlTid0 + kKlMaxK <= kFusedBlock, "payload threads");
+    __shared__ double kl_sums[KL ? kKlWaves * 3 : 1];
+    __shared__ double kl_pn[kKlN], kl_q[kKlN];  // p_n = exp(a_n), q at the payload column
+    __shared__ double kl_beta, kl_kappa;
+    __shared__ int kl_zero;
+    __shared__ int kl_head[KL ? kFusedBlock : 1];
+    __shared__ int kl_next[kKlN];
+    __shared__ int kl_col[kKlN];   // the payload column ids
+    __shared__ float kl_val[kKlN];  // the teacher log-probs, then the payload gradients
 
     const int64_t i = blockIdx.x;  // output row
     const int32_t tid = static_cast<int32_t>(threadIdx.x);
     const int64_t r = p.row_idx ? static_cast<int64_t>(p.row_idx[i]) : i;
     if (r < 0 || r >= p.n_rows) {  // row id outside the tensor: NaN outputs, nothing written
         if (tid == 0) {
-            if (p.logprob) p.logprob[i] = NAN;
+            if (!KL && p.logprob) p.logprob[i] = NAN;
             p.lse[i] = NAN;
             if (W && p.entropy) p.entropy[i] = NAN;
+            if (KL) {
+                if (p.kl_loss) p.kl_loss[i] = NAN;
+                p.kl_P[i] = NAN;
+                p.kl_Q[i] = NAN;
+                p.kl_S[i] = NAN;
+            }
         }
         return;
     }
@@ -1216,6 +1257,16 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     // the register units still arrive.  Each thread reads back only what its
     // own wave's loads wrote.  The edge and target loads are unconditional
     // (clamped to the row) so that no branch makes the compiler wait for them.
+    // KL: this thread's payload entry (threads past k load entry k - 1 and
+    // ignore it, so that every wave issues the same loads).
+    int32_t kj = 0;
+    float ka = 0.f;
+    if constexpr (KL) {
+        const int64_t n = i * p.kl_k + min(max(tid - kKlTid0, 0), p.kl_k - 1);
+        kj = p.kl_idx[n];
+        ka = p.kl_tlp[n];
+        kl_head[tid] = -1;
+    }
     const int32_t edge = edge_column(head, nunits * N, p.vocab, tid);
     typename Us::T ev[1] = {reinterpret_cast<const typename Us::T *>(row)[max(edge, 0)]};
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -1234,9 +1285,20 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
                                           0, 2));
     __builtin_amdgcn_sched_barrier(0);
     const float g = p.grad_out[i];
-    const int32_t t = p.targets[r];
+    // The target (logprob mode), or this thread's payload column (KL): one more
+    // load each, after the row's.
+    const int32_t t = KL ? -1 : p.targets[r];
     const bool t_ok = t >= 0 && t < p.vocab;
-    const typename Us::T t_raw = reinterpret_cast<const typename Us::T *>(row)[t_ok ? t : 0];
+    const bool kj_ok = kj >= 0 && kj < p.vocab;
+    const typename Us::T t_raw =
+        reinterpret_cast<const typename Us::T *>(row)[KL ? (kj_ok ? kj : 0) : (t_ok ? t : 0)];
+    if constexpr (KL) {  // the payload entry's id and log-prob wait in LDS
+        const int32_t n = tid - kKlTid0;
+        if (n >= 0 && n < p.kl_k) {
+            kl_col[n] = kj_ok ? kj : -1;
+            kl_val[n] = ka;
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // s_waitcnt vmcnt(kFusedReg + 1) (6-bit count: low 4 bits at [3:0], high 2
     // at [15:14]; expcnt and lgkmcnt not waited on).
@@ -1283,24 +1345,124 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     const Lane Wv = wave_reduce_rescaled(L);
     if ((tid & 63) == 0) wave_state[wave] = Wv;
     __syncthreads();
+    // KL, while wave 0 forms the row's lse: the payload's sums that do not need
+    // it, P = sum p_n, D = sum p_n (a_n - x_n / tau) and
+    // E = sum exp((x_n - mr) / tau) against the row's largest logit mr, so that
+    // Q = exp(mr / tau - lse) E and S = D + lse P once lse is known.  An entry
+    // outside the row adds NaN to P, which then makes P, Q and S NaN.
+    if constexpr (KL) {
+        if (wave >= 1 && wave <= kKlWaves) {
+            const int32_t n = tid - kKlTid0;
+            const bool mine = n < p.kl_k;
+            float mr = -INFINITY;
+            for (int w = 0; w < kFusedBlock / 64; ++w) mr = fmaxf(mr, wave_state[w].m);
+            double sP = 0.0, sD = 0.0, sE = 0.0;
+            if (mine) {
+                if (kl_col[n] < 0) {
+                    sP = NAN;
+                } else {
+                    const double a = static_cast<double>(kl_val[n]);
+                    const double x = static_cast<double>(Us::get(t_raw, 0)) / p.tau;
+                    const double pn = exp(a);
+                    kl_pn[n] = pn;
+                    sP = pn;
+                    sD = pn * (a - x);
+                    sE = exp(x - static_cast<double>(mr) / p.tau);
+                }
+            }
+            sP = wave_sum(sP);
+            sD = wave_sum(sD);
+            sE = wave_sum(sE);
+            if ((tid & 63) == 0) {
+                double *o = kl_sums + (wave - 1) * 3;
+                o[0] = sP;
+                o[1] = sD;
+                o[2] = sE;
+            }
+        }
+    }
     if (wave == 0) {
         const Lane Lw = (tid < kFusedBlock / 64) ? wave_state[tid] : lane_init();
         const Lane Rw = wave_reduce_rescaled(Lw);
         if (tid == 0) {
-            const double tx = !t_ok ? NAN : static_cast<double>(Us::get(t_raw, 0));
+            const double tx = KL ? -INFINITY : !t_ok ? NAN : static_cast<double>(Us::get(t_raw, 0));
             const P64 part = to_partial(Rw, p.c, tx);
             const Merged mg = merge_partials([&](int) { return part; }, 1, p.tau);
-            write_final(mg, p.tau, i, p.logprob, p.lse, W ? p.entropy : nullptr);
+            write_final(mg, p.tau, i, KL ? nullptr : p.logprob, p.lse, W ? p.entropy : nullptr);
             const float lse32 = static_cast<float>(mg.M / p.tau + log(mg.S));  // lse[i]
-            const RowGrad R0 = row_grad(p.gc_hi, p.gc_lo, p.tau, lse32, g, 0.f, 0.0,
-                                        -static_cast<double>(g) / p.tau);
             row_lse = lse32;
-            row_B = R0.B;
-            row_gs = R0.gs;
-            row_gt = R0.gt;
+            if constexpr (!KL) {
+                const RowGrad R0 = row_grad(p.gc_hi, p.gc_lo, p.tau, lse32, g, 0.f, 0.0,
+                                            -static_cast<double>(g) / p.tau);
+                row_B = R0.B;
+                row_gs = R0.gs;
+                row_gt = R0.gt;
+            }
         }
     }
     __syncthreads();
+
+    if constexpr (KL) {
+        const double lse = static_cast<double>(row_lse);
+        const int32_t n = tid - kKlTid0;
+        const bool mine = n >= 0 && n < p.kl_k;
+        if (tid == 0) {
+            // P, Q and S in the top-k forward's definitions; bad entries make
+            // them NaN.  Then the gradient's coefficients from their float
+            // values, as the separate backward reads them back.
+            double P = 0.0, D = 0.0, E = 0.0;
+            for (int w = 0; w < kKlWaves; ++w) {
+                P += kl_sums[w * 3 + 0];
+                D += kl_sums[w * 3 + 1];
+                E += kl_sums[w * 3 + 2];
+            }
+            float mr = -INFINITY;
+            for (int w = 0; w < kFusedBlock / 64; ++w) mr = fmaxf(mr, wave_state[w].m);
+            double Q = exp(static_cast<double>(mr) / p.tau - lse) * E;
+            double S = D + lse * P;
+            if (P != P) P = Q = S = NAN;  // an entry outside the row
+            kl_sums[0] = P;  // kept for the loss at the end
+            kl_sums[1] = Q;
+            kl_sums[2] = S;
+            const float Pf = static_cast<float>(P), Qf = static_cast<float>(Q),
+                        Sf = static_cast<float>(S);
+            p.kl_P[i] = Pf;
+            p.kl_Q[i] = Qf;
+            p.kl_S[i] = Sf;
+            KlCoef kc{0.0, 0.0, 0.0, false};
+            if (g != 0.f)
+                kc = kl_coef(p.kl_mode, p.kl_eps, static_cast<double>(Pf),
+                             static_cast<double>(Qf), static_cast<double>(Sf));
+            const double gt = static_cast<double>(g) / p.tau;
+            const RowGrad R0 = row_grad(p.gc_hi, p.gc_lo, p.tau, row_lse, g, 0.f, 0.0,
+                                        gt * kc.alpha);
+            row_B = R0.B;
+            row_gs = R0.gs;
+            row_gt = R0.gt;
+            kl_beta = kc.beta;
+            kl_kappa = kc.kappa;
+            kl_zero = (g == 0.f || kc.dead) ? 1 : 0;
+        } else if (mine && kl_col[n] >= 0) {
+            // q at the payload column, as the separate backward forms it.
+            kl_q[n] = exp(static_cast<double>(Us::get(t_raw, 0)) / p.tau - lse);
+        }
+        __syncthreads();
+        // Each payload column's gradient (beta q - kappa p_n) g / tau, filed under
+        // the thread that stores its unit (or, outside the whole vectors, its
+        // edge element).
+        if (mine && kl_zero == 0) {
+            const int32_t pj = kl_col[n];
+            if (pj >= 0) {
+                kl_val[n] = kl_payload_value(kl_q[n], kl_pn[n], row_gt, kl_beta, kl_kappa);
+                const int32_t body = nunits * N;
+                const int32_t owner = pj < head          ? pj
+                                      : pj >= head + body ? pj - body
+                                                          : ((pj - head) / N) % kFusedBlock;
+                kl_next[n] = atomicExch(&kl_head[owner], n);
+            }
+        }
+        __syncthreads();
+    }
 
     // Phase 2: the gradient, as the backward computes it from the saved fp32 lse
     // (the row constants row_grad gives for it).
@@ -1317,7 +1479,8 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     R.lse = static_cast<double>(row_lse);
     R.tau = p.tau;
     R.t = t;
-    const bool zero = g == 0.f;  // a row without loss: +0.0, nothing computed
+    // A row without loss (or a clamped truncated KL row): +0.0, nothing computed.
+    const bool zero = KL ? kl_zero != 0 : g == 0.f;
     // p' = 2^u' with u' increasing in x, so the thread's smallest logit gives
     // its smallest exponent: when that one lies at or above -126 every unit of
     // the thread takes the bare exp2 (exp2f's bits there), else every unit takes
@@ -1391,7 +1554,7 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     // above from this thread; this later store from the same thread replaces
     // the element with the one-hot term included.
     const int32_t tcol = t_ok ? t - head : -1;
-    if (!zero && tcol >= 0 && tcol < nunits * N && (tcol / N) % kFusedBlock == tid) {
+    if (!KL && !zero && tcol >= 0 && tcol < nunits * N && (tcol / N) % kFusedBlock == tid) {
         const double d = static_cast<double>(Us::get(t_raw, 0)) / R.tau - R.lse;
         float o[1] = {static_cast<float>(R.gt * -expm1(d))};
         GradStore<DT, 1>::store(grow + static_cast<int64_t>(t) * kE, o);
@@ -1405,6 +1568,27 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
                 unit_grad<DT, false, false, kExpPerUnit, false>(ev[0], edge, R, o);
         }
         GradStore<DT, 1>::store(grow + static_cast<int64_t>(edge) * kE, o);
+    }
+    // KL: the payload columns this thread's units (or edge element) hold, after
+    // those stores.  The list holds at most k entries.
+    if constexpr (KL) {
+        if (!zero)
+            for (int e = kl_head[tid]; e >= 0; e = kl_next[e]) {
+                const float o[1] = {kl_val[e]};
+                GradStore<DT, 1>::store(grow + static_cast<int64_t>(kl_col[e]) * kE, o);
+            }
+        if (tid == 0 && p.kl_loss) {  // the loss, as the top-k forward defines it
+            const double P = kl_sums[0], Q = kl_sums[1], S = kl_sums[2];
+            double Lk;
+            if (p.kl_mode == VWC_KL_TRUNCATED) {
+                Lk = S < 0.0 ? 0.0 : S;
+            } else {
+                const double pt = P < 1.0 ? 1.0 - P : 0.0;
+                const double qt = fmax(1.0 - Q, p.kl_eps);
+                Lk = S + (pt == 0.0 ? 0.0 : pt * (log(pt) - log(qt)));
+            }
+            p.kl_loss[i] = static_cast<float>(Lk);
+        }
     }
 }
 
@@ -1660,7 +1844,12 @@ hipError_t launch_bwd(const BwdPlan &p, hipStream_t stream) {
 hipError_t launch_fused(const FusedPlan &p, hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>(p.m)), block(kFusedBlock);
     const bool w = p.entropy != nullptr;
-    if (p.dt == VWC_BF16) {
+    if (p.kl_idx) {
+        if (p.dt == VWC_BF16)
+            hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, false, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fused_row_kernel<VWC_FP32, false, true>), grid, block, 0, stream, p);
+    } else if (p.dt == VWC_BF16) {
         if (w)
             hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, true>), grid, block, 0, stream, p);
         else

@@ -430,6 +430,21 @@ vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same over the row set row_idx[0..m): the payload, grad_loss and the
+ * outputs are indexed by list position (as for vwc_topk_kl_fwd_rows), layout
+ * as for vwc_topk_kl_bwd_rows.  Each listed row gets the dense call's bits.
+ */
+vwc_status vwc_topk_kl_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                    int64_t vocab, int64_t ld, const int32_t *row_idx, int64_t m,
+                                    const int32_t *topk_idx, const float *teacher_logprob,
+                                    int32_t k, vwc_kl_mode mode, float tail_mass_eps,
+                                    float temperature, const float *grad_loss, float *loss,
+                                    float *student_mass, float *teacher_mass, float *topk_sum,
+                                    float *lse, void *grad_logits, vwc_dtype grad_dt,
+                                    int64_t ld_grad, vwc_grad_layout layout, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Partial of one vocabulary slice ([E] "Implementation", steps 1-3 in one
  * pass).  logits_slice points at global column v_start of row 0; the slice is
  * columns [0, v_local) of each row, rows ld elements apart.  targets hold

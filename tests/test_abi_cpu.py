@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
 
@@ -236,6 +236,20 @@ def test_topk_kl_one_call_validation(lib):
     # in place without the single-pass payload (k > 256) runs nothing
     assert call(k=300, grad=FAKE) == UNSUPPORTED
     assert b"in-place top-k KL" in err_str(lib)
+    fr = lib.vwc_topk_kl_fwd_bwd_rows
+    fr.argtypes = [p, ctypes.c_int, i64, i64, i64, p, i64, p, p, ctypes.c_int32, ctypes.c_int, f32,
+                   f32, p, p, p, p, p, p, p, ctypes.c_int, i64, ctypes.c_int, p, ctypes.c_size_t, p]
+    fr.restype = ctypes.c_int
+
+    def rows(m=2, idx=FAKE, layout=0, grad=g):
+        return fr(FAKE, BF16, 4, 1000, 1000, idx, m, FAKE, FAKE, 8, 1, 1e-6, 1.0, FAKE, None,
+                  FAKE, FAKE, FAKE, FAKE, grad, BF16, 1000, layout, None, 0, None)
+
+    assert rows(m=0, idx=None) == OK                         # empty row set
+    assert rows(idx=None) == INVALID and b"row_idx" in err_str(lib)
+    assert rows(layout=7) == INVALID and b"layout" in err_str(lib)
+    # in place needs gradient rows indexed by row id (the scatter layout)
+    assert rows(grad=FAKE) == INVALID and b"row id" in err_str(lib)
 
 
 def test_partial_combine_and_mask_validation(lib):

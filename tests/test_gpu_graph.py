@@ -132,6 +132,8 @@ def test_split_vocabulary_and_topk_kl_replay_bitwise():
             f = vwc.topk_kl_fwd(x, cols, tlp, mode=mode)
             g = vwc.topk_kl_bwd(x, cols, tlp, f, gl, mode=mode)
             outs += [f["loss"], f["lse"], g]
+            f1, g1 = vwc.topk_kl_fwd_bwd(x, cols, tlp, gl, mode=mode)  # the one call
+            outs += [f1["loss"], f1["teacher_mass"], f1["lse"], g1]
         return outs
 
     refill(-1)

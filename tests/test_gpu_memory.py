@@ -114,6 +114,11 @@ def test_topk_kl_allocates_only_outputs_and_row_workspace(inputs):
     grew, gl = _peak_growth(lambda: vwc.topk_kl_bwd(logits, idx, tlp, fwd, grad_out))
     log(f"top-k KL bwd: grew {grew} B")
     assert grew <= _bytes(gl) + SLACK
+    del gl
+    grew, (f1, g1) = _peak_growth(lambda: vwc.topk_kl_fwd_bwd(logits, idx, tlp, grad_out))
+    log(f"top-k KL one call: grew {grew} B")
+    assert grew <= (_bytes(g1, *f1.values()) + vwc.workspace_bytes(N, V, torch.bfloat16) +
+                    SLACK)
 
 
 def test_lmhead_never_allocates_logits():

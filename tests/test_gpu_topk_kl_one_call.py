@@ -189,3 +189,41 @@ def test_one_call_full_size_k128():
         del grad
     del x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_one_call_rows_equal_dense_rows(mode):
+    """The row-set one call gives each listed row the dense one call's bits (outputs
+    and gradient, compact and scatter layouts); bad row ids give NaN outputs and no
+    gradient."""
+    w = W.scaled("distill_bf16_4096x248320_k128", 16, 151936)
+    x = W.all_logits(w)
+    idx, tlp = W.topk_payload(w)
+    g = np.random.default_rng(8).uniform(-1, 1, w.n_rows).astype(np.float32)
+    g[5] = 0.0
+    xd = to_dev_logits(x)
+    idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
+    dense, dgrad = vwc.topk_kl_fwd_bwd(xd, idd, tld, gd, mode)
+    rows = np.array([15, 0, 5, 9, 3], np.int32)
+    rl = torch.from_numpy(rows).to(DEV).long()
+    rd = torch.from_numpy(rows).to(DEV)
+    pay = (idd[rl].contiguous(), tld[rl].contiguous())
+    sub, comp = vwc.topk_kl_fwd_bwd_rows(xd, rd, *pay, gd[rl].contiguous(), mode)
+    for key in dense:
+        assert torch.equal(sub[key], dense[key][rl]), key
+    assert torch.equal(_bits(comp), _bits(dgrad[rl]))
+    scat = torch.full_like(xd, float("nan"))
+    vwc.topk_kl_fwd_bwd_rows(xd, rd, *pay, gd[rl].contiguous(), mode, grad_logits=scat,
+                             layout=vwc.VWC_GRAD_SCATTER)
+    assert torch.equal(_bits(scat[rl]), _bits(dgrad[rl]))
+    others = np.setdiff1d(np.arange(w.n_rows), rows)
+    assert torch.isnan(scat[others].float()).all()  # rows outside the list untouched
+    bad = torch.tensor([2, -1, 16], dtype=torch.int32, device=DEV)
+    bl = torch.tensor([2, 0, 0], device=DEV).long()
+    cg = torch.full((3, 151936), 7.0, dtype=torch.bfloat16, device=DEV)
+    sb, _ = vwc.topk_kl_fwd_bwd_rows(xd, bad, idd[bl].contiguous(), tld[bl].contiguous(),
+                                     gd[bl].contiguous(), mode, grad_logits=cg)
+    assert torch.isnan(sb["loss"][1:]).all() and torch.isnan(sb["lse"][1:]).all()
+    assert torch.isfinite(sb["loss"][0])
+    assert torch.equal(_bits(cg[0]), _bits(dgrad[2]))
+    assert torch.all(cg[1:].float() == 7.0)  # no gradient written for bad ids

@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     partial_combine, selected_logprob_bwd, selected_logprob_bwd_rows, selected_logprob_fwd,
     selected_logprob_fwd_bwd, selected_logprob_fwd_bwd_rows, selected_logprob_fwd_noalloc,
     selected_logprob_fwd_rows, topk_kl_bwd, topk_kl_bwd_rows, topk_kl_fwd, topk_kl_fwd_bwd,
-    topk_kl_fwd_rows,
+    topk_kl_fwd_bwd_rows, topk_kl_fwd_rows,
     vocab_partial, workspace_bytes,
 )
 from .autograd import selected_logprob  # noqa: F401,E402

@@ -68,6 +68,9 @@ def _load() -> ctypes.CDLL:
                                   f32, p, p, p, p, p, p, i32, i64, i32, p], i32),
         "vwc_topk_kl_fwd_bwd": ([p, i32, i64, i64, i64, p, p, ctypes.c_int32, i32, f32, f32, p,
                                  p, p, p, p, p, p, i32, i64, p, sz, p], i32),
+        "vwc_topk_kl_fwd_bwd_rows": ([p, i32, i64, i64, i64, p, i64, p, p, ctypes.c_int32, i32,
+                                      f32, f32, p, p, p, p, p, p, p, i32, i64, i32, p, sz, p],
+                                     i32),
         "vwc_vocab_partial": ([p, i32, i64, i64, i64, i64, p, p, i64, f32, p, p, sz, p], i32),
         "vwc_partial_combine": ([p, ctypes.c_int32, i64, f32, p, p, p, p], i32),
         "vwc_mask_to_index": ([p, i64, p, p, p], i32),
@@ -462,6 +465,39 @@ def topk_kl_fwd_bwd(logits, topk_idx, teacher_logprob, grad_loss, mode=VWC_KL_TA
                                     _ptr(out["lse"]), _ptr(g), _dtype(g), gld, _ptr(ws), wsb,
                                     _stream(stream, logits)))
     return out, g
+
+
+def topk_kl_fwd_bwd_rows(logits, row_idx, topk_idx, teacher_logprob, grad_loss,
+                         mode=VWC_KL_TAIL, tail_mass_eps=1e-6, temperature=1.0, grad_logits=None,
+                         grad_dtype=None, layout=VWC_GRAD_COMPACT, workspace=None, stream=None):
+    """The one-call top-k KL over the rows row_idx; payload [m, k], grad_loss and outputs [m];
+    returns (dict as topk_kl_fwd_rows, grad_logits compact [m, vocab] or scattered)."""
+    n, v, ld = _rows_view(logits)
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    _i32(topk_idx, "topk_idx")
+    if topk_idx.dim() != 2 or topk_idx.size(0) != m or teacher_logprob.shape != topk_idx.shape:
+        raise ValueError("topk_idx and teacher_logprob must both be [m, k]")
+    _f32_in(teacher_logprob, topk_idx.numel(), "teacher_logprob")
+    _f32_in(grad_loss, m, "grad_loss")
+    out = {name: torch.empty(m, dtype=torch.float32, device=logits.device)
+           for name in ("loss", "student_mass", "teacher_mass", "topk_sum", "lse")}
+    rows = m if layout == VWC_GRAD_COMPACT else n
+    if grad_logits is None:
+        grad_logits = _grad_out(logits, rows, None, grad_dtype)
+        if layout == VWC_GRAD_SCATTER:
+            grad_logits.zero_()
+    gld = _grad_rows(grad_logits, rows, v)
+    ws, wsb = _workspace(m, v, logits, workspace)
+    _check(_lib.vwc_topk_kl_fwd_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld, _ptr(row_idx),
+                                         m, _ptr(topk_idx), _ptr(teacher_logprob),
+                                         topk_idx.size(1), int(mode), float(tail_mass_eps),
+                                         float(temperature), _ptr(grad_loss), _ptr(out["loss"]),
+                                         _ptr(out["student_mass"]), _ptr(out["teacher_mass"]),
+                                         _ptr(out["topk_sum"]), _ptr(out["lse"]),
+                                         _ptr(grad_logits), _dtype(grad_logits), gld, layout,
+                                         _ptr(ws), wsb, _stream(stream, logits)))
+    return out, grad_logits
 
 
 def topk_kl_fwd_rows(logits, row_idx, topk_idx, teacher_logprob, mode=VWC_KL_TAIL,

@@ -719,37 +719,45 @@ vwc_status vwc_topk_kl_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows
                            ld_grad, layout == VWC_GRAD_SCATTER, stream);
 }
 
-vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
-                               int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
-                               int32_t k, vwc_kl_mode mode, float tail_mass_eps,
-                               float temperature, const float *grad_loss, float *loss,
-                               float *student_mass, float *teacher_mass, float *topk_sum,
-                               float *lse, void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
-                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    const char *fn = "vwc_topk_kl_fwd_bwd";
+static vwc_status topk_fwd_bwd_common(const char *fn, const void *logits, int dt, int64_t n_rows,
+                                      int64_t vocab, int64_t ld, const int32_t *row_idx,
+                                      int64_t m, const int32_t *topk_idx,
+                                      const float *teacher_logprob, int32_t k, int mode,
+                                      float tail_mass_eps, float temperature,
+                                      const float *grad_loss, float *loss, float *student_mass,
+                                      float *teacher_mass, float *topk_sum, float *lse,
+                                      void *grad_logits, int grad_dt, int64_t ld_grad,
+                                      bool by_row_id, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
-    if ((st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps, n_rows)) !=
+    if (m < 0) return fail(VWC_ERR_INVALID_ARG, "%s: m < 0", fn);
+    if ((st = check_topk(fn, topk_idx, teacher_logprob, k, vocab, mode, tail_mass_eps, m)) !=
         VWC_OK)
         return st;
     if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
     if (ld_grad < vocab) return fail(VWC_ERR_INVALID_ARG, "%s: ld_grad < vocab", fn);
-    if (n_rows == 0) return ok();
+    if (m == 0) return ok();
+    if (!row_idx && m != n_rows)
+        return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
+    if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
     if (!grad_loss || !lse || !student_mass || !teacher_mass || !topk_sum || !grad_logits)
         return fail(VWC_ERR_INVALID_ARG,
                     "%s: null grad_loss, lse, student_mass, teacher_mass, topk_sum or grad_logits",
                     fn);
-    if (n_rows > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
     const int64_t e = esize(dt);
     bool in_place = false;
     st = check_grad_buffer(fn, logits, dt, n_rows, vocab, ld, grad_logits, grad_dt, ld_grad,
-                           n_rows, &in_place);
+                           by_row_id ? n_rows : m, &in_place);
     if (st != VWC_OK) return st;
+    if (in_place && row_idx && !by_row_id)
+        return fail(VWC_ERR_INVALID_ARG,
+                    "%s: an in-place gradient needs gradient rows indexed by row id", fn);
     // One workgroup per row with the row on chip, as the logprob one-call;
     // otherwise the forward and the backward as their own calls.
     const bool fused = grad_dt == dt && k <= vwc::kKlMaxK &&
                        vocab / (16 / e) <= vwc::kFusedMaxUnits &&
-                       vector_rows(logits, ld, e, grad_logits, ld_grad, e, true);
+                       vector_rows(logits, ld, e, grad_logits, ld_grad, e, !row_idx || by_row_id);
     if (!fused) {
         // In place, the separate backward must write the payload columns in its
         // own pass (checked here, before anything runs).
@@ -758,23 +766,25 @@ vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
             return fail(VWC_ERR_UNSUPPORTED,
                         "%s: an in-place top-k KL gradient needs rows on 16 bytes and k <= %d",
                         fn, vwc::kKlMaxK);
-        st = topk_fwd_common(fn, logits, dt, n_rows, vocab, ld, nullptr, n_rows, topk_idx,
+        st = topk_fwd_common(fn, logits, dt, n_rows, vocab, ld, row_idx, m, topk_idx,
                              teacher_logprob, k, mode, tail_mass_eps, temperature, loss,
                              student_mass, teacher_mass, topk_sum, lse, workspace,
                              workspace_bytes, stream);
         if (st != VWC_OK) return st;
-        return topk_bwd_common(fn, logits, dt, n_rows, vocab, ld, nullptr, n_rows, topk_idx,
+        return topk_bwd_common(fn, logits, dt, n_rows, vocab, ld, row_idx, m, topk_idx,
                                teacher_logprob, k, mode, tail_mass_eps, temperature, lse,
                                student_mass, teacher_mass, topk_sum, grad_loss, grad_logits,
-                               grad_dt, ld_grad, true, stream);
+                               grad_dt, ld_grad, by_row_id, stream);
     }
+    if (m > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
     vwc::FusedPlan p{};
     p.logits = logits;
     p.ld = ld;
     p.vocab = static_cast<int32_t>(vocab);
     p.dt = dt;
+    p.row_idx = row_idx;
     p.n_rows = n_rows;
-    p.m = n_rows;
+    p.m = m;
     p.tau = static_cast<double>(temperature);
     p.c = static_cast<float>(1.44269504088896340736 / p.tau);
     const vwc::ScaleSplit cs = vwc::split_scale(p.tau);
@@ -784,7 +794,7 @@ vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
     p.lse = lse;
     p.grad = grad_logits;
     p.ld_grad = ld_grad;
-    p.grad_by_row_id = true;
+    p.grad_by_row_id = by_row_id;
     p.kl_idx = topk_idx;
     p.kl_tlp = teacher_logprob;
     p.kl_k = k;
@@ -795,6 +805,40 @@ vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
     p.kl_Q = student_mass;
     p.kl_S = topk_sum;
     return hip_status(vwc::launch_fused(p, stream), fn);
+}
+
+vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows, int64_t vocab,
+                               int64_t ld, const int32_t *topk_idx, const float *teacher_logprob,
+                               int32_t k, vwc_kl_mode mode, float tail_mass_eps,
+                               float temperature, const float *grad_loss, float *loss,
+                               float *student_mass, float *teacher_mass, float *topk_sum,
+                               float *lse, void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return topk_fwd_bwd_common("vwc_topk_kl_fwd_bwd", logits, dt, n_rows, vocab, ld, nullptr,
+                               n_rows, topk_idx, teacher_logprob, k, mode, tail_mass_eps,
+                               temperature, grad_loss, loss, student_mass, teacher_mass,
+                               topk_sum, lse, grad_logits, grad_dt, ld_grad, true, workspace,
+                               workspace_bytes, stream);
+}
+
+vwc_status vwc_topk_kl_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                    int64_t vocab, int64_t ld, const int32_t *row_idx, int64_t m,
+                                    const int32_t *topk_idx, const float *teacher_logprob,
+                                    int32_t k, vwc_kl_mode mode, float tail_mass_eps,
+                                    float temperature, const float *grad_loss, float *loss,
+                                    float *student_mass, float *teacher_mass, float *topk_sum,
+                                    float *lse, void *grad_logits, vwc_dtype grad_dt,
+                                    int64_t ld_grad, vwc_grad_layout layout, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "vwc_topk_kl_fwd_bwd_rows";
+    if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    return topk_fwd_bwd_common(fn, logits, dt, n_rows, vocab, ld, row_idx, m, topk_idx,
+                               teacher_logprob, k, mode, tail_mass_eps, temperature, grad_loss,
+                               loss, student_mass, teacher_mass, topk_sum, lse, grad_logits,
+                               grad_dt, ld_grad, layout == VWC_GRAD_SCATTER, workspace,
+                               workspace_bytes, stream);
 }
 
 vwc_status vwc_vocab_partial(const void *logits_slice, vwc_dtype dt, int64_t n_rows,

@@ -572,9 +572,9 @@ def lmhead_order(args, w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU per process; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
+        print("bench.py: only --gpus 1 is supported (the measured path is one GPU's share)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

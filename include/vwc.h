@@ -85,7 +85,7 @@ extern "C" {
 typedef enum vwc_status {
     VWC_OK = 0,
     VWC_ERR_INVALID_ARG = 1, /* a null required pointer, a negative size, ld < vocab, ... */
-    VWC_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle (e.g. misaligned dtype) */
+    VWC_ERR_UNSUPPORTED = 2, /* a valid request the library does not handle (e.g. misaligned dtype) */
     VWC_ERR_HIP = 3,         /* a HIP launch failed; see vwc_last_error() */
     VWC_STATUS_INT_RANGE_LO_ = -0x7fffffff - 1, /* (these two make every int a value */
     VWC_STATUS_INT_RANGE_HI_ = 0x7fffffff       /*  of the type: callers pass ints) */

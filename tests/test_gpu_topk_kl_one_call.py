@@ -64,7 +64,8 @@ LAYOUTS = [("bf16", 151939, 64), ("bf16", 151939, 256), ("fp32", 70001, 32)]
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=[f"{a}-V{b}-k{c}" for a, b, c in LAYOUTS])
 @pytest.mark.parametrize("mode", MODES)
-def test_one_call_payload_layouts(layout, mode):
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+def test_one_call_payload_layouts(layout, mode, tau):
     dt, V, K = layout
     n = 6
     N = 8 if dt == "bf16" else 4
@@ -82,23 +83,24 @@ def test_one_call_payload_layouts(layout, mode):
     xv = np.ascontiguousarray(x[:, :V])
     g = rng.uniform(-1, 1, n).astype(np.float32)
     g[1] = 0.0
-    log(f"one-call top-k KL layout {layout} mode={mode}")
+    log(f"one-call top-k KL layout {layout} mode={mode} tau={tau}")
     xd = to_dev_logits(x)[:, :V]
     idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
     gdtype = torch.bfloat16 if dt == "bf16" else torch.float32
     gbuf = torch.full((n, ld), float("nan"), dtype=gdtype, device=DEV)
-    fwd, grad = vwc.topk_kl_fwd_bwd(xd, idd, tld, gd, mode, grad_logits=gbuf[:, :V])
-    ref_fwd = check_fwd(fwd, xv, idx, tlp, mode, 1.0)
-    ref = oracle.topk_kl_backward(xv, idx, tlp, mode, g)
+    fwd, grad = vwc.topk_kl_fwd_bwd(xd, idd, tld, gd, mode, temperature=tau,
+                                    grad_logits=gbuf[:, :V])
+    ref_fwd = check_fwd(fwd, xv, idx, tlp, mode, tau)
+    ref = oracle.topk_kl_backward(xv, idx, tlp, mode, g, tau=tau)
     if dt == "fp32":
         err = np.abs(_np(grad).astype(np.float64) - ref).max()
         assert err <= 1e-6, f"fp32 grad err {err}"
     else:
         nb = check_bf16_grad(grad_bits(grad.contiguous()), ref,
-                             grad_bound(xv, idx, tlp, mode, 1.0, fwd, ref_fwd, g))
+                             grad_bound(xv, idx, tlp, mode, tau, fwd, ref_fwd, g))
         log(f"  {nb} elements beyond one bf16 step (within the bar)")
     sbuf = torch.full((n, ld), float("nan"), dtype=gdtype, device=DEV)
-    sep = vwc.topk_kl_bwd(xd, idd, tld, fwd, gd, mode, grad_logits=sbuf[:, :V])
+    sep = vwc.topk_kl_bwd(xd, idd, tld, fwd, gd, mode, temperature=tau, grad_logits=sbuf[:, :V])
     assert torch.equal(_bits(grad), _bits(sep))
     assert np.all(_np(grad[1].float()) == 0.0)
     assert torch.isnan(gbuf[:, V:].float()).all()  # nothing written past the vocabulary
@@ -227,3 +229,33 @@ def test_one_call_rows_equal_dense_rows(mode):
     assert torch.isfinite(sb["loss"][0])
     assert torch.equal(_bits(cg[0]), _bits(dgrad[2]))
     assert torch.all(cg[1:].float() == 7.0)  # no gradient written for bad ids
+
+
+@pytest.mark.parametrize("k", [64, 300], ids=["on-chip", "two-call"])
+def test_one_call_without_loss_output(k):
+    """The loss output may be null (the C ABI allows it): the other outputs and the
+    gradient are those of the call that writes the loss, in the on-chip pass and in
+    the two-call fallback."""
+    from vocab_wide_cross_amd import _binding as B
+    w = W.scaled("distill_bf16_4096x248320_k128", 6, 151936, topk=k)
+    x = W.all_logits(w)
+    idx, tlp = W.topk_payload(w)
+    g = np.random.default_rng(17).uniform(-1, 1, w.n_rows).astype(np.float32)
+    xd = to_dev_logits(x)
+    idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
+    ref, rgrad = vwc.topk_kl_fwd_bwd(xd, idd, tld, gd, vwc.VWC_KL_TAIL, temperature=0.7)
+    n, V = w.n_rows, w.vocab
+    out = {key: torch.full((n,), 7.0, device=DEV)
+           for key in ("student_mass", "teacher_mass", "topk_sum", "lse")}
+    grad = torch.full_like(xd, 3.0)
+    ws, wsb = B._workspace(n, V, xd, None)
+    st = B._lib.vwc_topk_kl_fwd_bwd(
+        B._ptr(xd), B._dtype(xd), n, V, V, B._ptr(idd), B._ptr(tld), k, vwc.VWC_KL_TAIL, 1e-6,
+        0.7, B._ptr(gd), None, B._ptr(out["student_mass"]), B._ptr(out["teacher_mass"]),
+        B._ptr(out["topk_sum"]), B._ptr(out["lse"]), B._ptr(grad), B._dtype(grad), V,
+        B._ptr(ws), wsb, B._stream(None, xd))
+    assert st == 0, B._lib.vwc_last_error().decode()
+    torch.cuda.synchronize()
+    for key, v in out.items():
+        assert torch.equal(v, ref[key]), key
+    assert torch.equal(_bits(grad), _bits(rgrad))

@@ -259,3 +259,47 @@ def test_one_call_without_loss_output(k):
     for key, v in out.items():
         assert torch.equal(v, ref[key]), key
     assert torch.equal(_bits(grad), _bits(rgrad))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_one_call_rows_at_every_16_byte_phase(mode):
+    """Rows at an odd stride (151941 bf16) start at all eight 16-byte phases.  With a
+    gradient of the same layout (a buffer of that stride, or in place) the on-chip
+    pass runs with head elements before the first whole vector; payload columns in
+    the head and the tail are stored by the threads that own those elements.  The
+    result meets the oracle's bars and equals, bit for bit, the separate backward
+    from the call's own outputs."""
+    V, K, n = 151939, 64, 9
+    ld = V + 2
+    rng = np.random.default_rng(77)
+    idx = np.stack([_payload_columns(V, 8, 64 * 8, K, rng) for _ in range(n)])
+    w_ = rng.exponential(size=(n, K))
+    mass = rng.uniform(0.5, 0.98, size=(n, 1))
+    tlp = np.log(mass * w_ / w_.sum(1, keepdims=True)).astype(np.float32)
+    xf = np.full((n, ld), np.nan, np.float32)
+    xf[:, :V] = rng.standard_normal((n, V)) * 2.0
+    for r in range(n):
+        xf[r, idx[r]] = tlp[r] + 9.0 + rng.normal(0, 0.05, K).astype(np.float32)
+    x = _bf16_round(xf)
+    xv = np.ascontiguousarray(x[:, :V])
+    g = rng.uniform(-1, 1, n).astype(np.float32)
+    g[2] = 0.0
+    xd = to_dev_logits(x)[:, :V]
+    assert xd.stride(0) == ld
+    idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
+    gbuf = torch.full((n, ld), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fwd, grad = vwc.topk_kl_fwd_bwd(xd, idd, tld, gd, mode, grad_logits=gbuf[:, :V])
+    ref_fwd = check_fwd(fwd, xv, idx, tlp, mode, 1.0)
+    ref = oracle.topk_kl_backward(xv, idx, tlp, mode, g)
+    check_bf16_grad(grad_bits(grad.contiguous()), ref,
+                    grad_bound(xv, idx, tlp, mode, 1.0, fwd, ref_fwd, g))
+    sbuf = torch.full((n, ld), float("nan"), dtype=torch.bfloat16, device=DEV)
+    sep = vwc.topk_kl_bwd(xd, idd, tld, fwd, gd, mode, grad_logits=sbuf[:, :V])
+    assert torch.equal(_bits(grad), _bits(sep))
+    assert torch.isnan(gbuf[:, V:].float()).all()
+    assert torch.all(grad[2] == 0)
+    xin = to_dev_logits(x)[:, :V]
+    fwd2, gin = vwc.topk_kl_fwd_bwd(xin, idd, tld, gd, mode, grad_logits=xin)
+    for key in fwd:
+        assert torch.equal(fwd2[key], fwd[key]), key
+    assert torch.equal(_bits(gin), _bits(grad))

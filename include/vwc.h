@@ -432,7 +432,12 @@ vwc_status vwc_topk_kl_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
 /*
  * The same over the row set row_idx[0..m): the payload, grad_loss and the
  * outputs are indexed by list position (as for vwc_topk_kl_fwd_rows), layout
- * as for vwc_topk_kl_bwd_rows.  Each listed row gets the dense call's bits.
+ * as for vwc_topk_kl_bwd_rows (compact: gradient row i is list entry i;
+ * scatter: row id r of a [n_rows, ld_grad] buffer, other rows untouched,
+ * duplicate ids race).  Each listed row gets the dense call's bits.  A row id
+ * outside [0, n_rows) gives NaN outputs and leaves its gradient row unwritten.
+ * In place (grad_logits == logits) needs VWC_GRAD_SCATTER, else
+ * VWC_ERR_INVALID_ARG before anything runs, and distinct ids (not checked).
  */
 vwc_status vwc_topk_kl_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
                                     int64_t vocab, int64_t ld, const int32_t *row_idx, int64_t m,

@@ -356,3 +356,59 @@ def test_lmhead_validation(lib):
     assert call(hidden=None, weight=None, targets=None, lp=None, m=0, n=0, w=None,
                 wsb=0) == OK
     assert err() == b""
+
+
+def _signatures():
+    """(name, [(type, parameter)]) of every entry point that takes a logits tensor,
+    read from the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = []
+    for name, params in re.findall(r"\bvwc_status\s+(vwc_[a-z_0-9]+)\s*\((.*?)\);", text, flags=re.S):
+        ps = []
+        for p in " ".join(params.split()).split(","):
+            p = p.strip()
+            m = re.match(r"(.*?)(\w+)$", p)
+            ps.append((m.group(1).replace(" ", ""), m.group(2)))
+        if ps[0][1] in ("logits", "logits_slice"):
+            out.append((name, ps))
+    return out
+
+
+_CTYPE = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int, "vwc_dtype": ctypes.c_int,
+          "vwc_kl_mode": ctypes.c_int, "vwc_grad_layout": ctypes.c_int, "float": ctypes.c_float,
+          "size_t": ctypes.c_size_t, "hipStream_t": ctypes.c_void_p}
+_BASE = {"dt": BF16, "grad_dt": BF16, "n_rows": 4, "vocab": 64, "v_local": 64, "ld": 64,
+         "ld_grad": 64, "m": 4, "v_start": 0, "temperature": 1.0, "k": 2, "mode": 0,
+         "tail_mass_eps": 1e-6, "layout": 0, "workspace_bytes": 0}
+# Each of these alone must be refused by the host checks (VWC_ERR_INVALID_ARG, the
+# entry point's name in the message) before any HIP call.
+_BAD = [("dt", 7), ("n_rows", -1), ("vocab", 0), ("ld", 63), ("temperature", 0.0),
+        ("temperature", float("nan")), ("temperature", float("inf")), ("logits", None)]
+
+
+@pytest.mark.parametrize("name,params", _signatures(), ids=[n for n, _ in _signatures()])
+def test_every_logits_entry_point_checks_its_arguments(lib, name, params):
+    assert len(params) >= 8
+    f = getattr(lib, name)
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p if t.endswith("*") else _CTYPE[t] for t, _ in params]
+    lib.vwc_last_error.restype = ctypes.c_char_p
+    names = [n for _, n in params]
+    for key, val in _BAD:
+        key = {"vocab": "v_local", "logits": "logits_slice"}.get(key, key) \
+            if key not in names else key
+        assert key in names, (name, key)
+        args = []
+        for t, n in params:
+            if n == key:
+                args.append(val)
+            elif t.endswith("*"):
+                args.append(None if n == "workspace" else FAKE)
+            elif n == "stream":
+                args.append(None)
+            else:
+                args.append(_BASE[n])
+        st = f(*args)
+        msg = lib.vwc_last_error().decode()
+        assert st == INVALID, (name, key, val, st, msg)
+        assert msg.startswith(name), (name, msg)

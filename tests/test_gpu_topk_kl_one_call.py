@@ -303,3 +303,42 @@ def test_one_call_rows_at_every_16_byte_phase(mode):
     for key in fwd:
         assert torch.equal(fwd2[key], fwd[key]), key
     assert torch.equal(_bits(gin), _bits(grad))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_one_call_special_values(mode):
+    """-inf logits off the payload (masked entries, a whole leading stretch of them)
+    and a NaN logit in one row: outputs as the separate forward gives them (NaN in
+    the same places), the gradient the separate backward's bits from the call's own
+    outputs, and the oracle's values on the finite rows."""
+    V, K, n = 3001, 16, 12
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((n, V)).astype(np.float32)
+    idx = np.stack([rng.choice(np.arange(400, V), K, replace=False) for _ in range(n)]).astype(np.int32)
+    tlp = np.log(np.full((n, K), 0.6 / K)).astype(np.float32)
+    mask = rng.random(x.shape) < 0.3
+    mask[:, :300] = True
+    for r in range(n):
+        mask[r, idx[r]] = False
+    x[mask] = -np.inf
+    x[5, 2000] = np.nan
+    g = rng.uniform(-1, 1, n).astype(np.float32)
+    xd, idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (x, idx, tlp, g))
+    fwd, grad = vwc.topk_kl_fwd_bwd(xd, idd, tld, gd, mode, temperature=0.7)
+    sf = vwc.topk_kl_fwd(xd, idd, tld, mode, temperature=0.7)
+    for key in fwd:
+        a, b = _np(fwd[key]).astype(np.float64), _np(sf[key]).astype(np.float64)
+        assert np.array_equal(np.isnan(a), np.isnan(b)), key
+        ok = ~np.isnan(a)
+        assert np.abs(a[ok] - b[ok]).max() <= 1e-4, key
+    assert np.isnan(_np(fwd["lse"])[5])
+    sep = vwc.topk_kl_bwd(xd, idd, tld, fwd, gd, mode, temperature=0.7)
+    a, b = _np(grad), _np(sep)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+    rows = np.array([r for r in range(n) if r != 5])
+    check_fwd({k: v[torch.from_numpy(rows).to(DEV)] for k, v in fwd.items()}, x[rows], idx[rows],
+              tlp[rows], mode, 0.7)
+    ref = oracle.topk_kl_backward(x[rows], idx[rows], tlp[rows], mode, g[rows], tau=0.7)
+    assert np.abs(a[rows].astype(np.float64) - ref).max() <= 1e-6
+    assert np.all(a[rows][mask[rows]] == 0.0)  # masked entries: probability 0

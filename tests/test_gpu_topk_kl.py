@@ -130,28 +130,39 @@ def test_topk_kl_clamp_guard_and_bad_index():
     assert np.isnan(loss[2]) and np.all(np.isfinite(np.delete(loss, 2)))
 
 
+def check_all_rows(fwd, grad, xh, idx, tlp, mode, tau, g, what, block=128):
+    """Every row's forward outputs and bf16 gradient against the oracle, in blocks
+    of rows (the oracle's gradient of a block is [block, V] fp64).  Returns the
+    number of elements beyond one bf16 step (all within the bar)."""
+    n_beyond = 0
+    for r0 in range(0, xh.shape[0], block):
+        rows = np.arange(r0, min(r0 + block, xh.shape[0]))
+        ri = torch.from_numpy(rows).to(DEV)
+        sub = {k: v[ri] for k, v in fwd.items()}
+        ref_fwd = check_fwd(sub, xh[rows], idx[rows], tlp[rows], mode, tau)
+        ref = oracle.topk_kl_backward(xh[rows], idx[rows], tlp[rows], mode, g[rows], tau=tau)
+        n_beyond += check_bf16_grad(grad_bits(grad[ri]), ref,
+                                    grad_bound(xh[rows], idx[rows], tlp[rows], mode, tau, sub,
+                                               ref_fwd, g[rows]))
+    log(f"{what} mode={mode}: all {xh.shape[0]} rows checked, {n_beyond} elements beyond one "
+        f"bf16 step (within the bar)")
+    return n_beyond
+
+
 @pytest.mark.timeout(900)
 def test_topk_kl_full_size_k128():
-    """The page's distillation dimensions: N=4096, V=248320 bf16, K=128; sampled
-    rows against the oracle for both objectives."""
+    """The page's distillation dimensions: N=4096, V=248320 bf16, K=128; every row
+    against the oracle, for both objectives."""
     w = W.get("distill_bf16_4096x248320_k128")
-    x = upload_workload(w)
+    x, xh = upload_workload(w, keep_rows=True)
     idx, tlp = W.topk_payload(w)
     g = np.random.default_rng(5).uniform(-1, 1, w.n_rows).astype(np.float32)
     idd, tld, gd = (torch.from_numpy(a).to(DEV) for a in (idx, tlp, g))
-    rows = np.array([0, 1777, 4095])
-    xh = W.logits_rows(w, rows)
-    ri = torch.from_numpy(rows).to(DEV)
     for mode in MODES:
         fwd = vwc.topk_kl_fwd(x, idd, tld, mode)
         grad = vwc.topk_kl_bwd(x, idd, tld, fwd, gd, mode)
         torch.cuda.synchronize()
-        sub = {k: v[ri] for k, v in fwd.items()}
-        ref_fwd = check_fwd(sub, xh, idx[rows], tlp[rows], mode, 1.0)
-        ref = oracle.topk_kl_backward(xh, idx[rows], tlp[rows], mode, g[rows])
-        n = check_bf16_grad(grad_bits(grad[ri]), ref,
-                            grad_bound(xh, idx[rows], tlp[rows], mode, 1.0, sub, ref_fwd, g[rows]))
-        log(f"top-k KL full size mode={mode}: {n} elements beyond one bf16 step (within the bar)")
+        check_all_rows(fwd, grad, xh, idx, tlp, mode, 1.0, g, "top-k KL full size")
         assert torch.all(torch.isfinite(fwd["loss"]))
         if mode == vwc.VWC_KL_TAIL:
             assert torch.all(fwd["loss"] >= -5e-5)

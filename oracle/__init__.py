@@ -6,7 +6,10 @@ Python binding) never imports, links or calls it.  It shares no code with the HI
 path; the two meet only in the seeded input generators of ``workloads``.
 
 The arithmetic lives in ``oracle.c`` (plain C, double precision, one row at a
-time).  This module is marshalling: numpy arrays in, numpy arrays out.
+time).  This module is marshalling: numpy arrays in, numpy arrays out.  The one
+exception is ``lmhead_blocked``: the LM head's definition in float64 numpy with
+the projection of a block of kept rows as one BLAS matrix product, fast enough to
+check every kept row of a full-size call.
 """
 from __future__ import annotations
 

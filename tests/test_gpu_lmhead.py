@@ -183,6 +183,10 @@ def _sample(m):
 
 
 def _fullsize(w):
+    """The GPU's outputs for every kept row, and the oracle's: oracle.c's fixed-order
+    sums on sampled rows, and the blocked oracle (a float64 BLAS product per block
+    of rows) on every kept row, the two checked against each other first."""
+    from oracle.lmhead_blocked import lmhead_forward_blocked
     log(f"generating {w.name}")
     wt = W.lmhead_weight(w)
     h = W.lmhead_hidden(w, weight=wt)
@@ -193,23 +197,27 @@ def _fullsize(w):
     log("  gpu done")
     sel = _sample(rows.size)
     ref = oracle.lmhead_forward(h, wt, tg, rows=rows[sel], err_scale=True)
-    log(f"  oracle done on {sel.size} rows")
-    return got, ref, sel
+    log(f"  oracle.c done on {sel.size} rows")
+    full = lmhead_forward_blocked(h, wt, tg, rows=rows, err_scale=True)
+    log(f"  blocked oracle done on all {rows.size} rows")
+    for k in ("logprob", "lse", "entropy", "err_scale"):
+        np.testing.assert_allclose(full[k][sel], ref[k], rtol=1e-12, atol=1e-11)
+    return got, full
 
 
 def test_fullsize_lattice():
     w = W.scaled("lmhead_bf16_16384x248320_d2560", 16384, 248320, lattice=True)
-    got, ref, sel = _fullsize(w)
-    errs = _compare({k: v[sel] for k, v in got.items()}, ref, 5e-5, "full lattice")
-    log(f"  max errors {errs}")
+    got, ref = _fullsize(w)
+    errs = _compare(got, ref, 5e-5, "full lattice")
+    log(f"  max errors over every kept row {errs}")
 
 
 def test_fullsize_gaussian():
     w = W.get("lmhead_bf16_16384x248320_d2560")
-    got, ref, sel = _fullsize(w)
+    got, ref = _fullsize(w)
     tol = _gauss_tol(w, ref)
     for k in ("logprob", "lse", "entropy"):
-        err = np.abs(got[k][sel].astype(np.float64) - ref[k])
+        err = np.abs(got[k].astype(np.float64) - ref[k])
         assert (err <= tol).all(), f"{k}: max err {err.max():.3g}, allowance {tol.min():.3g}"
-        log(f"  {k}: max err {err.max():.3g} (allowance >= {tol.min():.3g})")
+        log(f"  {k}: max err {err.max():.3g} over every kept row (allowance >= {tol.min():.3g})")
     assert np.isfinite(got["logprob"]).all() and (got["logprob"] <= 1e-6).all()

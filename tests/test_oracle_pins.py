@@ -785,3 +785,70 @@ def test_lmhead_rejects_bad_arguments(lm_tiny):
         oracle.lmhead_forward(h, wt, t, rows=np.array([300], np.int32))
     with pytest.raises(oracle.OracleError):
         oracle.lmhead_forward(h, wt, t, d=321)
+
+
+# The blocked LM-head oracle (a float64 BLAS product per block of kept rows, then
+# the definition) that lets the full-size GPU test check every kept row.
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7])
+@pytest.mark.parametrize("block", [1, 7, 256])
+def test_lmhead_blocked_matches_torch_fp64(lm_tiny, tau, block):
+    """torch fp64 matmul of the decoded operands, cross_entropy, logsumexp and
+    Categorical entropy; any block size."""
+    from oracle.lmhead_blocked import lmhead_forward_blocked
+    _, h, wt, t = lm_tiny
+    rows = np.array([0, 5, 17, 255, 256, 299, 5], np.int64)
+    o = lmhead_forward_blocked(h, wt, t, tau=tau, rows=rows, block=block)
+    hf = torch.from_numpy(W.bf16_bits_to_float32(h[rows])).double()
+    wf = torch.from_numpy(W.bf16_bits_to_float32(wt)).double()
+    z = (hf @ wf.T) / float(np.float32(tau))
+    ce = torch.nn.functional.cross_entropy(z, torch.from_numpy(t[rows]).long(), reduction="none")
+    np.testing.assert_allclose(o["logprob"], -ce.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(o["lse"], torch.logsumexp(z, 1).numpy(), rtol=0, atol=1e-11)
+    ent = torch.distributions.Categorical(logits=z).entropy().numpy()
+    np.testing.assert_allclose(o["entropy"], ent, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("lattice", [False, True])
+def test_lmhead_blocked_matches_the_c_oracle(lattice):
+    """Every row and the error scale agree with oracle.c's fixed-order sums (ragged
+    hidden size, NaN padding past d, rows in any order with repeats)."""
+    from oracle.lmhead_blocked import lmhead_forward_blocked
+    w = W.scaled("lmhead_bf16_300x2000_d320", 300, 2000, lattice=lattice)
+    wt = W.lmhead_weight(w)
+    h = W.lmhead_hidden(w, weight=wt)
+    t = W.targets(w)
+    d = w.hidden - 3
+    hp = np.full((h.shape[0], w.hidden + 5), 0x7FC0, np.uint16)
+    hp[:, :d] = h[:, :d]
+    wp = np.full((wt.shape[0], w.hidden + 8), 0x7FC0, np.uint16)
+    wp[:, :d] = wt[:, :d]
+    rows = np.concatenate([np.arange(299, -1, -1), [7, 7]])
+    a = lmhead_forward_blocked(hp, wp, t, tau=0.7, rows=rows, d=d, block=64, err_scale=True)
+    b = oracle.lmhead_forward(hp, wp, t, tau=0.7, rows=rows.astype(np.int32), d=d,
+                              err_scale=True)
+    for k in ("logprob", "lse", "entropy", "err_scale"):
+        np.testing.assert_allclose(a[k], b[k], rtol=1e-12, atol=1e-11)
+
+
+def test_lmhead_blocked_closed_form_and_bad_arguments():
+    """Two vocabulary entries: lse = log(e^a + e^b) (the two-entry closed form), and
+    row ids or targets outside their ranges are refused."""
+    from oracle.lmhead_blocked import lmhead_forward_blocked
+    h = _bf16(np.array([[1.0, 2.0], [0.5, -1.0]]))
+    wt = _bf16(np.array([[1.0, 0.0], [0.0, 1.0]]))
+    t = np.array([1, 0], np.int32)
+    o = lmhead_forward_blocked(h, wt, t)
+    x = np.array([[1.0, 2.0], [0.5, -1.0]])
+    lse = np.log(np.exp(x).sum(1))
+    np.testing.assert_allclose(o["lse"], lse, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o["logprob"], x[np.arange(2), t] - lse, rtol=0, atol=1e-15)
+    p = np.exp(x - lse[:, None])
+    np.testing.assert_allclose(o["entropy"], -(p * np.log(p)).sum(1), rtol=0, atol=1e-15)
+    with pytest.raises(IndexError):
+        lmhead_forward_blocked(h, wt, np.array([2, 0], np.int32))
+    with pytest.raises(IndexError):
+        lmhead_forward_blocked(h, wt, t, rows=np.array([2]))
+    with pytest.raises(ValueError):
+        lmhead_forward_blocked(h, wt, t, d=3)

@@ -79,6 +79,36 @@ def test_bf16_forward_backward_shapes(vocab):
     assert np.all(gb[zero] == 0), "rows with zero grad_out must be +0.0"
 
 
+@pytest.mark.parametrize("dtype,vocab", [("bf16", 1048579), ("fp32", 4194311)])
+def test_very_wide_rows(dtype, vocab):
+    """Rows far wider than any vocabulary on the pages, with a ragged tail: 17 bf16
+    (2 MiB rows) or 129 fp32 (16 MiB rows) forward segments of at most 128 KiB,
+    merged by the combine kernel; the backward in 9 bf16 pieces of at most 256 KiB
+    or 128 fp32 pieces of about 128 KiB; the one call runs the two calls (the rows
+    do not fit on chip) with their bits."""
+    n = 3
+    base = "spiked_bf16_8192x248320" if dtype == "bf16" else "tiny_fp32_64x2048"
+    w = W.scaled(base, n, vocab)
+    x, t, g = _host(w)
+    log(f"{dtype} [{n}, {vocab}]")
+    xd, td, gd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)
+    lp, lse, ent = vwc.selected_logprob_fwd(xd, td, want=("logprob", "lse", "entropy"))
+    grad = vwc.selected_logprob_bwd(xd, td, lse, gd)
+    ref = oracle.forward(x, t)
+    for k, v in (("logprob", lp), ("lse", lse), ("entropy", ent)):
+        assert_close_scalar(_np(v), ref[k], f"{k} V={vocab}")
+    gref = oracle.backward(x, t, g)
+    if dtype == "bf16":
+        assert_bf16_grad(grad_bits(grad), gref, f"grad V={vocab}", oracle)
+    else:
+        err = np.abs(_np(grad).astype(np.float64) - gref).max()
+        assert err <= 1e-6, f"fp32 grad err {err}"
+    olp, olse, _, ograd = vwc.selected_logprob_fwd_bwd(xd, td, gd)
+    assert torch.equal(olp, lp) and torch.equal(olse, lse)
+    bits = (lambda a: a.view(torch.int16)) if dtype == "bf16" else (lambda a: a.view(torch.int32))
+    assert torch.equal(bits(ograd), bits(grad))
+
+
 def test_confident_target_gradient_limited_by_saved_lse():
     """Rows whose target holds nearly all the mass (1 - p_t down to 1e-9).  The
     target column g/tau (1 - p_t) is computed from the saved fp32 lse, so its

@@ -77,3 +77,62 @@ def test_pins_catch_planted_mistake(tmp_path, name, orig, mut, select):
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, (f"the pins did not catch '{name}' (exit {r.returncode}):\n"
                                f"{r.stdout[-2000:]}")
+
+
+# The blocked LM-head oracle (numpy): each case plants one mistake in a copy of the
+# module, which a subprocess installs in place of oracle.lmhead_blocked before it
+# runs the blocked oracle's pins.
+BLOCKED_SRC = os.path.join(ROOT, "oracle", "lmhead_blocked.py")
+BLOCKED_MUTATIONS = [
+    ("tau dropped", "z = (h @ w.T) / tau", "z = (h @ w.T)"),
+    ("tau taken as a double", "tau = float(np.float32(tau))", "tau = float(tau)"),
+    ("weight rows reversed", "z = (h @ w.T) / tau", "z = (h @ w[::-1].T) / tau"),
+    ("max dropped from lse", "lse = zmax[:, 0] + np.log(s)", "lse = np.log(s)"),
+    ("entropy sign", 'out["entropy"][sel] = lse - (e * z).sum(axis=1) / s',
+     'out["entropy"][sel] = (e * z).sum(axis=1) / s - lse'),
+    ("targets by output index", "t = np.asarray(targets, np.int64)[rows]",
+     "t = np.asarray(targets, np.int64)[: rows.size]"),
+    ("bf16 decode off by one bit", "(b.astype(np.uint32) << 16)", "(b.astype(np.uint32) << 15)"),
+    ("last hidden column dropped", "w = _decode_bf16(weight[:, :d])",
+     "d = d - 1\n    w = _decode_bf16(weight[:, :d])"),
+    ("error scale without absolute values", "a = np.abs(h) @ wabs.T", "a = h @ wabs.T"),
+]
+
+_RUN_BLOCKED_PINS = r"""
+import importlib.util, os, sys
+sys.path.insert(0, os.environ["VWC_ROOT"])
+import oracle
+spec = importlib.util.spec_from_file_location("oracle.lmhead_blocked", os.environ["MUT_SRC"])
+mod = importlib.util.module_from_spec(spec)
+spec.loader.exec_module(mod)
+sys.modules["oracle.lmhead_blocked"] = mod
+oracle.lmhead_blocked = mod
+import pytest
+sys.exit(pytest.main(["-q", "-x", "-p", "no:cacheprovider",
+                      os.path.join(os.environ["VWC_ROOT"], "tests", "test_oracle_pins.py"),
+                      "-k", "blocked"]))
+"""
+
+
+@pytest.mark.parametrize("name,orig,mut", BLOCKED_MUTATIONS, ids=[m[0] for m in BLOCKED_MUTATIONS])
+def test_blocked_lmhead_pins_catch_planted_mistake(tmp_path, name, orig, mut):
+    src = open(BLOCKED_SRC).read()
+    assert src.count(orig) >= 1, f"mutation anchor for '{name}' not found in lmhead_blocked.py"
+    path = tmp_path / "lmhead_blocked.py"
+    path.write_text(src.replace(orig, mut, 1))
+    env = dict(os.environ, VWC_ROOT=ROOT, MUT_SRC=str(path))
+    r = subprocess.run([sys.executable, "-c", _RUN_BLOCKED_PINS], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, (f"the pins did not catch '{name}' (exit {r.returncode}):\n"
+                               f"{r.stdout[-2000:]}")
+
+
+def test_blocked_lmhead_pins_pass_unmutated(tmp_path):
+    """The same harness on the module as it stands passes (so the cases above fail
+    for their mistake, not for the harness)."""
+    path = tmp_path / "lmhead_blocked.py"
+    path.write_text(open(BLOCKED_SRC).read())
+    env = dict(os.environ, VWC_ROOT=ROOT, MUT_SRC=str(path))
+    r = subprocess.run([sys.executable, "-c", _RUN_BLOCKED_PINS], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]

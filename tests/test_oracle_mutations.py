@@ -47,6 +47,15 @@ MUTATIONS = [
      "/* no clamp */", "topk"),
     ("bf16 rounding ties away", "double r = rint(v / q) * q;", "double r = round(v / q) * q;",
      "bf16"),
+    ("KL gradient without tau", "gi[j] = g * d / tau;", "gi[j] = g * d;", "topk"),
+    ("KL d log q sign", "double dlogq = (idx[n] == j ? 1.0 : 0.0) - qj;",
+     "double dlogq = qj - (idx[n] == j ? 1.0 : 0.0);", "topk"),
+    ("KL tail term sign", "d += dl_dlogqt * (-(qj * in_t - qj * Q) / (1.0 - Q));",
+     "d += dl_dlogqt * ((qj * in_t - qj * Q) / (1.0 - Q));", "topk"),
+    ("KL tail guard inverted", "if (mode == 1 && 1.0 - Q >= tail_eps)",
+     "if (mode == 1 && 1.0 - Q < tail_eps)", "topk"),
+    ("KL clamped row keeps its gradient",
+     "int row_dead = (mode == 0 && Lraw < 0.0) || g == 0.0;", "int row_dead = g == 0.0;", "topk"),
     ("LM head reads the weight transposed",
      "double p = decode_bf16(h[k]) * decode_bf16(w[k]);",
      "double p = decode_bf16(h[k]) * decode_bf16(weight[k * ldw + j]);", "lmhead"),

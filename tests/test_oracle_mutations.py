@@ -47,6 +47,16 @@ MUTATIONS = [
      "/* no clamp */", "topk"),
     ("bf16 rounding ties away", "double r = rint(v / q) * q;", "double r = round(v / q) * q;",
      "bf16"),
+    # (a slice that also claimed the first column past its end would read that same
+    # logit, which the merge's max leaves unchanged, so the case drops the first one)
+    ("slice misses its first column", "if (t >= v_start && t < v_start + v_local)",
+     "if (t > v_start && t < v_start + v_local)", "vocab_chunks or split4 or slice"),
+    ("slice target read at the global column",
+     "pt[i] = logit_at(logits_slice, dtype, ld, r, t - v_start) / tau;",
+     "pt[i] = logit_at(logits_slice, dtype, ld, r, t) / tau;", "vocab_chunks or split4 or slice"),
+    ("combine target summed instead of maximised", "if (pt && pt[q * m + i] > T) T = pt[q * m + i];",
+     "if (pt && pt[q * m + i] > -INFINITY) T = (T == -INFINITY ? 0.0 : T) + pt[q * m + i];",
+     "vocab_chunks or split4 or slice"),
     ("KL gradient without tau", "gi[j] = g * d / tau;", "gi[j] = g * d;", "topk"),
     ("KL d log q sign", "double dlogq = (idx[n] == j ? 1.0 : 0.0) - qj;",
      "double dlogq = qj - (idx[n] == j ? 1.0 : 0.0);", "topk"),

@@ -54,9 +54,8 @@ MUTATIONS = [
     ("slice target read at the global column",
      "pt[i] = logit_at(logits_slice, dtype, ld, r, t - v_start) / tau;",
      "pt[i] = logit_at(logits_slice, dtype, ld, r, t) / tau;", "vocab_chunks or split4 or slice"),
-    ("combine target summed instead of maximised", "if (pt && pt[q * m + i] > T) T = pt[q * m + i];",
-     "if (pt && pt[q * m + i] > -INFINITY) T = (T == -INFINITY ? 0.0 : T) + pt[q * m + i];",
-     "vocab_chunks or split4 or slice"),
+    ("combine takes the last slice's target", "if (pt && pt[q * m + i] > T) T = pt[q * m + i];",
+     "if (pt) T = pt[q * m + i];", "vocab_chunks or split4 or slice"),
     ("KL gradient without tau", "gi[j] = g * d / tau;", "gi[j] = g * d;", "topk"),
     ("KL d log q sign", "double dlogq = (idx[n] == j ? 1.0 : 0.0) - qj;",
      "double dlogq = qj - (idx[n] == j ? 1.0 : 0.0);", "topk"),

@@ -97,3 +97,61 @@ def selected_logprob(logits, targets, temperature=1.0, row_idx=None, with_entrop
     logits are gone afterwards."""
     return _SelectedLogprob.apply(logits, targets, float(temperature), row_idx,
                                   bool(with_entropy), bool(inplace_backward))
+
+
+class _TopkKL(torch.autograd.Function):
+    """The chunked top-k KL of "[megatron] feat: add memory-efficient chunked top-k KL
+    computation" ("Design & Code Changes"): the forward keeps the student logits, the
+    teacher's top-k payload and the per-row logZ with the payload's masses and sum; the
+    backward recomputes the student softmax in one library call."""
+
+    @staticmethod
+    def forward(ctx, logits, topk_idx, teacher_logprob, mode, tail_mass_eps, temperature,
+                row_idx, inplace_backward):
+        kw = dict(mode=mode, tail_mass_eps=tail_mass_eps, temperature=temperature)
+        if row_idx is None:
+            fwd = B.topk_kl_fwd(logits, topk_idx, teacher_logprob, **kw)
+        else:
+            fwd = B.topk_kl_fwd_rows(logits, row_idx, topk_idx, teacher_logprob, **kw)
+        ctx.kw = kw
+        ctx.inplace_backward = inplace_backward
+        ctx.has_rows = row_idx is not None
+        saved = [logits, topk_idx, teacher_logprob, fwd["lse"], fwd["student_mass"],
+                 fwd["teacher_mass"], fwd["topk_sum"]]
+        if row_idx is not None:
+            saved.append(row_idx)
+        ctx.save_for_backward(*saved)
+        return fwd["loss"]
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        saved = list(ctx.saved_tensors)
+        logits, idx, tlp = saved[:3]
+        fwd = dict(zip(("lse", "student_mass", "teacher_mass", "topk_sum"), saved[3:7]))
+        g = grad_loss.contiguous().float()
+        if not ctx.has_rows:
+            out = logits if ctx.inplace_backward else None
+            grad = B.topk_kl_bwd(logits, idx, tlp, fwd, g, grad_logits=out, **ctx.kw)
+        else:  # the listed rows scattered into a zeroed [rows, vocab] gradient
+            grad = torch.zeros_like(logits)
+            B.topk_kl_bwd_rows(logits, saved[7], idx, tlp, fwd, g, grad_logits=grad,
+                               layout=B.VWC_GRAD_SCATTER, **ctx.kw)
+        return grad, None, None, None, None, None, None, None
+
+
+def topk_kl(logits, topk_idx, teacher_logprob, mode=B.VWC_KL_TAIL, tail_mass_eps=1e-6,
+            temperature=1.0, row_idx=None, inplace_backward=False):
+    """Per-row top-k KL between a teacher's top-k payload (column ids topk_idx and
+    log-probabilities teacher_logprob, [rows, k]) and the student softmax of
+    logits / temperature, differentiable with respect to `logits`.
+
+    mode: VWC_KL_TAIL (the k + 1-category KL with the tail masses) or
+    VWC_KL_TRUNCATED (the top-k sum, clamped at 0).  row_idx (distinct int32 row
+    ids) computes only those rows, with the payload given per listed row ([m, k]);
+    their gradient is scattered into a zeroed [rows, vocab] tensor.  With
+    inplace_backward=True (dense rows only) the backward writes the gradient over
+    `logits` itself and returns that tensor; the logits are gone afterwards."""
+    if inplace_backward and row_idx is not None:
+        raise ValueError("inplace_backward needs every row (row_idx=None)")
+    return _TopkKL.apply(logits, topk_idx, teacher_logprob, int(mode), float(tail_mass_eps),
+                         float(temperature), row_idx, bool(inplace_backward))

@@ -59,3 +59,14 @@ def test_topk_and_lmhead_shapes_are_checked():
         vwc.lmhead_logprob_fwd(h.float(), w, torch.zeros(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="targets"):
         vwc.lmhead_logprob_fwd(h, w, torch.zeros(2, dtype=torch.int32))
+
+
+def test_topk_kl_autograd_refuses_inplace_rows():
+    x = _x()
+    idx = torch.zeros(2, 3, dtype=torch.int32)
+    tlp = torch.zeros(2, 3)
+    rows = torch.tensor([0, 2], dtype=torch.int32)
+    with pytest.raises(ValueError, match="inplace_backward"):
+        vwc.topk_kl(x, idx, tlp, row_idx=rows, inplace_backward=True)
+    with pytest.raises(ValueError, match="GPU"):  # host tensors never reach the library
+        vwc.topk_kl(x, torch.zeros(4, 3, dtype=torch.int32), torch.zeros(4, 3))

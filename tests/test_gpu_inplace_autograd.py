@@ -149,3 +149,40 @@ def test_autograd_rows_with_duplicates_and_inplace():
     (lp2 * gcd).sum().backward()
     assert _same(logits.detach(), leaf.grad)  # the logits' storage now holds the gradient
     assert _same(base.grad, leaf.grad)
+
+
+@pytest.mark.parametrize("dtype,vocab", [("bf16", 151939), ("fp32", 20011), ("bf16", 253953)])
+def test_weighted_nll_one_call(dtype, vocab):
+    """weighted_nll: the loss -sum w lp and its gradient from the one-call kernel in
+    the forward (the two calls for a row too wide to hold), scaled in the backward;
+    against the oracle, the direct one call's bits, and in place."""
+    w, x, t, wt = _case(dtype, 24, vocab)
+    xd, td, wd = to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(wt).to(DEV)
+    leaf = xd.clone().requires_grad_(True)
+    loss, lp = vwc.weighted_nll(leaf, td, wd)
+    assert not lp.requires_grad
+    loss.backward()
+    ref = oracle.forward(x, t)
+    assert abs(float(loss.detach()) + float((wt.astype(np.float64) * ref["logprob"]).sum())) <= 24 * 5e-5
+    assert np.abs(_np(lp).astype(np.float64) - ref["logprob"]).max() <= 5e-5
+    gref = oracle.backward(x, t, -wt)
+    if dtype == "bf16":
+        assert_bf16_grad(grad_bits(leaf.grad), gref, "weighted_nll grad", oracle)
+    else:
+        assert np.abs(_np(leaf.grad).astype(np.float64) - gref).max() <= 1e-6
+    _, _, _, direct = vwc.selected_logprob_fwd_bwd(xd, td, -wd)
+    assert _same(leaf.grad, direct)
+    assert np.all(grad_bits(leaf.grad)[wt == 0] == 0)
+    # a scaled loss: the gradient times the scale, as torch multiplies it
+    leaf2 = xd.clone().requires_grad_(True)
+    loss2, _ = vwc.weighted_nll(leaf2, td, wd)
+    (2.5 * loss2).backward()
+    assert _same(leaf2.grad, direct * torch.tensor(2.5, dtype=direct.dtype, device=DEV))
+    # in place: the gradient is written over the logits in the forward
+    base = xd.clone().requires_grad_(True)
+    logits = base * 1.0
+    loss3, _ = vwc.weighted_nll(logits, td, wd, inplace=True)
+    assert torch.equal(loss3, loss)
+    assert _same(logits.detach(), direct)
+    loss3.backward()
+    assert _same(base.grad, direct)

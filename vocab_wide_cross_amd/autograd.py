@@ -155,3 +155,42 @@ def topk_kl(logits, topk_idx, teacher_logprob, mode=B.VWC_KL_TAIL, tail_mass_eps
         raise ValueError("inplace_backward needs every row (row_idx=None)")
     return _TopkKL.apply(logits, topk_idx, teacher_logprob, int(mode), float(tail_mass_eps),
                          float(temperature), row_idx, bool(inplace_backward))
+
+
+class _WeightedNLL(torch.autograd.Function):
+    """loss = -sum_r w_r logprob_r with the weights known before the forward (a token
+    mean, say): the forward is the one-call forward + backward, which reads each row
+    once and writes the gradient of the loss with respect to the logits; the backward
+    only scales it by the incoming gradient (nothing when that is 1)."""
+
+    @staticmethod
+    def forward(ctx, logits, targets, weights, temperature, inplace):
+        w = weights.contiguous().float()
+        lp, _, _, grad = B.selected_logprob_fwd_bwd(
+            logits, targets, -w, temperature, want=("logprob", "lse"),
+            grad_logits=logits if inplace else None)
+        if inplace:  # the library overwrote the logits: let autograd see the write
+            torch.autograd.graph.increment_version(logits)
+        ctx.save_for_backward(grad)
+        ctx.mark_non_differentiable(lp)
+        return -(w * lp).sum(), lp
+
+    @staticmethod
+    def backward(ctx, grad_loss, grad_lp=None):
+        (grad,) = ctx.saved_tensors
+        if grad_loss is None:
+            return None, None, None, None, None
+        if not (grad_loss.numel() == 1 and float(grad_loss) == 1.0):
+            grad = grad * grad_loss.to(grad.dtype)
+        return grad, None, None, None, None
+
+
+def weighted_nll(logits, targets, weights, temperature=1.0, inplace=False):
+    """The weighted negative log-likelihood -sum_r weights[r] * logprob[r] (logprob as in
+    selected_logprob), differentiable with respect to `logits`, for weights known
+    before the forward.  The gradient is computed in the forward by the one-call
+    kernel (one read and one write of the logits instead of two reads and one write)
+    and kept until the backward; with inplace=True it is written over `logits`, which
+    are gone afterwards (no second [rows, vocab] tensor).  Returns (loss, logprob),
+    logprob detached."""
+    return _WeightedNLL.apply(logits, targets, weights, float(temperature), bool(inplace))

@@ -79,3 +79,38 @@ def test_topk_kl_autograd_bf16_inplace_and_rows():
     with pytest.raises(ValueError):
         vwc.topk_kl(xc, idd[rl].contiguous(), tld[rl].contiguous(), mode,
                     row_idx=torch.from_numpy(rows).to(DEV), inplace_backward=True)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_weighted_topk_kl_one_call(mode):
+    """weighted_topk_kl: sum w KL and its gradient from the one-call top-k KL in the
+    forward, scaled in the backward; equal to topk_kl's loss and gradient computed by
+    the one call directly, and in place."""
+    w = W.scaled("distill_bf16_4096x248320_k128", 12, 151936)
+    x = W.all_logits(w)
+    idx, tlp = W.topk_payload(w)
+    wt = np.random.default_rng(6).uniform(-1, 1, w.n_rows).astype(np.float32)
+    wt[3] = 0.0
+    wd = torch.from_numpy(wt).to(DEV)
+    idd, tld = torch.from_numpy(idx).to(DEV), torch.from_numpy(tlp).to(DEV)
+    xd = to_dev_logits(x)
+    out, direct = vwc.topk_kl_fwd_bwd(xd, idd, tld, wd, mode)
+    leaf = xd.clone().requires_grad_(True)
+    loss, rows = vwc.weighted_topk_kl(leaf, idd, tld, wd, mode)
+    assert not rows.requires_grad and torch.equal(rows, out["loss"])
+    assert torch.equal(loss.detach(), (wd * out["loss"]).sum())
+    (3.0 * loss).backward()
+    assert torch.equal(_bits(leaf.grad), _bits(direct * torch.tensor(3.0, dtype=direct.dtype,
+                                                                     device=DEV)))
+    ref = oracle.topk_kl_backward(x, idx, tlp, mode, wt)
+    from test_gpu_topk_kl import check_bf16_grad, grad_bound
+    from gpu_util import grad_bits
+    ref_fwd = check_fwd(out, x, idx, tlp, mode, 1.0)
+    check_bf16_grad(grad_bits(direct), ref, grad_bound(x, idx, tlp, mode, 1.0, out, ref_fwd, wt))
+    base = xd.clone().requires_grad_(True)
+    logits = base * 1.0
+    loss2, _ = vwc.weighted_topk_kl(logits, idd, tld, wd, mode, inplace=True)
+    assert torch.equal(loss2, loss.detach())
+    loss2.backward()
+    assert torch.equal(_bits(logits.detach()), _bits(direct))
+    assert torch.equal(_bits(base.grad), _bits(direct))

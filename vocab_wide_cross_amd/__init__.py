@@ -17,4 +17,4 @@ from ._binding import (  # noqa: F401
     topk_kl_fwd_bwd_rows, topk_kl_fwd_rows,
     vocab_partial, workspace_bytes,
 )
-from .autograd import selected_logprob, topk_kl, weighted_nll  # noqa: F401,E402
+from .autograd import selected_logprob, topk_kl, weighted_nll, weighted_topk_kl  # noqa: F401,E402

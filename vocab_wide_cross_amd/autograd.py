@@ -194,3 +194,43 @@ def weighted_nll(logits, targets, weights, temperature=1.0, inplace=False):
     are gone afterwards (no second [rows, vocab] tensor).  Returns (loss, logprob),
     logprob detached."""
     return _WeightedNLL.apply(logits, targets, weights, float(temperature), bool(inplace))
+
+
+class _WeightedTopkKL(torch.autograd.Function):
+    """loss = sum_r w_r KL_r (the top-k KL of topk_kl) with the weights known before the
+    forward: the forward is the one-call top-k KL, which writes the loss's gradient
+    while it holds each row; the backward only scales it."""
+
+    @staticmethod
+    def forward(ctx, logits, topk_idx, teacher_logprob, weights, mode, tail_mass_eps,
+                temperature, inplace):
+        w = weights.contiguous().float()
+        out, grad = B.topk_kl_fwd_bwd(logits, topk_idx, teacher_logprob, w, mode=mode,
+                                      tail_mass_eps=tail_mass_eps, temperature=temperature,
+                                      grad_logits=logits if inplace else None)
+        if inplace:  # the library overwrote the logits: let autograd see the write
+            torch.autograd.graph.increment_version(logits)
+        ctx.save_for_backward(grad)
+        ctx.mark_non_differentiable(out["loss"])
+        return (w * out["loss"]).sum(), out["loss"]
+
+    @staticmethod
+    def backward(ctx, grad_loss, grad_rows=None):
+        (grad,) = ctx.saved_tensors
+        if grad_loss is None:
+            return None, None, None, None, None, None, None, None
+        if not (grad_loss.numel() == 1 and float(grad_loss) == 1.0):
+            grad = grad * grad_loss.to(grad.dtype)
+        return grad, None, None, None, None, None, None, None
+
+
+def weighted_topk_kl(logits, topk_idx, teacher_logprob, weights, mode=B.VWC_KL_TAIL,
+                     tail_mass_eps=1e-6, temperature=1.0, inplace=False):
+    """sum_r weights[r] * KL_r (KL_r as topk_kl computes it), differentiable with respect
+    to `logits`, for weights known before the forward (a token mean).  The gradient is
+    computed in the forward by the one-call top-k KL (one read and one write of the
+    logits where the row fits on chip) and kept until the backward; with inplace=True
+    it is written over `logits`, which are gone afterwards.  Returns (loss, per-row KL),
+    the latter detached."""
+    return _WeightedTopkKL.apply(logits, topk_idx, teacher_logprob, weights, int(mode),
+                                 float(tail_mass_eps), float(temperature), bool(inplace))

@@ -70,3 +70,13 @@ def test_topk_kl_autograd_refuses_inplace_rows():
         vwc.topk_kl(x, idx, tlp, row_idx=rows, inplace_backward=True)
     with pytest.raises(ValueError, match="GPU"):  # host tensors never reach the library
         vwc.topk_kl(x, torch.zeros(4, 3, dtype=torch.int32), torch.zeros(4, 3))
+
+
+def test_weighted_losses_refuse_host_tensors():
+    x = _x()
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        vwc.weighted_nll(x, t, torch.zeros(4))
+    with pytest.raises(ValueError, match="GPU"):
+        vwc.weighted_topk_kl(x, torch.zeros(4, 3, dtype=torch.int32), torch.zeros(4, 3),
+                             torch.zeros(4))

@@ -92,6 +92,19 @@ def test_one_call_forward_backward_allocates_only_its_outputs(inputs):
     assert grew <= _bytes(*outs) + vwc.workspace_bytes(N, V, torch.bfloat16) + SLACK
 
 
+def test_weighted_nll_in_place_allocates_only_row_outputs(inputs):
+    """weighted_nll with inplace=True: the one call writes the gradient over the
+    logits, so its forward allocates only per-row outputs and workspace."""
+    logits, targets, grad_out = inputs
+    base = logits.clone().requires_grad_(True)
+    x = base * 1.0  # the logits as an op's output, as from an LM head
+    w = grad_out.abs()
+    grew, (loss, lp) = _peak_growth(lambda: vwc.weighted_nll(x, targets, w, inplace=True))
+    log(f"weighted_nll in place: grew {grew} B")
+    assert grew <= N * PER_ROW_CAP + SLACK
+    del loss, lp, x, base
+
+
 def test_entropy_gradient_allocates_only_the_gradient(inputs):
     logits, targets, grad_out = inputs
     _, lse, ent = vwc.selected_logprob_fwd(logits, targets, want=("lse", "entropy"))

@@ -349,6 +349,42 @@ def test_run_to_run_deterministic():
     assert torch.equal(ga.view(torch.int16), gb.view(torch.int16))
 
 
+def test_concurrent_streams_give_sequential_bits():
+    """The library holds no state between calls: forward, backward and the one call
+    issued on two streams at once, on different inputs (4-segment rows that use
+    the workspace), give the bits of the same calls made one after another."""
+    outs = []
+    cases = []
+    for seed, n in ((1, 96), (2, 80)):
+        w = W.scaled("spiked_bf16_8192x248320", n, 248320 + seed)
+        x, t, g = _host(w)
+        cases.append((to_dev_logits(x), torch.from_numpy(t).to(DEV), torch.from_numpy(g).to(DEV)))
+
+    def work(xd, td, gd, stream):
+        lp, lse, ent = vwc.selected_logprob_fwd(xd, td, want=("logprob", "lse", "entropy"),
+                                                stream=stream)
+        grad = vwc.selected_logprob_bwd(xd, td, lse, gd, stream=stream)
+        one = vwc.selected_logprob_fwd_bwd(xd, td, gd, stream=stream)
+        return (lp, lse, ent, grad, one[0], one[1], one[3])
+
+    seq = [work(*c, torch.cuda.current_stream()) for c in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for c, st in zip(cases, streams):
+            with torch.cuda.stream(st):
+                outs.append(work(*c, st))
+    torch.cuda.synchronize()
+    for k, o in enumerate(outs):
+        ref = seq[k % 2]
+        for a, b in zip(o, ref):
+            va = a.view(torch.int16) if a.dtype == torch.bfloat16 else a
+            vb = b.view(torch.int16) if b.dtype == torch.bfloat16 else b
+            assert torch.equal(va, vb)
+
+
 # ------------------------------------------------------------------ split vocabulary
 
 

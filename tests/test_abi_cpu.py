@@ -412,3 +412,29 @@ def test_every_logits_entry_point_checks_its_arguments(lib, name, params):
         msg = lib.vwc_last_error().decode()
         assert st == INVALID, (name, key, val, st, msg)
         assert msg.startswith(name), (name, msg)
+
+
+def test_last_error_is_per_thread(lib):
+    """Each host thread reads back its own last failure (the detail is thread-local)."""
+    import threading
+    f = _fwd(lib)
+    lib.vwc_last_error.restype = ctypes.c_char_p
+    results = {}
+
+    def worker(name, n_rows, vocab):
+        msgs = set()
+        for _ in range(2000):
+            st = f(FAKE, BF16, n_rows, vocab, max(vocab, 1), FAKE, 1.0, FAKE, FAKE, None, None, 0,
+                   None)
+            assert st == INVALID
+            msgs.add(lib.vwc_last_error().decode())
+        results[name] = msgs
+
+    ts = [threading.Thread(target=worker, args=("rows", -1, 64)),
+          threading.Thread(target=worker, args=("vocab", 4, 0))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert results["rows"] == {"vwc_selected_logprob_fwd: n_rows < 0"}
+    assert results["vocab"] == {"vwc_selected_logprob_fwd: vocab must be positive"}

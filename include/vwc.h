@@ -316,6 +316,45 @@ vwc_status vwc_logprob_entropy_bwd_rows(const void *logits, vwc_dtype dt, int64_
                                         void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
                                         vwc_grad_layout layout, hipStream_t stream);
 
+/*
+ * Forward and the logprob + entropy backward in one call, for a loss
+ *   L = sum_r g_r * logprob_r + h_r * entropy_r
+ * whose weights g (grad_logprob, nullable: 0) and h (grad_entropy, required)
+ * are known before the forward ("[Bug] Training/log-prob forward materializes
+ * full-vocab fp32 logits ..." section "Bug Description": RL losses that use the
+ * log-probabilities and the entropy of the same logits, e.g. an entropy bonus
+ * with a token-mean weight).  The results are those of vwc_selected_logprob_fwd
+ * with the entropy, followed by vwc_logprob_entropy_bwd with the lse and entropy
+ * it wrote: lse and entropy (float[n_rows]) are required outputs, logprob is
+ * nullable; targets may be NULL when neither grad_logprob nor logprob is given.
+ * When a row fits on chip (as for vwc_selected_logprob_fwd_bwd) one workgroup
+ * per row reads it once and writes its gradient from the held values;
+ * otherwise the two calls run in turn.  lse, entropy and logprob may differ from
+ * the separate forward's in the last bits (another reduction order); the
+ * gradient is the separate backward's from these outputs, bit for bit.  Rows
+ * with g == 0 and h == 0 get +0.0.  In place (grad_logits == logits) as for
+ * the backward.  Other arguments and errors as vwc_selected_logprob_fwd_bwd.
+ */
+vwc_status vwc_logprob_entropy_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                       int64_t vocab, int64_t ld, const int32_t *targets,
+                                       float temperature, const float *grad_logprob,
+                                       const float *grad_entropy, float *logprob, float *lse,
+                                       float *entropy, void *grad_logits, vwc_dtype grad_dt,
+                                       int64_t ld_grad, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* The same over the row set row_idx[0..m): grad_logprob, grad_entropy and the
+   outputs are float[m] (compact); layout, bad row ids and the in-place rule as
+   for vwc_selected_logprob_fwd_bwd_rows. */
+vwc_status vwc_logprob_entropy_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                            int64_t vocab, int64_t ld, const int32_t *targets,
+                                            const int32_t *row_idx, int64_t m, float temperature,
+                                            const float *grad_logprob, const float *grad_entropy,
+                                            float *logprob, float *lse, float *entropy,
+                                            void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                            vwc_grad_layout layout, void *workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
+
 typedef enum vwc_kl_mode {
     VWC_KL_TRUNCATED = 0, /* sum over the teacher top-k, clamped at 0 */
     VWC_KL_TAIL = 1,      /* K+1 categories: the top-k plus one aggregate tail */

@@ -53,6 +53,10 @@ def _load() -> ctypes.CDLL:
                                           p, sz, p], i32),
         "vwc_selected_logprob_fwd_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, p,
                                                i32, i64, i32, p, sz, p], i32),
+        "vwc_logprob_entropy_fwd_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, p, i32, i64,
+                                         p, sz, p], i32),
+        "vwc_logprob_entropy_fwd_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, p, p,
+                                              p, i32, i64, i32, p, sz, p], i32),
         "vwc_selected_logprob_bwd_rows": ([p, i32, i64, i64, i64, p, p, i64, f32, p, p, p, i32,
                                            i64, i32, p], i32),
         "vwc_logprob_entropy_bwd": ([p, i32, i64, i64, i64, p, f32, p, p, p, p, p, i32, i64, p], i32),
@@ -295,6 +299,66 @@ def selected_logprob_fwd_bwd(logits, targets, grad_logprob, temperature=1.0, log
                                              _ptr(g), _dtype(g), gld, _ptr(ws), wsb,
                                              _stream(stream, logits)))
     return lp, ls, en, g
+
+
+def logprob_entropy_fwd_bwd(logits, targets, grad_logprob, grad_entropy, temperature=1.0,
+                            logprob=None, lse=None, entropy=None, want=("logprob", "lse", "entropy"),
+                            grad_logits=None, grad_dtype=None, workspace=None, stream=None):
+    """Forward and the logprob + entropy backward in one call for loss weights
+    grad_logprob (g, or None: 0) and grad_entropy (h) known up front; returns (logprob,
+    lse, entropy, grad_logits), None for logprob when not asked for."""
+    n, v, ld = _rows_view(logits)
+    if targets is not None:
+        _i32(targets, "targets", n)
+    if grad_logprob is not None:
+        _f32_in(grad_logprob, n, "grad_logprob")
+    _f32_in(grad_entropy, n, "grad_entropy")
+    lp = _f32(n, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(n, logits, lse)
+    en = _f32(n, logits, entropy)
+    g = _grad_out(logits, n, grad_logits, grad_dtype)
+    gld = _grad_rows(g, n, v)
+    ws, wsb = _workspace(n, v, logits, workspace)
+    _check(_lib.vwc_logprob_entropy_fwd_bwd(_ptr(logits), _dtype(logits), n, v, ld,
+                                            _ptr(targets), float(temperature), _ptr(grad_logprob),
+                                            _ptr(grad_entropy), _ptr(lp), _ptr(ls), _ptr(en),
+                                            _ptr(g), _dtype(g), gld, _ptr(ws), wsb,
+                                            _stream(stream, logits)))
+    return lp, ls, en, g
+
+
+def logprob_entropy_fwd_bwd_rows(logits, targets, row_idx, grad_logprob, grad_entropy,
+                                 temperature=1.0, logprob=None, lse=None, entropy=None,
+                                 want=("logprob", "lse", "entropy"), grad_logits=None,
+                                 grad_dtype=None, layout=VWC_GRAD_COMPACT, workspace=None,
+                                 stream=None):
+    """The one-call logprob + entropy forward and backward over a row set; weights and
+    outputs compact [m]; returns (logprob, lse, entropy, grad_logits)."""
+    n, v, ld = _rows_view(logits)
+    if targets is not None:
+        _i32(targets, "targets", n)
+    _i32(row_idx, "row_idx")
+    m = row_idx.numel()
+    if grad_logprob is not None:
+        _f32_in(grad_logprob, m, "grad_logprob")
+    _f32_in(grad_entropy, m, "grad_entropy")
+    lp = _f32(m, logits, logprob) if (logprob is not None or "logprob" in want) else None
+    ls = _f32(m, logits, lse)
+    en = _f32(m, logits, entropy)
+    rows = m if layout == VWC_GRAD_COMPACT else n
+    if grad_logits is None:
+        grad_logits = _grad_out(logits, rows, None, grad_dtype)
+        if layout == VWC_GRAD_SCATTER:
+            grad_logits.zero_()
+    gld = _grad_rows(grad_logits, rows, v)
+    ws, wsb = _workspace(m, v, logits, workspace)
+    _check(_lib.vwc_logprob_entropy_fwd_bwd_rows(_ptr(logits), _dtype(logits), n, v, ld,
+                                                 _ptr(targets), _ptr(row_idx), m,
+                                                 float(temperature), _ptr(grad_logprob),
+                                                 _ptr(grad_entropy), _ptr(lp), _ptr(ls), _ptr(en),
+                                                 _ptr(grad_logits), _dtype(grad_logits), gld,
+                                                 layout, _ptr(ws), wsb, _stream(stream, logits)))
+    return lp, ls, en, grad_logits
 
 
 def selected_logprob_fwd_bwd_rows(logits, targets, row_idx, grad_logprob, temperature=1.0,

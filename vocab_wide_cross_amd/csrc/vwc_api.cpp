@@ -419,10 +419,10 @@ vwc_status vwc_selected_logprob_bwd(const void *logits, vwc_dtype dt, int64_t n_
 static vwc_status fwd_bwd_common(const char *fn, const void *logits, int dt, int64_t n_rows,
                                  int64_t vocab, int64_t ld, const int32_t *targets,
                                  const int32_t *row_idx, int64_t m, float temperature,
-                                 const float *grad_logprob, float *logprob, float *lse,
-                                 float *entropy, void *grad_logits, int grad_dt, int64_t ld_grad,
-                                 bool by_row_id, void *workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
+                                 const float *grad_logprob, const float *grad_entropy,
+                                 float *logprob, float *lse, float *entropy, void *grad_logits,
+                                 int grad_dt, int64_t ld_grad, bool by_row_id, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
     vwc_status st = check_logits(fn, logits, dt, n_rows, vocab, ld, temperature);
     if (st != VWC_OK) return st;
     if (!dtype_ok(grad_dt)) return fail(VWC_ERR_INVALID_ARG, "%s: unknown grad dtype", fn);
@@ -432,9 +432,18 @@ static vwc_status fwd_bwd_common(const char *fn, const void *logits, int dt, int
     if (!row_idx && m != n_rows)
         return fail(VWC_ERR_INVALID_ARG, "%s: without row_idx, m must equal n_rows", fn);
     if (n_rows == 0) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx given but n_rows == 0", fn);
-    if (!targets || !grad_logprob || !lse || !grad_logits)
-        return fail(VWC_ERR_INVALID_ARG, "%s: null targets, grad_logprob, lse or grad_logits",
-                    fn);
+    if (!grad_entropy) {
+        if (!targets || !grad_logprob || !lse || !grad_logits)
+            return fail(VWC_ERR_INVALID_ARG,
+                        "%s: null targets, grad_logprob, lse or grad_logits", fn);
+    } else {
+        // The entropy-gradient term: g may be absent (0), and then the targets too
+        // unless logprob is asked for; the entropy is an output the gradient needs.
+        if (!lse || !entropy || !grad_logits)
+            return fail(VWC_ERR_INVALID_ARG, "%s: null lse, entropy or grad_logits", fn);
+        if ((grad_logprob || logprob) && !targets)
+            return fail(VWC_ERR_INVALID_ARG, "%s: targets is null", fn);
+    }
     if (m > INT32_MAX) return fail(VWC_ERR_UNSUPPORTED, "%s: too many rows", fn);
     const int64_t e = esize(dt);
     bool in_place = false;
@@ -456,8 +465,8 @@ static vwc_status fwd_bwd_common(const char *fn, const void *logits, int dt, int
                             workspace_bytes, stream);
         if (st != VWC_OK) return st;
         return backward_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m,
-                               temperature, lse, nullptr, grad_logprob, nullptr, grad_logits,
-                               grad_dt, ld_grad, by_row_id, stream);
+                               temperature, lse, grad_entropy ? entropy : nullptr, grad_logprob,
+                               grad_entropy, grad_logits, grad_dt, ld_grad, by_row_id, stream);
     }
     vwc::FusedPlan p{};
     p.logits = logits;
@@ -474,6 +483,7 @@ static vwc_status fwd_bwd_common(const char *fn, const void *logits, int dt, int
     p.gc_hi = cs.hi;
     p.gc_lo = cs.lo;
     p.grad_out = grad_logprob;
+    p.grad_ent = grad_entropy;
     p.logprob = logprob;
     p.lse = lse;
     p.entropy = entropy;
@@ -491,7 +501,22 @@ vwc_status vwc_selected_logprob_fwd_bwd(const void *logits, vwc_dtype dt, int64_
                                         void *workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
     return fwd_bwd_common("vwc_selected_logprob_fwd_bwd", logits, dt, n_rows, vocab, ld, targets,
-                          nullptr, n_rows, temperature, grad_logprob, logprob, lse, entropy,
+                          nullptr, n_rows, temperature, grad_logprob, nullptr, logprob, lse,
+                          entropy, grad_logits, grad_dt, ld_grad, true, workspace,
+                          workspace_bytes, stream);
+}
+
+vwc_status vwc_logprob_entropy_fwd_bwd(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                       int64_t vocab, int64_t ld, const int32_t *targets,
+                                       float temperature, const float *grad_logprob,
+                                       const float *grad_entropy, float *logprob, float *lse,
+                                       float *entropy, void *grad_logits, vwc_dtype grad_dt,
+                                       int64_t ld_grad, void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    const char *fn = "vwc_logprob_entropy_fwd_bwd";
+    if (!grad_entropy) return fail(VWC_ERR_INVALID_ARG, "%s: grad_entropy is null", fn);
+    return fwd_bwd_common(fn, logits, dt, n_rows, vocab, ld, targets, nullptr, n_rows,
+                          temperature, grad_logprob, grad_entropy, logprob, lse, entropy,
                           grad_logits, grad_dt, ld_grad, true, workspace, workspace_bytes,
                           stream);
 }
@@ -510,8 +535,28 @@ vwc_status vwc_selected_logprob_fwd_bwd_rows(const void *logits, vwc_dtype dt, i
         return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
     if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
     return fwd_bwd_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
-                          grad_logprob, logprob, lse, entropy, grad_logits, grad_dt, ld_grad,
-                          layout == VWC_GRAD_SCATTER, workspace, workspace_bytes, stream);
+                          grad_logprob, nullptr, logprob, lse, entropy, grad_logits, grad_dt,
+                          ld_grad, layout == VWC_GRAD_SCATTER, workspace, workspace_bytes,
+                          stream);
+}
+
+vwc_status vwc_logprob_entropy_fwd_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,
+                                            int64_t vocab, int64_t ld, const int32_t *targets,
+                                            const int32_t *row_idx, int64_t m, float temperature,
+                                            const float *grad_logprob, const float *grad_entropy,
+                                            float *logprob, float *lse, float *entropy,
+                                            void *grad_logits, vwc_dtype grad_dt, int64_t ld_grad,
+                                            vwc_grad_layout layout, void *workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+    const char *fn = "vwc_logprob_entropy_fwd_bwd_rows";
+    if (layout != VWC_GRAD_COMPACT && layout != VWC_GRAD_SCATTER)
+        return fail(VWC_ERR_INVALID_ARG, "%s: unknown layout %d", fn, static_cast<int>(layout));
+    if (m > 0 && !row_idx) return fail(VWC_ERR_INVALID_ARG, "%s: row_idx is null", fn);
+    if (!grad_entropy) return fail(VWC_ERR_INVALID_ARG, "%s: grad_entropy is null", fn);
+    return fwd_bwd_common(fn, logits, dt, n_rows, vocab, ld, targets, row_idx, m, temperature,
+                          grad_logprob, grad_entropy, logprob, lse, entropy, grad_logits, grad_dt,
+                          ld_grad, layout == VWC_GRAD_SCATTER, workspace, workspace_bytes,
+                          stream);
 }
 
 vwc_status vwc_selected_logprob_bwd_rows(const void *logits, vwc_dtype dt, int64_t n_rows,

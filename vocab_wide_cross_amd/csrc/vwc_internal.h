@@ -163,6 +163,7 @@ struct FusedPlan {
     float gc_hi, gc_lo;       // log2(e) / tau as a float pair (the gradient; split_scale)
     double tau;
     const float *grad_out;    // [m]
+    const float *grad_ent;    // [m] incoming d/d entropy (the entropy-gradient term), or null
     float *logprob, *lse, *entropy;  // [m]; lse non-null, the others nullable
     void *grad;
     int64_t ld_grad;

@@ -1189,9 +1189,10 @@ __global__ __launch_bounds__(kTopkBlock) void topk_fixup_kernel(TopkPlan p) {
 // under the thread that stores that column's unit, which writes it after the
 // unit (same thread, later store).  The loss, which the gradient does not
 // need, is written at the end.
-template <int DT, bool W, bool KL = false>
+template <int DT, bool W, bool KL = false, bool WH = false>
 __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     static_assert(!(KL && W), "the top-k KL call writes no entropy");
+    static_assert(!WH || (W && !KL), "the entropy gradient needs the entropy, no top-k KL");
     using Un = Unit<DT, true>;
     using T = typename Un::T;
     using Us = Unit<DT, false>;
@@ -1202,6 +1203,10 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     __shared__ Lane wave_state[kFusedBlock / 64];
     __shared__ double row_gt;
     __shared__ float row_lse, row_B, row_gs;
+    // the entropy gradient's row constants (WH): o = p' (a + b u'), and for the
+    // target column -h/tau and the saved entropy
+    __shared__ float row_a, row_b;
+    __shared__ double row_hs, row_H;
     // KL: the waves' payload sums (P, Q, S, bad), the row's coefficients, the
     // payload gradients and, per thread, the list of those its units hold.
     constexpr int kKlN = KL ? kKlMaxK : 1;
@@ -1284,10 +1289,11 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
                                           rsrc, static_cast<uint32_t>(tid * 16 + (kFusedLds + kr) * kStride),
                                           0, 2));
     __builtin_amdgcn_sched_barrier(0);
-    const float g = p.grad_out[i];
+    const float g = (!WH || p.grad_out) ? p.grad_out[i] : 0.f;  // WH: g may be absent
+    const float h = WH ? p.grad_ent[i] : 0.f;
     // The target (logprob mode), or this thread's payload column (KL): one more
     // load each, after the row's.
-    const int32_t t = KL ? -1 : p.targets[r];
+    const int32_t t = (KL || (WH && !p.targets)) ? -1 : p.targets[r];
     const bool t_ok = t >= 0 && t < p.vocab;
     const bool kj_ok = kj >= 0 && kj < p.vocab;
     const typename Us::T t_raw =
@@ -1392,11 +1398,21 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
             const float lse32 = static_cast<float>(mg.M / p.tau + log(mg.S));  // lse[i]
             row_lse = lse32;
             if constexpr (!KL) {
-                const RowGrad R0 = row_grad(p.gc_hi, p.gc_lo, p.tau, lse32, g, 0.f, 0.0,
+                // WH: the entropy as written (its float), as the separate backward reads it
+                const double H32 = WH ? static_cast<double>(static_cast<float>(
+                                            log(mg.S) - mg.W / mg.S))
+                                      : 0.0;
+                const RowGrad R0 = row_grad(p.gc_hi, p.gc_lo, p.tau, lse32, g, h, H32,
                                             -static_cast<double>(g) / p.tau);
                 row_B = R0.B;
                 row_gs = R0.gs;
                 row_gt = R0.gt;
+                if constexpr (WH) {
+                    row_a = R0.a;
+                    row_b = R0.b;
+                    row_hs = R0.hs;
+                    row_H = R0.H;
+                }
             }
         }
     }
@@ -1471,16 +1487,16 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     R.c_lo = p.gc_lo;
     R.B = row_B;
     R.gs = row_gs;
-    R.a = 0.f;
-    R.b = 0.f;
+    R.a = WH ? row_a : 0.f;
+    R.b = WH ? row_b : 0.f;
     R.gt = row_gt;
-    R.hs = 0.0;
-    R.H = 0.0;
+    R.hs = WH ? row_hs : 0.0;
+    R.H = WH ? row_H : 0.0;
     R.lse = static_cast<double>(row_lse);
     R.tau = p.tau;
-    R.t = t;
+    R.t = g != 0.f ? t : -1;  // no one-hot term without a logprob weight, as in the backward
     // A row without loss (or a clamped truncated KL row): +0.0, nothing computed.
-    const bool zero = KL ? kl_zero != 0 : g == 0.f;
+    const bool zero = KL ? kl_zero != 0 : (g == 0.f && h == 0.f);
     // p' = 2^u' with u' increasing in x, so the thread's smallest logit gives
     // its smallest exponent: when that one lies at or above -126 every unit of
     // the thread takes the bare exp2 (exp2f's bits there), else every unit takes
@@ -1496,7 +1512,7 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
 #pragma unroll
                 for (int k = 0; k < N; ++k) o[k] = 0.f;
             } else {
-                unit_grad<DT, true, false, kExp, kPair, false>(x, head + u * N, R, o);
+                unit_grad<DT, true, WH, kExp, kPair, false>(x, head + u * N, R, o);
             }
             GradStore<DT, N>::store(dst, o);
         };
@@ -1545,7 +1561,7 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
 #pragma unroll
                 for (int e = 0; e < N; ++e) o[e] = 0.f;
             } else {
-                unit_grad<DT, true, false, kExpRescale, true, false>(Un::load(src + u), head + u * N, R, o);
+                unit_grad<DT, true, WH, kExpRescale, true, false>(Un::load(src + u), head + u * N, R, o);
             }
             GradStore<DT, N>::store(vgrow + k * kStride, o);
         }
@@ -1553,19 +1569,24 @@ __global__ __launch_bounds__(kFusedBlock) void fused_row_kernel(FusedPlan p) {
     // The target column, when it lies in the whole vectors: its unit went out
     // above from this thread; this later store from the same thread replaces
     // the element with the one-hot term included.
-    const int32_t tcol = t_ok ? t - head : -1;
+    const int32_t tcol = t_ok && R.t >= 0 ? t - head : -1;
     if (!KL && !zero && tcol >= 0 && tcol < nunits * N && (tcol / N) % kFusedBlock == tid) {
         const double d = static_cast<double>(Us::get(t_raw, 0)) / R.tau - R.lse;
-        float o[1] = {static_cast<float>(R.gt * -expm1(d))};
+        double ot = R.gt * -expm1(d);  // as unit_grad forms the target column
+        if constexpr (WH) {
+            const double pt = exp(d);
+            if (pt != 0.0) ot += R.hs * pt * (d + R.H);
+        }
+        float o[1] = {static_cast<float>(ot)};
         GradStore<DT, 1>::store(grow + static_cast<int64_t>(t) * kE, o);
     }
     if (edge >= 0) {
         float o[1] = {0.f};
         if (!zero) {
             if (pair)
-                unit_grad<DT, false, false, kExpPerUnit, true>(ev[0], edge, R, o);
+                unit_grad<DT, false, WH, kExpPerUnit, true>(ev[0], edge, R, o);
             else
-                unit_grad<DT, false, false, kExpPerUnit, false>(ev[0], edge, R, o);
+                unit_grad<DT, false, WH, kExpPerUnit, false>(ev[0], edge, R, o);
         }
         GradStore<DT, 1>::store(grow + static_cast<int64_t>(edge) * kE, o);
     }
@@ -1849,6 +1870,13 @@ hipError_t launch_fused(const FusedPlan &p, hipStream_t stream) {
             hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, false, true>), grid, block, 0, stream, p);
         else
             hipLaunchKernelGGL((fused_row_kernel<VWC_FP32, false, true>), grid, block, 0, stream, p);
+    } else if (p.grad_ent) {  // the host checked: the entropy output is requested
+        if (p.dt == VWC_BF16)
+            hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, true, false, true>), grid, block, 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((fused_row_kernel<VWC_FP32, true, false, true>), grid, block, 0,
+                               stream, p);
     } else if (p.dt == VWC_BF16) {
         if (w)
             hipLaunchKernelGGL((fused_row_kernel<VWC_BF16, true>), grid, block, 0, stream, p);

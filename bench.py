@@ -715,6 +715,36 @@ def main():
     # one read of the logits, grad_out and targets; logprob, lse and the gradient written
     fused_b = w.n_rows * (w.vocab * esize + 8) + w.n_rows * (8 + w.vocab * esize)
 
+    # With the entropy term as well (d(g logprob + h H)/dx): the fused backward after
+    # the forward with the entropy, and the same as one call
+    # (vwc_logprob_entropy_fwd_bwd).  h ~ U(-1, 1) with 20 % zeros.
+    hgen = torch.Generator(device=dev).manual_seed(8)
+    h_out = torch.rand(w.n_rows, device=dev, generator=hgen) * 2 - 1
+    h_out[torch.rand(w.n_rows, device=dev, generator=hgen) < 0.2] = 0
+
+    def time_calls(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            ev[k][0].record(stream)
+            fn()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return ms_stats([e[0].elapsed_time(e[1]) for e in ev])
+
+    ent_bwd_st = time_calls(lambda: vwc.logprob_entropy_bwd(
+        x, targets, lse, ent_buf, grad_out, h_out, w.tau, grad_logits=grad, stream=stream))
+    ent_one_st = time_calls(lambda: vwc.logprob_entropy_fwd_bwd(
+        x, targets, grad_out, h_out, w.tau, logprob=lp, lse=lse, entropy=ent_buf,
+        grad_logits=grad, workspace=ws, stream=stream))
+    live_e = int(((grad_out != 0) | (h_out != 0)).sum().item())
+    # every row reads g and h and writes its gradient; live rows also read the logits,
+    # the target, lse and the entropy
+    ent_bwd_b = w.n_rows * (8 + w.vocab * esize) + live_e * (w.vocab * esize + 12)
+    # one read of the logits, targets, g and h; logprob, lse, entropy and the gradient written
+    ent_one_b = w.n_rows * (w.vocab * esize + 12) + w.n_rows * (12 + w.vocab * esize)
+
     # Dominant kernel: the launch with the longest average duration.  The
     # backward is one kernel; the forward is the segment kernel plus a small
     # merge kernel (its events bracket both).
@@ -760,6 +790,19 @@ def main():
                           "frac": gbs(fused_b, fused_st["ms"]) / HBM_PEAK_GBS,
                           "bytes_alg": fused_b,
                           "note": "one call, loss weight known before the forward"},
+        "entropy_grad": {
+            "live_rows": live_e,
+            "bwd": {**ent_bwd_st, "gbs_alg": gbs(ent_bwd_b, ent_bwd_st["ms"]),
+                    "frac": gbs(ent_bwd_b, ent_bwd_st["ms"]) / HBM_PEAK_GBS,
+                    "bytes_alg": ent_bwd_b},
+            "fwd_bwd": {"ms": fwd_e_avg + ent_bwd_st["ms"],
+                        "tokens_per_s": w.n_rows / ((fwd_e_avg + ent_bwd_st["ms"]) * 1e-3)},
+            "one_call": {**ent_one_st, "tokens_per_s": w.n_rows / (ent_one_st["ms"] * 1e-3),
+                         "gbs_alg": gbs(ent_one_b, ent_one_st["ms"]),
+                         "frac": gbs(ent_one_b, ent_one_st["ms"]) / HBM_PEAK_GBS,
+                         "bytes_alg": ent_one_b},
+            "note": "loss g logprob + h entropy, h ~ U(-1,1) with 20% zeros: forward with the "
+                    "entropy then the fused backward, against the same as one call"},
         "roofline": {"bound": "hbm", "kernel": dom[0],
                      "achieved": gbs(dom[1], dom[2]), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs(dom[1], dom[2]) / HBM_PEAK_GBS, "traffic": traffic,

@@ -95,7 +95,9 @@ def test_logprob_path_replays_bitwise(dtype, n, vocab):
         h = vwc.entropy(x)
         vwc.mask_to_index(mask, row_idx=row_ids, count=count)
         f_lp, f_lse, _, f_g = vwc.selected_logprob_fwd_bwd(x, t, go)
-        return [lp, lse, ent, g, lp_r, lse_r, ent_r, g_r, g_s, h, row_ids, count, f_lp, f_lse, f_g]
+        e_lp, e_lse, e_ent, e_g = vwc.logprob_entropy_fwd_bwd(x, t, go, ho)
+        return [lp, lse, ent, g, lp_r, lse_r, ent_r, g_r, g_s, h, row_ids, count, f_lp, f_lse, f_g,
+                e_lp, e_lse, e_ent, e_g]
 
     refill(-1)
     graph, outs = _capture(run)

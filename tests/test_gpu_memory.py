@@ -92,6 +92,14 @@ def test_one_call_forward_backward_allocates_only_its_outputs(inputs):
     assert grew <= _bytes(*outs) + vwc.workspace_bytes(N, V, torch.bfloat16) + SLACK
 
 
+def test_entropy_one_call_allocates_only_its_outputs(inputs):
+    logits, targets, grad_out = inputs
+    h = grad_out.flip(0).contiguous()
+    grew, outs = _peak_growth(lambda: vwc.logprob_entropy_fwd_bwd(logits, targets, grad_out, h))
+    log(f"logprob + entropy fwd+bwd in one call: grew {grew} B")
+    assert grew <= _bytes(*outs) + vwc.workspace_bytes(N, V, torch.bfloat16) + SLACK
+
+
 def test_weighted_nll_in_place_allocates_only_row_outputs(inputs):
     """weighted_nll with inplace=True: the one call writes the gradient over the
     logits, so its forward allocates only per-row outputs and workspace."""

@@ -82,14 +82,21 @@ int64_t segments(int64_t vocab, int dt, int64_t seg_bytes) {
 }
 
 // Backward segments.  bf16 rows: ceil(bytes / kBwdSegBytes).  fp32 rows: the
-// whole number of kBwdSegBytes / 2 pieces nearest to the row's size, at least
-// one (measured: fp32 rows stream faster in pieces of about 128 KiB, while the
-// bf16 step with its write-only zero rows is fastest in pieces of up to 256 KiB).
+// whole number of kBwdPieceF32 pieces nearest to the row's size, at least one.
 int64_t bwd_segments(int64_t vocab, int dt) {
     if (dt == VWC_BF16) return segments(vocab, dt, vwc::kBwdSegBytes);
-    const int64_t piece = vwc::kBwdSegBytes / 2;
+    const int64_t piece = vwc::kBwdPieceF32;
     const int64_t s = (vocab * esize(dt) + piece / 2) / piece;
     return s < 1 ? 1 : s;
+}
+
+// Units per segment: the row's units split into nseg parts, rounded up to a
+// multiple of kSegAlignUnits (element-wise rows: no rounding).  The last
+// segment takes what is left (possibly nothing but the row's edge elements).
+int32_t seg_units_of(int64_t nunits, int64_t nseg, bool vector) {
+    int64_t s = (nunits + nseg - 1) / nseg;
+    if (vector) s = (s + vwc::kSegAlignUnits - 1) / vwc::kSegAlignUnits * vwc::kSegAlignUnits;
+    return static_cast<int32_t>(s < 1 ? 1 : s);
 }
 
 bool rows_aligned16(const void *p, int64_t ld, int64_t e) {
@@ -206,8 +213,7 @@ vwc_status forward_common(const char *fn, const void *logits, int dt, int64_t n_
     // Every row streams 16-byte vectors from its first 16-byte boundary on.
     const int64_t nunits = vocab / (16 / esize(dt));
     p.nseg = static_cast<int>(nseg);
-    p.seg_units = static_cast<int32_t>((nunits + nseg - 1) / nseg);
-    if (p.seg_units < 1) p.seg_units = 1;
+    p.seg_units = seg_units_of(nunits, nseg, true);
     p.want_entropy = entropy != nullptr || partial_out != nullptr;
     p.logprob = logprob;
     p.lse = lse;
@@ -318,8 +324,7 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     const int64_t unit = p.vector ? 16 / esize(dt) : 1;
     const int64_t nunits = vocab / unit;
     p.nseg = static_cast<int>(nseg);
-    p.seg_units = static_cast<int32_t>((nunits + nseg - 1) / nseg);
-    if (p.seg_units < 1) p.seg_units = 1;
+    p.seg_units = seg_units_of(nunits, nseg, p.vector);
     if (kl) {
         // The payload columns go into the same pass when the rows are 16-byte
         // vectors and a segment's payload fits the in-LDS table; otherwise the

@@ -26,17 +26,28 @@ constexpr int kCombineBlock = 64;
 // (vocab, dtype) only, so a row's reduction order never depends on how many
 // rows a call covers.  The backward has no reduction; its segment size only
 // sets the work per workgroup.  bf16 rows are cut into ceil(vocab * 2 /
-// kBwdSegBytes) pieces; fp32 rows into the whole number of kBwdSegBytes / 2
+// kBwdSegBytes) pieces; fp32 rows into the whole number of kBwdPieceF32
 // pieces nearest to their size (at least one), i.e. pieces of about 85 to
 // 192 KiB.  Sizes and rules were chosen by timing on MI355X.
 #ifndef VWC_FWD_SEG_BYTES
 #define VWC_FWD_SEG_BYTES (128 * 1024)
 #endif
 #ifndef VWC_BWD_SEG_BYTES
-#define VWC_BWD_SEG_BYTES (256 * 1024)
+#define VWC_BWD_SEG_BYTES (64 * 1024)
 #endif
+#ifndef VWC_BWD_PIECE_F32
+#define VWC_BWD_PIECE_F32 (128 * 1024)
+#endif
+// Segment boundaries fall on multiples of this many 16-byte units from the
+// row's first 16-byte boundary, so that every wave's 1 KiB load or store
+// covers whole 128-byte lines when the row is so aligned.
+#ifndef VWC_SEG_ALIGN_UNITS
+#define VWC_SEG_ALIGN_UNITS 64
+#endif
+constexpr int64_t kSegAlignUnits = VWC_SEG_ALIGN_UNITS;
 constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;
+constexpr int64_t kBwdPieceF32 = VWC_BWD_PIECE_F32;
 
 // Rows of at most this many forward segments are reduced by one workgroup of
 // nseg * kFwdBlock threads that also merges the segment partials (no

@@ -107,6 +107,56 @@ __device__ __forceinline__ void stream_store(T v, T *p) {
 
 __device__ __forceinline__ float bits_to_float(uint32_t b) { return __builtin_bit_cast(float, b); }
 
+// Gradient vectors leave through buffer stores on a resource that spans the
+// bytes one workgroup writes (a segment of a gradient row), with the cache
+// policy bits of gfx950 (sc0 = 1, nt = 2, sc1 = 16).  Non-temporal at device
+// scope (nt | sc1) wrote the backward's mixed read/write stream 2-3 % faster
+// on MI355X than the non-temporal global store (nt alone), which
+// __builtin_nontemporal_store emits; the stronger scope changes no result.
+// 0 keeps the global stores.
+#ifndef VWC_BUF_STORE
+#define VWC_BUF_STORE 1
+#endif
+#ifndef VWC_STORE_CPOL
+#define VWC_STORE_CPOL 18
+#endif
+
+// A buffer resource over `bytes` bytes from `base` (raw, untyped access; the
+// range check drops stores past the end).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes),
+                                             0x00020000);
+}
+
+// Where a vector store goes: byte voff (per lane) of the resource rs, which
+// the global pointer dst also addresses.  The stores never take an SGPR
+// offset: with one, the compiler lets the next VALU instruction overwrite the
+// store's data registers at once, and on MI355X such 16-byte stores were seen
+// to write a stale first dword in some lanes; with the offset field 0 it
+// inserts the wait state.  A uniform part of the offset goes into the
+// resource's base instead.
+struct VecDst {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff;
+    char *dst;
+};
+
+// One 16- or 8-byte vector store.
+__device__ __forceinline__ void vec_store(u32x4 v, const VecDst &d) {
+#if VWC_BUF_STORE
+    __builtin_amdgcn_raw_buffer_store_b128(v, d.rs, static_cast<int>(d.voff), 0, VWC_STORE_CPOL);
+#else
+    stream_store(v, reinterpret_cast<u32x4 *>(d.dst));
+#endif
+}
+__device__ __forceinline__ void vec_store(u32x2 v, const VecDst &d) {
+#if VWC_BUF_STORE
+    __builtin_amdgcn_raw_buffer_store_b64(v, d.rs, static_cast<int>(d.voff), 0, VWC_STORE_CPOL);
+#else
+    stream_store(v, reinterpret_cast<u32x2 *>(d.dst));
+#endif
+}
+
 // ---------------------------------------------------------------- load units
 // A load unit is a 16-byte vector (vector path) or one element (any layout).
 
@@ -704,6 +754,20 @@ struct GradStore<VWC_BF16, N> {
                                             reinterpret_cast<u32x2 *>(dst));
         }
     }
+    // The same vector (N > 1) at d.
+    static __device__ __forceinline__ void store(const VecDst &d, const float (&o)[N]) {
+        static_assert(N == 4 || N == 8, "vector units");
+        uint32_t packed[N / 2];
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            const bf16x2 b = __builtin_convertvector((f32x2{o[2 * k], o[2 * k + 1]}), bf16x2);
+            packed[k] = __builtin_bit_cast(uint32_t, b);
+        }
+        if constexpr (N == 8)
+            vec_store(u32x4{packed[0], packed[1], packed[2], packed[3]}, d);
+        else
+            vec_store(u32x2{packed[0], packed[1]}, d);
+    }
 };
 
 template <int N>
@@ -717,6 +781,13 @@ struct GradStore<VWC_FP32, N> {
                 stream_store(f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]},
                                             reinterpret_cast<f32x4 *>(dst + 4 * k));
         }
+    }
+    static __device__ __forceinline__ void store(const VecDst &d, const float (&o)[N]) {
+        static_assert(N == 4 || N == 8, "vector units");
+#pragma unroll
+        for (int k = 0; k < N; k += 4)
+            vec_store(__builtin_bit_cast(u32x4, (f32x4{o[k], o[k + 1], o[k + 2], o[k + 3]})),
+                      VecDst{d.rs, d.voff + 4u * k, d.dst + 4 * k});
     }
 };
 
@@ -948,6 +1019,22 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
     const int32_t u0 = q * p.seg_units;
     const int32_t u1 = min(u0 + p.seg_units, nunits);
     const bool last = q == p.nseg - 1;
+    // Unit b + j kBwdBlock of this thread (j uniform): byte (b - u0) N kGE of a
+    // buffer resource over this segment's whole gradient vectors from unit
+    // u0 + j kBwdBlock on.
+    const int64_t seg_bytes = static_cast<int64_t>(max(u1 - u0, 0)) * N * kGE;
+    auto put = [&](int32_t b, int j, const float (&o)[N]) {
+        char *dst = vgrow + static_cast<int64_t>(b + j * kBwdBlock) * N * kGE;
+        if constexpr (VEC) {
+            const int64_t lead = static_cast<int64_t>(j) * kBwdBlock * N * kGE;
+            const __amdgpu_buffer_rsrc_t rs =
+                span_rsrc(vgrow + static_cast<int64_t>(u0) * N * kGE + lead,
+                          static_cast<uint32_t>(max(seg_bytes - lead, int64_t{0})));
+            GradStore<GDT, N>::store(VecDst{rs, static_cast<uint32_t>((b - u0) * N * kGE), dst}, o);
+        } else {
+            GradStore<GDT, N>::store(dst, o);
+        }
+    };
     const float g = p.grad_out ? p.grad_out[i] : 0.f;
     const float h = WH ? p.grad_ent[i] : 0.f;
     const bool kl = p.kl_P != nullptr;
@@ -961,8 +1048,7 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         float z[N];
 #pragma unroll
         for (int k = 0; k < N; ++k) z[k] = 0.f;
-        for (int32_t b = u0 + static_cast<int32_t>(threadIdx.x); b < u1; b += kBwdBlock)
-            GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(b) * N * kGE, z);
+        for (int32_t b = u0 + static_cast<int32_t>(threadIdx.x); b < u1; b += kBwdBlock) put(b, 0, z);
         if (VEC && last) {
             const int32_t j = edge_column(head, nunits * N, p.vocab,
                                           static_cast<int32_t>(threadIdx.x));
@@ -1035,15 +1121,25 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
                 unit_grad<DT, VEC, WH, kExpRescale, kPair>(v[j], head + unit * N, R, o);
                 if (KLF && ((kl_mine >> ((unit - u0) / kBwdBlock)) & 1u))
                     kl_patch<N>(kl_tab, unit - u0, o);
-                GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(unit) * N * kGE, o);
+                put(b, j, o);
             }
         }
-        for (; b < u1; b += kBwdBlock) {
-            const T v = Un::load(src + b);
-            float o[N];
-            unit_grad<DT, VEC, WH, kExpRescale, kPair>(v, head + b * N, R, o);
-            if (KLF && ((kl_mine >> ((b - u0) / kBwdBlock)) & 1u)) kl_patch<N>(kl_tab, b - u0, o);
-            GradStore<GDT, N>::store(vgrow + static_cast<int64_t>(b) * N * kGE, o);
+        // The last (at most U - 1) units of this thread: all loads first, as above.
+        if (b < u1) {
+            T v[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) v[j] = b + j * kBwdBlock < u1 ? Un::load(src + b + j * kBwdBlock) : T{};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < U - 1; ++j) {
+                const int32_t unit = b + j * kBwdBlock;
+                if (unit >= u1) break;
+                float o[N];
+                unit_grad<DT, VEC, WH, kExpRescale, kPair>(v[j], head + unit * N, R, o);
+                if (KLF && ((kl_mine >> ((unit - u0) / kBwdBlock)) & 1u))
+                    kl_patch<N>(kl_tab, unit - u0, o);
+                put(b, j, o);
+            }
         }
         if (VEC && last) {
             const int32_t j = edge_column(head, nunits * N, p.vocab, static_cast<int32_t>(threadIdx.x));

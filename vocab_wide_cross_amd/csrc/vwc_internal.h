@@ -26,14 +26,21 @@ constexpr int kCombineBlock = 64;
 // (vocab, dtype) only, so a row's reduction order never depends on how many
 // rows a call covers.  The backward has no reduction; its segment size only
 // sets the work per workgroup.  bf16 rows are cut into ceil(vocab * 2 /
-// kBwdSegBytes) pieces; fp32 rows into the whole number of kBwdPieceF32
-// pieces nearest to their size (at least one), i.e. pieces of about 85 to
-// 192 KiB.  Sizes and rules were chosen by timing on MI355X.
+// kBwdSegBytes) pieces (kBwdSegBytesWH with the entropy-gradient term, whose
+// heavier arithmetic favours longer pieces); fp32 rows into the whole number
+// of kBwdPieceF32 pieces nearest to their size (at least one), i.e. pieces of
+// about 85 to 192 KiB.  Sizes and rules were chosen by timing on MI355X: with
+// 64 KiB pieces a 1024-thread workgroup issues all its loads in one round (at
+// most four 16-byte loads per lane), which the default step streamed 6.5 %
+// faster than 256 KiB pieces.
 #ifndef VWC_FWD_SEG_BYTES
 #define VWC_FWD_SEG_BYTES (128 * 1024)
 #endif
 #ifndef VWC_BWD_SEG_BYTES
 #define VWC_BWD_SEG_BYTES (64 * 1024)
+#endif
+#ifndef VWC_BWD_SEG_BYTES_WH
+#define VWC_BWD_SEG_BYTES_WH (128 * 1024)
 #endif
 #ifndef VWC_BWD_PIECE_F32
 #define VWC_BWD_PIECE_F32 (128 * 1024)
@@ -47,6 +54,7 @@ constexpr int kCombineBlock = 64;
 constexpr int64_t kSegAlignUnits = VWC_SEG_ALIGN_UNITS;
 constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;
+constexpr int64_t kBwdSegBytesWH = VWC_BWD_SEG_BYTES_WH;  // bf16 rows with the entropy-gradient term
 constexpr int64_t kBwdPieceF32 = VWC_BWD_PIECE_F32;
 
 // Rows of at most this many forward segments are reduced by one workgroup of

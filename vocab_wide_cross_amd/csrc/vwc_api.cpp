@@ -82,11 +82,15 @@ int64_t segments(int64_t vocab, int dt, int64_t seg_bytes) {
 }
 
 // Backward segments.  bf16 rows: ceil(bytes / kBwdSegBytes), or
-// kBwdSegBytesWH with the entropy-gradient term.  fp32 rows: the whole number
-// of kBwdPieceF32 pieces nearest to the row's size, at least one.
-int64_t bwd_segments(int64_t vocab, int dt, bool entropy_term) {
+// kBwdSegBytesWH with the entropy-gradient term, kBwdSegBytesKL for the top-k
+// KL.  fp32 rows: the whole number of kBwdPieceF32 pieces nearest to the
+// row's size, at least one.
+int64_t bwd_segments(int64_t vocab, int dt, bool entropy_term, bool topk_kl) {
     if (dt == VWC_BF16)
-        return segments(vocab, dt, entropy_term ? vwc::kBwdSegBytesWH : vwc::kBwdSegBytes);
+        return segments(vocab, dt,
+                        topk_kl        ? vwc::kBwdSegBytesKL
+                        : entropy_term ? vwc::kBwdSegBytesWH
+                                       : vwc::kBwdSegBytes);
     const int64_t piece = vwc::kBwdPieceF32;
     const int64_t s = (vocab * esize(dt) + piece / 2) / piece;
     return s < 1 ? 1 : s;
@@ -280,7 +284,7 @@ vwc_status backward_common(const char *fn, const void *logits, int dt, int64_t n
     if (grad_entropy && !entropy) return fail(VWC_ERR_INVALID_ARG, "%s: entropy is null", fn);
     if (!lse || !grad_logits)
         return fail(VWC_ERR_INVALID_ARG, "%s: null lse or grad_logits", fn);
-    const int64_t nseg = bwd_segments(vocab, dt, grad_entropy != nullptr);
+    const int64_t nseg = bwd_segments(vocab, dt, grad_entropy != nullptr, kl != nullptr);
     if ((st = check_grid(fn, m, nseg)) != VWC_OK) return st;  // first: bounds m for the sizes below
     const int64_t grad_rows = by_row_id ? n_rows : m;
     bool in_place = false;

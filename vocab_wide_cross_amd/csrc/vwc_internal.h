@@ -42,6 +42,9 @@ constexpr int kCombineBlock = 64;
 #ifndef VWC_BWD_SEG_BYTES_WH
 #define VWC_BWD_SEG_BYTES_WH (128 * 1024)
 #endif
+#ifndef VWC_BWD_SEG_BYTES_KL
+#define VWC_BWD_SEG_BYTES_KL (256 * 1024)
+#endif
 #ifndef VWC_BWD_PIECE_F32
 #define VWC_BWD_PIECE_F32 (128 * 1024)
 #endif
@@ -55,6 +58,9 @@ constexpr int64_t kSegAlignUnits = VWC_SEG_ALIGN_UNITS;
 constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytesWH = VWC_BWD_SEG_BYTES_WH;  // bf16 rows with the entropy-gradient term
+// bf16 rows of the top-k KL backward, whose workgroups each first table the
+// payload columns of their segment.
+constexpr int64_t kBwdSegBytesKL = VWC_BWD_SEG_BYTES_KL;
 constexpr int64_t kBwdPieceF32 = VWC_BWD_PIECE_F32;
 
 // Rows of at most this many forward segments are reduced by one workgroup of

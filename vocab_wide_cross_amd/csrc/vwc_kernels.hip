@@ -119,10 +119,10 @@ __device__ __forceinline__ float bits_to_float(uint32_t b) { return __builtin_bi
 // Gradient vectors leave through buffer stores on a resource that spans the
 // bytes one workgroup writes (a segment of a gradient row), with the cache
 // policy bits of gfx950 (sc0 = 1, nt = 2, sc1 = 16).  Non-temporal at device
-// scope (nt | sc1) wrote the backward's mixed read/write stream 2-3 % faster
-// on MI355X than the non-temporal global store (nt alone), which
+// scope (nt | sc1) ran the backward 0.9-1.7 % faster on MI355X (a copy probe
+// of its traffic 2-3 %) than the non-temporal global store (nt alone), which
 // __builtin_nontemporal_store emits; the stronger scope changes no result.
-// 0 keeps the global stores.
+// VWC_BUF_STORE 0 keeps the global stores.
 #ifndef VWC_BUF_STORE
 #define VWC_BUF_STORE 1
 #endif
@@ -1136,9 +1136,10 @@ __device__ __forceinline__ void bwd_item(const BwdPlan &p, int64_t i, int q) {
         }
         // The last (at most U - 1) units of this thread: all loads first, as above.
         if (b < u1) {
-            T v[U];
+            T v[U - 1];
 #pragma unroll
-            for (int j = 0; j < U; ++j) v[j] = b + j * kBwdBlock < u1 ? Un::load(src + b + j * kBwdBlock) : T{};
+            for (int j = 0; j < U - 1; ++j)
+                v[j] = b + j * kBwdBlock < u1 ? Un::load(src + b + j * kBwdBlock) : T{};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < U - 1; ++j) {

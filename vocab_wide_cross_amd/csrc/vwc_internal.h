@@ -43,7 +43,7 @@ constexpr int kCombineBlock = 64;
 #define VWC_BWD_SEG_BYTES_WH (128 * 1024)
 #endif
 #ifndef VWC_BWD_SEG_BYTES_KL
-#define VWC_BWD_SEG_BYTES_KL (256 * 1024)
+#define VWC_BWD_SEG_BYTES_KL (128 * 1024)
 #endif
 #ifndef VWC_BWD_PIECE_F32
 #define VWC_BWD_PIECE_F32 (128 * 1024)

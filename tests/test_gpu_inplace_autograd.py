@@ -4,7 +4,7 @@ from) and the autograd wrapper.
 In place, every backward call must give the bits of the same call with a
 separate gradient buffer; the autograd wrapper must give the bits of the
 library calls it stands for, and the fp64 oracle's gradient (one bf16 step,
-fp32 within 1e-6).  Shapes span two 256 KiB backward segments and a ragged
+fp32 within 1e-6).  Shapes span several 64 KiB backward segments and a ragged
 tail; row sets include duplicates, whose gradients add.
 """
 import numpy as np

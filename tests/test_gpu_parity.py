@@ -83,11 +83,11 @@ def test_bf16_forward_backward_shapes(vocab):
 def test_very_wide_rows(dtype, vocab):
     """Rows far wider than any vocabulary on the pages, with a ragged tail: 17 or 33
     bf16 (2 or 4 MiB rows) or 129 fp32 (16 MiB rows) forward segments of at most
-    128 KiB, merged by the combine kernel; the backward in 33 or 65 bf16 pieces of
-    at most 64 KiB or 128 fp32 pieces of about 128 KiB.  At 2097155 columns the
-    1 KiB rounding of the segment boundaries leaves the backward's last piece with
-    no whole vector, only the row's three tail elements.  The one call runs the two
-    calls (the rows do not fit on chip) with their bits."""
+    128 KiB, merged by the combine kernel; the backward in 33, 65 or 257 pieces of
+    at most 64 KiB.  At 2097155 bf16 columns the 1 KiB rounding of the segment
+    boundaries leaves the backward's last piece with no whole vector, only the
+    row's three tail elements.  The one call runs the two calls (the rows do not
+    fit on chip) with their bits."""
     n = 3
     base = "spiked_bf16_8192x248320" if dtype == "bf16" else "tiny_fp32_64x2048"
     w = W.scaled(base, n, vocab)

@@ -81,19 +81,14 @@ int64_t segments(int64_t vocab, int dt, int64_t seg_bytes) {
     return s < 1 ? 1 : s;
 }
 
-// Backward segments.  bf16 rows: ceil(bytes / kBwdSegBytes), or
-// kBwdSegBytesWH with the entropy-gradient term, kBwdSegBytesKL for the top-k
-// KL.  fp32 rows: the whole number of kBwdPieceF32 pieces nearest to the
-// row's size, at least one.
+// Backward segments: ceil(row bytes / kBwdSegBytes), or kBwdSegBytesKL for
+// the top-k KL, or kBwdSegBytesWH for bf16 rows with the entropy-gradient
+// term (fp32 rows with that term stream fastest in kBwdSegBytes pieces too).
 int64_t bwd_segments(int64_t vocab, int dt, bool entropy_term, bool topk_kl) {
-    if (dt == VWC_BF16)
-        return segments(vocab, dt,
-                        topk_kl        ? vwc::kBwdSegBytesKL
-                        : entropy_term ? vwc::kBwdSegBytesWH
-                                       : vwc::kBwdSegBytes);
-    const int64_t piece = vwc::kBwdPieceF32;
-    const int64_t s = (vocab * esize(dt) + piece / 2) / piece;
-    return s < 1 ? 1 : s;
+    return segments(vocab, dt,
+                    topk_kl                              ? vwc::kBwdSegBytesKL
+                    : (entropy_term && dt == VWC_BF16) ? vwc::kBwdSegBytesWH
+                                                         : vwc::kBwdSegBytes);
 }
 
 // Units per segment: the row's units split into nseg parts, rounded up to a

@@ -25,14 +25,13 @@ constexpr int kCombineBlock = 64;
 // elements is cut into ceil(vocab * e / kFwdSegBytes) segments, a function of
 // (vocab, dtype) only, so a row's reduction order never depends on how many
 // rows a call covers.  The backward has no reduction; its segment size only
-// sets the work per workgroup.  bf16 rows are cut into ceil(vocab * 2 /
-// kBwdSegBytes) pieces (kBwdSegBytesWH with the entropy-gradient term, whose
-// heavier arithmetic favours longer pieces); fp32 rows into the whole number
-// of kBwdPieceF32 pieces nearest to their size (at least one), i.e. pieces of
-// about 85 to 192 KiB.  Sizes and rules were chosen by timing on MI355X: with
+// sets the work per workgroup: rows are cut into ceil(vocab * e /
+// kBwdSegBytes) pieces (kBwdSegBytesKL for the top-k KL, kBwdSegBytesWH for
+// bf16 rows with the entropy-gradient term, whose heavier arithmetic favours
+// longer pieces).  Sizes and rules were chosen by timing on MI355X: with
 // 64 KiB pieces a 1024-thread workgroup issues all its loads in one round (at
-// most four 16-byte loads per lane), which the default step streamed 6.5 %
-// faster than 256 KiB pieces.
+// most four 16-byte loads per lane), which streamed the default step's bf16
+// backward 6.5 % and an fp32 one 7 % faster than pieces of 128-256 KiB.
 #ifndef VWC_FWD_SEG_BYTES
 #define VWC_FWD_SEG_BYTES (128 * 1024)
 #endif
@@ -45,9 +44,6 @@ constexpr int kCombineBlock = 64;
 #ifndef VWC_BWD_SEG_BYTES_KL
 #define VWC_BWD_SEG_BYTES_KL (128 * 1024)
 #endif
-#ifndef VWC_BWD_PIECE_F32
-#define VWC_BWD_PIECE_F32 (128 * 1024)
-#endif
 // Segment boundaries fall on multiples of this many 16-byte units from the
 // row's first 16-byte boundary, so that every wave's 1 KiB load or store
 // covers whole 128-byte lines when the row is so aligned.
@@ -58,10 +54,9 @@ constexpr int64_t kSegAlignUnits = VWC_SEG_ALIGN_UNITS;
 constexpr int64_t kFwdSegBytes = VWC_FWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytes = VWC_BWD_SEG_BYTES;
 constexpr int64_t kBwdSegBytesWH = VWC_BWD_SEG_BYTES_WH;  // bf16 rows with the entropy-gradient term
-// bf16 rows of the top-k KL backward, whose workgroups each first table the
+// Rows of the top-k KL backward, whose workgroups each first table the
 // payload columns of their segment.
 constexpr int64_t kBwdSegBytesKL = VWC_BWD_SEG_BYTES_KL;
-constexpr int64_t kBwdPieceF32 = VWC_BWD_PIECE_F32;
 
 // Rows of at most this many forward segments are reduced by one workgroup of
 // nseg * kFwdBlock threads that also merges the segment partials (no
